@@ -1,0 +1,237 @@
+"""Benchmark: fused sampling at B=256, V=2^18 (bf16 logits, grammar bitmask,
+penalties, logit bias, mixed per-request settings) on one MI355X.
+
+One step = one full pass of the hot path over the batch: Stage 1 (per-tile
+prelude + top-128) and Stage 2 (merge, temperature, top-p / min-p,
+Gumbel-max) for all 256 rows, replayed from a hipGraph with the Philox
+offset advanced on the device.  Inputs are resident in HBM; four copies of
+the logits and bitmask are rotated so the 256 MB last-level cache cannot
+serve a step from the previous one.
+
+Printed: one JSON line with the headline rate (sampled tokens/s), the
+Stage-1 roofline (algorithmic bytes / measured kernel time against the 8
+TB/s HBM peak), the end-to-end logits GB/s, the verification latency of the
+B=64, gamma=4, V=2^17 workload, and the CPU oracle timed on a bounded
+sample of the same rows.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+B_HEAD, V_HEAD = 256, 262144
+PRIOR, NBIAS = 64, 16
+
+
+def alg_bytes_per_row(V, prior, nbias, grammar=True, dtype_bytes=2):
+    """Bytes one row must move: logits, grammar bitmask, prior list (id +
+    count), bias list (id + value), the 32-byte request record and the
+    4-byte token."""
+    return V * dtype_bytes + ((V + 31) // 32) * 4 * grammar + prior * 8 + nbias * 8 + 32 + 4
+
+
+def stage1_bytes_per_row(V, prior, nbias, grammar=True, dtype_bytes=2):
+    return alg_bytes_per_row(V, prior, nbias, grammar, dtype_bytes) - 4
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-verify", action="store_true", help="skip the verification latency")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the sampling path runs on a single MI355X "
+              "(rows shard across GPUs with no communication); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from speculative_decoding_verification_stage1_amd import _lib as L
+    from speculative_decoding_verification_stage1_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_gen = time.time()
+    wl = W.workload_c2()
+    B, V = wl.B, wl.V
+    gen_s = time.time() - t_gen
+
+    # ---- device inputs: rotating copies of logits + bitmask ----
+    x0 = torch.from_numpy(wl.logits.view(np.int16)).to(dev).view(torch.bfloat16)
+    bm0 = torch.from_numpy(wl.req.bitmask.view(np.int32)).to(dev)
+    xs = [x0] + [x0.clone() for _ in range(args.copies - 1)]
+    bms = [bm0] + [bm0.clone() for _ in range(args.copies - 1)]
+    dreqs = [L.DeviceRequests(wl.req).with_bitmask(bm) for bm in bms]
+    rng = L.make_rng(0, 0)
+    toks = torch.zeros(B, dtype=torch.int32, device=dev)
+    ws = L.workspace(B, V, L.SS_BF16)
+
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    graphs = []
+    for i in range(args.copies):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            L.ss_sample_step(xs[i], dreqs[i], rng, toks, ws=ws, stream=stream)
+            L.ss_rng_advance(rng, 1, stream=stream)
+        graphs.append(g)
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        graphs[i % args.copies].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % args.copies].replay()
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / args.steps
+    tokens_per_s = B / step_s
+    e2e_bytes = alg_bytes_per_row(V, PRIOR, NBIAS) * B
+    e2e_gbps = e2e_bytes / step_s / 1e9
+    logits_gbps = V * 2 * B / step_s / 1e9
+
+    # ---- Stage 1 alone, HIP events on the stream it is launched on ----
+    cur = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        L.ss_tile_topk(xs[i % args.copies], 1, dreqs[i % args.copies], None, ws)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    n1 = args.steps
+    ev0.record(cur)
+    for i in range(n1):
+        L.ss_tile_topk(xs[i % args.copies], 1, dreqs[i % args.copies], None, ws)
+    ev1.record(cur)
+    torch.cuda.synchronize()
+    s1_us = ev0.elapsed_time(ev1) * 1000.0 / n1
+    s1_bytes = stage1_bytes_per_row(V, PRIOR, NBIAS) * B
+    s1_gbps = s1_bytes / (s1_us * 1e-6) / 1e9
+
+    # ---- Stage 2 alone (for the split): full step minus Stage 1 is not
+    # separable in a graph, so time the eager full step too ----
+    ev0.record(cur)
+    for i in range(n1):
+        L.ss_sample_step(xs[i % args.copies], dreqs[i % args.copies], rng, toks, ws=ws)
+    ev1.record(cur)
+    torch.cuda.synchronize()
+    eager_us = ev0.elapsed_time(ev1) * 1000.0 / n1
+
+    result = {
+        "metric": "sampled tokens/s and logits GB/s (% HBM peak) at B=256, V=2^18; verify us",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "c2: B=256 V=262144 bf16 logits 2*N(0,1)+10 on 8 ids, grammar bitmask 5% allowed, "
+                        "repetition/frequency/presence over 64 prior ids, 16 bias ids, mixed greedy/top-k/"
+                        "top-p/min-p; hipGraph replay, 4 rotating input copies",
+            "global_batch": B, "vocab": V, "tile": L.ss_tile_size(L.SS_BF16), "parallelism": "single-gpu",
+        },
+        "logits_GBps": round(logits_gbps, 1),
+        "e2e_alg_GBps": round(e2e_gbps, 1),
+        "e2e_hbm_frac": round(e2e_gbps / HBM_PEAK_GBPS, 4),
+        "stage1_us": round(s1_us, 3),
+        "eager_step_us": round(eager_us, 3),
+        "roofline": {
+            "kernel": "stage1_kernel<bf16>",
+            "bound": "hbm",
+            "achieved": round(s1_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(s1_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+        },
+        "input_gen_s": round(gen_s, 2),
+    }
+
+    # ---- verification latency (B=64, gamma=4, V=2^17) ----
+    if not args.no_verify:
+        vw = W.workload_verify()
+        G = vw.gamma
+        tcopies = 3
+        t0d = torch.from_numpy(vw.target.view(np.int16)).to(dev).view(torch.bfloat16)
+        ts = [t0d] + [t0d.clone() for _ in range(tcopies - 1)]
+        vreq = L.DeviceRequests(vw.req)
+        d = torch.from_numpy(vw.draft_ids).to(dev)
+        q = torch.from_numpy(vw.draft_probs).to(dev)
+        vout = torch.zeros((vw.B, G + 1), dtype=torch.int32, device=dev)
+        vne = torch.zeros(vw.B, dtype=torch.int32, device=dev)
+        vws = L.workspace(vw.B * (G + 1), vw.V, L.SS_BF16)
+        vgraphs = []
+        for i in range(tcopies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                L.ss_verify_step(ts[i], vw.B, G, vreq, rng, d, q, vout, vne, None, vws, stream=stream)
+                L.ss_rng_advance(rng, 1, stream=stream)
+            vgraphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            vgraphs[i % tcopies].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        nv = max(args.steps, 20)
+        for i in range(nv):
+            vgraphs[i % tcopies].replay()
+        torch.cuda.synchronize()
+        v_us = (time.perf_counter() - t0) / nv * 1e6
+        result["verify_us"] = round(v_us, 2)
+        result["verify_config"] = "c3: B=64 gamma=4 V=131072 bf16 target, fp32 draft probs (gathered)"
+        result["verify_mean_emitted"] = round(float(vne.float().mean().item()), 3)
+
+    # ---- CPU oracle on a bounded sample of the same workload ----
+    if not args.no_cpu:
+        import oracle
+        try:
+            cores = len(os.sched_getaffinity(0))
+        except AttributeError:
+            cores = os.cpu_count() or 1
+        cores = max(1, min(cores, 16))
+        rows = 8
+        t0 = time.perf_counter()
+        oracle.sample(wl.logits[:rows], wl.dtype, _subset(wl.req, rows), threads=cores)
+        per = (time.perf_counter() - t0) / rows
+        rows = int(min(B, max(rows, args.cpu_seconds / max(per, 1e-6))))
+        sub = _subset(wl.req, rows)
+        t0 = time.perf_counter()
+        oracle.sample(wl.logits[:rows], wl.dtype, sub, threads=cores)
+        cpu_s = time.perf_counter() - t0
+        result["cpu_baseline"] = {
+            "value": round(rows / cpu_s, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {rows} of the 256 rows of the same workload, oracle.sample with {cores} threads, "
+                      f"{cpu_s:.1f} s",
+        }
+
+    print(json.dumps(result))
+
+
+def _subset(req, n):
+    import dataclasses
+    kw = {}
+    for f in dataclasses.fields(req):
+        v = getattr(req, f.name)
+        kw[f.name] = None if v is None else v[:n]
+    return type(req)(**kw)
+
+
+if __name__ == "__main__":
+    main()

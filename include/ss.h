@@ -1,0 +1,240 @@
+/*
+ * ss.h - C ABI of libss, the MI355X (gfx950) fused LLM sampling and
+ * speculative-verification library.
+ *
+ * What the library computes is the sampling pipeline of "SonicSampler:
+ * Unified Tile-Aware Kernels for LLM Sampling and Speculative Verification"
+ * (arXiv 2607.20475):
+ *   - per-request logits processing (section 3.1 "Logits processing"):
+ *     grammar bitmask, repetition penalty, frequency and presence
+ *     penalties, logit bias, temperature;
+ *   - a two-stage tile-aware top-k with a bounded candidate set k = 128
+ *     (section 3.2 "Workload-aware execution model", section 3.3, Fig. 1);
+ *   - top-p / min-p truncation (section 3.1 "Probability truncation", the
+ *     min-p condition evaluated without a softmax);
+ *   - Gumbel-max token selection (section 3.1 "Sampling");
+ *   - speculative rejection-sampling verification with residual
+ *     max(0, p - q) resampling (section 3.1 "Speculative verification").
+ * The notes page "Decoding and sampling" (sections "Temperature", "Top-k",
+ * "Top-p", "Min-p", "Combination order", "Rejection Sampler") supplies the
+ * set definitions and the rejection-sampling identities.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers unless marked "host".  The caller owns
+ *     every buffer, the workspace included.  The library never allocates,
+ *     frees, or synchronises; all work is queued on `stream` (a
+ *     hipStream_t passed as void*, NULL = the default stream).  Every
+ *     launch uses a grid fixed by the shapes, and the random seed/offset
+ *     are read from device memory, so a call can be captured in a hipGraph
+ *     and replayed.
+ *   - Return value: SS_OK, or a negative ss_status for problems found on
+ *     the host before anything is launched (then nothing is launched), or
+ *     SS_ERR_HIP when a launch failed.  Data-dependent problems never stop
+ *     the call; they are reported per row in `out_status` (SS_ROW_*).
+ *   - Logits: row-major, `rows` rows of `V` values with a row stride of
+ *     `ld` elements (ld >= V), fp32 or bf16 (raw 16-bit patterns).
+ *   - Tokens are int32 ids in [0, V); -1 means "no token".
+ *   - Results are deterministic functions of the inputs and of
+ *     (seed, offset); they do not depend on launch order or timing.
+ */
+#ifndef SS_H
+#define SS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SS_KMAX 128        /* bounded candidate set (SonicSampler section 3.3) */
+#define SS_GAMMA_MAX 16    /* largest number of draft tokens per request */
+#define SS_V_MAX (1 << 24) /* largest vocabulary */
+
+typedef enum {
+    SS_OK = 0,
+    SS_ERR_INVALID_ARG = -1, /* null pointer, bad size, bad stride */
+    SS_ERR_UNSUPPORTED = -2, /* dtype, V or gamma outside what is supported */
+    SS_ERR_WORKSPACE = -3,   /* workspace missing, too small or misaligned */
+    SS_ERR_HIP = -4          /* a kernel launch failed */
+} ss_status;
+
+typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
+
+/* Per-row status written to out_status. */
+enum {
+    SS_ROW_OK = 0,
+    SS_ROW_ALL_MASKED = 1,   /* every candidate is -inf: token -1 */
+    SS_ROW_INVALID = 2,      /* a request field is out of range: token -1 */
+    SS_ROW_TOPK_CLAMPED = 3  /* top_k > 128 was clamped to 128; token valid */
+};
+
+/* Per-request bit-level indicators (SonicSampler section 1: "compact
+ * bit-level indicators" select each request's behaviour). */
+enum {
+    SS_GREEDY = 1u << 0,    /* argmax of the processed logits */
+    SS_GRAMMAR = 1u << 1,   /* apply the row's grammar bitmask */
+    SS_REP = 1u << 2,       /* repetition penalty over the prior list */
+    SS_FREQPRES = 1u << 3,  /* frequency and presence penalties over the prior list */
+    SS_BIAS = 1u << 4,      /* additive logit bias list */
+    SS_TOPK = 1u << 5,      /* keep the top_k best candidates */
+    SS_TOPP = 1u << 6,      /* nucleus truncation at top_p */
+    SS_MINP = 1u << 7       /* keep p_i >= min_p * p_max */
+};
+
+/* One request, 32 bytes, in device memory (so a captured graph can be
+ * replayed with new settings).  Field semantics:
+ *   temperature  stochastic rows need a finite T > 0; T <= 0 means greedy;
+ *                NaN or +inf makes the row invalid (unless SS_GREEDY).
+ *   top_k        with SS_TOPK: 1 means greedy, 2..128 bound the candidates,
+ *                > 128 is clamped (SS_ROW_TOPK_CLAMPED), 0 is invalid.
+ *                Without SS_TOPK the bound is 128.
+ *   n_prior      entries of the row's prior list used (<= prior_stride).
+ *   n_bias       entries of the row's bias list used (<= bias_stride).
+ *   top_p        with SS_TOPP: in (0, 1]; 1 keeps every candidate.
+ *   min_p        with SS_MINP: in [0, 1]; 0 keeps every candidate.
+ *   rep_penalty  with SS_REP: finite, > 0 (theta).
+ *   freq_penalty, pres_penalty  with SS_FREQPRES: finite. */
+typedef struct ss_req {
+    uint32_t flags;
+    float temperature;
+    uint16_t top_k;
+    uint8_t n_prior;
+    uint8_t n_bias;
+    float top_p;
+    float min_p;
+    float rep_penalty;
+    float freq_penalty;
+    float pres_penalty;
+} ss_req;
+
+/* Philox seed and offset, in DEVICE memory; the kernels read them at run
+ * time, so a captured graph draws new noise after ss_rng_advance. */
+typedef struct ss_rng {
+    uint64_t seed;
+    uint64_t offset;
+} ss_rng;
+
+/* Side arrays, passed as a HOST struct of device pointers.  Row r of a
+ * call uses list row `r` (sample/tile calls) or `r / (gamma+1)` (verify,
+ * i.e. the request), and bitmask row `r`.
+ *   prior_ids/prior_cnt  [*, prior_stride] int32: token id and its count in
+ *                        the request's history; entries with count < 1 or an
+ *                        id outside [0, V) are ignored.
+ *   bias_ids/bias_val    [*, bias_stride]: token id and additive bias
+ *                        (finite); ids outside [0, V) are ignored.
+ *   bitmask              [rows, bitmask_stride] uint32, bitmask_stride >=
+ *                        ceil(V/32): token i is allowed iff bit (i & 31) of
+ *                        word (i >> 5) is 1.
+ * Any pointer may be NULL when no row uses it; a row whose flags need a
+ * NULL array is SS_ROW_INVALID.
+ * Processing order per token (SonicSampler section 3.1): mask (-inf), then
+ * every prior entry in list order z = z>0 ? z/theta : z*theta (SS_REP), then
+ * every prior entry z = z - (count*freq + presence) (SS_FREQPRES), then
+ * every bias entry z = z + bias (SS_BIAS); finally NaN -> -inf,
+ * +inf -> FLT_MAX, -0 -> +0. */
+typedef struct ss_aux {
+    const int32_t* prior_ids;
+    const int32_t* prior_cnt;
+    int32_t prior_stride;
+    const int32_t* bias_ids;
+    const float* bias_val;
+    int32_t bias_stride;
+    const uint32_t* bitmask;
+    int64_t bitmask_stride;
+} ss_aux;
+
+/* Bytes of workspace a call over `rows` logits rows of width V needs (rows
+ * = B for sampling and top-k, B*(gamma+1) for verification).  Pure host
+ * function; the workspace must be 256-byte aligned. */
+size_t ss_workspace_bytes(int rows, int V, int dtype);
+
+/* Vocabulary tile width used for `dtype` (B_N of the two-stage top-k). */
+int ss_tile_size(int dtype);
+
+/* Single-step sampling (SonicSampler "single-step mode").
+ * For every row b of the B x V logits:
+ *   z   = processed logits (see ss_aux);
+ *   K   = min(top_k if SS_TOPK else 128, 128, V) best tokens by
+ *         (z descending, token id ascending);
+ *   greedy rows (SS_GREEDY, T <= 0 or top_k == 1): token = best id;
+ *   otherwise v_k = z_k / T computed as z_k * (1/T) and clamped to the
+ *   finite range, e_k = exp(v_k - v_1) (fixed polynomial exp), Z = e_1 +
+ *   ... + e_K summed left to right, E_k the running sums; top-p keeps rank
+ *   k while E_{k-1} < top_p * Z, min-p keeps v_k - v_1 >= ln(min_p); the
+ *   token is the argmax over the kept ranks of v_k + g(id_k), with Gumbel
+ *   noise g = -ln(-ln u) from Philox4x32-10 (counter = {id, b, 0,
+ *   offset_lo}, key = {seed_lo, seed_hi ^ offset_hi}, u = ((w0 >> 9) +
+ *   1/2) * 2^-23); ties go to the lower id.
+ * Outputs (all optional except out_tokens):
+ *   out_tokens [B] int32, out_topk_ids [B,128] int32 (the K candidates, -1
+ *   after), out_probs [B,128] float (e_k / Z; greedy rows 1,0,...),
+ *   out_kept [B] int32 (kept count), out_mass [B] float (kept mass / Z),
+ *   out_status [B] int32 (SS_ROW_*). */
+int ss_sample_step(const void* logits, int dtype, int B, int V, int64_t ld,
+                   const ss_req* req, const ss_aux* aux, const ss_rng* rng,
+                   int32_t* out_tokens, int32_t* out_topk_ids, float* out_probs,
+                   int32_t* out_kept, float* out_mass, int32_t* out_status,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* Speculative verification of `gamma` draft tokens per request
+ * (SonicSampler "multi-step mode").  target_logits has B*(gamma+1) rows;
+ * row b*(gamma+1)+j is the target distribution for position j of request b
+ * (position gamma gives the bonus token).  req[b] and the prior/bias list
+ * row b belong to request b; bitmask rows follow the target rows.
+ * p_j is the request's truncated, renormalised target distribution at
+ * position j (ss_sample_step's kept set, p = e_k / E_n).  draft_ids [B,
+ * gamma] int32 and draft_probs [B, gamma, V] fp32 (q_j, read only at the
+ * draft token and at the kept candidates).
+ * Stochastic requests, for j = 0..gamma-1: accept d_j iff q_j(d_j) > 0 and
+ * u_j * q_j(d_j) <= p_j(d_j) with u_j from Philox counter {0, b, (1<<24)|j,
+ * offset_lo}; at the first rejection emit argmax over kept ranks with
+ * rho_k = max(0, p_j - q_j) > 0 of ln(rho_k) + g (counter {id, b,
+ * (2<<24)|j}) - or, if every rho_k is 0, the Gumbel-max draw from p_j with
+ * that counter - and stop.  If all are accepted emit the Gumbel-max draw
+ * from position gamma (counter {id, b, gamma}).  Greedy requests accept
+ * d_j iff it equals the best id of row j, emit the best id at the first
+ * mismatch and stop, and emit the best id of row gamma when all match.
+ * Outputs: out_tokens [B, gamma+1] (-1 after the emitted ones), out_n_emit
+ * [B], out_status [B] (optional; SS_ROW_ALL_MASKED when a target row that
+ * is reached has no finite candidate). */
+int ss_verify_step(const void* target_logits, int dtype, int B, int gamma, int V, int64_t ld,
+                   const ss_req* req, const ss_aux* aux, const ss_rng* rng,
+                   const int32_t* draft_ids, const float* draft_probs,
+                   int32_t* out_tokens, int32_t* out_n_emit, int32_t* out_status,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* Two-stage top-k of raw logits (no processing beyond NaN -> -inf, +inf ->
+ * FLT_MAX, -0 -> +0): out_ids [B, k] in order (value descending, id
+ * ascending) and out_vals [B, k] (optional) their values; positions past V
+ * hold -1 / -inf.  1 <= k <= 128. */
+int ss_topk_step(const void* logits, int dtype, int B, int V, int64_t ld, int k,
+                 int32_t* out_ids, float* out_vals, void* ws, size_t ws_bytes, void* stream);
+
+/* The same result from a single-program-per-row streaming kernel (one
+ * workgroup walks the whole vocabulary; the design the two-stage method
+ * replaces, SonicSampler section 3.2).  Needs no workspace. */
+int ss_topk_single_pass(const void* logits, int dtype, int B, int V, int64_t ld, int k,
+                        int32_t* out_ids, float* out_vals, void* stream);
+
+/* Stage 1 alone (diagnostic and timing): fills the workspace with every
+ * tile's 128 best tokens, and when out_ids is not NULL also writes them as
+ * token ids, [rows, ceil(V/tile), 128] int32 (-1 where a tile has fewer).
+ * Tokens named by an active penalty or bias list are left out of the
+ * tiles (they are ranked in Stage 2).  `rows_per_req` maps row r to
+ * request r / rows_per_req (1 for sampling).  req and aux may be NULL. */
+int ss_tile_topk(const void* logits, int dtype, int rows, int V, int64_t ld, int rows_per_req,
+                 const ss_req* req, const ss_aux* aux, int32_t* out_ids,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/* rng->offset += delta on the device (one tiny kernel; capturable). */
+int ss_rng_advance(ss_rng* rng, uint64_t delta, void* stream);
+
+/* Static description of a status code. */
+const char* ss_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SS_H */

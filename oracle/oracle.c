@@ -420,6 +420,15 @@ static void prelude_for(const sample_job* J, const oreq* r, int64_t row, int64_t
                        r->rep, r->freq, r->pres, z);
 }
 
+/* A row whose flags need a side array that was not given is invalid. */
+static int arrays_ok(const oreq* r, const sample_job* J)
+{
+    if ((r->flags & OF_GRAMMAR) && !J->bitmask) return 0;
+    if ((r->flags & (OF_REP | OF_FREQPRES)) && r->n_prior > 0 && (!J->prior_ids || !J->prior_cnt)) return 0;
+    if ((r->flags & OF_BIAS) && r->n_bias > 0 && (!J->bias_ids || !J->bias_val)) return 0;
+    return 1;
+}
+
 static void* sample_worker(void* arg)
 {
     const sample_job* J = (const sample_job*)arg;
@@ -430,7 +439,7 @@ static void* sample_worker(void* arg)
         const oreq* r = &J->req[b];
         const float* bv = J->bias_val ? J->bias_val + (int64_t)b * J->bias_stride : NULL;
         int valid_shape = (r->n_prior >= 0 && r->n_prior <= J->prior_stride &&
-                           r->n_bias >= 0 && r->n_bias <= J->bias_stride);
+                           r->n_bias >= 0 && r->n_bias <= J->bias_stride) && arrays_ok(r, J);
         if (valid_shape) prelude_for(J, r, b, b, z);
         if (valid_shape) decide_row(r, z, J->V, J->prior_stride, J->bias_stride, bv, work, d);
         else { memset(d, 0, sizeof(*d)); d->status = OST_INVALID; }
@@ -572,7 +581,7 @@ static void* verify_worker(void* arg)
         int st = OST_OK;
         const float* bv = J->bias_val ? J->bias_val + (int64_t)b * J->bias_stride : NULL;
         if (!(r->n_prior >= 0 && r->n_prior <= J->prior_stride &&
-              r->n_bias >= 0 && r->n_bias <= J->bias_stride)) {
+              r->n_bias >= 0 && r->n_bias <= J->bias_stride) || !arrays_ok(r, &S)) {
             st = OST_INVALID;
         }
         for (int j = 0; j <= G && st != OST_INVALID; ++j) {

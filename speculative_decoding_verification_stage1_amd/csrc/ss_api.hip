@@ -1,0 +1,295 @@
+// libss: C ABI entry points (declared in include/ss.h).  Host code checks
+// the arguments, carves the caller's workspace and queues fixed-grid
+// kernels on the caller's stream; it never allocates or synchronises.
+#include "ss_verify.h"
+
+using namespace ssd;
+
+namespace {
+
+constexpr int KERNEL_ROWS_MAX = 1 << 24;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int tile_of(int dtype) { return dtype == SS_BF16 ? S1Traits<SS_BF16>::BN : S1Traits<SS_F32>::BN; }
+size_t key_bytes(int dtype) { return dtype == SS_BF16 ? sizeof(uint32_t) : sizeof(uint64_t); }
+int tiles_of(int V, int dtype) { return (V + tile_of(dtype) - 1) / tile_of(dtype); }
+
+size_t scratch_bytes(int rows, int V, int dtype) {
+    return align256((size_t)rows * (size_t)tiles_of(V, dtype) * KMAX * key_bytes(dtype));
+}
+size_t rec_bytes(int rows) { return align256((size_t)rows * sizeof(RowRec)); }
+
+int check_logits(const void* logits, int dtype, int rows, int V, int64_t ld) {
+    if (dtype != SS_F32 && dtype != SS_BF16) return SS_ERR_UNSUPPORTED;
+    if (rows < 0 || V < 1 || ld < V) return SS_ERR_INVALID_ARG;
+    if (V > SS_V_MAX || rows > KERNEL_ROWS_MAX) return SS_ERR_UNSUPPORTED;
+    if (rows > 0 && !logits) return SS_ERR_INVALID_ARG;
+    if ((int64_t)rows * tiles_of(V, dtype) > 0x7FFFFFFFLL) return SS_ERR_UNSUPPORTED;
+    return SS_OK;
+}
+
+int check_aux(const ss_aux* aux, int V) {
+    if (!aux) return SS_OK;
+    if (aux->prior_stride < 0 || aux->bias_stride < 0 || aux->bitmask_stride < 0) return SS_ERR_INVALID_ARG;
+    if (aux->bitmask && aux->bitmask_stride < ((int64_t)V + 31) / 32) return SS_ERR_INVALID_ARG;
+    return SS_OK;
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+    if (need == 0) return SS_OK;
+    if (!ws || ws_bytes < need || ((uintptr_t)ws & 255u)) return SS_ERR_WORKSPACE;
+    return SS_OK;
+}
+
+int aligned16(const void* logits, int dtype, int64_t ld) {
+    const size_t es = dtype == SS_BF16 ? 2 : 4;
+    return (((uintptr_t)logits & 15u) == 0) && (((size_t)ld * es) % 16 == 0);
+}
+
+ss_aux aux_or_empty(const ss_aux* aux) {
+    ss_aux a{};
+    if (aux) a = *aux;
+    return a;
+}
+
+int launched() { return hipGetLastError() == hipSuccess ? SS_OK : SS_ERR_HIP; }
+
+Stage1Params make_s1(const void* logits, int dtype, int rows, int V, int64_t ld, int rows_per_req,
+                     const ss_req* req, const ss_aux* aux, void* ws, int32_t* out_ids) {
+    Stage1Params p{};
+    p.logits = logits;
+    p.ld = ld;
+    p.V = V;
+    p.rows = rows;
+    p.Zv = tiles_of(V, dtype);
+    p.rows_per_req = rows_per_req;
+    p.req = req;
+    p.aux = aux_or_empty(aux);
+    p.scratch = ws;
+    p.out_ids = out_ids;
+    p.aligned16 = aligned16(logits, dtype, ld);
+    return p;
+}
+
+void launch_stage1(int dtype, const Stage1Params& p, hipStream_t s) {
+    const dim3 grid((unsigned)(p.rows * p.Zv)), block(S1_THREADS);
+    if (dtype == SS_BF16) hipLaunchKernelGGL(stage1_kernel<SS_BF16>, grid, block, 0, s, p);
+    else hipLaunchKernelGGL(stage1_kernel<SS_F32>, grid, block, 0, s, p);
+}
+
+void launch_stage2(int dtype, const Stage2Params& p, hipStream_t s) {
+    const dim3 grid((unsigned)p.rows), block(S2_THREADS);
+    if (dtype == SS_BF16) hipLaunchKernelGGL(stage2_kernel<SS_BF16>, grid, block, 0, s, p);
+    else hipLaunchKernelGGL(stage2_kernel<SS_F32>, grid, block, 0, s, p);
+}
+
+Stage2Params make_s2(const Stage1Params& s1, const ss_rng* rng, int mode) {
+    Stage2Params p{};
+    p.logits = s1.logits;
+    p.ld = s1.ld;
+    p.V = s1.V;
+    p.rows = s1.rows;
+    p.Zv = s1.Zv;
+    p.rows_per_req = s1.rows_per_req;
+    p.req = s1.req;
+    p.aux = s1.aux;
+    p.rng = rng;
+    p.scratch = s1.scratch;
+    p.mode = mode;
+    return p;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// single-program-per-row top-k: one workgroup walks every tile of its row
+// and folds each tile's 128 best into a running list
+// ---------------------------------------------------------------------------
+namespace ssd {
+
+template <int DT>
+__global__ __launch_bounds__(S1_THREADS) void topk_single_pass_kernel(Stage1Params P, int k, int32_t* out_ids,
+                                                                      float* out_vals) {
+    __shared__ S1Shared<DT> sh;
+    __shared__ uint64_t acc[KMAX];
+    const int row = blockIdx.x;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < KMAX; i += S1_THREADS) acc[i] = 0ull;
+    for (int t = 0; t < P.Zv; ++t) {
+        stage1_tile<DT>(P, row, t, sh);   // ends with a barrier
+        if (tid < KMAX) {
+            const uint64_t a = acc[tid];
+            const uint64_t bb = merge_key<DT>(sh.surv[KMAX - 1 - tid], t);
+            acc[tid] = a > bb ? a : bb;
+        }
+        __syncthreads();
+        for (int j = KMAX / 2; j > 0; j >>= 1) {
+            if (tid < KMAX / 2) {
+                const int i = (tid / j) * 2 * j + (tid % j);
+                const uint64_t a = acc[i], c = acc[i + j];
+                if (a < c) {
+                    acc[i] = c;
+                    acc[i + j] = a;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    if (tid < k) {
+        const uint64_t key = acc[tid];
+        const bool have = key != 0ull && tid < P.V;
+        out_ids[(int64_t)row * k + tid] = have ? (int)(0xFFFFFFFFu - (uint32_t)key) : -1;
+        if (out_vals)
+            out_vals[(int64_t)row * k + tid] = have ? unord32((uint32_t)(key >> 32)) : bitsf(F32_NINF_BITS);
+    }
+}
+
+__global__ void rng_advance_kernel(ss_rng* rng, uint64_t delta) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) rng->offset += delta;
+}
+
+}  // namespace ssd
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+extern "C" {
+
+int ss_tile_size(int dtype) {
+    if (dtype != SS_F32 && dtype != SS_BF16) return 0;
+    return tile_of(dtype);
+}
+
+size_t ss_workspace_bytes(int rows, int V, int dtype) {
+    if (rows < 0 || V < 1 || (dtype != SS_F32 && dtype != SS_BF16)) return 0;
+    return scratch_bytes(rows, V, dtype) + rec_bytes(rows);
+}
+
+const char* ss_status_str(int status) {
+    switch (status) {
+        case SS_OK: return "ok";
+        case SS_ERR_INVALID_ARG: return "invalid argument";
+        case SS_ERR_UNSUPPORTED: return "unsupported dtype, size or gamma";
+        case SS_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+        case SS_ERR_HIP: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int ss_sample_step(const void* logits, int dtype, int B, int V, int64_t ld, const ss_req* req,
+                   const ss_aux* aux, const ss_rng* rng, int32_t* out_tokens, int32_t* out_topk_ids,
+                   float* out_probs, int32_t* out_kept, float* out_mass, int32_t* out_status, void* ws,
+                   size_t ws_bytes, void* stream) {
+    int rc = check_logits(logits, dtype, B, V, ld);
+    if (rc) return rc;
+    if ((rc = check_aux(aux, V))) return rc;
+    if (B == 0) return SS_OK;
+    if (!req || !rng || !out_tokens) return SS_ERR_INVALID_ARG;
+    if ((rc = check_ws(ws, ws_bytes, ss_workspace_bytes(B, V, dtype)))) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    Stage1Params s1 = make_s1(logits, dtype, B, V, ld, 1, req, aux, ws, nullptr);
+    launch_stage1(dtype, s1, s);
+    Stage2Params s2 = make_s2(s1, rng, MODE_SAMPLE);
+    s2.tokens = out_tokens;
+    s2.topk_ids = out_topk_ids;
+    s2.probs = out_probs;
+    s2.kept = out_kept;
+    s2.mass = out_mass;
+    s2.status = out_status;
+    launch_stage2(dtype, s2, s);
+    return launched();
+}
+
+int ss_verify_step(const void* target_logits, int dtype, int B, int gamma, int V, int64_t ld,
+                   const ss_req* req, const ss_aux* aux, const ss_rng* rng, const int32_t* draft_ids,
+                   const float* draft_probs, int32_t* out_tokens, int32_t* out_n_emit, int32_t* out_status,
+                   void* ws, size_t ws_bytes, void* stream) {
+    if (gamma < 1 || gamma > SS_GAMMA_MAX) return SS_ERR_UNSUPPORTED;
+    if (B < 0 || (int64_t)B * (gamma + 1) > KERNEL_ROWS_MAX) return B < 0 ? SS_ERR_INVALID_ARG : SS_ERR_UNSUPPORTED;
+    const int rows = B * (gamma + 1);
+    int rc = check_logits(target_logits, dtype, rows, V, ld);
+    if (rc) return rc;
+    if ((rc = check_aux(aux, V))) return rc;
+    if (B == 0) return SS_OK;
+    if (!req || !rng || !draft_ids || !draft_probs || !out_tokens || !out_n_emit) return SS_ERR_INVALID_ARG;
+    if ((rc = check_ws(ws, ws_bytes, ss_workspace_bytes(rows, V, dtype)))) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    Stage1Params s1 = make_s1(target_logits, dtype, rows, V, ld, gamma + 1, req, aux, ws, nullptr);
+    launch_stage1(dtype, s1, s);
+    Stage2Params s2 = make_s2(s1, rng, MODE_VERIFY);
+    s2.recs = (RowRec*)((char*)ws + scratch_bytes(rows, V, dtype));
+    launch_stage2(dtype, s2, s);
+    VerifyParams vp{};
+    vp.B = B;
+    vp.gamma = gamma;
+    vp.V = V;
+    vp.recs = s2.recs;
+    vp.draft_ids = draft_ids;
+    vp.draft_probs = draft_probs;
+    vp.rng = rng;
+    vp.out_tokens = out_tokens;
+    vp.out_n_emit = out_n_emit;
+    vp.out_status = out_status;
+    hipLaunchKernelGGL(verify_kernel, dim3((unsigned)B), dim3(VF_THREADS), 0, s, vp);
+    return launched();
+}
+
+int ss_topk_step(const void* logits, int dtype, int B, int V, int64_t ld, int k, int32_t* out_ids,
+                 float* out_vals, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_logits(logits, dtype, B, V, ld);
+    if (rc) return rc;
+    if (k < 1 || k > KMAX) return SS_ERR_UNSUPPORTED;
+    if (B == 0) return SS_OK;
+    if (!out_ids) return SS_ERR_INVALID_ARG;
+    if ((rc = check_ws(ws, ws_bytes, ss_workspace_bytes(B, V, dtype)))) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    Stage1Params s1 = make_s1(logits, dtype, B, V, ld, 1, nullptr, nullptr, ws, nullptr);
+    launch_stage1(dtype, s1, s);
+    Stage2Params s2 = make_s2(s1, nullptr, MODE_TOPK);
+    s2.topk_k = k;
+    s2.topk_ids = out_ids;
+    s2.topk_vals = out_vals;
+    launch_stage2(dtype, s2, s);
+    return launched();
+}
+
+int ss_topk_single_pass(const void* logits, int dtype, int B, int V, int64_t ld, int k, int32_t* out_ids,
+                        float* out_vals, void* stream) {
+    int rc = check_logits(logits, dtype, B, V, ld);
+    if (rc) return rc;
+    if (k < 1 || k > KMAX) return SS_ERR_UNSUPPORTED;
+    if (B == 0) return SS_OK;
+    if (!out_ids) return SS_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    Stage1Params s1 = make_s1(logits, dtype, B, V, ld, 1, nullptr, nullptr, nullptr, nullptr);
+    if (dtype == SS_BF16)
+        hipLaunchKernelGGL(topk_single_pass_kernel<SS_BF16>, dim3((unsigned)B), dim3(S1_THREADS), 0, s, s1, k,
+                           out_ids, out_vals);
+    else
+        hipLaunchKernelGGL(topk_single_pass_kernel<SS_F32>, dim3((unsigned)B), dim3(S1_THREADS), 0, s, s1, k,
+                           out_ids, out_vals);
+    return launched();
+}
+
+int ss_tile_topk(const void* logits, int dtype, int rows, int V, int64_t ld, int rows_per_req, const ss_req* req,
+                 const ss_aux* aux, int32_t* out_ids, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_logits(logits, dtype, rows, V, ld);
+    if (rc) return rc;
+    if ((rc = check_aux(aux, V))) return rc;
+    if (rows_per_req < 1) return SS_ERR_INVALID_ARG;
+    if (rows == 0) return SS_OK;
+    if ((rc = check_ws(ws, ws_bytes, ss_workspace_bytes(rows, V, dtype)))) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    Stage1Params s1 = make_s1(logits, dtype, rows, V, ld, rows_per_req, req, aux, ws, out_ids);
+    launch_stage1(dtype, s1, s);
+    return launched();
+}
+
+int ss_rng_advance(ss_rng* rng, uint64_t delta, void* stream) {
+    if (!rng) return SS_ERR_INVALID_ARG;
+    hipLaunchKernelGGL(rng_advance_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, rng, delta);
+    return launched();
+}
+
+}  // extern "C"

@@ -1,0 +1,175 @@
+// Device-side building blocks of libss: order keys, Philox4x32-10, the
+// fixed exp/log used by the epilogue, and small wave/block helpers.
+//
+// Everything here is compiled with -ffp-contract=off; every fused
+// multiply-add is an explicit __builtin_fmaf so the arithmetic is the same
+// IEEE binary32 sequence on every run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ss.h"
+
+namespace ssd {
+
+constexpr int KMAX = SS_KMAX;
+constexpr int WAVE = 64;
+
+// ---------------------------------------------------------------------------
+// bit views
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t fbits(float f) { return __float_as_uint(f); }
+__device__ __forceinline__ float bitsf(uint32_t u) { return __uint_as_float(u); }
+
+constexpr uint32_t F32_MAX_BITS = 0x7F7FFFFFu;
+constexpr uint32_t F32_PINF_BITS = 0x7F800000u;
+constexpr uint32_t F32_NINF_BITS = 0xFF800000u;
+
+// Canonical value: NaN -> -inf, +inf -> FLT_MAX, -0 -> +0.
+__device__ __forceinline__ float canon(float z) {
+    if (z != z) return bitsf(F32_NINF_BITS);
+    if (z == bitsf(F32_PINF_BITS)) return bitsf(F32_MAX_BITS);
+    if (z == 0.0f) return 0.0f;
+    return z;
+}
+
+// Order-preserving unsigned key of a (non-NaN) float: larger value <=> larger key.
+__device__ __forceinline__ uint32_t ord32(float f) {
+    uint32_t b = fbits(f);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float unord32(uint32_t k) {
+    return bitsf((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// bf16 raw pattern -> 16-bit order key of its canonical value.  NaN maps to
+// the key of -inf, -0 to the key of +0.  +inf keeps its own key (0xFF80),
+// which ranks above every finite bf16 and is read back as FLT_MAX.
+__device__ __forceinline__ uint32_t ord16_canon(uint32_t h) {
+    h &= 0xFFFFu;
+    if ((h & 0x7FFFu) > 0x7F80u) h = 0xFF80u;     // NaN -> -inf
+    if (h == 0x8000u) h = 0u;                      // -0 -> +0
+    return (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u);
+}
+constexpr uint32_t K16_NINF = 0x007Fu;   // ord16(-inf)
+constexpr uint32_t K16_PINF = 0xFF80u;   // ord16(+inf)
+
+// 16-bit key -> the 32-bit key of the canonical fp32 value.
+__device__ __forceinline__ uint32_t k16_to_k32(uint32_t k16) {
+    if (k16 == K16_PINF) return ord32(bitsf(F32_MAX_BITS));
+    return (k16 & 0x8000u) ? (k16 << 16) : ((k16 << 16) | 0xFFFFu);
+}
+
+__device__ __forceinline__ float widen_bf16(uint32_t h) { return bitsf((h & 0xFFFFu) << 16); }
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon et al., SC'11): per round, words 0 and 2 are
+// multiplied by the round constants, the high halves are mixed with words 1
+// and 3 and the key, and the key advances by the Weyl increments.
+// ---------------------------------------------------------------------------
+struct u32x4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ u32x4 philox10(u32x4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+        const uint32_t a = 0xD2511F53u * c.x, ah = __umulhi(0xD2511F53u, c.x);
+        const uint32_t b = 0xCD9E8D57u * c.z, bh = __umulhi(0xCD9E8D57u, c.z);
+        c = u32x4{bh ^ c.y ^ k0, b, ah ^ c.w ^ k1, a};
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return c;
+}
+
+// First output word for counter {c0, c1, c2, offset_lo} under key
+// {seed_lo, seed_hi ^ offset_hi}.
+__device__ __forceinline__ uint32_t philox_w0(uint64_t seed, uint64_t offset, uint32_t c0,
+                                              uint32_t c1, uint32_t c2) {
+    u32x4 c{c0, c1, c2, (uint32_t)offset};
+    return philox10(c, (uint32_t)seed, (uint32_t)(seed >> 32) ^ (uint32_t)(offset >> 32)).x;
+}
+
+// u in (0,1): top 23 bits of the word, centred in their cell.
+__device__ __forceinline__ float unit_open(uint32_t w) {
+    return ((float)(w >> 9) + 0.5f) * 0x1p-23f;
+}
+
+// ---------------------------------------------------------------------------
+// Fixed exp / log.  exp: Cody-Waite reduction x = n ln2 + r with a two-part
+// ln 2, degree-7 Taylor polynomial of e^r, scale by 2^n; arguments below -86
+// give 0.  log: x = 2^e m, m in (sqrt(1/2), sqrt(2)], ln m = 2 atanh((m-1)/
+// (m+1)) by its odd series to the 9th power.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float exp_fixed(float x) {
+    if (x != x) return x;
+    if (x < -86.0f) return 0.0f;
+    if (x > 88.0f) return bitsf(F32_PINF_BITS);
+    const float n = __builtin_rintf(x * 0x1.715476p+0f);
+    float r = __builtin_fmaf(-n, 0x1.62e4p-1f, x);
+    r = __builtin_fmaf(-n, 0x1.7f7d1cp-20f, r);
+    float p = __builtin_fmaf(0x1.a01a02p-13f, r, 0x1.6c16c2p-10f);
+    p = __builtin_fmaf(p, r, 0x1.111112p-7f);
+    p = __builtin_fmaf(p, r, 0x1.555556p-5f);
+    p = __builtin_fmaf(p, r, 0x1.555556p-3f);
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    return __builtin_ldexpf(p, (int)n);
+}
+
+__device__ __forceinline__ float log_fixed(float x) {
+    if (x != x || x < 0.0f) return bitsf(0x7FC00000u);
+    if (x == 0.0f) return bitsf(F32_NINF_BITS);
+    if (x == bitsf(F32_PINF_BITS)) return x;
+    int e = -127;
+    if (x < 0x1p-126f) {   // subnormal: scale into the normal range (exact)
+        x *= 0x1p24f;
+        e -= 24;
+    }
+    const uint32_t b = fbits(x);
+    e += (int)(b >> 23);
+    float m = bitsf((b & 0x007FFFFFu) | 0x3F800000u);
+    if (m > 0x1.6a09e6p+0f) {
+        m *= 0.5f;
+        e += 1;
+    }
+    const float s = (m - 1.0f) / (m + 1.0f);
+    const float s2 = s * s;
+    float q = __builtin_fmaf(0x1.c71c72p-4f, s2, 0x1.24924ap-3f);
+    q = __builtin_fmaf(q, s2, 0x1.99999ap-3f);
+    q = __builtin_fmaf(q, s2, 0x1.555556p-2f);
+    const float h = __builtin_fmaf(s * s2, q, s);
+    const float ef = (float)e;
+    return __builtin_fmaf(ef, 0x1.62e4p-1f, __builtin_fmaf(ef, 0x1.7f7d1cp-20f, h + h));
+}
+
+__device__ __forceinline__ float gumbel_noise(uint64_t seed, uint64_t offset, uint32_t c0,
+                                              uint32_t c1, uint32_t c2) {
+    const float u = unit_open(philox_w0(seed, offset, c0, c1, c2));
+    return -log_fixed(-log_fixed(u));
+}
+
+// ---------------------------------------------------------------------------
+// wave helpers (wave64)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+    return v;
+}
+
+// inclusive prefix sum over the wave
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    const int l = lane_id();
+#pragma unroll
+    for (int o = 1; o < WAVE; o <<= 1) {
+        const int t = __shfl_up(v, o, WAVE);
+        if (l >= o) v += t;
+    }
+    return v;
+}
+
+}  // namespace ssd

@@ -1,0 +1,400 @@
+"""HIP path vs the CPU oracle, element by element, through the C ABI.
+
+Integer results (token ids, candidate lists, kept counts, statuses, emitted
+drafts) must be bit-exact.  Probabilities and kept mass must agree within
+1e-5 relative; the arithmetic is specified identically on both sides, so
+they are in fact expected to be equal.
+
+Sizes: small cases that span several vocabulary tiles with a ragged tail,
+the five full workloads (all rows where the oracle finishes in seconds,
+otherwise a fixed sample of rows), and the edge cases the method has:
+all-equal logits, bf16 ties, fully masked rows, NaN/inf/-0 inputs, V below
+the candidate bound, V = 1, invalid settings, top-k above the bound,
+duplicated list entries.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from speculative_decoding_verification_stage1_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+RTOL = 1e-5
+
+
+def L():
+    from speculative_decoding_verification_stage1_amd import _lib
+    return _lib
+
+
+def _dev_logits(wl_logits, dtype):
+    x = np.ascontiguousarray(wl_logits)
+    if dtype == W.DTYPE_BF16:
+        return torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(x).cuda()
+
+
+def run_sample(logits_np, dtype, req, seed=0, offset=0, flags=None):
+    lib = L()
+    x = _dev_logits(logits_np, dtype)
+    B, V = x.shape
+    dreq = lib.DeviceRequests(req, flags=flags)
+    rng = lib.make_rng(seed, offset)
+    out = dict(tokens=torch.full((B,), -7, dtype=torch.int32, device="cuda"),
+               topk_ids=torch.full((B, 128), -7, dtype=torch.int32, device="cuda"),
+               probs=torch.full((B, 128), -7.0, dtype=torch.float32, device="cuda"),
+               kept=torch.full((B,), -7, dtype=torch.int32, device="cuda"),
+               mass=torch.full((B,), -7.0, dtype=torch.float32, device="cuda"),
+               status=torch.full((B,), -7, dtype=torch.int32, device="cuda"))
+    ws = lib.workspace(B, V, dtype)
+    lib.ss_sample_step(x, dreq, rng, out["tokens"], out["topk_ids"], out["probs"], out["kept"],
+                       out["mass"], out["status"], ws)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def compare_sample(g, o, rows=None, tag=""):
+    rows = range(len(o["tokens"])) if rows is None else rows
+    for r in rows:
+        gi = r if len(g["tokens"]) == len(o["tokens"]) else rows.index(r)
+        msg = f"{tag} row {r}"
+        assert g["status"][gi] == o["status"][r], msg
+        assert np.array_equal(g["topk_ids"][gi], o["topk_ids"][r]), msg
+        assert g["kept"][gi] == o["kept"][r], msg
+        assert g["tokens"][gi] == o["tokens"][r], msg
+        np.testing.assert_allclose(g["probs"][gi], o["probs"][r], rtol=RTOL, atol=1e-30, err_msg=msg)
+        np.testing.assert_allclose(g["mass"][gi], o["mass"][r], rtol=RTOL, atol=1e-30, err_msg=msg)
+
+
+def sample_parity(wl, seed=0, offset=0, flags=None, threads=16, tag=""):
+    g = run_sample(wl.logits, wl.dtype, wl.req, seed, offset, flags)
+    o = oracle.sample(wl.logits, wl.dtype, wl.req, seed=seed, offset=offset, threads=threads, flags=flags)
+    compare_sample(g, o, tag=tag or wl.name)
+    return g, o
+
+
+# ---------------------------------------------------------------------------
+# Stage 1 alone: per-tile 128 best
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [W.DTYPE_BF16, W.DTYPE_F32])
+def test_tile_topk_parity(dtype):
+    lib = L()
+    wl = W.workload_mixed(2, 5, 70001, grammar=True)
+    logits = wl.logits if dtype == W.DTYPE_BF16 else W.bf16_bits_to_f32(wl.logits) * np.float32(1.37)
+    tile = lib.ss_tile_size(dtype)
+    x = _dev_logits(logits, dtype)
+    rows, V = x.shape
+    Zv = (V + tile - 1) // tile
+    dreq = lib.DeviceRequests(wl.req)
+    out = torch.full((rows, Zv, 128), -7, dtype=torch.int32, device="cuda")
+    ws = lib.workspace(rows, V, dtype)
+    lib.ss_tile_topk(x, 1, dreq, out, ws)
+    torch.cuda.synchronize()
+    ref = oracle.tile_topk(logits, dtype, tile, wl.req)
+    assert np.array_equal(out.cpu().numpy(), ref)
+
+
+# ---------------------------------------------------------------------------
+# sampling
+# ---------------------------------------------------------------------------
+
+def test_sample_c0_both_runs():
+    for greedy in (True, False):
+        sample_parity(W.workload_c0(greedy))
+
+
+@pytest.mark.parametrize("V", [1, 5, 127, 128, 129, 16383, 16385, 50001])
+def test_sample_small_shapes(V):
+    rng = np.random.default_rng(V)
+    for dtype in (W.DTYPE_BF16, W.DTYPE_F32):
+        B = 6
+        x = (rng.standard_normal((B, V)) * 2).astype(np.float32)
+        logits = W.to_bf16_bits(x) if dtype == W.DTYPE_BF16 else x
+        req = W.plain_requests(B, temperature=0.9, top_p=0.95)
+        req.greedy[0] = True
+        req.top_k[1] = 3
+        req.min_p[2] = 0.1
+        sample_parity(W.SampleWorkload(f"small-V{V}-dt{dtype}", dtype, logits, req), seed=5, offset=77)
+
+
+def test_sample_mixed_small_with_grammar_and_lists():
+    for cfg, grammar in [(1, False), (2, True)]:
+        wl = W.workload_mixed(cfg, 12, 90000, grammar=grammar)
+        sample_parity(wl, seed=3, offset=2)
+
+
+def test_sample_c1_full():
+    sample_parity(W.workload_c1(), seed=0, offset=0)
+
+
+def test_sample_c2_full():
+    sample_parity(W.workload_c2(), seed=0, offset=0)
+
+
+def test_sample_offsets_change_tokens():
+    wl = W.workload_mixed(1, 16, 40000, grammar=False)
+    wl.req.greedy[:] = False
+    a, _ = sample_parity(wl, seed=1, offset=10)
+    b, _ = sample_parity(wl, seed=1, offset=11)
+    assert not np.array_equal(a["tokens"], b["tokens"])
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+
+def test_all_equal_and_bf16_ties():
+    V = 40000
+    B = 4
+    x = np.full((B, V), 0x3F80, np.uint16)        # all 1.0
+    x[1, ::7] = 0x3F81                             # ties between many ids
+    x[2, 20000:] = 0x4000
+    x[3] = W.to_bf16_bits(np.round(np.random.default_rng(0).standard_normal(V) * 4) / 4)
+    req = W.plain_requests(B, temperature=1.0)
+    req.greedy[0] = True
+    sample_parity(W.SampleWorkload("ties", W.DTYPE_BF16, x, req), seed=2)
+    # the same as fp32
+    sample_parity(W.SampleWorkload("ties-f32", W.DTYPE_F32, W.bf16_bits_to_f32(x), req), seed=2)
+
+
+def test_special_values():
+    V = 20000
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal((6, V)) * 2).astype(np.float32)
+    x[0, 5] = np.nan
+    x[0, 17000] = np.inf
+    x[1, :] = -0.0
+    x[1, 100] = 0.0
+    x[2, ::3] = np.nan
+    x[3, :] = -np.inf
+    x[3, 12345] = -1e30
+    x[4, 1:] = np.nan
+    x[5, 7] = -np.nan
+    x[5, 9] = np.float32(3.0e38)
+    req = W.plain_requests(6, temperature=0.5, top_p=0.99)
+    for dtype in (W.DTYPE_F32, W.DTYPE_BF16):
+        logits = x if dtype == W.DTYPE_F32 else W.to_bf16_bits(x)
+        sample_parity(W.SampleWorkload("special", dtype, logits, req), seed=9)
+
+
+def test_masked_rows_and_invalid_settings():
+    V = 33000
+    B = 8
+    rng = np.random.default_rng(8)
+    x = W.to_bf16_bits((rng.standard_normal((B, V)) * 2).astype(np.float32))
+    req = W.plain_requests(B, temperature=1.0, prior_len=4, bias_len=4)
+    bm = np.full((B, (V + 31) // 32), 0xFFFFFFFF, np.uint32)
+    req.bitmask = bm
+    req.use_grammar[:] = True
+    bm[0] = 0                         # fully masked
+    bm[1] = 0
+    bm[1, 1000] = 1 << 3              # a single allowed token
+    bm[2, :5] = 0x0F0F0F0F            # sparse
+    bm[2, 5:] = 0
+    req.temperature[3] = np.nan       # invalid
+    req.top_k[4] = 500                # clamped
+    req.use_penalties[5] = True
+    req.rep_penalty[5] = 0.0          # invalid
+    req.n_prior[5] = 1
+    req.use_bias[6] = True
+    req.bias_ids[6, :3] = [5, 5, 70000]   # duplicate and out-of-range ids
+    req.bias_val[6, :3] = [30.0, -1.0, 9.0]
+    req.n_bias[6] = 3
+    req.use_penalties[7] = True
+    req.prior_ids[7, :4] = [9, 9, 11, -3]
+    req.prior_cnt[7, :4] = [1, 2, 0, 4]
+    req.n_prior[7] = 4
+    req.rep_penalty[7] = 1.7
+    req.freq_penalty[7] = 0.5
+    req.pres_penalty[7] = 0.25
+    sample_parity(W.SampleWorkload("masked", W.DTYPE_BF16, x, req), seed=4)
+
+
+def test_heavy_lists():
+    """255 prior and 255 bias entries, many landing in one tile."""
+    V = 40000
+    B = 3
+    rng = np.random.default_rng(10)
+    x = W.to_bf16_bits((rng.standard_normal((B, V)) * 2).astype(np.float32))
+    req = W.plain_requests(B, temperature=0.7, prior_len=255, bias_len=255)
+    for r in range(B):
+        req.prior_ids[r] = rng.integers(0, 3000, 255)
+        req.prior_cnt[r] = rng.integers(0, 4, 255)
+        req.bias_ids[r] = rng.integers(0, 3000, 255)
+        req.bias_val[r] = rng.uniform(-3, 8, 255)
+    req.n_prior[:] = 255
+    req.n_bias[:] = 255
+    req.use_penalties[:] = True
+    req.use_bias[:] = True
+    req.rep_penalty[:] = 1.3
+    req.freq_penalty[:] = 0.3
+    req.pres_penalty[:] = 0.2
+    req.greedy[0] = True
+    sample_parity(W.SampleWorkload("lists", W.DTYPE_BF16, x, req), seed=6)
+    sample_parity(W.SampleWorkload("lists-f32", W.DTYPE_F32, W.bf16_bits_to_f32(x), req), seed=6)
+
+
+def test_determinism_repeated_runs():
+    wl = W.workload_mixed(2, 32, 131072, grammar=True)
+    a = run_sample(wl.logits, wl.dtype, wl.req, 1, 2)
+    for _ in range(5):
+        b = run_sample(wl.logits, wl.dtype, wl.req, 1, 2)
+        for k in a:
+            assert np.array_equal(a[k], b[k]), k
+
+
+# ---------------------------------------------------------------------------
+# verification
+# ---------------------------------------------------------------------------
+
+def run_verify(wl, seed=0, offset=0):
+    lib = L()
+    x = _dev_logits(wl.target, wl.dtype)
+    rows, V = x.shape
+    B, G = wl.B, wl.gamma
+    dreq = lib.DeviceRequests(wl.req)
+    if getattr(wl, "bitmask", None) is not None:
+        dreq.with_bitmask(torch.from_numpy(wl.bitmask.view(np.int32)).cuda())
+    rng = lib.make_rng(seed, offset)
+    d = torch.from_numpy(np.ascontiguousarray(wl.draft_ids, np.int32)).cuda()
+    q = torch.from_numpy(np.ascontiguousarray(wl.draft_probs, np.float32)).cuda()
+    toks = torch.full((B, G + 1), -7, dtype=torch.int32, device="cuda")
+    ne = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    st = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    ws = lib.workspace(rows, V, wl.dtype)
+    lib.ss_verify_step(x, B, G, dreq, rng, d, q, toks, ne, st, ws)
+    torch.cuda.synchronize()
+    return dict(tokens=toks.cpu().numpy(), n_emit=ne.cpu().numpy(), status=st.cpu().numpy())
+
+
+def verify_parity(wl, seed=0, offset=0):
+    g = run_verify(wl, seed, offset)
+    o = oracle.verify(wl.target, wl.dtype, wl.B, wl.gamma, wl.req, wl.draft_ids, wl.draft_probs,
+                      bitmask=getattr(wl, "bitmask", None), seed=seed, offset=offset, threads=16)
+    for k in ("tokens", "n_emit", "status"):
+        assert np.array_equal(g[k], o[k]), (k, np.nonzero((g[k] != o[k]).reshape(wl.B, -1).any(1))[0][:10])
+    return g
+
+
+def test_verify_small():
+    wl = W.workload_verify(B=16, gamma=4, V=20000)
+    verify_parity(wl, seed=1, offset=5)
+
+
+def test_verify_c3_full():
+    g = verify_parity(W.workload_verify())
+    assert g["n_emit"].min() >= 1
+
+
+def test_verify_accept_all_and_mixed_settings():
+    V, B, G = 3000, 8, 3
+    rng = np.random.default_rng(21)
+    raw = (rng.standard_normal((B * (G + 1), V)) * 2).astype(np.float32)
+    req = W.plain_requests(B, temperature=1.0, top_k=20)
+    req.top_p[2:4] = 0.8
+    req.min_p[4:6] = 0.05
+    req.greedy[6] = True
+    req.temperature[7] = 0.6
+    # q = the target's own truncated probabilities -> accept everything (stochastic rows)
+    out = oracle.sample(raw, W.DTYPE_F32, W.plain_requests(B * (G + 1), temperature=1.0, top_k=20))
+    q = np.zeros((B, G, V), np.float32)
+    d = np.zeros((B, G), np.int32)
+    for b in range(B):
+        for j in range(G):
+            r = b * (G + 1) + j
+            q[b, j, out["topk_ids"][r, :20]] = out["probs"][r, :20]
+            d[b, j] = out["topk_ids"][r, j % 3]
+    wl = W.VerifyWorkload("acc", W.DTYPE_F32, raw, q, d, req, G)
+    verify_parity(wl, seed=11)
+
+
+def test_verify_grammar_rows():
+    wl = W.workload_verify(B=6, gamma=2, V=9000)
+    rows = wl.B * (wl.gamma + 1)
+    bm = np.full((rows, (wl.V + 31) // 32), 0x55555555, np.uint32)
+    bm[4] = 0   # request 1, position 1 fully masked
+    wl.bitmask = bm
+    wl.req.use_grammar[:] = True
+    verify_parity(wl, seed=2)
+
+
+# ---------------------------------------------------------------------------
+# plain top-k (two-stage and single pass)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("regime", ["peaked", "flat"])
+def test_topk_c4_rows(regime):
+    lib = L()
+    wl = W.workload_c4(regime, rows=24)
+    x = _dev_logits(wl.logits, wl.dtype)
+    B, V = x.shape
+    ref_ids, ref_vals = oracle.topk(wl.logits, wl.dtype, 128, threads=16)
+    ids = torch.full((B, 128), -7, dtype=torch.int32, device="cuda")
+    vals = torch.zeros((B, 128), dtype=torch.float32, device="cuda")
+    ws = lib.workspace(B, V, wl.dtype)
+    lib.ss_topk_step(x, 128, ids, vals, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    assert np.array_equal(vals.cpu().numpy(), ref_vals)
+    ids.fill_(-7)
+    vals.zero_()
+    lib.ss_topk_single_pass(x, 128, ids, vals)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    assert np.array_equal(vals.cpu().numpy(), ref_vals)
+
+
+@pytest.mark.parametrize("k", [1, 7, 128])
+def test_topk_small_k_and_bf16(k):
+    lib = L()
+    rng = np.random.default_rng(k)
+    x_np = W.to_bf16_bits((rng.standard_normal((5, 30001)) * 3).astype(np.float32))
+    x = _dev_logits(x_np, W.DTYPE_BF16)
+    ref_ids, ref_vals = oracle.topk(x_np, W.DTYPE_BF16, k)
+    ids = torch.full((5, k), -7, dtype=torch.int32, device="cuda")
+    vals = torch.zeros((5, k), dtype=torch.float32, device="cuda")
+    lib.ss_topk_step(x, k, ids, vals, lib.workspace(5, 30001, W.DTYPE_BF16))
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    assert np.array_equal(vals.cpu().numpy(), ref_vals)
+    lib.ss_topk_single_pass(x, k, ids, vals)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+
+
+# ---------------------------------------------------------------------------
+# graph capture: replays with a device-side offset equal eager calls
+# ---------------------------------------------------------------------------
+
+def test_graph_replay_matches_eager_offsets():
+    lib = L()
+    wl = W.workload_mixed(2, 16, 65536, grammar=True)
+    wl.req.greedy[:] = False
+    x = _dev_logits(wl.logits, wl.dtype)
+    B, V = x.shape
+    dreq = lib.DeviceRequests(wl.req)
+    rng = lib.make_rng(42, 0)
+    ws = lib.workspace(B, V, wl.dtype)
+    toks = torch.zeros(B, dtype=torch.int32, device="cuda")
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        lib.ss_sample_step(x, dreq, rng, toks, ws=ws, stream=s)
+        lib.ss_rng_advance(rng, 1, stream=s)
+    torch.cuda.synchronize()
+    # capture does not execute: reset the offset, then replay N steps
+    rng.copy_(lib.make_rng(42, 0))
+    got = []
+    for i in range(4):
+        g.replay()
+        torch.cuda.synchronize()
+        got.append(toks.cpu().numpy().copy())
+        # eager work between replays
+        _ = (x.float().sum()).item()
+    for i in range(4):
+        o = oracle.sample(wl.logits, wl.dtype, wl.req, seed=42, offset=i, threads=16)
+        assert np.array_equal(got[i], o["tokens"]), i

@@ -1,0 +1,136 @@
+"""The C ABI library on the host (no GPU needed).
+
+* libss.so loads and exports every function include/ss.h declares;
+* the binding's struct layouts match the header (checked by compiling a
+  probe against the header with gcc);
+* argument errors are returned before anything is launched.
+"""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ss.h")
+LIBSO = os.path.join(ROOT, "speculative_decoding_verification_stage1_amd", "libss.so")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(LIBSO):
+        from speculative_decoding_verification_stage1_amd import build
+        build.build()
+    from speculative_decoding_verification_stage1_amd import _lib
+    return _lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(ss_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L.lib, n), n
+    assert sorted(L.EXPORTS) == names
+
+
+def test_struct_layouts_match_header(L):
+    probe = r"""
+#include <stdio.h>
+#include <stddef.h>
+#include "ss.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(ss_req), offsetof(ss_req, top_k),
+         offsetof(ss_req, n_prior), offsetof(ss_req, n_bias), offsetof(ss_req, top_p),
+         offsetof(ss_req, pres_penalty), sizeof(ss_aux), offsetof(ss_aux, bias_ids),
+         offsetof(ss_aux, bitmask), offsetof(ss_aux, bitmask_stride));
+  printf("%zu\n", sizeof(ss_rng));
+  return 0;
+}
+"""
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "p.c")
+        exe = os.path.join(d, "p")
+        open(src, "w").write(probe)
+        subprocess.run(["gcc", "-I", os.path.dirname(HEADER), "-o", exe, src], check=True)
+        out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout.split()
+    vals = [int(v) for v in out]
+    R = L.SS_REQ
+    assert vals[0] == R.itemsize
+    assert vals[1] == R.fields["top_k"][1]
+    assert vals[2] == R.fields["n_prior"][1]
+    assert vals[3] == R.fields["n_bias"][1]
+    assert vals[4] == R.fields["top_p"][1]
+    assert vals[5] == R.fields["pres_penalty"][1]
+    assert vals[6] == ctypes.sizeof(L.SsAux)
+    assert vals[7] == L.SsAux.bias_ids.offset
+    assert vals[8] == L.SsAux.bitmask.offset
+    assert vals[9] == L.SsAux.bitmask_stride.offset
+    assert vals[10] == 16
+
+
+def test_sizes(L):
+    assert L.ss_tile_size(L.SS_BF16) == 16384
+    assert L.ss_tile_size(L.SS_F32) == 8192
+    assert L.ss_tile_size(9) == 0
+    # 256 rows x 16 tiles x 128 keys x 4 B + per-row records
+    ws = L.ss_workspace_bytes(256, 262144, L.SS_BF16)
+    assert ws >= 256 * 16 * 128 * 4
+    assert ws % 256 == 0
+    assert L.ss_workspace_bytes(-1, 10, 0) == 0
+    assert L.ss_workspace_bytes(1, 0, 0) == 0
+
+
+def test_argument_errors_return_before_launch(L):
+    lib = L.lib
+    P = None
+    fake = ctypes.c_void_p(0x1000)
+    # sample: bad dtype, V, ld, missing pointers, workspace
+    assert lib.ss_sample_step(fake, 5, 4, 100, 100, fake, None, fake, fake, P, P, P, P, P, fake, 10**9, P) == L.SS_ERR_UNSUPPORTED
+    assert lib.ss_sample_step(fake, 1, 4, 0, 100, fake, None, fake, fake, P, P, P, P, P, fake, 10**9, P) == L.SS_ERR_INVALID_ARG
+    assert lib.ss_sample_step(fake, 1, 4, 100, 99, fake, None, fake, fake, P, P, P, P, P, fake, 10**9, P) == L.SS_ERR_INVALID_ARG
+    assert lib.ss_sample_step(P, 1, 4, 100, 100, fake, None, fake, fake, P, P, P, P, P, fake, 10**9, P) == L.SS_ERR_INVALID_ARG
+    assert lib.ss_sample_step(fake, 1, 4, 100, 100, P, None, fake, fake, P, P, P, P, P, fake, 10**9, P) == L.SS_ERR_INVALID_ARG
+    assert lib.ss_sample_step(fake, 1, 4, 100, 100, fake, None, fake, fake, P, P, P, P, P, P, 0, P) == L.SS_ERR_WORKSPACE
+    assert lib.ss_sample_step(fake, 1, 4, 100, 100, fake, None, fake, fake, P, P, P, P, P,
+                              ctypes.c_void_p(0x1010), 10**9, P) == L.SS_ERR_WORKSPACE
+    assert lib.ss_sample_step(fake, 1, 4, 100, 100, fake, None, fake, fake, P, P, P, P, P, fake, 16, P) == L.SS_ERR_WORKSPACE
+    assert lib.ss_sample_step(fake, 1, 4, (1 << 24) + 1, (1 << 24) + 1, fake, None, fake, fake, P, P, P, P, P,
+                              fake, 10**12, P) == L.SS_ERR_UNSUPPORTED
+    # bitmask stride shorter than ceil(V/32)
+    aux = L.SsAux(None, None, 0, None, None, 0, 0x2000, 3)
+    assert lib.ss_sample_step(fake, 1, 4, 100, 100, fake, ctypes.byref(aux), fake, fake, P, P, P, P, P,
+                              fake, 10**9, P) == L.SS_ERR_INVALID_ARG
+    # B = 0 is a no-op
+    assert lib.ss_sample_step(fake, 1, 0, 100, 100, P, None, P, P, P, P, P, P, P, P, 0, P) == L.SS_OK
+    # verify: gamma range
+    assert lib.ss_verify_step(fake, 1, 2, 0, 100, 100, fake, None, fake, fake, fake, fake, fake, P, fake, 10**9, P) == L.SS_ERR_UNSUPPORTED
+    assert lib.ss_verify_step(fake, 1, 2, 17, 100, 100, fake, None, fake, fake, fake, fake, fake, P, fake, 10**9, P) == L.SS_ERR_UNSUPPORTED
+    assert lib.ss_verify_step(fake, 1, 2, 4, 100, 100, fake, None, fake, P, fake, fake, fake, P, fake, 10**9, P) == L.SS_ERR_INVALID_ARG
+    # top-k: k range
+    assert lib.ss_topk_step(fake, 0, 2, 100, 100, 0, fake, P, fake, 10**9, P) == L.SS_ERR_UNSUPPORTED
+    assert lib.ss_topk_step(fake, 0, 2, 100, 100, 129, fake, P, fake, 10**9, P) == L.SS_ERR_UNSUPPORTED
+    assert lib.ss_topk_single_pass(fake, 0, 2, 100, 100, 129, fake, P, P) == L.SS_ERR_UNSUPPORTED
+    assert lib.ss_tile_topk(fake, 0, 2, 100, 100, 0, P, None, P, fake, 10**9, P) == L.SS_ERR_INVALID_ARG
+    assert lib.ss_rng_advance(P, 1, P) == L.SS_ERR_INVALID_ARG
+    assert lib.ss_status_str(L.SS_ERR_WORKSPACE).startswith(b"workspace")
+
+
+def test_request_packing(L):
+    from speculative_decoding_verification_stage1_amd import workloads as W
+    wl = W.workload_mixed(2, 6, 4096, grammar=True)
+    a = L.pack_requests(wl.req)
+    assert a.dtype.itemsize == 32
+    for i in range(6):
+        f = int(a["flags"][i])
+        assert bool(f & L.SS_GREEDY) == bool(wl.req.greedy[i])
+        assert bool(f & L.SS_GRAMMAR)
+        assert bool(f & L.SS_TOPK) == (wl.req.top_k[i] > 0)
+    assert np.all(a["n_prior"] == 64) and np.all(a["n_bias"] == 16)
