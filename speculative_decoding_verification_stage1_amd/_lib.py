@@ -191,10 +191,11 @@ def make_rng(seed: int = 0, offset: int = 0, device="cuda"):
 
 
 def workspace(rows: int, V: int, dtype: int, device="cuda"):
+    """A zero-filled workspace (the library keeps its counters at zero
+    between calls; torch allocations are 256-byte aligned)."""
     import torch
     n = int(lib.ss_workspace_bytes(rows, V, dtype))
-    # torch allocations are at least 256-byte aligned
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
 
 
 def dtype_code(t) -> int:

@@ -1,7 +1,7 @@
 // libss: C ABI entry points (declared in include/ss.h).  Host code checks
 // the arguments, carves the caller's workspace and queues fixed-grid
 // kernels on the caller's stream; it never allocates or synchronises.
-#include "ss_verify.h"
+#include "ss_fused.h"
 
 using namespace ssd;
 
@@ -19,6 +19,27 @@ size_t scratch_bytes(int rows, int V, int dtype) {
     return align256((size_t)rows * (size_t)tiles_of(V, dtype) * KMAX * key_bytes(dtype));
 }
 size_t rec_bytes(int rows) { return align256((size_t)rows * sizeof(RowRec)); }
+size_t cnt_bytes(int rows) { return align256((size_t)rows * sizeof(uint32_t)); }
+
+// workspace: [tile keys][row records][row counters][request counters]
+struct WsLayout {
+    void* scratch;
+    RowRec* recs;
+    uint32_t* row_cnt;
+    uint32_t* req_cnt;
+};
+WsLayout ws_layout(void* ws, int rows, int V, int dtype) {
+    char* p = (char*)ws;
+    WsLayout L;
+    L.scratch = p;
+    p += scratch_bytes(rows, V, dtype);
+    L.recs = (RowRec*)p;
+    p += rec_bytes(rows);
+    L.row_cnt = (uint32_t*)p;
+    p += cnt_bytes(rows);
+    L.req_cnt = (uint32_t*)p;
+    return L;
+}
 
 int check_logits(const void* logits, int dtype, int rows, int V, int64_t ld) {
     if (dtype != SS_F32 && dtype != SS_BF16) return SS_ERR_UNSUPPORTED;
@@ -72,32 +93,22 @@ Stage1Params make_s1(const void* logits, int dtype, int rows, int V, int64_t ld,
     return p;
 }
 
-void launch_stage1(int dtype, const Stage1Params& p, hipStream_t s) {
-    const dim3 grid((unsigned)(p.rows * p.Zv)), block(S1_THREADS);
-    if (dtype == SS_BF16) hipLaunchKernelGGL(stage1_kernel<SS_BF16>, grid, block, 0, s, p);
-    else hipLaunchKernelGGL(stage1_kernel<SS_F32>, grid, block, 0, s, p);
+template <int MODE>
+void launch_fused(int dtype, const FusedParams& f, hipStream_t s) {
+    const dim3 grid((unsigned)(f.s1.rows * f.s1.Zv)), block(S1_THREADS);
+    if (dtype == SS_BF16) hipLaunchKernelGGL((fused_kernel<SS_BF16, MODE>), grid, block, 0, s, f);
+    else hipLaunchKernelGGL((fused_kernel<SS_F32, MODE>), grid, block, 0, s, f);
 }
 
-void launch_stage2(int dtype, const Stage2Params& p, hipStream_t s) {
-    const dim3 grid((unsigned)p.rows), block(S2_THREADS);
-    if (dtype == SS_BF16) hipLaunchKernelGGL(stage2_kernel<SS_BF16>, grid, block, 0, s, p);
-    else hipLaunchKernelGGL(stage2_kernel<SS_F32>, grid, block, 0, s, p);
-}
-
-Stage2Params make_s2(const Stage1Params& s1, const ss_rng* rng, int mode) {
-    Stage2Params p{};
-    p.logits = s1.logits;
-    p.ld = s1.ld;
-    p.V = s1.V;
-    p.rows = s1.rows;
-    p.Zv = s1.Zv;
-    p.rows_per_req = s1.rows_per_req;
-    p.req = s1.req;
-    p.aux = s1.aux;
-    p.rng = rng;
-    p.scratch = s1.scratch;
-    p.mode = mode;
-    return p;
+FusedParams make_fused(const Stage1Params& s1, const ss_rng* rng, int mode, const WsLayout& L) {
+    FusedParams f{};
+    f.s1 = s1;
+    f.rng = rng;
+    f.mode = mode;
+    f.row_cnt = L.row_cnt;
+    f.req_cnt = L.req_cnt;
+    f.recs = L.recs;
+    return f;
 }
 
 }  // namespace
@@ -163,7 +174,7 @@ int ss_tile_size(int dtype) {
 
 size_t ss_workspace_bytes(int rows, int V, int dtype) {
     if (rows < 0 || V < 1 || (dtype != SS_F32 && dtype != SS_BF16)) return 0;
-    return scratch_bytes(rows, V, dtype) + rec_bytes(rows);
+    return scratch_bytes(rows, V, dtype) + rec_bytes(rows) + 2 * cnt_bytes(rows);
 }
 
 const char* ss_status_str(int status) {
@@ -188,16 +199,16 @@ int ss_sample_step(const void* logits, int dtype, int B, int V, int64_t ld, cons
     if (!req || !rng || !out_tokens) return SS_ERR_INVALID_ARG;
     if ((rc = check_ws(ws, ws_bytes, ss_workspace_bytes(B, V, dtype)))) return rc;
     hipStream_t s = (hipStream_t)stream;
-    Stage1Params s1 = make_s1(logits, dtype, B, V, ld, 1, req, aux, ws, nullptr);
-    launch_stage1(dtype, s1, s);
-    Stage2Params s2 = make_s2(s1, rng, MODE_SAMPLE);
-    s2.tokens = out_tokens;
-    s2.topk_ids = out_topk_ids;
-    s2.probs = out_probs;
-    s2.kept = out_kept;
-    s2.mass = out_mass;
-    s2.status = out_status;
-    launch_stage2(dtype, s2, s);
+    const WsLayout W = ws_layout(ws, B, V, dtype);
+    Stage1Params s1 = make_s1(logits, dtype, B, V, ld, 1, req, aux, W.scratch, nullptr);
+    FusedParams f = make_fused(s1, rng, MODE_SAMPLE, W);
+    f.tokens = out_tokens;
+    f.topk_ids = out_topk_ids;
+    f.probs = out_probs;
+    f.kept = out_kept;
+    f.mass = out_mass;
+    f.status = out_status;
+    launch_fused<MODE_SAMPLE>(dtype, f, s);
     return launched();
 }
 
@@ -215,23 +226,16 @@ int ss_verify_step(const void* target_logits, int dtype, int B, int gamma, int V
     if (!req || !rng || !draft_ids || !draft_probs || !out_tokens || !out_n_emit) return SS_ERR_INVALID_ARG;
     if ((rc = check_ws(ws, ws_bytes, ss_workspace_bytes(rows, V, dtype)))) return rc;
     hipStream_t s = (hipStream_t)stream;
-    Stage1Params s1 = make_s1(target_logits, dtype, rows, V, ld, gamma + 1, req, aux, ws, nullptr);
-    launch_stage1(dtype, s1, s);
-    Stage2Params s2 = make_s2(s1, rng, MODE_VERIFY);
-    s2.recs = (RowRec*)((char*)ws + scratch_bytes(rows, V, dtype));
-    launch_stage2(dtype, s2, s);
-    VerifyParams vp{};
-    vp.B = B;
-    vp.gamma = gamma;
-    vp.V = V;
-    vp.recs = s2.recs;
-    vp.draft_ids = draft_ids;
-    vp.draft_probs = draft_probs;
-    vp.rng = rng;
-    vp.out_tokens = out_tokens;
-    vp.out_n_emit = out_n_emit;
-    vp.out_status = out_status;
-    hipLaunchKernelGGL(verify_kernel, dim3((unsigned)B), dim3(VF_THREADS), 0, s, vp);
+    const WsLayout W = ws_layout(ws, rows, V, dtype);
+    Stage1Params s1 = make_s1(target_logits, dtype, rows, V, ld, gamma + 1, req, aux, W.scratch, nullptr);
+    FusedParams f = make_fused(s1, rng, MODE_VERIFY, W);
+    f.gamma = gamma;
+    f.draft_ids = draft_ids;
+    f.draft_probs = draft_probs;
+    f.v_tokens = out_tokens;
+    f.v_n_emit = out_n_emit;
+    f.v_status = out_status;
+    launch_fused<MODE_VERIFY>(dtype, f, s);
     return launched();
 }
 
@@ -244,13 +248,13 @@ int ss_topk_step(const void* logits, int dtype, int B, int V, int64_t ld, int k,
     if (!out_ids) return SS_ERR_INVALID_ARG;
     if ((rc = check_ws(ws, ws_bytes, ss_workspace_bytes(B, V, dtype)))) return rc;
     hipStream_t s = (hipStream_t)stream;
-    Stage1Params s1 = make_s1(logits, dtype, B, V, ld, 1, nullptr, nullptr, ws, nullptr);
-    launch_stage1(dtype, s1, s);
-    Stage2Params s2 = make_s2(s1, nullptr, MODE_TOPK);
-    s2.topk_k = k;
-    s2.topk_ids = out_ids;
-    s2.topk_vals = out_vals;
-    launch_stage2(dtype, s2, s);
+    const WsLayout W = ws_layout(ws, B, V, dtype);
+    Stage1Params s1 = make_s1(logits, dtype, B, V, ld, 1, nullptr, nullptr, W.scratch, nullptr);
+    FusedParams f = make_fused(s1, nullptr, MODE_TOPK, W);
+    f.topk_k = k;
+    f.topk_ids = out_ids;
+    f.topk_vals = out_vals;
+    launch_fused<MODE_TOPK>(dtype, f, s);
     return launched();
 }
 
@@ -281,8 +285,10 @@ int ss_tile_topk(const void* logits, int dtype, int rows, int V, int64_t ld, int
     if (rows == 0) return SS_OK;
     if ((rc = check_ws(ws, ws_bytes, ss_workspace_bytes(rows, V, dtype)))) return rc;
     hipStream_t s = (hipStream_t)stream;
-    Stage1Params s1 = make_s1(logits, dtype, rows, V, ld, rows_per_req, req, aux, ws, out_ids);
-    launch_stage1(dtype, s1, s);
+    const WsLayout W = ws_layout(ws, rows, V, dtype);
+    Stage1Params s1 = make_s1(logits, dtype, rows, V, ld, rows_per_req, req, aux, W.scratch, out_ids);
+    FusedParams f = make_fused(s1, nullptr, MODE_TILES, W);
+    launch_fused<MODE_TILES>(dtype, f, s);
     return launched();
 }
 

@@ -451,28 +451,4 @@ __device__ void stage1_tile(const Stage1Params& P, int row, int tile, S1Shared<D
     block_sort_desc<Key, S1_THREADS>(surv, Pn);
 }
 
-template <int DT>
-__global__ __launch_bounds__(S1_THREADS) void stage1_kernel(Stage1Params P) {
-    using Key = typename S1Traits<DT>::Key;
-    __shared__ S1Shared<DT> sh;
-    const int row = blockIdx.x / P.Zv;
-    const int tile = blockIdx.x - row * P.Zv;
-    stage1_tile<DT>(P, row, tile, sh);
-    const int tid = threadIdx.x;
-    if (tid < KMAX) {
-        const int64_t o = ((int64_t)row * P.Zv + tile) * KMAX + tid;
-        const Key k = sh.surv[tid];
-        ((Key*)P.scratch)[o] = k;
-        if (P.out_ids) {
-            int id = -1;
-            if (k != 0) {
-                const uint32_t lo = DT == SS_BF16 ? (0xFFFFu - ((uint32_t)k & 0xFFFFu))
-                                                  : (0xFFFFFFFFu - (uint32_t)k);
-                id = tile * S1Traits<DT>::BN + (int)lo;
-            }
-            P.out_ids[o] = id;
-        }
-    }
-}
-
 }  // namespace ssd

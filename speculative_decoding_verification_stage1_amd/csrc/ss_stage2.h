@@ -1,9 +1,12 @@
-// Stage 2 (SonicSampler section 3.2 and Fig. 1, stage 2): one workgroup per
-// row gathers the row's Z_v tile lists, re-indexes them to global token ids,
-// merges them with bitonic merge networks into the row's 128 best tokens,
-// and runs the fused epilogue: temperature, softmax weights, top-p / min-p
-// truncation and Gumbel-max selection (section 3.1 "Probability
-// truncation", "Sampling").
+// Stage 2 (SonicSampler section 3.2 and Fig. 1, stage 2) for one row: the
+// row's Z_v tile lists are re-indexed to global token ids and merged with
+// bitonic merge networks into the row's 128 best tokens; then the fused
+// epilogue runs: temperature, softmax weights, top-p / min-p truncation
+// and Gumbel-max selection (section 3.1 "Probability truncation",
+// "Sampling").
+//
+// Stage 2 runs inside the workgroup that finished the row's last tile (see
+// ss_fused.h), so each row's merge overlaps other rows' Stage-1 streaming.
 //
 // Tokens named by an active penalty or bias list never enter the tiles;
 // Stage 2 computes their processed logits directly (gather + the list
@@ -16,13 +19,11 @@
 
 namespace ssd {
 
-constexpr int S2_THREADS = 256;
-constexpr int S2_WAVES = S2_THREADS / WAVE;
-constexpr int S2_GROUP = 32;   // tile lists merged per LDS pass
+constexpr int S2_GROUP = 8;   // tile lists merged per LDS pass
 
-enum { MODE_SAMPLE = 0, MODE_VERIFY = 1, MODE_TOPK = 2 };
+enum { MODE_TILES = 0, MODE_SAMPLE = 1, MODE_VERIFY = 2, MODE_TOPK = 3 };
 
-// Per target row, written by Stage 2 in verification mode.
+// Per target row, written in verification mode.
 struct RowRec {
     int32_t ids[KMAX];   // candidates in order (-1 past K)
     float v[KMAX];       // z * (1/T), clamped
@@ -35,27 +36,39 @@ struct RowRec {
     int32_t pad[3];
 };
 
-struct Stage2Params {
-    const void* logits;
-    int64_t ld;
-    int V;
-    int rows;
-    int Zv;
-    int rows_per_req;
-    const ss_req* req;
-    ss_aux aux;
+struct FusedParams {
+    Stage1Params s1;
     const ss_rng* rng;
-    const void* scratch;
     int mode;
     int topk_k;
+    uint32_t* row_cnt;   // [rows] tiles finished per row (kept at 0 between calls)
+    uint32_t* req_cnt;   // [requests] rows finished per request (verification)
+    // sampling outputs
     int32_t* tokens;
     int32_t* topk_ids;
     float* probs;
     int32_t* kept;
     float* mass;
     int32_t* status;
+    // verification
     RowRec* recs;
+    int gamma;
+    const int32_t* draft_ids;
+    const float* draft_probs;
+    int32_t* v_tokens;
+    int32_t* v_n_emit;
+    int32_t* v_status;
+    // top-k
     float* topk_vals;
+};
+
+struct S2Shared {
+    uint64_t buf[S2_GROUP][KMAX];
+    uint64_t acc[KMAX];
+    uint64_t lkeys[S1_LIST_CAP];
+    float redf[S1_WAVES];
+    int redi[S1_WAVES];
+    float pd;
 };
 
 struct RowParams {
@@ -76,8 +89,9 @@ struct RowParams {
 
 __device__ __forceinline__ bool finitef(float x) { return x == x && x - x == 0.0f; }
 
-// Row validation and parameters (one thread).
-__device__ inline RowParams row_params(const Stage2Params& P, int b) {
+// Row validation and parameters; every thread computes the same values from
+// the (uniform) request record.
+__device__ inline RowParams row_params(const Stage1Params& P, int b) {
     RowParams rp{};
     if (!P.req) {   // plain top-k: no processing
         rp.valid = 1;
@@ -103,8 +117,9 @@ __device__ inline RowParams row_params(const Stage2Params& P, int b) {
     if ((f & SS_FREQPRES) && !(finitef(r.freq_penalty) && finitef(r.pres_penalty))) ok = false;
     if (ok && (f & SS_BIAS)) {
         const float* bv = P.aux.bias_val + (int64_t)b * P.aux.bias_stride;
-        for (int j = 0; j < (int)r.n_bias; ++j)
-            if (!finitef(bv[j])) ok = false;
+        bool fin = true;
+        for (int j = 0; j < (int)r.n_bias; ++j) fin &= finitef(bv[j]);
+        ok = fin;
     }
     bool g = (f & SS_GREEDY) != 0;
     if (!g) {
@@ -146,12 +161,17 @@ __device__ __forceinline__ uint64_t merge_key(typename S1Traits<DT>::Key e, int 
     return ((uint64_t)k32 << 32) | (uint64_t)(0xFFFFFFFFu - gid);
 }
 
+__device__ __forceinline__ int key_id(uint64_t k) { return k ? (int)(0xFFFFFFFFu - (uint32_t)k) : -1; }
+__device__ __forceinline__ float key_z(uint64_t k) {
+    return k ? unord32((uint32_t)(k >> 32)) : bitsf(F32_NINF_BITS);
+}
+
 // Merge sorted-descending lists A and B (128 each) into A: the elementwise
 // max of A and reversed B is bitonic and holds the 128 best; seven
 // half-cleaner steps sort it.  `npairs` merges run together; pair m uses
 // lists slot(m) and slot(m) + stride.
 __device__ __forceinline__ void merge_level(uint64_t (*buf)[KMAX], int npairs, int stride) {
-    for (int idx = threadIdx.x; idx < npairs * KMAX; idx += S2_THREADS) {
+    for (int idx = threadIdx.x; idx < npairs * KMAX; idx += S1_THREADS) {
         const int m = idx / KMAX, i = idx % KMAX;
         uint64_t* A = buf[m * 2 * stride];
         const uint64_t* Bl = buf[m * 2 * stride + stride];
@@ -160,7 +180,7 @@ __device__ __forceinline__ void merge_level(uint64_t (*buf)[KMAX], int npairs, i
     }
     __syncthreads();
     for (int j = KMAX / 2; j > 0; j >>= 1) {
-        for (int idx = threadIdx.x; idx < npairs * (KMAX / 2); idx += S2_THREADS) {
+        for (int idx = threadIdx.x; idx < npairs * (KMAX / 2); idx += S1_THREADS) {
             const int m = idx / (KMAX / 2), q = idx % (KMAX / 2);
             uint64_t* A = buf[m * 2 * stride];
             const int i = (q / j) * 2 * j + (q % j);
@@ -174,8 +194,30 @@ __device__ __forceinline__ void merge_level(uint64_t (*buf)[KMAX], int npairs, i
     }
 }
 
-// Best (score desc, id asc) across the block; invalid lanes pass ok=false.
-__device__ __forceinline__ int block_argmax(float s, int id, bool ok, float* ws, int* wi) {
+// acc <- the 128 best of acc and B (both sorted descending).
+__device__ __forceinline__ void merge_into(uint64_t* acc, const uint64_t* B) {
+    if (threadIdx.x < KMAX) {
+        const int i = threadIdx.x;
+        const uint64_t a = acc[i], bb = B[KMAX - 1 - i];
+        acc[i] = a > bb ? a : bb;
+    }
+    __syncthreads();
+    for (int j = KMAX / 2; j > 0; j >>= 1) {
+        if (threadIdx.x < KMAX / 2) {
+            const int q = threadIdx.x;
+            const int i = (q / j) * 2 * j + (q % j);
+            const uint64_t a = acc[i], c = acc[i + j];
+            if (a < c) {
+                acc[i] = c;
+                acc[i + j] = a;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// Wave-wide best (score desc, id asc); lanes with ok=false do not compete.
+__device__ __forceinline__ int wave_argmax(float s, int id, bool ok) {
     float bs = s;
     int bi = ok ? id : -1;
 #pragma unroll
@@ -188,168 +230,131 @@ __device__ __forceinline__ int block_argmax(float s, int id, bool ok, float* ws,
             bi = oi;
         }
     }
-    const int w = threadIdx.x / WAVE;
-    if (lane_id() == 0) {
-        ws[w] = bs;
-        wi[w] = bi;
-    }
-    __syncthreads();
-    float rs = ws[0];
-    int ri = wi[0];
-    for (int i = 1; i < (int)(blockDim.x / WAVE); ++i) {
-        const float os = ws[i];
-        const int oi = wi[i];
-        if (oi >= 0 && (ri < 0 || os > rs || (os == rs && oi < ri))) {
-            rs = os;
-            ri = oi;
-        }
-    }
-    __syncthreads();
-    return ri;
+    return bi;
 }
 
-__device__ __forceinline__ int block_count(bool c, int* tmp) {
-    const uint64_t bal = __ballot(c);
-    const int w = threadIdx.x / WAVE;
-    if (lane_id() == 0) tmp[w] = __popcll(bal);
-    __syncthreads();
-    int t = 0;
-    for (int i = 0; i < (int)(blockDim.x / WAVE); ++i) t += tmp[i];
-    __syncthreads();
-    return t;
+__device__ __forceinline__ float readlane_f(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
+// The row's 128 best (merge keys, descending) into sh.acc.  Ends with a barrier.
 template <int DT>
-__global__ __launch_bounds__(S2_THREADS) void stage2_kernel(Stage2Params P) {
+__device__ void row_merge(const FusedParams& F, const RowParams& rp, int row, int b, S2Shared& sh) {
     using Key = typename S1Traits<DT>::Key;
-    __shared__ uint64_t buf[S2_GROUP][KMAX];
-    __shared__ uint64_t acc[KMAX];
-    __shared__ uint64_t lkeys[S1_LIST_CAP];
-    __shared__ int32_t s_pid[256], s_pcnt[256], s_bid[256];
-    __shared__ float s_bval[256];
-    __shared__ float s_e[KMAX];
-    __shared__ float s_E[KMAX + 1];
-    __shared__ float s_redf[S2_WAVES];
-    __shared__ int s_redi[S2_WAVES];
-    __shared__ RowParams s_rp;
-
+    const Stage1Params& P = F.s1;
     const int tid = threadIdx.x;
-    const int row = blockIdx.x;
-    const int b = row / P.rows_per_req;
-    if (tid == 0) s_rp = row_params(P, b);
-    __syncthreads();
-    const RowParams rp = s_rp;
 
-    // ---- listed tokens: exact processed logits, as one sorted list ----
+    // ---- listed tokens: exact processed logits, one sorted list ----
     const int np = rp.valid ? rp.n_prior : 0;
     const int nb = rp.valid ? rp.n_bias : 0;
-    for (int j = tid; j < np; j += S2_THREADS) {
-        s_pid[j] = P.aux.prior_ids[(int64_t)b * P.aux.prior_stride + j];
-        s_pcnt[j] = P.aux.prior_cnt[(int64_t)b * P.aux.prior_stride + j];
-    }
-    for (int j = tid; j < nb; j += S2_THREADS) {
-        s_bid[j] = P.aux.bias_ids[(int64_t)b * P.aux.bias_stride + j];
-        s_bval[j] = P.aux.bias_val[(int64_t)b * P.aux.bias_stride + j];
-    }
-    for (int i = tid; i < KMAX; i += S2_THREADS) acc[i] = 0ull;
-    __syncthreads();
     const int ncomb = np + nb;
+    if (tid < KMAX) sh.acc[tid] = 0ull;
     if (ncomb > 0) {
+        const int32_t* pid = P.aux.prior_ids + (int64_t)b * P.aux.prior_stride;
+        const int32_t* pct = P.aux.prior_cnt + (int64_t)b * P.aux.prior_stride;
+        const int32_t* bid = P.aux.bias_ids + (int64_t)b * P.aux.bias_stride;
+        const float* bvl = P.aux.bias_val + (int64_t)b * P.aux.bias_stride;
         const bool grammar = (rp.flags & SS_GRAMMAR) != 0;
-        for (int t = tid; t < ncomb; t += S2_THREADS) {
-            int id;
-            bool ok;
+        for (int t0 = 0; t0 < ncomb; t0 += S1_THREADS) {   // uniform loop
+            const int t = t0 + tid;
+            int id = -1;
+            bool ok = false;
             if (t < np) {
-                id = s_pid[t];
-                ok = s_pcnt[t] >= 1 && id >= 0 && id < P.V;
-            } else {
-                id = s_bid[t - np];
+                id = pid[t];
+                ok = pct[t] >= 1 && id >= 0 && id < P.V;
+            } else if (t < ncomb) {
+                id = bid[t - np];
                 ok = id >= 0 && id < P.V;
             }
-            for (int u = 0; u < t && ok; ++u) {   // keep the first entry of each id
-                const bool uok = u < np ? (s_pcnt[u] >= 1 && s_pid[u] == id) : (s_bid[u - np] == id);
-                if (uok) ok = false;
-            }
-            uint64_t key = 0ull;
+            float z = 0.0f;
+            bool allowed = true;
             if (ok) {
-                float z;
                 if (DT == SS_BF16) z = widen_bf16(((const uint16_t*)P.logits)[(int64_t)row * P.ld + id]);
                 else z = ((const float*)P.logits)[(int64_t)row * P.ld + id];
-                if (grammar && !((P.aux.bitmask[(int64_t)row * P.aux.bitmask_stride + (id >> 5)] >> (id & 31)) & 1u))
-                    z = bitsf(F32_NINF_BITS);
-                if (rp.flags & SS_REP)
-                    for (int j = 0; j < np; ++j)
-                        if (s_pcnt[j] >= 1 && s_pid[j] == id) z = (z > 0.0f) ? z / rp.rep : z * rp.rep;
-                if (rp.flags & SS_FREQPRES)
-                    for (int j = 0; j < np; ++j)
-                        if (s_pcnt[j] >= 1 && s_pid[j] == id) {
-                            const float pen = (float)s_pcnt[j] * rp.freq + rp.pres;
-                            z = z - pen;
-                        }
-                if (rp.flags & SS_BIAS)
-                    for (int j = 0; j < nb; ++j)
-                        if (s_bid[j] == id) z = z + s_bval[j];
-                key = ((uint64_t)ord32(canon(z)) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id);
+                if (grammar)
+                    allowed = (P.aux.bitmask[(int64_t)row * P.aux.bitmask_stride + (id >> 5)] >> (id & 31)) & 1u;
             }
-            lkeys[t] = key;
+            if (!allowed) z = bitsf(F32_NINF_BITS);
+            // the list entries are the same for every lane: uniform loads
+            bool dup = false;
+            const bool do_rep = (rp.flags & SS_REP) != 0;
+#pragma unroll 8
+            for (int u = 0; u < np; ++u) {
+                const bool m = pct[u] >= 1 && pid[u] == id;
+                dup |= m && u < t;
+                if (do_rep && m) z = (z > 0.0f) ? z / rp.rep : z * rp.rep;
+            }
+            if (rp.flags & SS_FREQPRES) {
+#pragma unroll 8
+                for (int u = 0; u < np; ++u) {
+                    const int c = pct[u];
+                    if (c >= 1 && pid[u] == id) {
+                        const float pen = (float)c * rp.freq + rp.pres;
+                        z = z - pen;
+                    }
+                }
+            }
+#pragma unroll 8
+            for (int u = 0; u < nb; ++u) {
+                const bool m = bid[u] == id;
+                dup |= m && np + u < t;
+                if (m) z = z + bvl[u];
+            }
+            if (t < ncomb)
+                sh.lkeys[t] = (ok && !dup)
+                                  ? (((uint64_t)ord32(canon(z)) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id))
+                                  : 0ull;
         }
         int Pl = KMAX;
         while (Pl < ncomb) Pl <<= 1;
-        for (int t = ncomb + tid; t < Pl; t += S2_THREADS) lkeys[t] = 0ull;
+        for (int t = ncomb + tid; t < Pl; t += S1_THREADS) sh.lkeys[t] = 0ull;
         __syncthreads();
-        block_sort_desc<uint64_t, S2_THREADS>(lkeys, Pl);
-        for (int i = tid; i < KMAX; i += S2_THREADS) acc[i] = lkeys[i];
-        __syncthreads();
+        block_sort_desc<uint64_t, S1_THREADS>(sh.lkeys, Pl);
+        if (tid < KMAX) sh.acc[tid] = sh.lkeys[tid];
     }
+    __syncthreads();
 
     // ---- tile lists: load a group, merge it down to one list, fold into acc ----
     const Key* sc = (const Key*)P.scratch + (int64_t)row * P.Zv * KMAX;
     for (int g0 = 0; g0 < P.Zv; g0 += S2_GROUP) {
         const int G = min(S2_GROUP, P.Zv - g0);
-        for (int idx = tid; idx < G * KMAX; idx += S2_THREADS) {
+        for (int idx = tid; idx < G * KMAX; idx += S1_THREADS) {
             const int l = idx / KMAX, i = idx % KMAX;
-            buf[l][i] = merge_key<DT>(sc[(int64_t)(g0 + l) * KMAX + i], g0 + l);
+            sh.buf[l][i] = merge_key<DT>(sc[(int64_t)(g0 + l) * KMAX + i], g0 + l);
         }
         __syncthreads();
         for (int s = 1; s < G; s <<= 1) {
             const int npairs = (G - s + 2 * s - 1) / (2 * s);   // m with m*2s + s < G
-            merge_level(buf, npairs, s);
+            merge_level(sh.buf, npairs, s);
         }
-        // acc <- merge(acc, buf[0])
-        for (int i = tid; i < KMAX; i += S2_THREADS) {
-            const uint64_t a = acc[i], bb = buf[0][KMAX - 1 - i];
-            acc[i] = a > bb ? a : bb;
-        }
-        __syncthreads();
-        for (int j = KMAX / 2; j > 0; j >>= 1) {
-            for (int q = tid; q < KMAX / 2; q += S2_THREADS) {
-                const int i = (q / j) * 2 * j + (q % j);
-                const uint64_t a = acc[i], c = acc[i + j];
-                if (a < c) {
-                    acc[i] = c;
-                    acc[i + j] = a;
-                }
-            }
-            __syncthreads();
-        }
+        merge_into(sh.acc, sh.buf[0]);
     }
+}
 
-    // ---- epilogue: threads 0..127 hold rank k = tid ----
-    const int k = tid;
-    const bool lane_k = k < KMAX;
-    uint64_t key = lane_k ? acc[k] : 0ull;
-    const int id_k = key ? (int)(0xFFFFFFFFu - (uint32_t)key) : -1;
-    const float z_k = key ? unord32((uint32_t)(key >> 32)) : bitsf(F32_NINF_BITS);
-    const uint64_t key0 = acc[0];
-    const int id0 = key0 ? (int)(0xFFFFFFFFu - (uint32_t)key0) : -1;
-    const float z0 = key0 ? unord32((uint32_t)(key0 >> 32)) : bitsf(F32_NINF_BITS);
+// Epilogue on wave 0 (ranks k = lane and lane + 64).  Writes the mode's
+// outputs for the row.  Uses no barrier.
+template <int DT>
+__device__ void row_epilogue(const FusedParams& F, const RowParams& rp, int row, int b, S2Shared& sh) {
+    const Stage1Params& P = F.s1;
+    const int lane = lane_id();
+    const uint64_t k_lo = sh.acc[lane], k_hi = sh.acc[lane + 64];
+    const int id_lo = key_id(k_lo), id_hi = key_id(k_hi);
+    const float z_lo = key_z(k_lo), z_hi = key_z(k_hi);
+    const uint64_t k0 = sh.acc[0];
+    const int id0 = key_id(k0);
+    const float z0 = key_z(k0);
+    const float NINF = bitsf(F32_NINF_BITS);
 
-    if (P.mode == MODE_TOPK) {
-        const int kk = P.topk_k;
-        if (k < kk) {
-            const bool have = k < P.V && id_k >= 0;
-            P.topk_ids[(int64_t)row * kk + k] = have ? id_k : -1;
-            if (P.topk_vals) P.topk_vals[(int64_t)row * kk + k] = have ? z_k : bitsf(F32_NINF_BITS);
+    if (F.mode == MODE_TOPK) {
+        const int kk = F.topk_k;
+        for (int h = 0; h < 2; ++h) {
+            const int k = lane + 64 * h;
+            const int id = h ? id_hi : id_lo;
+            if (k < kk) {
+                const bool have = k < P.V && id >= 0;
+                F.topk_ids[(int64_t)row * kk + k] = have ? id : -1;
+                if (F.topk_vals) F.topk_vals[(int64_t)row * kk + k] = have ? (h ? z_hi : z_lo) : NINF;
+            }
         }
         return;
     }
@@ -357,90 +362,110 @@ __global__ __launch_bounds__(S2_THREADS) void stage2_kernel(Stage2Params P) {
     const int K = rp.K;
     int status = SS_ROW_OK;
     if (!rp.valid) status = SS_ROW_INVALID;
-    else if (z0 == bitsf(F32_NINF_BITS)) status = SS_ROW_ALL_MASKED;
+    else if (z0 == NINF) status = SS_ROW_ALL_MASKED;
     else if (rp.clamped) status = SS_ROW_TOPK_CLAMPED;
     const bool live = status == SS_ROW_OK || status == SS_ROW_TOPK_CLAMPED;
 
     int token = -1, n = 0;
-    float vk = bitsf(F32_NINF_BITS), ek = 0.0f, Z = 1.0f, En = 0.0f;
+    float v_lo = NINF, v_hi = NINF, e_lo = 0.0f, e_hi = 0.0f, Z = 1.0f, En = 0.0f;
     if (live && rp.greedy) {
         token = id0;
         n = 1;
     } else if (live) {
         const float invT = 1.0f / rp.temperature;
+        const float FMAX = bitsf(F32_MAX_BITS);
         auto vscale = [&](float z) -> float {
-            if (z == bitsf(F32_NINF_BITS)) return z;
+            if (z == NINF) return z;
             float v = z * invT;
-            v = v > bitsf(F32_MAX_BITS) ? bitsf(F32_MAX_BITS) : v;
-            v = v < -bitsf(F32_MAX_BITS) ? -bitsf(F32_MAX_BITS) : v;
+            v = v > FMAX ? FMAX : v;
+            v = v < -FMAX ? -FMAX : v;
             return v;
         };
         const float m = vscale(z0);
-        if (k < K) {
-            vk = vscale(z_k);
-            ek = exp_fixed(vk - m);
+        if (lane < K) {
+            v_lo = vscale(z_lo);
+            e_lo = exp_fixed(v_lo - m);
         }
-        if (lane_k) s_e[k] = ek;
-        __syncthreads();
-        if (tid == 0) {
-            float E = 0.0f;
-            s_E[0] = 0.0f;
-            for (int i = 0; i < K; ++i) {
-                E = E + s_e[i];
-                s_E[i + 1] = E;
-            }
+        if (lane + 64 < K) {
+            v_hi = vscale(z_hi);
+            e_hi = exp_fixed(v_hi - m);
         }
-        __syncthreads();
-        Z = s_E[K];
+        // running sums E_k = e_0 + ... + e_{k-1}, left to right
+        float E = 0.0f, E_lo = 0.0f, E_hi = 0.0f;
+        const int k1 = min(K, 64);
+        for (int k = 0; k < k1; ++k) {
+            if (lane == k) E_lo = E;
+            E = E + readlane_f(e_lo, k);
+        }
+        for (int k = 64; k < K; ++k) {
+            if (lane == k - 64) E_hi = E;
+            E = E + readlane_f(e_hi, k - 64);
+        }
+        Z = E;
         int n_p = K, n_m = K;
         if ((rp.flags & SS_TOPP) && rp.top_p < 1.0f) {
             const float thr = rp.top_p * Z;
-            n_p = block_count(k < K && s_E[k] < thr, s_redi);
+            n_p = __popcll(__ballot(lane < K && E_lo < thr)) + __popcll(__ballot(lane + 64 < K && E_hi < thr));
         }
         if ((rp.flags & SS_MINP) && rp.min_p > 0.0f) {
             const float L = log_fixed(rp.min_p);
-            n_m = block_count(k < K && (vk - m) >= L, s_redi);
+            n_m = __popcll(__ballot(lane < K && (v_lo - m) >= L)) +
+                  __popcll(__ballot(lane + 64 < K && (v_hi - m) >= L));
         }
         n = min(n_p, n_m);
-        En = s_E[n];
+        // E_n: the running sum before rank n (Z when n = K)
+        if (n >= K) En = Z;
+        else if (n < 64) En = readlane_f(E_lo, n);
+        else En = readlane_f(E_hi, n - 64);
         uint32_t c1, c2;
-        if (P.mode == MODE_VERIFY) {
+        if (F.mode == MODE_VERIFY) {
             c1 = (uint32_t)b;
             c2 = (uint32_t)(row - b * P.rows_per_req);
         } else {
             c1 = (uint32_t)row;
             c2 = 0u;
         }
-        const ss_rng rg = *P.rng;
-        float s = 0.0f;
-        const bool cand = k < n;
-        if (cand) s = vk + gumbel_noise(rg.seed, rg.offset, (uint32_t)id_k, c1, c2);
-        token = block_argmax(s, id_k, cand, s_redf, s_redi);
+        const ss_rng rg = *F.rng;
+        float s_lo = 0.0f, s_hi = 0.0f;
+        const bool c_lo = lane < n, c_hi = lane + 64 < n;
+        if (c_lo) s_lo = v_lo + gumbel_noise(rg.seed, rg.offset, (uint32_t)id_lo, c1, c2);
+        if (c_hi) s_hi = v_hi + gumbel_noise(rg.seed, rg.offset, (uint32_t)id_hi, c1, c2);
+        // best of the lane's two, then across the wave
+        float s = s_lo;
+        int id = c_lo ? id_lo : -1;
+        if (c_hi && (id < 0 || s_hi > s || (s_hi == s && id_hi < id))) {
+            s = s_hi;
+            id = id_hi;
+        }
+        token = wave_argmax(s, id, id >= 0);
     }
 
-    if (P.mode == MODE_SAMPLE) {
-        if (tid == 0) {
-            P.tokens[row] = token;
-            if (P.status) P.status[row] = status;
-            if (P.kept) P.kept[row] = live ? n : 0;
-            if (P.mass) P.mass[row] = live ? (rp.greedy ? 1.0f : En / Z) : 0.0f;
+    if (F.mode == MODE_SAMPLE) {
+        if (lane == 0) {
+            F.tokens[row] = token;
+            if (F.status) F.status[row] = status;
+            if (F.kept) F.kept[row] = live ? n : 0;
+            if (F.mass) F.mass[row] = live ? (rp.greedy ? 1.0f : En / Z) : 0.0f;
         }
-        if (lane_k) {
-            if (P.topk_ids) P.topk_ids[(int64_t)row * KMAX + k] = (status != SS_ROW_INVALID && k < K) ? id_k : -1;
-            if (P.probs) {
+        for (int h = 0; h < 2; ++h) {
+            const int k = lane + 64 * h;
+            if (F.topk_ids)
+                F.topk_ids[(int64_t)row * KMAX + k] = (status != SS_ROW_INVALID && k < K) ? (h ? id_hi : id_lo) : -1;
+            if (F.probs) {
                 float pk = 0.0f;
-                if (live) pk = rp.greedy ? (k == 0 ? 1.0f : 0.0f) : (k < K ? ek / Z : 0.0f);
-                P.probs[(int64_t)row * KMAX + k] = pk;
+                if (live) pk = rp.greedy ? (k == 0 ? 1.0f : 0.0f) : (k < K ? (h ? e_hi : e_lo) / Z : 0.0f);
+                F.probs[(int64_t)row * KMAX + k] = pk;
             }
         }
     } else {   // MODE_VERIFY
-        RowRec* rec = P.recs + row;
-        if (lane_k) {
-            rec->ids[k] = (status != SS_ROW_INVALID && k < K) ? id_k : -1;
-            rec->v[k] = vk;
-            rec->p[k] = (live && !rp.greedy && k < n) ? ek / En : 0.0f;
+        RowRec* rec = F.recs + row;
+        for (int h = 0; h < 2; ++h) {
+            const int k = lane + 64 * h;
+            rec->ids[k] = (status != SS_ROW_INVALID && k < K) ? (h ? id_hi : id_lo) : -1;
+            rec->v[k] = h ? v_hi : v_lo;
+            rec->p[k] = (live && !rp.greedy && k < n) ? (h ? e_hi : e_lo) / En : 0.0f;
         }
-        if (tid == 0) {
+        if (lane == 0) {
             rec->n = live ? n : 0;
             rec->K = K;
             rec->token = token;
