@@ -146,12 +146,8 @@ typedef struct ss_aux {
 
 /* Bytes of workspace a call over `rows` logits rows of width V needs (rows
  * = B for sampling and top-k, B*(gamma+1) for verification).  Pure host
- * function.  The workspace must be 256-byte aligned and ZERO-FILLED before
- * its first use: it holds per-row and per-request arrival counters that
- * let the workgroup finishing a row's last tile run that row's merge
- * (one launch per call); every call returns them to zero, so a workspace
- * can be reused by any later call (and by graph replays) without clearing.
- * Calls that share a workspace must not overlap in time. */
+ * function; the workspace must be 256-byte aligned.  Its contents need no
+ * initialisation; calls that share a workspace must not overlap in time. */
 size_t ss_workspace_bytes(int rows, int V, int dtype);
 
 /* Vocabulary tile width used for `dtype` (B_N of the two-stage top-k). */

@@ -1,7 +1,7 @@
 // libss: C ABI entry points (declared in include/ss.h).  Host code checks
 // the arguments, carves the caller's workspace and queues fixed-grid
 // kernels on the caller's stream; it never allocates or synchronises.
-#include "ss_fused.h"
+#include "ss_kernels.h"
 
 using namespace ssd;
 
@@ -19,25 +19,19 @@ size_t scratch_bytes(int rows, int V, int dtype) {
     return align256((size_t)rows * (size_t)tiles_of(V, dtype) * KMAX * key_bytes(dtype));
 }
 size_t rec_bytes(int rows) { return align256((size_t)rows * sizeof(RowRec)); }
-size_t cnt_bytes(int rows) { return align256((size_t)rows * sizeof(uint32_t)); }
+size_t listed_bytes(int rows) { return align256((size_t)rows * KMAX * sizeof(uint64_t)); }
 
-// workspace: [tile keys][row records][row counters][request counters]
+// workspace: [tile keys][listed-token keys][row records]
 struct WsLayout {
     void* scratch;
+    uint64_t* listed;
     RowRec* recs;
-    uint32_t* row_cnt;
-    uint32_t* req_cnt;
 };
 WsLayout ws_layout(void* ws, int rows, int V, int dtype) {
-    char* p = (char*)ws;
     WsLayout L;
-    L.scratch = p;
-    p += scratch_bytes(rows, V, dtype);
-    L.recs = (RowRec*)p;
-    p += rec_bytes(rows);
-    L.row_cnt = (uint32_t*)p;
-    p += cnt_bytes(rows);
-    L.req_cnt = (uint32_t*)p;
+    L.scratch = ws;
+    L.listed = (uint64_t*)((char*)ws + scratch_bytes(rows, V, dtype));
+    L.recs = (RowRec*)((char*)L.listed + listed_bytes(rows));
     return L;
 }
 
@@ -93,21 +87,26 @@ Stage1Params make_s1(const void* logits, int dtype, int rows, int V, int64_t ld,
     return p;
 }
 
-template <int MODE>
-void launch_fused(int dtype, const FusedParams& f, hipStream_t s) {
-    const dim3 grid((unsigned)(f.s1.rows * f.s1.Zv)), block(S1_THREADS);
-    if (dtype == SS_BF16) hipLaunchKernelGGL((fused_kernel<SS_BF16, MODE>), grid, block, 0, s, f);
-    else hipLaunchKernelGGL((fused_kernel<SS_F32, MODE>), grid, block, 0, s, f);
+void launch_stage1(int dtype, const Stage1Params& p, hipStream_t s) {
+    const dim3 grid((unsigned)(p.listed_rows + p.rows * p.Zv)), block(S1_THREADS);
+    if (dtype == SS_BF16) hipLaunchKernelGGL(stage1_kernel<SS_BF16>, grid, block, 0, s, p);
+    else hipLaunchKernelGGL(stage1_kernel<SS_F32>, grid, block, 0, s, p);
 }
 
-FusedParams make_fused(const Stage1Params& s1, const ss_rng* rng, int mode, const WsLayout& L) {
-    FusedParams f{};
+template <int MODE>
+void launch_stage2(int dtype, const Stage2Params& f, hipStream_t s) {
+    const dim3 grid((unsigned)f.s1.rows), block(S2_THREADS);
+    if (dtype == SS_BF16) hipLaunchKernelGGL((stage2_kernel<SS_BF16, MODE>), grid, block, 0, s, f);
+    else hipLaunchKernelGGL((stage2_kernel<SS_F32, MODE>), grid, block, 0, s, f);
+}
+
+Stage2Params make_s2(const Stage1Params& s1, const ss_rng* rng, int mode, const WsLayout& L) {
+    Stage2Params f{};
     f.s1 = s1;
     f.rng = rng;
     f.mode = mode;
-    f.row_cnt = L.row_cnt;
-    f.req_cnt = L.req_cnt;
     f.recs = L.recs;
+    f.listed = L.listed;
     return f;
 }
 
@@ -174,7 +173,7 @@ int ss_tile_size(int dtype) {
 
 size_t ss_workspace_bytes(int rows, int V, int dtype) {
     if (rows < 0 || V < 1 || (dtype != SS_F32 && dtype != SS_BF16)) return 0;
-    return scratch_bytes(rows, V, dtype) + rec_bytes(rows) + 2 * cnt_bytes(rows);
+    return scratch_bytes(rows, V, dtype) + listed_bytes(rows) + rec_bytes(rows);
 }
 
 const char* ss_status_str(int status) {
@@ -201,14 +200,17 @@ int ss_sample_step(const void* logits, int dtype, int B, int V, int64_t ld, cons
     hipStream_t s = (hipStream_t)stream;
     const WsLayout W = ws_layout(ws, B, V, dtype);
     Stage1Params s1 = make_s1(logits, dtype, B, V, ld, 1, req, aux, W.scratch, nullptr);
-    FusedParams f = make_fused(s1, rng, MODE_SAMPLE, W);
+    s1.listed = W.listed;
+    s1.listed_rows = B;
+    launch_stage1(dtype, s1, s);
+    Stage2Params f = make_s2(s1, rng, MODE_SAMPLE, W);
     f.tokens = out_tokens;
     f.topk_ids = out_topk_ids;
     f.probs = out_probs;
     f.kept = out_kept;
     f.mass = out_mass;
     f.status = out_status;
-    launch_fused<MODE_SAMPLE>(dtype, f, s);
+    launch_stage2<MODE_SAMPLE>(dtype, f, s);
     return launched();
 }
 
@@ -228,14 +230,18 @@ int ss_verify_step(const void* target_logits, int dtype, int B, int gamma, int V
     hipStream_t s = (hipStream_t)stream;
     const WsLayout W = ws_layout(ws, rows, V, dtype);
     Stage1Params s1 = make_s1(target_logits, dtype, rows, V, ld, gamma + 1, req, aux, W.scratch, nullptr);
-    FusedParams f = make_fused(s1, rng, MODE_VERIFY, W);
+    s1.listed = W.listed;
+    s1.listed_rows = rows;
+    launch_stage1(dtype, s1, s);
+    Stage2Params f = make_s2(s1, rng, MODE_VERIFY, W);
     f.gamma = gamma;
     f.draft_ids = draft_ids;
     f.draft_probs = draft_probs;
     f.v_tokens = out_tokens;
     f.v_n_emit = out_n_emit;
     f.v_status = out_status;
-    launch_fused<MODE_VERIFY>(dtype, f, s);
+    launch_stage2<MODE_VERIFY>(dtype, f, s);
+    hipLaunchKernelGGL(verify_kernel, dim3((unsigned)B), dim3(VF_THREADS), 0, s, f);
     return launched();
 }
 
@@ -250,11 +256,12 @@ int ss_topk_step(const void* logits, int dtype, int B, int V, int64_t ld, int k,
     hipStream_t s = (hipStream_t)stream;
     const WsLayout W = ws_layout(ws, B, V, dtype);
     Stage1Params s1 = make_s1(logits, dtype, B, V, ld, 1, nullptr, nullptr, W.scratch, nullptr);
-    FusedParams f = make_fused(s1, nullptr, MODE_TOPK, W);
+    launch_stage1(dtype, s1, s);
+    Stage2Params f = make_s2(s1, nullptr, MODE_TOPK, W);
     f.topk_k = k;
     f.topk_ids = out_ids;
     f.topk_vals = out_vals;
-    launch_fused<MODE_TOPK>(dtype, f, s);
+    launch_stage2<MODE_TOPK>(dtype, f, s);
     return launched();
 }
 
@@ -287,8 +294,7 @@ int ss_tile_topk(const void* logits, int dtype, int rows, int V, int64_t ld, int
     hipStream_t s = (hipStream_t)stream;
     const WsLayout W = ws_layout(ws, rows, V, dtype);
     Stage1Params s1 = make_s1(logits, dtype, rows, V, ld, rows_per_req, req, aux, W.scratch, out_ids);
-    FusedParams f = make_fused(s1, nullptr, MODE_TILES, W);
-    launch_fused<MODE_TILES>(dtype, f, s);
+    launch_stage1(dtype, s1, s);
     return launched();
 }
 

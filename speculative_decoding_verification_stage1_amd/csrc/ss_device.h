@@ -172,4 +172,32 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
     return v;
 }
 
+// ---------------------------------------------------------------------------
+// lane exchange v(lane ^ J) without LDS traffic where the ISA allows:
+// DPP quad permutes for J = 1, 2; ds_swizzle (bit mode) for J = 4, 8;
+// the gfx950 row-swap permutes for J = 16, 32.
+// ---------------------------------------------------------------------------
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+    if constexpr (J == 1) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+    } else if constexpr (J == 2) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+    } else if constexpr (J == 4 || J == 8) {
+        return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (J << 10) | 0x1F);
+    } else if constexpr (J == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (lane_id() & 16) ? r[0] : r[1];
+    } else {
+        static_assert(J == 32, "xor distance");
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (lane_id() & 32) ? r[0] : r[1];
+    }
+}
+
+template <int J>
+__device__ __forceinline__ uint64_t xor_lane64(uint64_t v) {
+    return ((uint64_t)xor_lane<J>((uint32_t)(v >> 32)) << 32) | xor_lane<J>((uint32_t)v);
+}
+
 }  // namespace ssd

@@ -1,0 +1,51 @@
+// Kernel entry points.  A sampling step is two launches: Stage 1 over all
+// (row, tile) pairs, then Stage 2 with one workgroup per row; verification
+// adds one launch with one workgroup per request.  The kernel boundaries are
+// the only synchronisation between workgroups (the Stage-1 keys cross in
+// the workspace).
+#pragma once
+
+#include "ss_verify.h"
+
+namespace ssd {
+
+template <int DT>
+union S1KernelShared {
+    S1Shared<DT> tile;
+    S2Lists lists;
+};
+
+// Workgroups 0 .. listed_rows-1 compute each row's listed tokens (ranked
+// in Stage 2); the rest each own one (row, tile).  The listed workgroups
+// come first so they run alongside the streaming, not after it.
+template <int DT>
+__global__ __launch_bounds__(S1_THREADS) void stage1_kernel(Stage1Params P) {
+    using Key = typename S1Traits<DT>::Key;
+    __shared__ S1KernelShared<DT> shu;
+    const int tid = threadIdx.x;
+    if ((int)blockIdx.x < P.listed_rows) {
+        listed_row<DT>(P, P.listed, blockIdx.x, shu.lists);
+        return;
+    }
+    S1Shared<DT>& sh = shu.tile;
+    const int wg = blockIdx.x - P.listed_rows;
+    const int row = wg / P.Zv;
+    const int tile = wg - row * P.Zv;
+    stage1_tile<DT>(P, row, tile, sh);
+    if (tid < KMAX) {
+        const int64_t o = ((int64_t)row * P.Zv + tile) * KMAX + tid;
+        const Key k = sh.surv[tid];
+        ((Key*)P.scratch)[o] = k;
+        if (P.out_ids) {
+            int id = -1;
+            if (k != 0) {
+                const uint32_t lo = DT == SS_BF16 ? (0xFFFFu - ((uint32_t)k & 0xFFFFu))
+                                                  : (0xFFFFFFFFu - (uint32_t)k);
+                id = tile * S1Traits<DT>::BN + (int)lo;
+            }
+            P.out_ids[o] = id;
+        }
+    }
+}
+
+}  // namespace ssd

@@ -22,10 +22,12 @@
 // the fast path needs no per-element key transform.  Tiles where the test
 // does not apply (tau <= 0, a positive NaN, too many survivors) take the
 // general path: exact keys for every element and a bisection for the 128th
-// key.  Both paths end in a bitonic sort of the survivors in LDS.
+// key.  Both paths end in bitonic sorts of the survivors held in registers
+// (one 128-key chunk per wave) and a merge of the per-wave lists.
 #pragma once
 
 #include "ss_device.h"
+#include "ss_wavesort.h"
 
 namespace ssd {
 
@@ -63,6 +65,8 @@ struct Stage1Params {
     ss_aux aux;
     void* scratch;       // keys [rows][Zv][128]
     int32_t* out_ids;    // optional [rows][Zv][128]
+    uint64_t* listed;    // [rows][128] listed tokens' merge keys (sampling / verification)
+    int listed_rows;     // workgroups 0 .. listed_rows-1 compute them
     int aligned16;       // rows start on 16-byte boundaries
 };
 
@@ -110,27 +114,6 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
     return before + incl - v;
 }
 
-// Bitonic sort (descending) of buf[0..P), P a power of two.
-template <typename K, int NT>
-__device__ __forceinline__ void block_sort_desc(K* buf, int P) {
-    for (int k = 2; k <= P; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = threadIdx.x; i < P; i += NT) {
-                const int l = i ^ j;
-                if (l > i) {
-                    const K a = buf[i], b = buf[l];
-                    const bool desc = (i & k) == 0;
-                    if (desc ? (a < b) : (a > b)) {
-                        buf[i] = b;
-                        buf[l] = a;
-                    }
-                }
-            }
-            __syncthreads();
-        }
-    }
-}
-
 // Exact key of one element of a bf16 tile.
 __device__ __forceinline__ uint32_t key_bf16(uint32_t raw16, int local, bool present, bool allowed) {
     if (!present) return 0u;
@@ -146,6 +129,7 @@ __device__ __forceinline__ uint64_t key_f32(uint32_t raw, int local, bool presen
 template <int DT>
 struct S1Shared {
     typename S1Traits<DT>::Key surv[S1_SURV_CAP];
+    typename S1Traits<DT>::Key wl[S1_WAVES][KMAX];
     int listed[S1_LIST_CAP];
     int nlisted;
     int tau[S1_WAVES];
@@ -443,12 +427,31 @@ __device__ void stage1_tile(const Stage1Params& P, int row, int tile, S1Shared<D
             }
     }
 
-    // ---- sort the survivors (padded with "no token") and keep 128 ----
-    int Pn = KMAX;
-    while (Pn < nsurv) Pn <<= 1;
-    for (int i = nsurv + tid; i < Pn; i += S1_THREADS) surv[i] = 0;
+    // ---- the 128 best survivors, sorted: each wave sorts 128-key chunks in
+    // registers and keeps the best 128 of its chunks; wave 0 merges the
+    // per-wave lists (key 0 = no token) ----
+    __syncthreads();   // survivors complete
+    const int nchunks = (nsurv + KMAX - 1) / KMAX;
+    WList<Key> mine{0, 0};
+    for (int c = wave; c < nchunks; c += S1_WAVES) {
+        const int i0 = c * KMAX + lane, i1 = i0 + WAVE;
+        WList<Key> l{i0 < nsurv ? surv[i0] : (Key)0, i1 < nsurv ? surv[i1] : (Key)0};
+        l = wave_sort128(l);
+        mine = c == wave ? l : wave_merge(mine, l);
+    }
+    if (nchunks > 1) {
+        sh.wl[wave][lane] = mine.lo;
+        sh.wl[wave][lane + WAVE] = mine.hi;
+        __syncthreads();
+        if (wave == 0)
+            for (int w = 1; w < S1_WAVES && w < nchunks; ++w)
+                mine = wave_merge(mine, WList<Key>{sh.wl[w][lane], sh.wl[w][lane + WAVE]});
+    }
+    if (wave == 0) {
+        surv[lane] = mine.lo;
+        surv[lane + WAVE] = mine.hi;
+    }
     __syncthreads();
-    block_sort_desc<Key, S1_THREADS>(surv, Pn);
 }
 
 }  // namespace ssd

@@ -5,8 +5,11 @@
 // and Gumbel-max selection (section 3.1 "Probability truncation",
 // "Sampling").
 //
-// Stage 2 runs inside the workgroup that finished the row's last tile (see
-// ss_fused.h), so each row's merge overlaps other rows' Stage-1 streaming.
+// One workgroup per row.  Each wave folds a share of the row's tile lists
+// into one sorted list held in registers (two keys per lane: ranks lane and
+// lane + 64), with bitonic merge networks built from cross-lane shuffles;
+// wave 0 then folds the per-wave lists and the listed tokens and runs the
+// epilogue, so the whole stage needs two workgroup barriers.
 //
 // Tokens named by an active penalty or bias list never enter the tiles;
 // Stage 2 computes their processed logits directly (gather + the list
@@ -16,10 +19,9 @@
 #pragma once
 
 #include "ss_stage1.h"
+#include "ss_wavesort.h"
 
 namespace ssd {
-
-constexpr int S2_GROUP = 8;   // tile lists merged per LDS pass
 
 enum { MODE_TILES = 0, MODE_SAMPLE = 1, MODE_VERIFY = 2, MODE_TOPK = 3 };
 
@@ -36,13 +38,12 @@ struct RowRec {
     int32_t pad[3];
 };
 
-struct FusedParams {
+struct Stage2Params {
     Stage1Params s1;
     const ss_rng* rng;
+    const uint64_t* listed;   // [rows][128] sorted merge keys of listed tokens
     int mode;
     int topk_k;
-    uint32_t* row_cnt;   // [rows] tiles finished per row (kept at 0 between calls)
-    uint32_t* req_cnt;   // [requests] rows finished per request (verification)
     // sampling outputs
     int32_t* tokens;
     int32_t* topk_ids;
@@ -63,12 +64,7 @@ struct FusedParams {
 };
 
 struct S2Shared {
-    uint64_t buf[S2_GROUP][KMAX];
-    uint64_t acc[KMAX];
-    uint64_t lkeys[S1_LIST_CAP];
-    float redf[S1_WAVES];
-    int redi[S1_WAVES];
-    float pd;
+    uint64_t wl[4][2][WAVE];   // per-wave folded lists (lo, hi)
 };
 
 struct RowParams {
@@ -166,56 +162,6 @@ __device__ __forceinline__ float key_z(uint64_t k) {
     return k ? unord32((uint32_t)(k >> 32)) : bitsf(F32_NINF_BITS);
 }
 
-// Merge sorted-descending lists A and B (128 each) into A: the elementwise
-// max of A and reversed B is bitonic and holds the 128 best; seven
-// half-cleaner steps sort it.  `npairs` merges run together; pair m uses
-// lists slot(m) and slot(m) + stride.
-__device__ __forceinline__ void merge_level(uint64_t (*buf)[KMAX], int npairs, int stride) {
-    for (int idx = threadIdx.x; idx < npairs * KMAX; idx += S1_THREADS) {
-        const int m = idx / KMAX, i = idx % KMAX;
-        uint64_t* A = buf[m * 2 * stride];
-        const uint64_t* Bl = buf[m * 2 * stride + stride];
-        const uint64_t a = A[i], bb = Bl[KMAX - 1 - i];
-        A[i] = a > bb ? a : bb;
-    }
-    __syncthreads();
-    for (int j = KMAX / 2; j > 0; j >>= 1) {
-        for (int idx = threadIdx.x; idx < npairs * (KMAX / 2); idx += S1_THREADS) {
-            const int m = idx / (KMAX / 2), q = idx % (KMAX / 2);
-            uint64_t* A = buf[m * 2 * stride];
-            const int i = (q / j) * 2 * j + (q % j);
-            const uint64_t a = A[i], c = A[i + j];
-            if (a < c) {
-                A[i] = c;
-                A[i + j] = a;
-            }
-        }
-        __syncthreads();
-    }
-}
-
-// acc <- the 128 best of acc and B (both sorted descending).
-__device__ __forceinline__ void merge_into(uint64_t* acc, const uint64_t* B) {
-    if (threadIdx.x < KMAX) {
-        const int i = threadIdx.x;
-        const uint64_t a = acc[i], bb = B[KMAX - 1 - i];
-        acc[i] = a > bb ? a : bb;
-    }
-    __syncthreads();
-    for (int j = KMAX / 2; j > 0; j >>= 1) {
-        if (threadIdx.x < KMAX / 2) {
-            const int q = threadIdx.x;
-            const int i = (q / j) * 2 * j + (q % j);
-            const uint64_t a = acc[i], c = acc[i + j];
-            if (a < c) {
-                acc[i] = c;
-                acc[i + j] = a;
-            }
-        }
-        __syncthreads();
-    }
-}
-
 // Wave-wide best (score desc, id asc); lanes with ok=false do not compete.
 __device__ __forceinline__ int wave_argmax(float s, int id, bool ok) {
     float bs = s;
@@ -237,110 +183,238 @@ __device__ __forceinline__ float readlane_f(float v, int l) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-// The row's 128 best (merge keys, descending) into sh.acc.  Ends with a barrier.
-template <int DT>
-__device__ void row_merge(const FusedParams& F, const RowParams& rp, int row, int b, S2Shared& sh) {
-    using Key = typename S1Traits<DT>::Key;
-    const Stage1Params& P = F.s1;
-    const int tid = threadIdx.x;
+using WL64 = WList<uint64_t>;
 
-    // ---- listed tokens: exact processed logits, one sorted list ----
-    const int np = rp.valid ? rp.n_prior : 0;
-    const int nb = rp.valid ? rp.n_bias : 0;
+// The row's side lists, staged in LDS by the listed-token workgroup.
+struct S2Lists {
+    int32_t pid[256];
+    int32_t pct[256];
+    int32_t bid[256];
+    float bval[256];
+};
+
+// Listed tokens: exact processed logits of the first
+// valid entry of every id named by an active list, sorted; at most 510
+// entries, 128 per pass (two per lane).
+//
+// One pass over each list counts, per token, its matching entries and
+// remembers one of them.  The repetition penalty is the same map for every
+// entry, so m matching entries apply it m times.  Frequency/presence and
+// bias differ per entry and must be applied in list order; with one
+// matching entry (the usual case) that is a single subtraction / addition,
+// and tokens with several entries take a sequential walk of the list.
+template <int DT>
+__device__ WL64 listed_list(const Stage1Params& P, const RowParams& rp, int row, int np, int nb,
+                            const S2Lists& L) {
+    const int lane = lane_id();
     const int ncomb = np + nb;
-    if (tid < KMAX) sh.acc[tid] = 0ull;
-    if (ncomb > 0) {
-        const int32_t* pid = P.aux.prior_ids + (int64_t)b * P.aux.prior_stride;
-        const int32_t* pct = P.aux.prior_cnt + (int64_t)b * P.aux.prior_stride;
-        const int32_t* bid = P.aux.bias_ids + (int64_t)b * P.aux.bias_stride;
-        const float* bvl = P.aux.bias_val + (int64_t)b * P.aux.bias_stride;
-        const bool grammar = (rp.flags & SS_GRAMMAR) != 0;
-        for (int t0 = 0; t0 < ncomb; t0 += S1_THREADS) {   // uniform loop
-            const int t = t0 + tid;
-            int id = -1;
-            bool ok = false;
-            if (t < np) {
-                id = pid[t];
-                ok = pct[t] >= 1 && id >= 0 && id < P.V;
-            } else if (t < ncomb) {
-                id = bid[t - np];
-                ok = id >= 0 && id < P.V;
+    const bool grammar = (rp.flags & SS_GRAMMAR) != 0;
+    const bool do_rep = (rp.flags & SS_REP) != 0;
+    const bool do_fp = (rp.flags & SS_FREQPRES) != 0;
+    const bool do_bias = (rp.flags & SS_BIAS) != 0;
+    WL64 acc{0ull, 0ull};
+    for (int c0 = 0; c0 < ncomb; c0 += 2 * WAVE) {   // uniform
+        int t[2], id[2], mp[2], ip[2], mb[2], ib[2];
+        bool ok[2], dup[2];
+        float z[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            t[h] = c0 + h * WAVE + lane;
+            id[h] = -1;
+            ok[h] = false;
+            if (t[h] < np) {
+                id[h] = L.pid[t[h]];
+                ok[h] = L.pct[t[h]] >= 1 && id[h] >= 0 && id[h] < P.V;
+            } else if (t[h] < ncomb) {
+                id[h] = L.bid[t[h] - np];
+                ok[h] = id[h] >= 0 && id[h] < P.V;
             }
-            float z = 0.0f;
-            bool allowed = true;
-            if (ok) {
-                if (DT == SS_BF16) z = widen_bf16(((const uint16_t*)P.logits)[(int64_t)row * P.ld + id]);
-                else z = ((const float*)P.logits)[(int64_t)row * P.ld + id];
-                if (grammar)
-                    allowed = (P.aux.bitmask[(int64_t)row * P.aux.bitmask_stride + (id >> 5)] >> (id & 31)) & 1u;
+            z[h] = 0.0f;
+            if (ok[h]) {
+                if (DT == SS_BF16) z[h] = widen_bf16(((const uint16_t*)P.logits)[(int64_t)row * P.ld + id[h]]);
+                else z[h] = ((const float*)P.logits)[(int64_t)row * P.ld + id[h]];
+                if (grammar &&
+                    !((P.aux.bitmask[(int64_t)row * P.aux.bitmask_stride + (id[h] >> 5)] >> (id[h] & 31)) & 1u))
+                    z[h] = bitsf(F32_NINF_BITS);
             }
-            if (!allowed) z = bitsf(F32_NINF_BITS);
-            // the list entries are the same for every lane: uniform loads
-            bool dup = false;
-            const bool do_rep = (rp.flags & SS_REP) != 0;
-#pragma unroll 8
-            for (int u = 0; u < np; ++u) {
-                const bool m = pct[u] >= 1 && pid[u] == id;
-                dup |= m && u < t;
-                if (do_rep && m) z = (z > 0.0f) ? z / rp.rep : z * rp.rep;
+            mp[h] = 0;
+            ip[h] = 0;
+            mb[h] = 0;
+            ib[h] = 0;
+            dup[h] = false;
+        }
+        // one pass over each list; entries are LDS broadcasts
+#pragma unroll 4
+        for (int u = 0; u < np; ++u) {
+            const int iu = L.pid[u];
+            const bool valid = L.pct[u] >= 1;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const bool m = valid && iu == id[h];
+                mp[h] += m;
+                ip[h] = m ? u : ip[h];
+                dup[h] |= m && u < t[h];
             }
-            if (rp.flags & SS_FREQPRES) {
-#pragma unroll 8
-                for (int u = 0; u < np; ++u) {
-                    const int c = pct[u];
-                    if (c >= 1 && pid[u] == id) {
-                        const float pen = (float)c * rp.freq + rp.pres;
-                        z = z - pen;
+        }
+#pragma unroll 4
+        for (int u = 0; u < nb; ++u) {
+            const int iu = L.bid[u];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const bool m = iu == id[h];
+                mb[h] += m;
+                ib[h] = m ? u : ib[h];
+                dup[h] |= m && np + u < t[h];
+            }
+        }
+        uint64_t key[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float zz = z[h];
+            if (ok[h] && !dup[h]) {
+                if (do_rep)
+                    for (int r = 0; r < mp[h]; ++r) zz = (zz > 0.0f) ? zz / rp.rep : zz * rp.rep;
+                if (do_fp) {
+                    if (mp[h] == 1) {
+                        const float pen = (float)L.pct[ip[h]] * rp.freq + rp.pres;
+                        zz = zz - pen;
+                    } else if (mp[h] > 1) {
+                        for (int u = 0; u < np; ++u)
+                            if (L.pct[u] >= 1 && L.pid[u] == id[h]) {
+                                const float pen = (float)L.pct[u] * rp.freq + rp.pres;
+                                zz = zz - pen;
+                            }
                     }
                 }
+                if (do_bias) {
+                    if (mb[h] == 1) zz = zz + L.bval[ib[h]];
+                    else if (mb[h] > 1)
+                        for (int u = 0; u < nb; ++u)
+                            if (L.bid[u] == id[h]) zz = zz + L.bval[u];
+                }
             }
-#pragma unroll 8
-            for (int u = 0; u < nb; ++u) {
-                const bool m = bid[u] == id;
-                dup |= m && np + u < t;
-                if (m) z = z + bvl[u];
-            }
-            if (t < ncomb)
-                sh.lkeys[t] = (ok && !dup)
-                                  ? (((uint64_t)ord32(canon(z)) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id))
-                                  : 0ull;
+            key[h] = (ok[h] && !dup[h])
+                         ? (((uint64_t)ord32(canon(zz)) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id[h]))
+                         : 0ull;
         }
-        int Pl = KMAX;
-        while (Pl < ncomb) Pl <<= 1;
-        for (int t = ncomb + tid; t < Pl; t += S1_THREADS) sh.lkeys[t] = 0ull;
-        __syncthreads();
-        block_sort_desc<uint64_t, S1_THREADS>(sh.lkeys, Pl);
-        if (tid < KMAX) sh.acc[tid] = sh.lkeys[tid];
+        const WL64 srt = wave_sort128(WL64{key[0], key[1]});
+        acc = c0 == 0 ? srt : wave_merge(acc, srt);
+    }
+    return acc;
+}
+
+// One workgroup of the Stage-1 launch per row computes the row's listed
+// tokens (wave 0) and stores the best 128 as merge keys; it runs alongside
+// the tile workgroups, so Stage 2 only has to load one more sorted list.
+template <int DT>
+__device__ void listed_row(const Stage1Params& P, uint64_t* out, int row, S2Lists& lists) {
+    const int b = row / P.rows_per_req;
+    const RowParams rp = row_params(P, b);
+    const int np = rp.valid ? rp.n_prior : 0;
+    const int nb = rp.valid ? rp.n_bias : 0;
+    if (np + nb == 0) return;   // block-uniform; Stage 2 skips rows without lists
+    const int32_t* pid = P.aux.prior_ids + (int64_t)b * P.aux.prior_stride;
+    const int32_t* pct = P.aux.prior_cnt + (int64_t)b * P.aux.prior_stride;
+    const int32_t* bid = P.aux.bias_ids + (int64_t)b * P.aux.bias_stride;
+    const float* bvl = P.aux.bias_val + (int64_t)b * P.aux.bias_stride;
+    for (int u = threadIdx.x; u < np; u += blockDim.x) {
+        lists.pid[u] = pid[u];
+        lists.pct[u] = pct[u];
+    }
+    for (int u = threadIdx.x; u < nb; u += blockDim.x) {
+        lists.bid[u] = bid[u];
+        lists.bval[u] = bvl[u];
     }
     __syncthreads();
+    if (threadIdx.x >= WAVE) return;
+    const WL64 l = listed_list<DT>(P, rp, row, np, nb, lists);
+    const int lane = lane_id();
+    out[(int64_t)row * KMAX + lane] = l.lo;
+    out[(int64_t)row * KMAX + lane + WAVE] = l.hi;
+}
 
-    // ---- tile lists: load a group, merge it down to one list, fold into acc ----
+constexpr int S2_THREADS = 256;
+constexpr int S2_WAVES = S2_THREADS / WAVE;
+constexpr int S2_PREFETCH = 4;   // tile lists per wave requested up front
+
+// The row's 128 best as a wave-0 register list.  Every load is issued
+// before any merging; one workgroup barrier.
+template <int DT>
+__device__ WL64 row_merge(const Stage2Params& F, const RowParams& rp, int row, S2Shared& sh) {
+    using Key = typename S1Traits<DT>::Key;
+    const Stage1Params& P = F.s1;
+    const int lane = lane_id();
+    const int wave = threadIdx.x / WAVE;
+    const bool has_listed = rp.valid && rp.n_prior + rp.n_bias > 0;
+
     const Key* sc = (const Key*)P.scratch + (int64_t)row * P.Zv * KMAX;
-    for (int g0 = 0; g0 < P.Zv; g0 += S2_GROUP) {
-        const int G = min(S2_GROUP, P.Zv - g0);
-        for (int idx = tid; idx < G * KMAX; idx += S1_THREADS) {
-            const int l = idx / KMAX, i = idx % KMAX;
-            sh.buf[l][i] = merge_key<DT>(sc[(int64_t)(g0 + l) * KMAX + i], g0 + l);
-        }
-        __syncthreads();
-        for (int s = 1; s < G; s <<= 1) {
-            const int npairs = (G - s + 2 * s - 1) / (2 * s);   // m with m*2s + s < G
-            merge_level(sh.buf, npairs, s);
-        }
-        merge_into(sh.acc, sh.buf[0]);
+    Key pre_lo[S2_PREFETCH], pre_hi[S2_PREFETCH];
+#pragma unroll
+    for (int i = 0; i < S2_PREFETCH; ++i) {
+        const int t = wave + S2_WAVES * i;
+        pre_lo[i] = t < P.Zv ? sc[(int64_t)t * KMAX + lane] : (Key)0;
+        pre_hi[i] = t < P.Zv ? sc[(int64_t)t * KMAX + lane + WAVE] : (Key)0;
     }
+    WL64 listed{0ull, 0ull};
+    if (wave == 0 && has_listed) {
+        const uint64_t* lk = F.listed + (int64_t)row * KMAX;
+        listed = WL64{lk[lane], lk[lane + WAVE]};
+    }
+
+    // fold this wave's tiles: four at a time as a tree
+    auto tl = [&](int i) -> WL64 {
+        const int t = wave + S2_WAVES * i;
+        return WL64{merge_key<DT>(pre_lo[i], t), merge_key<DT>(pre_hi[i], t)};
+    };
+    const int mine_n = wave < P.Zv ? (P.Zv - wave + S2_WAVES - 1) / S2_WAVES : 0;
+    WL64 mine{0ull, 0ull};
+    if (mine_n >= 1) mine = tl(0);
+    if (mine_n >= 2) {
+        WL64 a = tl(1);
+        if (mine_n >= 3) {
+            WL64 c = tl(2);
+            if (mine_n >= 4) c = wave_merge(c, tl(3));
+            mine = wave_merge(mine, c);   // pairs (0,1) and (2,3) are independent
+        }
+        mine = wave_merge(mine, a);
+    }
+    for (int t = wave + S2_WAVES * S2_PREFETCH; t < P.Zv; t += S2_WAVES)   // long vocabularies
+        mine = wave_merge(mine, WL64{merge_key<DT>(sc[(int64_t)t * KMAX + lane], t),
+                                     merge_key<DT>(sc[(int64_t)t * KMAX + lane + WAVE], t)});
+    sh.wl[wave][0][lane] = mine.lo;
+    sh.wl[wave][1][lane] = mine.hi;
+    __syncthreads();
+
+    WL64 res{0ull, 0ull};
+    if (wave == 0) {
+        const int nw = min(S2_WAVES, P.Zv);
+        auto wl = [&](int w) -> WL64 { return WL64{sh.wl[w][0][lane], sh.wl[w][1][lane]}; };
+        WL64 x = mine;
+        if (has_listed) x = wave_merge(x, listed);
+        WL64 y{0ull, 0ull};
+        if (nw >= 2) y = wl(1);
+        if (nw >= 3) {
+            WL64 z = wl(2);
+            if (nw >= 4) z = wave_merge(z, wl(3));
+            y = wave_merge(y, z);
+        }
+        res = nw >= 2 ? wave_merge(x, y) : x;
+    }
+    return res;
 }
 
 // Epilogue on wave 0 (ranks k = lane and lane + 64).  Writes the mode's
 // outputs for the row.  Uses no barrier.
 template <int DT>
-__device__ void row_epilogue(const FusedParams& F, const RowParams& rp, int row, int b, S2Shared& sh) {
+__device__ void row_epilogue(const Stage2Params& F, const RowParams& rp, int row, int b, const WL64& best,
+                             const ss_rng rg) {
     const Stage1Params& P = F.s1;
     const int lane = lane_id();
-    const uint64_t k_lo = sh.acc[lane], k_hi = sh.acc[lane + 64];
+    const uint64_t k_lo = best.lo, k_hi = best.hi;
     const int id_lo = key_id(k_lo), id_hi = key_id(k_hi);
     const float z_lo = key_z(k_lo), z_hi = key_z(k_hi);
-    const uint64_t k0 = sh.acc[0];
+    const uint64_t k0 = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)k_lo) |
+                        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(k_lo >> 32)) << 32);
     const int id0 = key_id(k0);
     const float z0 = key_z(k0);
     const float NINF = bitsf(F32_NINF_BITS);
@@ -390,16 +464,20 @@ __device__ void row_epilogue(const FusedParams& F, const RowParams& rp, int row,
             v_hi = vscale(z_hi);
             e_hi = exp_fixed(v_hi - m);
         }
-        // running sums E_k = e_0 + ... + e_{k-1}, left to right
+        // running sums E_k = e_0 + ... + e_{k-1}, left to right (ranks past
+        // K hold e = 0, which leaves E unchanged)
         float E = 0.0f, E_lo = 0.0f, E_hi = 0.0f;
-        const int k1 = min(K, 64);
-        for (int k = 0; k < k1; ++k) {
-            if (lane == k) E_lo = E;
+#pragma unroll
+        for (int k = 0; k < WAVE; ++k) {
+            E_lo = lane == k ? E : E_lo;
             E = E + readlane_f(e_lo, k);
         }
-        for (int k = 64; k < K; ++k) {
-            if (lane == k - 64) E_hi = E;
-            E = E + readlane_f(e_hi, k - 64);
+        if (K > WAVE) {
+#pragma unroll
+            for (int k = 0; k < WAVE; ++k) {
+                E_hi = lane == k ? E : E_hi;
+                E = E + readlane_f(e_hi, k);
+            }
         }
         Z = E;
         int n_p = K, n_m = K;
@@ -425,7 +503,6 @@ __device__ void row_epilogue(const FusedParams& F, const RowParams& rp, int row,
             c1 = (uint32_t)row;
             c2 = 0u;
         }
-        const ss_rng rg = *F.rng;
         float s_lo = 0.0f, s_hi = 0.0f;
         const bool c_lo = lane < n, c_hi = lane + 64 < n;
         if (c_lo) s_lo = v_lo + gumbel_noise(rg.seed, rg.offset, (uint32_t)id_lo, c1, c2);
@@ -473,6 +550,19 @@ __device__ void row_epilogue(const FusedParams& F, const RowParams& rp, int row,
             rec->greedy = rp.greedy;
         }
     }
+}
+
+template <int DT, int MODE>
+__global__ __launch_bounds__(S2_THREADS) void stage2_kernel(Stage2Params F) {
+    __shared__ S2Shared sh;
+    const int row = blockIdx.x;
+    const int b = row / F.s1.rows_per_req;
+    ss_rng rg{0ull, 0ull};
+    if (F.rng) rg = *F.rng;   // requested before the merge work
+    const RowParams rp = row_params(F.s1, b);
+    const WL64 best = row_merge<DT>(F, rp, row, sh);
+    if (threadIdx.x >= WAVE) return;
+    row_epilogue<DT>(F, rp, row, b, best, rg);
 }
 
 }  // namespace ssd

@@ -1,118 +1,131 @@
 // Speculative verification (SonicSampler section 3.1 "Speculative
 // verification"; rejection-sampling rules of the decoding notes, "Rejection
-// Sampler") for one request, on one wave.  Stage 2 has already reduced
-// every target row to its kept candidates and truncated, renormalised
-// probabilities p_j, so draft probabilities q_j are only gathered at the
-// draft token and at the <= 128 kept candidates; the residual
-// max(0, p_j - q_j) vanishes outside them.
+// Sampler").  Stage 2 has already reduced every target row to its kept
+// candidates and truncated, renormalised probabilities p_j, so draft
+// probabilities q_j are only gathered at the draft token and at the <= 128
+// kept candidates; the residual max(0, p_j - q_j) vanishes outside them.
+//
+// One workgroup per request.  What happens at position j depends only on
+// position j's data (accept or not, and the residual draw if not), so the
+// waves evaluate all positions at once; one lane then walks the positions
+// in order to emit the accepted prefix and the first rejection's draw (or
+// the bonus token).
 #pragma once
 
 #include "ss_stage2.h"
 
 namespace ssd {
 
-// Runs on wave 0 of the workgroup; lanes hold candidate ranks lane and
-// lane + 64.  Uses no barrier.
-__device__ void verify_request(const FusedParams& F, int b) {
+constexpr int VF_WAVES = 8;
+constexpr int VF_THREADS = VF_WAVES * WAVE;
+
+__global__ __launch_bounds__(VF_THREADS) void verify_kernel(Stage2Params F) {
+    __shared__ int s_accept[SS_GAMMA_MAX + 1];
+    __shared__ int s_token[SS_GAMMA_MAX + 1];
+    __shared__ int s_status[SS_GAMMA_MAX + 1];
+    const int b = blockIdx.x;
     const int lane = lane_id();
+    const int wave = threadIdx.x / WAVE;
     const int G = F.gamma;
     const int V = F.s1.V;
     const ss_rng rg = *F.rng;
-    int32_t* out = F.v_tokens + (int64_t)b * (G + 1);
-    if (lane == 0)
-        for (int j = 0; j <= G; ++j) out[j] = -1;
-
     const RowRec* r0 = F.recs + (int64_t)b * (G + 1);
-    int emitted = 0;
-    int st;
-    if (r0->status == SS_ROW_INVALID) {
-        st = SS_ROW_INVALID;
-    } else {
-        st = r0->status == SS_ROW_TOPK_CLAMPED ? SS_ROW_TOPK_CLAMPED : SS_ROW_OK;
-        for (int j = 0; j <= G; ++j) {
-            const RowRec* rec = r0 + j;
-            if (rec->status == SS_ROW_ALL_MASKED) {
-                st = SS_ROW_ALL_MASKED;
-                break;
-            }
-            if (j == G) {   // every draft accepted: bonus token
-                if (lane == 0) out[emitted] = rec->token;
-                ++emitted;
-                break;
-            }
+
+    for (int j = wave; j <= G; j += VF_WAVES) {
+        const RowRec* rec = r0 + j;
+        const int status = rec->status;
+        int accept = 0, token = -1;
+        const bool live = status == SS_ROW_OK || status == SS_ROW_TOPK_CLAMPED;
+        if (live && j == G) {          // bonus token
+            token = rec->token;
+            accept = 1;
+        } else if (live && rec->greedy) {
             const int d = F.draft_ids[(int64_t)b * G + j];
-            if (rec->greedy) {
-                const int a = rec->ids[0];
-                if (lane == 0) out[emitted] = d == a ? d : a;
-                ++emitted;
-                if (d == a) continue;
-                break;
-            }
+            token = rec->ids[0];
+            accept = d == token;
+        } else if (live) {
+            const int d = F.draft_ids[(int64_t)b * G + j];
             const int n = rec->n;
             const float* q = F.draft_probs + ((int64_t)b * G + j) * V;
             const int id_lo = lane < n ? rec->ids[lane] : -1;
             const int id_hi = lane + 64 < n ? rec->ids[lane + 64] : -1;
             const float p_lo = lane < n ? rec->p[lane] : 0.0f;
             const float p_hi = lane + 64 < n ? rec->p[lane + 64] : 0.0f;
+            const float q_lo = id_lo >= 0 ? q[id_lo] : 0.0f;
+            const float q_hi = id_hi >= 0 ? q[id_hi] : 0.0f;
+            const float qd = (d >= 0 && d < V) ? q[d] : 0.0f;
             // p_j(d): the kept candidate equal to d, if any (ids are unique)
             float pd = 0.0f;
             const uint64_t m_lo = __ballot(id_lo == d && id_lo >= 0);
             const uint64_t m_hi = __ballot(id_hi == d && id_hi >= 0);
             if (m_lo) pd = readlane_f(p_lo, __builtin_ctzll(m_lo));
             else if (m_hi) pd = readlane_f(p_hi, __builtin_ctzll(m_hi));
-            const float qd = (d >= 0 && d < V) ? q[d] : 0.0f;
             const float u = unit_open(philox_w0(rg.seed, rg.offset, 0u, (uint32_t)b, (1u << 24) | (uint32_t)j));
-            if (qd > 0.0f && u * qd <= pd) {
-                if (lane == 0) out[emitted] = d;
-                ++emitted;
-                continue;
-            }
-            // rejected: draw from norm(max(0, p - q)) by Gumbel-max on ln(rho)
-            const uint32_t c2 = (2u << 24) | (uint32_t)j;
-            float s_lo = 0.0f, s_hi = 0.0f;
-            bool ok_lo = false, ok_hi = false;
-            if (id_lo >= 0) {
-                const float rho = p_lo - q[id_lo];
-                if (rho > 0.0f) {
-                    ok_lo = true;
-                    s_lo = log_fixed(rho) + gumbel_noise(rg.seed, rg.offset, (uint32_t)id_lo, (uint32_t)b, c2);
+            accept = qd > 0.0f && u * qd <= pd;
+            if (!accept) {
+                // draw from norm(max(0, p - q)) by Gumbel-max on ln(rho)
+                const uint32_t c2 = (2u << 24) | (uint32_t)j;
+                const float g_lo =
+                    id_lo >= 0 ? gumbel_noise(rg.seed, rg.offset, (uint32_t)id_lo, (uint32_t)b, c2) : 0.0f;
+                const float g_hi =
+                    id_hi >= 0 ? gumbel_noise(rg.seed, rg.offset, (uint32_t)id_hi, (uint32_t)b, c2) : 0.0f;
+                const float rho_lo = p_lo - q_lo, rho_hi = p_hi - q_hi;
+                const bool ok_lo = id_lo >= 0 && rho_lo > 0.0f;
+                const bool ok_hi = id_hi >= 0 && rho_hi > 0.0f;
+                float s = ok_lo ? log_fixed(rho_lo) + g_lo : 0.0f;
+                int id = ok_lo ? id_lo : -1;
+                if (ok_hi) {
+                    const float sh = log_fixed(rho_hi) + g_hi;
+                    if (id < 0 || sh > s || (sh == s && id_hi < id)) {
+                        s = sh;
+                        id = id_hi;
+                    }
+                }
+                token = wave_argmax(s, id, id >= 0);
+                if (token < 0) {   // p <= q on every kept candidate: draw from p
+                    float s2 = id_lo >= 0 ? rec->v[lane] + g_lo : 0.0f;
+                    int i2 = id_lo;
+                    if (id_hi >= 0) {
+                        const float sh = rec->v[lane + 64] + g_hi;
+                        if (i2 < 0 || sh > s2 || (sh == s2 && id_hi < i2)) {
+                            s2 = sh;
+                            i2 = id_hi;
+                        }
+                    }
+                    token = wave_argmax(s2, i2, i2 >= 0);
                 }
             }
-            if (id_hi >= 0) {
-                const float rho = p_hi - q[id_hi];
-                if (rho > 0.0f) {
-                    ok_hi = true;
-                    s_hi = log_fixed(rho) + gumbel_noise(rg.seed, rg.offset, (uint32_t)id_hi, (uint32_t)b, c2);
-                }
-            }
-            float s = s_lo;
-            int id = ok_lo ? id_lo : -1;
-            if (ok_hi && (id < 0 || s_hi > s || (s_hi == s && id_hi < id))) {
-                s = s_hi;
-                id = id_hi;
-            }
-            int tok = wave_argmax(s, id, id >= 0);
-            if (tok < 0) {   // p <= q on every kept candidate: draw from p
-                s_lo = 0.0f;
-                s_hi = 0.0f;
-                if (id_lo >= 0) s_lo = rec->v[lane] + gumbel_noise(rg.seed, rg.offset, (uint32_t)id_lo, (uint32_t)b, c2);
-                if (id_hi >= 0)
-                    s_hi = rec->v[lane + 64] + gumbel_noise(rg.seed, rg.offset, (uint32_t)id_hi, (uint32_t)b, c2);
-                s = s_lo;
-                id = id_lo;
-                if (id_hi >= 0 && (id < 0 || s_hi > s || (s_hi == s && id_hi < id))) {
-                    s = s_hi;
-                    id = id_hi;
-                }
-                tok = wave_argmax(s, id, id >= 0);
-            }
-            if (lane == 0) out[emitted] = tok;
-            ++emitted;
-            break;
+        }
+        if (lane == 0) {
+            s_accept[j] = accept;
+            s_token[j] = token;
+            s_status[j] = status;
         }
     }
-    if (st == SS_ROW_INVALID) emitted = 0;
-    if (lane == 0) {
+    __syncthreads();
+
+    if (threadIdx.x == 0) {
+        int32_t* out = F.v_tokens + (int64_t)b * (G + 1);
+        int emitted = 0;
+        int st;
+        if (s_status[0] == SS_ROW_INVALID) {
+            st = SS_ROW_INVALID;
+        } else {
+            st = s_status[0] == SS_ROW_TOPK_CLAMPED ? SS_ROW_TOPK_CLAMPED : SS_ROW_OK;
+            for (int j = 0; j <= G; ++j) {
+                if (s_status[j] == SS_ROW_ALL_MASKED) {
+                    st = SS_ROW_ALL_MASKED;
+                    break;
+                }
+                if (j < G && s_accept[j]) {
+                    out[emitted++] = F.draft_ids[(int64_t)b * G + j];
+                    continue;
+                }
+                out[emitted++] = s_token[j];   // first rejection's draw, or the bonus
+                break;
+            }
+        }
+        for (int j = emitted; j <= G; ++j) out[j] = -1;
         F.v_n_emit[b] = emitted;
         if (F.v_status) F.v_status[b] = st;
     }

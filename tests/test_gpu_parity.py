@@ -237,6 +237,26 @@ def test_heavy_lists():
     sample_parity(W.SampleWorkload("lists-f32", W.DTYPE_F32, W.bf16_bits_to_f32(x), req), seed=6)
 
 
+def test_workspace_reuse_alternating_inputs():
+    """One workspace and one set of output buffers reused across calls with
+    different inputs: every call must match the oracle for its own input."""
+    lib = L()
+    wls = [W.workload_mixed(2, 8, 40000, grammar=True), W.workload_mixed(1, 8, 40000, grammar=False)]
+    xs = [_dev_logits(w.logits, w.dtype) for w in wls]
+    dreqs = [lib.DeviceRequests(w.req) for w in wls]
+    refs = [oracle.sample(w.logits, w.dtype, w.req, seed=3, offset=1, threads=8) for w in wls]
+    ws = lib.workspace(8, 40000, W.DTYPE_BF16)
+    toks = torch.zeros(8, dtype=torch.int32, device="cuda")
+    ids = torch.zeros((8, 128), dtype=torch.int32, device="cuda")
+    rng = lib.make_rng(3, 1)
+    for i in range(6):
+        k = i % 2
+        lib.ss_sample_step(xs[k], dreqs[k], rng, toks, ids, ws=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(toks.cpu().numpy(), refs[k]["tokens"]), i
+        assert np.array_equal(ids.cpu().numpy(), refs[k]["topk_ids"]), i
+
+
 def test_determinism_repeated_runs():
     wl = W.workload_mixed(2, 32, 131072, grammar=True)
     a = run_sample(wl.logits, wl.dtype, wl.req, 1, 2)
