@@ -63,6 +63,15 @@ __device__ __forceinline__ uint32_t k16_to_k32(uint32_t k16) {
 
 __device__ __forceinline__ float widen_bf16(uint32_t h) { return bitsf((h & 0xFFFFu) << 16); }
 
+// Global-memory view of a pointer: loads through it are global_load (vector
+// memory only) instead of flat loads, which also hold the LDS counter.
+typedef uint32_t vu32x4 __attribute__((ext_vector_type(4)));   // 16-byte load unit
+
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T* gmem(const T* p) {
+    return (const __attribute__((address_space(1))) T*)p;
+}
+
 // ---------------------------------------------------------------------------
 // Philox4x32-10 (Salmon et al., SC'11): per round, words 0 and 2 are
 // multiplied by the round constants, the high halves are mixed with words 1

@@ -13,17 +13,22 @@
 // token" (tail of a short tile).  Ties in value therefore rank the lower
 // token id first, the order used throughout.
 //
-// Selection is exact.  Fast path: each lane takes the maximum of its
-// elements; each wave finds the 32nd largest of its 64 lane maxima; the
-// smallest of the four is a threshold tau with at least 128 tokens at or
-// above it, so the tile's 128 best are among the survivors x >= tau
-// (typically ~200 of 16384).  On raw bit patterns read as signed integers
-// the comparison x >= tau agrees with the float order whenever tau > 0, so
-// the fast path needs no per-element key transform.  Tiles where the test
-// does not apply (tau <= 0, a positive NaN, too many survivors) take the
-// general path: exact keys for every element and a bisection for the 128th
-// key.  Both paths end in bitonic sorts of the survivors held in registers
-// (one 128-key chunk per wave) and a merge of the per-wave lists.
+// Selection is exact.  Fast path: raw bit patterns read as signed integers
+// order like the floats they hold whenever the threshold below is positive,
+// so no per-element key transform is needed.  Grammar-masked elements and
+// those past the end of V take the smallest pattern.  Each lane takes the
+// maximum of every 16-byte chunk and of its whole slice; each wave finds the
+// k-th largest of its 64 lane maxima, k = 32 + ceil(L/4) for L listed
+// tokens in the tile, and the smallest of the four is a threshold tau with
+// at least 128 + L tokens at or above it - so the 128 best unlisted tokens
+// are all at or above tau.  Chunks whose maximum reaches tau (typically a
+// few dozen per wave) are copied from registers to the wave's LDS area;
+// each lane then takes one such chunk, and the elements >= tau that are not
+// listed become keys.  Each wave sorts its keys in registers, and a
+// two-level merge tree gives the tile's 128.  Tiles where the test does not
+// apply (tau <= 0, a positive NaN, more listed tokens or survivors than the
+// LDS areas hold) take the general path: exact keys for every element and a
+// bisection for the 128th key.
 #pragma once
 
 #include "ss_device.h"
@@ -37,8 +42,10 @@ __device__ __forceinline__ uint32_t s16x2_bits(s16x2 v) { return __builtin_bit_c
 
 constexpr int S1_THREADS = 256;
 constexpr int S1_WAVES = S1_THREADS / WAVE;
-constexpr int S1_SURV_CAP = 1024;     // survivors held in LDS (fast path)
+constexpr int S1_CCAP = 128;          // flagged chunks held per wave (fast path)
+constexpr int S1_KCAP = 256;          // survivors held per wave (fast path)
 constexpr int S1_LIST_CAP = 512;      // >= 255 prior + 255 bias entries
+constexpr int S1_NL_FAST = 128;       // listed tokens per tile the fast path absorbs
 
 template <int DT> struct S1Traits;
 template <> struct S1Traits<SS_BF16> {
@@ -128,35 +135,135 @@ __device__ __forceinline__ uint64_t key_f32(uint32_t raw, int local, bool presen
 
 template <int DT>
 struct S1Shared {
-    typename S1Traits<DT>::Key surv[S1_SURV_CAP];
-    typename S1Traits<DT>::Key wl[S1_WAVES][KMAX];
-    int listed[S1_LIST_CAP];
-    int nlisted;
+    using Key = typename S1Traits<DT>::Key;
+    uint4 chunks[S1_WAVES][S1_CCAP];   // flagged 16-byte chunks, per wave (fast path)
+    int cid[S1_WAVES][S1_CCAP];        // their chunk index in the tile
+    Key keys[S1_WAVES][S1_KCAP];       // survivors per wave (fast path); general path: flat
+    Key wl[S1_WAVES][KMAX];            // per-wave sorted lists
+    Key surv[KMAX];                    // result: the tile's 128 best, sorted
+    int listed[S1_LIST_CAP];           // tile-local indices of listed tokens
     int tau[S1_WAVES];
     int special[S1_WAVES];
+    int ovf;
     int scan[S1_WAVES];
     int red[2][S1_WAVES];
 };
 
+// Orders one wave's LDS writes before its later LDS reads of other lanes'
+// entries (a wave's LDS operations complete in issue order).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Bitonic sort (descending) of 64 keys, one per lane.
+template <int KS, int J, typename K>
+__device__ __forceinline__ void sort64_substeps(K& v) {
+    const int lane = lane_id();
+    const bool keep_max = ((lane & J) == 0) == ((lane & KS) == 0);
+    const K p = xor_key<J>(v);
+    v = keep_max ? kmax(v, p) : kmin(v, p);
+    if constexpr (J > 1) sort64_substeps<KS, J / 2>(v);
+}
+template <int KS = 2, typename K>
+__device__ __forceinline__ void wave_sort64(K& v) {
+    sort64_substeps<KS, KS / 2>(v);
+    if constexpr (KS < 64) wave_sort64<KS * 2>(v);
+}
+
+// The best 128 of n keys held in LDS by one wave, sorted, as a wave list.
+template <typename Key>
+__device__ __forceinline__ WList<Key> wave_top128(const Key* keys, int n) {
+    const int lane = lane_id();
+    WList<Key> mine{0, 0};
+    if (n <= WAVE) {
+        Key k = lane < n ? keys[lane] : (Key)0;
+        wave_sort64(k);
+        mine.lo = k;
+        return mine;
+    }
+    for (int c0 = 0; c0 < n; c0 += KMAX) {
+        const int i0 = c0 + lane, i1 = i0 + WAVE;
+        WList<Key> l{i0 < n ? keys[i0] : (Key)0, i1 < n ? keys[i1] : (Key)0};
+        l = wave_sort128(l);
+        mine = c0 == 0 ? l : wave_merge(mine, l);
+    }
+    return mine;
+}
+
 // The 128 best tokens of tile `tile` of row `row`, sorted best first, left
 // in sh.surv[0..128) (key 0 = no token).  Ends with a barrier.
 template <int DT>
-__device__ void stage1_tile(const Stage1Params& P, int row, int tile, S1Shared<DT>& sh) {
+__device__ __forceinline__ void stage1_tile(const Stage1Params& P, int row, int tile, S1Shared<DT>& sh) {
     using T = S1Traits<DT>;
     using Key = typename T::Key;
     constexpr int EPC = T::EPC;
     constexpr int BN = T::BN;
     constexpr int CPT = BN / (EPC * S1_THREADS);   // 16-byte chunks per thread
-    static_assert(CPT * EPC <= 64, "per-thread exclusion mask holds 64 bits");
-    Key* surv = sh.surv;
-    int* listed = sh.listed;
+    constexpr int NQ = CPT * 4;                    // dwords per thread
+    static_assert(CPT * EPC <= 64, "per-thread masks hold 64 bits");
+    static_assert(S1_WAVES == 4, "merge tree");
+    // smallest pattern when read as signed 16-bit halves / 32-bit word: the
+    // value given to grammar-masked elements and to those past the end of V
+    constexpr uint32_t PAD = DT == SS_BF16 ? 0x80008000u : 0x80000000u;
 
     const int tid = threadIdx.x;
     const int wave = tid / WAVE;
     const int lane = lane_id();
+    const uint64_t lt = (1ull << lane) - 1ull;
     const int base = tile * BN;
     const int nvalid = min(BN, P.V - base);
     const int b = row / P.rows_per_req;
+
+    // ---- issue the tile's loads: chunk j of thread t is tile chunk j*256 + t
+    // (each wave instruction reads 1 KiB of consecutive bytes) ----
+    const bool full = (nvalid == BN);
+    const bool vec = full && P.aligned16;
+    const char* rowp = (const char*)P.logits + ((int64_t)row * P.ld + base) * (DT == SS_BF16 ? 2 : 4);
+    // dword q of thread tid = dword (q & 3) of chunk (q >> 2); elements past
+    // the end of V read as PAD
+    auto load_dword = [&](int q) -> uint32_t {
+        const int c = (q >> 2) * S1_THREADS + tid;
+        if (vec) return gmem((const uint32_t*)rowp)[c * 4 + (q & 3)];
+        if (DT == SS_BF16) {
+            const auto p16 = gmem((const uint16_t*)rowp);
+            const int e0 = c * EPC + 2 * (q & 3);
+            const uint32_t lo = e0 < nvalid ? p16[e0] : 0x8000u;
+            const uint32_t hi = e0 + 1 < nvalid ? p16[e0 + 1] : 0x8000u;
+            return lo | (hi << 16);
+        } else {
+            const int e = c * EPC + (q & 3);
+            return e < nvalid ? gmem((const uint32_t*)rowp)[e] : PAD;
+        }
+    };
+    uint32_t raw[NQ];
+    if (vec) {
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            const vu32x4 v = gmem((const vu32x4*)rowp)[j * S1_THREADS + tid];
+            raw[4 * j + 0] = v.x;
+            raw[4 * j + 1] = v.y;
+            raw[4 * j + 2] = v.z;
+            raw[4 * j + 3] = v.w;
+        }
+    } else {
+        // ragged or unaligned tile: whole chunks still load as 16 bytes
+        // where they can
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            const int c = j * S1_THREADS + tid;
+            if (P.aligned16 && (c + 1) * EPC <= nvalid) {
+                const vu32x4 v = gmem((const vu32x4*)rowp)[c];
+                raw[4 * j + 0] = v.x;
+                raw[4 * j + 1] = v.y;
+                raw[4 * j + 2] = v.z;
+                raw[4 * j + 3] = v.w;
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) raw[4 * j + k] = load_dword(4 * j + k);
+            }
+        }
+    }
 
     uint32_t flags = 0;
     int n_prior = 0, n_bias = 0;
@@ -172,85 +279,236 @@ __device__ void stage1_tile(const Stage1Params& P, int row, int tile, S1Shared<D
     const bool use_prior = (flags & (SS_REP | SS_FREQPRES)) && P.aux.prior_ids && P.aux.prior_cnt && n_prior > 0;
     const bool use_bias = (flags & SS_BIAS) && P.aux.bias_ids && n_bias > 0;
 
-    // ---- tokens of this tile named by an active list (left out here) ----
-    if (wave == 0) {
-        int cnt = 0;
-        const uint64_t lt = (1ull << lane) - 1ull;
-        if (use_prior) {
-            const int32_t* ids = P.aux.prior_ids + (int64_t)b * P.aux.prior_stride;
-            const int32_t* cts = P.aux.prior_cnt + (int64_t)b * P.aux.prior_stride;
-            for (int j0 = 0; j0 < n_prior; j0 += WAVE) {
-                const int j = j0 + lane;
-                bool ok = false;
-                int loc = 0;
-                if (j < n_prior) {
-                    const int id = ids[j];
-                    loc = id - base;
-                    ok = cts[j] >= 1 && id >= 0 && id < P.V && loc >= 0 && loc < nvalid;
-                }
-                const uint64_t bal = __ballot(ok);
-                if (ok) listed[cnt + __popcll(bal & lt)] = loc;
-                cnt += __popcll(bal);
-            }
-        }
-        if (use_bias) {
-            const int32_t* ids = P.aux.bias_ids + (int64_t)b * P.aux.bias_stride;
-            for (int j0 = 0; j0 < n_bias; j0 += WAVE) {
-                const int j = j0 + lane;
-                bool ok = false;
-                int loc = 0;
-                if (j < n_bias) {
-                    const int id = ids[j];
-                    loc = id - base;
-                    ok = id >= 0 && id < P.V && loc >= 0 && loc < nvalid;
-                }
-                const uint64_t bal = __ballot(ok);
-                if (ok) listed[cnt + __popcll(bal & lt)] = loc;
-                cnt += __popcll(bal);
-            }
-        }
-        if (lane == 0) sh.nlisted = cnt;
-    }
-
-    // ---- load the tile: chunk j of thread t is tile chunk j*256 + t ----
-    // (each wave instruction reads 1 KiB of consecutive bytes)
-    const bool full = (nvalid == BN);
-    const char* rowp = (const char*)P.logits + ((int64_t)row * P.ld + base) * (DT == SS_BF16 ? 2 : 4);
-    // dword q of thread tid = dword (q & 3) of chunk (q >> 2)
-    auto load_dword = [&](int q) -> uint32_t {
-        const int c = (q >> 2) * S1_THREADS + tid;
-        if (full && P.aligned16) return ((const uint32_t*)rowp)[c * 4 + (q & 3)];
-        if (DT == SS_BF16) {
-            const uint16_t* p16 = (const uint16_t*)rowp;
-            const int e0 = c * EPC + 2 * (q & 3);
-            const uint32_t lo = e0 < nvalid ? p16[e0] : 0u;
-            const uint32_t hi = e0 + 1 < nvalid ? p16[e0 + 1] : 0u;
-            return lo | (hi << 16);
-        } else {
-            const int e = c * EPC + (q & 3);
-            return e < nvalid ? ((const uint32_t*)rowp)[e] : 0u;
-        }
-    };
-    constexpr int NQ = CPT * 4;   // dwords per thread
-    uint32_t raw[NQ];
-    if (full && P.aligned16) {
+    // grammar bits of each chunk (bit e: element e allowed); one byte of
+    // the row's bitmask covers 8 tokens
+    uint32_t gbits[CPT];
+    if (use_grammar) {
+        const auto gm = gmem((const uint8_t*)(P.aux.bitmask + (int64_t)row * P.aux.bitmask_stride));
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
-            const uint4 v = *((const uint4*)rowp + (j * S1_THREADS + tid));
-            raw[4 * j + 0] = v.x;
-            raw[4 * j + 1] = v.y;
-            raw[4 * j + 2] = v.z;
-            raw[4 * j + 3] = v.w;
+            const int g0 = base + (j * S1_THREADS + tid) * EPC;
+            uint32_t g = g0 < P.V ? (uint32_t)gm[g0 >> 3] : 0u;
+            if (DT == SS_F32) g >>= (g0 & 4);
+            gbits[j] = g;
         }
-    } else {
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) raw[q] = load_dword(q);
     }
 
-    // ---- per-element bits: present (inside V), allowed by the grammar, not listed ----
-    // element e of chunk j is bit j*EPC + e
+    // ---- tokens of this tile named by an active list: ranked in Stage 2,
+    // left out here.  Every wave counts them; wave 0 also records them. ----
+    int nl = 0;
+    if (use_prior) {
+        const auto ids = gmem(P.aux.prior_ids + (int64_t)b * P.aux.prior_stride);
+        const auto cts = gmem(P.aux.prior_cnt + (int64_t)b * P.aux.prior_stride);
+        for (int j0 = 0; j0 < n_prior; j0 += WAVE) {
+            const int j = j0 + lane;
+            bool ok = false;
+            int loc = 0;
+            if (j < n_prior) {
+                const int id = ids[j];
+                loc = id - base;
+                ok = cts[j] >= 1 && id >= 0 && id < P.V && loc >= 0 && loc < nvalid;
+            }
+            const uint64_t bal = __ballot(ok);
+            if (wave == 0 && ok) sh.listed[nl + __popcll(bal & lt)] = loc;
+            nl += __popcll(bal);
+        }
+    }
+    if (use_bias) {
+        const auto ids = gmem(P.aux.bias_ids + (int64_t)b * P.aux.bias_stride);
+        for (int j0 = 0; j0 < n_bias; j0 += WAVE) {
+            const int j = j0 + lane;
+            bool ok = false;
+            int loc = 0;
+            if (j < n_bias) {
+                const int id = ids[j];
+                loc = id - base;
+                ok = id >= 0 && id < P.V && loc >= 0 && loc < nvalid;
+            }
+            const uint64_t bal = __ballot(ok);
+            if (wave == 0 && ok) sh.listed[nl + __popcll(bal & lt)] = loc;
+            nl += __popcll(bal);
+        }
+    }
+    if (tid == 0) sh.ovf = 0;
+
+    // ---- grammar: masked elements take PAD ----
+    if (use_grammar) {
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            const uint32_t g = gbits[j];
+            if (DT == SS_BF16) {
+                // bit 2k -> low half of dword k, bit 2k+1 -> high half
+                const s16x2 G = bits_s16x2(g | (g << 16));
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const s16x2 sh_l = {(short)(15 - 2 * k), (short)(14 - 2 * k)};
+                    const s16x2 sh_r = {15, 15};
+                    const uint32_t M = s16x2_bits((G << sh_l) >> sh_r);
+                    raw[4 * j + k] = (raw[4 * j + k] & M) | (PAD & ~M);
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t M = 0u - ((g >> k) & 1u);
+                    raw[4 * j + k] = (raw[4 * j + k] & M) | (PAD & ~M);
+                }
+            }
+        }
+    }
+
+    // ---- maxima per chunk and per lane (raw patterns read as signed) ----
+    uint32_t cmx[CPT];
+    int m;
+    if constexpr (DT == SS_BF16) {
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            const s16x2 a = __builtin_elementwise_max(bits_s16x2(raw[4 * j]), bits_s16x2(raw[4 * j + 1]));
+            const s16x2 c = __builtin_elementwise_max(bits_s16x2(raw[4 * j + 2]), bits_s16x2(raw[4 * j + 3]));
+            cmx[j] = s16x2_bits(__builtin_elementwise_max(a, c));
+        }
+        s16x2 mm = bits_s16x2(cmx[0]);
+#pragma unroll
+        for (int j = 1; j < CPT; ++j) mm = __builtin_elementwise_max(mm, bits_s16x2(cmx[j]));
+        m = max((int)mm.x, (int)mm.y);
+    } else {
+#pragma unroll
+        for (int j = 0; j < CPT; ++j)
+            cmx[j] = (uint32_t)max(max((int)raw[4 * j], (int)raw[4 * j + 1]),
+                                   max((int)raw[4 * j + 2], (int)raw[4 * j + 3]));
+        m = (int)cmx[0];
+#pragma unroll
+        for (int j = 1; j < CPT; ++j) m = max(m, (int)cmx[j]);
+    }
+
+    // positive NaN anywhere in the tile -> general path; +inf of fp32 counts
+    // as FLT_MAX for the threshold
+    const int nan_floor = DT == SS_BF16 ? 0x7F80 : (int)F32_PINF_BITS;
+    const bool special = m > nan_floor;
+    if (DT == SS_F32) m = min(m, (int)F32_MAX_BITS);
+    // at least 128 + nl tokens at or above tau, so that 128 remain once the
+    // listed ones are set aside
+    const bool nl_ok = nl <= S1_NL_FAST;
+    const int kw = KMAX / S1_WAVES + (nl_ok ? (nl + S1_WAVES - 1) / S1_WAVES : 0);
+    const int tau_w = wave_kth_largest<T::VAL_BITS>(m, kw);
+    const uint64_t sp = __ballot(special);
+    if (lane == 0) {
+        sh.tau[wave] = tau_w;
+        sh.special[wave] = sp != 0ull;
+    }
+    __syncthreads();   // tau, listed[], ovf
+    int tau = sh.tau[0];
+    bool any_special = false;
+#pragma unroll
+    for (int w = 0; w < S1_WAVES; ++w) {
+        tau = min(tau, sh.tau[w]);
+        any_special |= sh.special[w] != 0;
+    }
+    const bool fast = !any_special && tau >= 1 && nl_ok;   // block-uniform
+
+    if (fast) {
+        // ---- chunks holding a value >= tau go to the wave's LDS area ----
+        int wcnt = 0;
+        const uint32_t T2 = ((uint32_t)(tau - 1) & 0xFFFFu) * 0x10001u;
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            bool f;
+            if constexpr (DT == SS_BF16)
+                f = s16x2_bits(__builtin_elementwise_max(bits_s16x2(cmx[j]), bits_s16x2(T2))) != T2;
+            else
+                f = (int)cmx[j] >= tau;
+            const uint64_t bal = __ballot(f);
+            if (f) {
+                const int s = wcnt + __popcll(bal & lt);
+                if (s < S1_CCAP) {
+                    sh.chunks[wave][s] = make_uint4(raw[4 * j], raw[4 * j + 1], raw[4 * j + 2], raw[4 * j + 3]);
+                    sh.cid[wave][s] = j * S1_THREADS + tid;
+                }
+            }
+            wcnt += __popcll(bal);
+        }
+        wave_lds_sync();
+
+        // ---- the survivors of those chunks become keys (listed ones dropped) ----
+        const int nck = min(wcnt, S1_CCAP);
+        int nk = 0;
+        for (int s0 = 0; s0 < nck; s0 += WAVE) {
+            const int s = s0 + lane;
+            uint4 d = make_uint4(PAD, PAD, PAD, PAD);
+            int c = -1;
+            if (s < nck) {
+                d = sh.chunks[wave][s];
+                c = sh.cid[wave][s];
+            }
+            uint32_t ex = 0;
+            for (int i = 0; i < nl; ++i) {
+                const int loc = sh.listed[i];
+                if (loc / EPC == c) ex |= 1u << (loc % EPC);
+            }
+            const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) {
+                uint32_t h;
+                int v;
+                if constexpr (DT == SS_BF16) {
+                    h = (dw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                    v = (int)(short)h;
+                } else {
+                    h = dw[e];
+                    v = (int)h;
+                }
+                const bool sv = v >= tau && !((ex >> e) & 1u);
+                const uint64_t bal = __ballot(sv);
+                if (sv) {
+                    const int slot = nk + __popcll(bal & lt);
+                    const int local = c * EPC + e;
+                    if (slot < S1_KCAP) {
+                        // value > 0 and not NaN here
+                        if constexpr (DT == SS_BF16)
+                            sh.keys[wave][slot] = ((h | 0x8000u) << 16) | (0xFFFFu - (uint32_t)local);
+                        else
+                            sh.keys[wave][slot] = key_f32(h, local, true, true);
+                    }
+                }
+                nk += __popcll(bal);
+            }
+        }
+        wave_lds_sync();
+        if (wcnt > S1_CCAP || nk > S1_KCAP) {
+            if (lane == 0) sh.ovf = 1;
+        } else {
+            const WList<Key> mine = wave_top128(sh.keys[wave], nk);
+            sh.wl[wave][lane] = mine.lo;
+            sh.wl[wave][lane + WAVE] = mine.hi;
+        }
+    }
+    __syncthreads();   // wave lists, ovf
+
+    if (fast && sh.ovf == 0) {
+        // ---- merge tree: (0+1) on wave 0 and (2+3) on wave 1, then both ----
+        WList<Key> r{0, 0};
+        if (wave < 2) {
+            const int a = 2 * wave;
+            r = wave_merge(WList<Key>{sh.wl[a][lane], sh.wl[a][lane + WAVE]},
+                           WList<Key>{sh.wl[a + 1][lane], sh.wl[a + 1][lane + WAVE]});
+            if (wave == 1) {
+                sh.wl[2][lane] = r.lo;
+                sh.wl[2][lane + WAVE] = r.hi;
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+            r = wave_merge(r, WList<Key>{sh.wl[2][lane], sh.wl[2][lane + WAVE]});
+            sh.surv[lane] = r.lo;
+            sh.surv[lane + WAVE] = r.hi;
+        }
+        __syncthreads();
+        return;
+    }
+
+    // ---- general path: exact keys for every element (re-read from cache),
+    // bisection for the 128th key ----
     const uint32_t all_bits = (1u << EPC) - 1u;
-    uint64_t alw = ~0ull, pres = ~0ull;
+    uint64_t alw = ~0ull, pres = ~0ull, excl = 0;
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
         const int c0 = (j * S1_THREADS + tid) * EPC;
@@ -259,197 +517,67 @@ __device__ void stage1_tile(const Stage1Params& P, int row, int tile, S1Shared<D
         pres &= ~((uint64_t)(all_bits & ~pb) << (j * EPC));
         if (use_grammar && pb) {
             const int g0 = base + c0;
-            const uint32_t w = P.aux.bitmask[(int64_t)row * P.aux.bitmask_stride + (g0 >> 5)];
+            const uint32_t w = gmem(P.aux.bitmask)[(int64_t)row * P.aux.bitmask_stride + (g0 >> 5)];
             alw &= ~((uint64_t)(all_bits & ~((w >> (g0 & 31)) & all_bits)) << (j * EPC));
         }
     }
-    __syncthreads();   // listed[] ready
-    const int nlisted = sh.nlisted;
-    uint64_t excl = 0;
-    for (int i = 0; i < nlisted; ++i) {
-        const int loc = listed[i];
+    for (int i = 0; i < nl; ++i) {
+        const int loc = sh.listed[i];
         const int c = loc / EPC;
         if ((c & (S1_THREADS - 1)) == tid) excl |= 1ull << ((c / S1_THREADS) * EPC + (loc % EPC));
     }
-    const uint64_t inc = alw & pres & ~excl;
-    const bool need_mask = !full || use_grammar || nlisted > 0;   // block-uniform
-
-    // ---- fast-path values: raw patterns as signed integers; left-out -> minimum ----
-    if (need_mask) {
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            if (DT == SS_BF16) {
-                const uint32_t b2 = (uint32_t)(inc >> (2 * q)) & 3u;
-                const uint32_t M = ((b2 & 1u) ? 0x0000FFFFu : 0u) | ((b2 & 2u) ? 0xFFFF0000u : 0u);
-                raw[q] = (raw[q] & M) | (0x80008000u & ~M);
-            } else {
-                if (!((inc >> q) & 1ull)) raw[q] = 0x80000000u;
-            }
-        }
-    }
-    int m;
-    if (DT == SS_BF16) {
-        s16x2 mx = bits_s16x2(raw[0]);
-#pragma unroll
-        for (int q = 1; q < NQ; ++q) mx = __builtin_elementwise_max(mx, bits_s16x2(raw[q]));
-        m = max((int)mx.x, (int)mx.y);
-    } else {
-        m = (int)raw[0];
-#pragma unroll
-        for (int q = 1; q < NQ; ++q) m = max(m, (int)raw[q]);
-    }
-
-    // positive NaN anywhere in the tile -> general path; +inf of fp32 counts
-    // as FLT_MAX for the threshold
-    const int nan_floor = DT == SS_BF16 ? 0x7F80 : (int)F32_PINF_BITS;
-    const bool special = m > nan_floor;
-    if (DT == SS_F32) m = min(m, (int)F32_MAX_BITS);
-    const int tau_w = wave_kth_largest<T::VAL_BITS>(m, KMAX / S1_WAVES);
-    const uint64_t sp = __ballot(special);
-    if (lane == 0) {
-        sh.tau[wave] = tau_w;
-        sh.special[wave] = sp != 0ull;
-    }
-    __syncthreads();
-    int tau = sh.tau[0];
-    bool any_special = false;
-#pragma unroll
-    for (int w = 0; w < S1_WAVES; ++w) {
-        tau = min(tau, sh.tau[w]);
-        any_special |= sh.special[w] != 0;
-    }
-
-    bool fast = !any_special && tau >= 1;
-    int nsurv = 0;
-    if (fast) {
-        // dwords holding a survivor (value >= tau)
-        uint32_t smask = 0;
-        if (m >= tau) {
-            if (DT == SS_BF16) {
-                const uint32_t T2 = ((uint32_t)(tau - 1) & 0xFFFFu) * 0x10001u;
-                const s16x2 tv = bits_s16x2(T2);
-#pragma unroll
-                for (int q = 0; q < NQ; ++q) {
-                    const s16x2 r = __builtin_elementwise_max(bits_s16x2(raw[q]), tv);
-                    smask |= (s16x2_bits(r) != T2) ? (1u << q) : 0u;
-                }
-            } else {
-#pragma unroll
-                for (int q = 0; q < NQ; ++q) smask |= ((int)raw[q] >= tau) ? (1u << q) : 0u;
-            }
-        }
-        // survivors per thread (re-reading the few dwords from cache)
-        auto survivor_bits = [&](int q, uint32_t d) -> uint32_t {
-            if (DT == SS_BF16) {
-                const uint32_t b2 = (uint32_t)(inc >> (2 * q)) & 3u;
-                uint32_t r = 0;
-                if ((b2 & 1u) && (int)(short)(d & 0xFFFFu) >= tau) r |= 1u;
-                if ((b2 & 2u) && ((int)d >> 16) >= tau) r |= 2u;
-                return r;
-            } else {
-                return ((inc >> q) & 1ull) && (int)d >= tau ? 1u : 0u;
-            }
-        };
-        int cnt = 0;
-        for (uint32_t sm = smask; sm; sm &= sm - 1) {
-            const int q = __builtin_ctz(sm);
-            cnt += __builtin_popcount(survivor_bits(q, load_dword(q)));
-        }
-        int total;
-        int off = block_excl_scan(cnt, sh.scan, &total);
-        if (total <= S1_SURV_CAP) {
-            nsurv = total;
-            for (uint32_t sm = smask; sm; sm &= sm - 1) {
-                const int q = __builtin_ctz(sm);
-                const uint32_t d = load_dword(q);
-                const uint32_t sb = survivor_bits(q, d);
-                const int c = (q >> 2) * S1_THREADS + tid;
-                if (DT == SS_BF16) {
-                    const int e0 = c * EPC + 2 * (q & 3);
-                    if (sb & 1u) surv[off++] = (Key)key_bf16(d & 0xFFFFu, e0, true, true);
-                    if (sb & 2u) surv[off++] = (Key)key_bf16(d >> 16, e0 + 1, true, true);
-                } else {
-                    if (sb) surv[off++] = (Key)key_f32(d, c * EPC + (q & 3), true, true);
-                }
-            }
+    auto ekey = [&](int q, int h) -> Key {
+        const uint32_t d = load_dword(q);
+        const int c = (q >> 2) * S1_THREADS + tid;
+        if (DT == SS_BF16) {
+            const int e = 2 * (q & 3) + h;
+            const int bitpos = (q >> 2) * EPC + e;
+            const bool present = ((pres & ~excl) >> bitpos) & 1ull;
+            const bool allowed = (alw >> bitpos) & 1ull;
+            return (Key)key_bf16(h ? (d >> 16) : (d & 0xFFFFu), c * EPC + e, present, allowed);
         } else {
-            fast = false;   // block-uniform: total is the same everywhere
+            const int bitpos = q;
+            const bool present = ((pres & ~excl) >> bitpos) & 1ull;
+            const bool allowed = (alw >> bitpos) & 1ull;
+            return (Key)key_f32(d, c * EPC + (q & 3), present, allowed);
         }
-    }
-
-    if (!fast) {
-        // ---- general path: exact keys (re-read from cache), bisection for the 128th key ----
-        auto ekey = [&](int q, int h) -> Key {
-            const uint32_t d = load_dword(q);
-            const int c = (q >> 2) * S1_THREADS + tid;
-            if (DT == SS_BF16) {
-                const int e = 2 * (q & 3) + h;
-                const int bitpos = (q >> 2) * EPC + e;
-                const bool present = ((pres & ~excl) >> bitpos) & 1ull;
-                const bool allowed = (alw >> bitpos) & 1ull;
-                return (Key)key_bf16(h ? (d >> 16) : (d & 0xFFFFu), c * EPC + e, present, allowed);
-            } else {
-                const int bitpos = q;
-                const bool present = ((pres & ~excl) >> bitpos) & 1ull;
-                const bool allowed = (alw >> bitpos) & 1ull;
-                return (Key)key_f32(d, c * EPC + (q & 3), present, allowed);
-            }
-        };
-        constexpr int HALVES = DT == SS_BF16 ? 2 : 1;
-        constexpr int KB = (int)sizeof(Key) * 8;
-        Key res = 0;
-        int parity = 0;
-        for (int bit = KB - 1; bit >= 0; --bit) {
-            const Key cand = res | ((Key)1 << bit);
-            int c = 0;
-            for (int q = 0; q < NQ; ++q)
-                for (int h = 0; h < HALVES; ++h) c += ekey(q, h) >= cand;
-            c = wave_sum(c);
-            if (lane == 0) sh.red[parity][wave] = c;
-            __syncthreads();
-            int tot = 0;
-#pragma unroll
-            for (int w = 0; w < S1_WAVES; ++w) tot += sh.red[parity][w];
-            parity ^= 1;
-            if (tot >= KMAX) res = cand;
-        }
-        const Key thr = res > (Key)1 ? res : (Key)1;   // key 0 = no token
-        int cnt = 0;
+    };
+    constexpr int HALVES = DT == SS_BF16 ? 2 : 1;
+    constexpr int KB = (int)sizeof(Key) * 8;
+    Key res = 0;
+    int parity = 0;
+    for (int bit = KB - 1; bit >= 0; --bit) {
+        const Key cand = res | ((Key)1 << bit);
+        int c = 0;
         for (int q = 0; q < NQ; ++q)
-            for (int h = 0; h < HALVES; ++h) cnt += ekey(q, h) >= thr;
-        int total;
-        int off = block_excl_scan(cnt, sh.scan, &total);
-        nsurv = total;   // <= 128 (keys are unique)
-        for (int q = 0; q < NQ; ++q)
-            for (int h = 0; h < HALVES; ++h) {
-                const Key k = ekey(q, h);
-                if (k >= thr) surv[off++] = k;
-            }
-    }
-
-    // ---- the 128 best survivors, sorted: each wave sorts 128-key chunks in
-    // registers and keeps the best 128 of its chunks; wave 0 merges the
-    // per-wave lists (key 0 = no token) ----
-    __syncthreads();   // survivors complete
-    const int nchunks = (nsurv + KMAX - 1) / KMAX;
-    WList<Key> mine{0, 0};
-    for (int c = wave; c < nchunks; c += S1_WAVES) {
-        const int i0 = c * KMAX + lane, i1 = i0 + WAVE;
-        WList<Key> l{i0 < nsurv ? surv[i0] : (Key)0, i1 < nsurv ? surv[i1] : (Key)0};
-        l = wave_sort128(l);
-        mine = c == wave ? l : wave_merge(mine, l);
-    }
-    if (nchunks > 1) {
-        sh.wl[wave][lane] = mine.lo;
-        sh.wl[wave][lane + WAVE] = mine.hi;
+            for (int h = 0; h < HALVES; ++h) c += ekey(q, h) >= cand;
+        c = wave_sum(c);
+        if (lane == 0) sh.red[parity][wave] = c;
         __syncthreads();
-        if (wave == 0)
-            for (int w = 1; w < S1_WAVES && w < nchunks; ++w)
-                mine = wave_merge(mine, WList<Key>{sh.wl[w][lane], sh.wl[w][lane + WAVE]});
+        int tot = 0;
+#pragma unroll
+        for (int w = 0; w < S1_WAVES; ++w) tot += sh.red[parity][w];
+        parity ^= 1;
+        if (tot >= KMAX) res = cand;
     }
+    const Key thr = res > (Key)1 ? res : (Key)1;   // key 0 = no token
+    int cnt = 0;
+    for (int q = 0; q < NQ; ++q)
+        for (int h = 0; h < HALVES; ++h) cnt += ekey(q, h) >= thr;
+    int total;
+    int off = block_excl_scan(cnt, sh.scan, &total);   // total <= 128 (keys are unique)
+    Key* g = &sh.keys[0][0];
+    for (int q = 0; q < NQ; ++q)
+        for (int h = 0; h < HALVES; ++h) {
+            const Key k = ekey(q, h);
+            if (k >= thr) g[off++] = k;
+        }
+    __syncthreads();
     if (wave == 0) {
-        surv[lane] = mine.lo;
-        surv[lane + WAVE] = mine.hi;
+        WList<Key> l{lane < total ? g[lane] : (Key)0, lane + WAVE < total ? g[lane + WAVE] : (Key)0};
+        l = wave_sort128(l);
+        sh.surv[lane] = l.lo;
+        sh.surv[lane + WAVE] = l.hi;
     }
     __syncthreads();
 }

@@ -204,7 +204,7 @@ struct S2Lists {
 // matching entry (the usual case) that is a single subtraction / addition,
 // and tokens with several entries take a sequential walk of the list.
 template <int DT>
-__device__ WL64 listed_list(const Stage1Params& P, const RowParams& rp, int row, int np, int nb,
+__device__ __forceinline__ WL64 listed_list(const Stage1Params& P, const RowParams& rp, int row, int np, int nb,
                             const S2Lists& L) {
     const int lane = lane_id();
     const int ncomb = np + nb;
@@ -307,7 +307,7 @@ __device__ WL64 listed_list(const Stage1Params& P, const RowParams& rp, int row,
 // tokens (wave 0) and stores the best 128 as merge keys; it runs alongside
 // the tile workgroups, so Stage 2 only has to load one more sorted list.
 template <int DT>
-__device__ void listed_row(const Stage1Params& P, uint64_t* out, int row, S2Lists& lists) {
+__device__ __forceinline__ void listed_row(const Stage1Params& P, uint64_t* out, int row, S2Lists& lists) {
     const int b = row / P.rows_per_req;
     const RowParams rp = row_params(P, b);
     const int np = rp.valid ? rp.n_prior : 0;
@@ -340,7 +340,7 @@ constexpr int S2_PREFETCH = 4;   // tile lists per wave requested up front
 // The row's 128 best as a wave-0 register list.  Every load is issued
 // before any merging; one workgroup barrier.
 template <int DT>
-__device__ WL64 row_merge(const Stage2Params& F, const RowParams& rp, int row, S2Shared& sh) {
+__device__ __forceinline__ WL64 row_merge(const Stage2Params& F, const RowParams& rp, int row, S2Shared& sh) {
     using Key = typename S1Traits<DT>::Key;
     const Stage1Params& P = F.s1;
     const int lane = lane_id();
@@ -406,7 +406,7 @@ __device__ WL64 row_merge(const Stage2Params& F, const RowParams& rp, int row, S
 // Epilogue on wave 0 (ranks k = lane and lane + 64).  Writes the mode's
 // outputs for the row.  Uses no barrier.
 template <int DT>
-__device__ void row_epilogue(const Stage2Params& F, const RowParams& rp, int row, int b, const WL64& best,
+__device__ __forceinline__ void row_epilogue(const Stage2Params& F, const RowParams& rp, int row, int b, const WL64& best,
                              const ss_rng rg) {
     const Stage1Params& P = F.s1;
     const int lane = lane_id();
