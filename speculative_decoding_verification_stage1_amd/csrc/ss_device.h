@@ -170,6 +170,11 @@ __device__ __forceinline__ int wave_sum(int v) {
     return v;
 }
 
+// Number of lanes below this one whose bit is set in `bal`.
+__device__ __forceinline__ int lane_prefix(uint64_t bal) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+}
+
 // inclusive prefix sum over the wave
 __device__ __forceinline__ int wave_incl_scan(int v) {
     const int l = lane_id();

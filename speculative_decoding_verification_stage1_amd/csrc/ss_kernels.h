@@ -15,9 +15,9 @@ union S1KernelShared {
     S2Lists lists;
 };
 
-// Workgroups 0 .. listed_rows-1 compute each row's listed tokens (ranked
-// in Stage 2); the rest each own one (row, tile).  The listed workgroups
-// come first so they run alongside the streaming, not after it.
+// Workgroups 0 .. listed_rows-1 compute each row's listed tokens (ranked in
+// Stage 2); the rest each own one (row, tile).  The listed workgroups come
+// first so they run alongside the streaming, not after it.
 template <int DT>
 __global__ __launch_bounds__(S1_THREADS) void stage1_kernel(Stage1Params P) {
     using Key = typename S1Traits<DT>::Key;

@@ -16,19 +16,20 @@
 // Selection is exact.  Fast path: raw bit patterns read as signed integers
 // order like the floats they hold whenever the threshold below is positive,
 // so no per-element key transform is needed.  Grammar-masked elements and
-// those past the end of V take the smallest pattern.  Each lane takes the
-// maximum of every 16-byte chunk and of its whole slice; each wave finds the
-// k-th largest of its 64 lane maxima, k = 32 + ceil(L/4) for L listed
-// tokens in the tile, and the smallest of the four is a threshold tau with
-// at least 128 + L tokens at or above it - so the 128 best unlisted tokens
-// are all at or above tau.  Chunks whose maximum reaches tau (typically a
-// few dozen per wave) are copied from registers to the wave's LDS area;
-// each lane then takes one such chunk, and the elements >= tau that are not
-// listed become keys.  Each wave sorts its keys in registers, and a
-// two-level merge tree gives the tile's 128.  Tiles where the test does not
-// apply (tau <= 0, a positive NaN, more listed tokens or survivors than the
-// LDS areas hold) take the general path: exact keys for every element and a
-// bisection for the 128th key.
+// those past the end of V take the smallest pattern.  Each lane holds 16
+// chunks of 16 bytes and takes the maximum of every chunk and of its whole
+// slice; each wave finds the k-th largest of its 64 lane maxima, k = 32 +
+// ceil(L/4) for L listed tokens in the tile, and the smallest of the four is
+// a threshold tau with at least 128 + L tokens at or above it - so the 128
+// best unlisted tokens are all at or above tau.  Chunks whose maximum
+// reaches tau (typically a few dozen per wave) are copied from registers to
+// the wave's LDS area; each lane then takes one such chunk, and its elements
+// >= tau that are not listed become keys, one per lane per round.  Each
+// wave sorts its keys in registers, and a two-level merge tree gives the
+// tile's 128.  Tiles where the test does not apply (tau <= 0, a positive
+// NaN, more listed tokens or survivors than the LDS areas hold) take the
+// general path: exact keys for every element and a bisection for the 128th
+// key.
 #pragma once
 
 #include "ss_device.h"
@@ -42,6 +43,7 @@ __device__ __forceinline__ uint32_t s16x2_bits(s16x2 v) { return __builtin_bit_c
 
 constexpr int S1_THREADS = 256;
 constexpr int S1_WAVES = S1_THREADS / WAVE;
+constexpr int S1_CPT = 16;            // 16-byte chunks per thread
 constexpr int S1_CCAP = 128;          // flagged chunks held per wave (fast path)
 constexpr int S1_KCAP = 256;          // survivors held per wave (fast path)
 constexpr int S1_LIST_CAP = 512;      // >= 255 prior + 255 bias entries
@@ -50,14 +52,14 @@ constexpr int S1_NL_FAST = 128;       // listed tokens per tile the fast path ab
 template <int DT> struct S1Traits;
 template <> struct S1Traits<SS_BF16> {
     using Key = uint32_t;
-    static constexpr int EPC = 8;          // elements per 16-byte chunk
-    static constexpr int BN = 16384;       // tile width
-    static constexpr int VAL_BITS = 16;    // fast-path value range (int16)
+    static constexpr int EPC = 8;                            // elements per chunk
+    static constexpr int BN = EPC * S1_CPT * S1_THREADS;     // tile width 32768
+    static constexpr int VAL_BITS = 16;                      // fast-path value range (int16)
 };
 template <> struct S1Traits<SS_F32> {
     using Key = uint64_t;
     static constexpr int EPC = 4;
-    static constexpr int BN = 8192;
+    static constexpr int BN = EPC * S1_CPT * S1_THREADS;     // 16384
     static constexpr int VAL_BITS = 32;
 };
 
@@ -136,12 +138,16 @@ __device__ __forceinline__ uint64_t key_f32(uint32_t raw, int local, bool presen
 template <int DT>
 struct S1Shared {
     using Key = typename S1Traits<DT>::Key;
-    uint4 chunks[S1_WAVES][S1_CCAP];   // flagged 16-byte chunks, per wave (fast path)
-    int cid[S1_WAVES][S1_CCAP];        // their chunk index in the tile
+    uint4 chunks[S1_WAVES][S1_CCAP + WAVE];   // flagged chunks, per wave (fast path)
+    int cid[S1_WAVES][S1_CCAP + WAVE];        // their chunk index in the tile
     Key keys[S1_WAVES][S1_KCAP];       // survivors per wave (fast path); general path: flat
     Key wl[S1_WAVES][KMAX];            // per-wave sorted lists
     Key surv[KMAX];                    // result: the tile's 128 best, sorted
-    int listed[S1_LIST_CAP];           // tile-local indices of listed tokens
+    uint4 gtab[256];                   // bf16 grammar: dword masks of a chunk by its allowed byte
+    uint32_t gmw[S1Traits<DT>::BN / 32];   // the tile's grammar bitmask
+    int listed[S1_LIST_CAP];           // tile-local index of each listed token
+    int2 lcb[S1_LIST_CAP];             // its chunk, and its bit in a chunk's survivor mask
+    int nl;
     int tau[S1_WAVES];
     int special[S1_WAVES];
     int ovf;
@@ -154,21 +160,6 @@ struct S1Shared {
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
-}
-
-// Bitonic sort (descending) of 64 keys, one per lane.
-template <int KS, int J, typename K>
-__device__ __forceinline__ void sort64_substeps(K& v) {
-    const int lane = lane_id();
-    const bool keep_max = ((lane & J) == 0) == ((lane & KS) == 0);
-    const K p = xor_key<J>(v);
-    v = keep_max ? kmax(v, p) : kmin(v, p);
-    if constexpr (J > 1) sort64_substeps<KS, J / 2>(v);
-}
-template <int KS = 2, typename K>
-__device__ __forceinline__ void wave_sort64(K& v) {
-    sort64_substeps<KS, KS / 2>(v);
-    if constexpr (KS < 64) wave_sort64<KS * 2>(v);
 }
 
 // The best 128 of n keys held in LDS by one wave, sorted, as a wave list.
@@ -191,165 +182,292 @@ __device__ __forceinline__ WList<Key> wave_top128(const Key* keys, int n) {
     return mine;
 }
 
-// The 128 best tokens of tile `tile` of row `row`, sorted best first, left
-// in sh.surv[0..128) (key 0 = no token).  Ends with a barrier.
+// Bit of element e of a chunk in the survivor mask of that chunk.  bf16:
+// element 2k (low half of dword k) is bit 15 - k, element 2k + 1 is bit
+// 31 - k (the sign bits of a packed subtraction, see chunk_survivors).
 template <int DT>
-__device__ __forceinline__ void stage1_tile(const Stage1Params& P, int row, int tile, S1Shared<DT>& sh) {
-    using T = S1Traits<DT>;
-    using Key = typename T::Key;
-    constexpr int EPC = T::EPC;
-    constexpr int BN = T::BN;
-    constexpr int CPT = BN / (EPC * S1_THREADS);   // 16-byte chunks per thread
-    constexpr int NQ = CPT * 4;                    // dwords per thread
-    static_assert(CPT * EPC <= 64, "per-thread masks hold 64 bits");
-    static_assert(S1_WAVES == 4, "merge tree");
-    // smallest pattern when read as signed 16-bit halves / 32-bit word: the
-    // value given to grammar-masked elements and to those past the end of V
-    constexpr uint32_t PAD = DT == SS_BF16 ? 0x80008000u : 0x80000000u;
+__device__ __forceinline__ uint32_t chunk_bit(int e) {
+    if constexpr (DT == SS_BF16) return 1u << ((15 - (e >> 1)) + 16 * (e & 1));
+    else return 1u << e;
+}
+template <int DT>
+__device__ __forceinline__ int chunk_elem(int p) {
+    if constexpr (DT == SS_BF16) return 2 * (15 - (p & 15)) + (p >> 4);
+    else return p;
+}
+// Elements of a chunk whose value (raw pattern read as signed) is >= tau.
+template <int DT>
+__device__ __forceinline__ uint32_t chunk_survivors(const uint4& d, int tau) {
+    if constexpr (DT == SS_BF16) {
+        const s16x2 t2 = {(short)tau, (short)tau};
+        const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+        uint32_t below = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)   // saturating: the sign says x < tau
+            below |= (s16x2_bits(__builtin_elementwise_sub_sat(bits_s16x2(w[k]), t2)) & 0x80008000u) >> k;
+        return ~below & 0xF000F000u;
+    } else {
+        return ((int)d.x >= tau ? 1u : 0u) | ((int)d.y >= tau ? 2u : 0u) | ((int)d.z >= tau ? 4u : 0u) |
+               ((int)d.w >= tau ? 8u : 0u);
+    }
+}
 
-    const int tid = threadIdx.x;
-    const int wave = tid / WAVE;
-    const int lane = lane_id();
-    const uint64_t lt = (1ull << lane) - 1ull;
-    const int base = tile * BN;
-    const int nvalid = min(BN, P.V - base);
-    const int b = row / P.rows_per_req;
+// What one tile needs from global memory, all requested before any of it
+// is used.
+template <int DT>
+struct S1In {
+    uint32_t raw[S1_CPT * 4];   // dword q: dword (q & 3) of this thread's chunk (q >> 2)
+    uint32_t gw[S1_CPT * S1Traits<DT>::EPC / 32];   // the tile's bitmask words tid + 256k
+    int l_pid, l_pct, l_bid;    // wave 0: first 64 entries of the request's lists
+    uint32_t rq_flags, rq_lists; // the request's flags and its n_prior | n_bias << 8
+};
 
-    // ---- issue the tile's loads: chunk j of thread t is tile chunk j*256 + t
-    // (each wave instruction reads 1 KiB of consecutive bytes) ----
-    const bool full = (nvalid == BN);
-    const bool vec = full && P.aligned16;
-    const char* rowp = (const char*)P.logits + ((int64_t)row * P.ld + base) * (DT == SS_BF16 ? 2 : 4);
-    // dword q of thread tid = dword (q & 3) of chunk (q >> 2); elements past
-    // the end of V read as PAD
-    auto load_dword = [&](int q) -> uint32_t {
-        const int c = (q >> 2) * S1_THREADS + tid;
-        if (vec) return gmem((const uint32_t*)rowp)[c * 4 + (q & 3)];
-        if (DT == SS_BF16) {
-            const auto p16 = gmem((const uint16_t*)rowp);
-            const int e0 = c * EPC + 2 * (q & 3);
-            const uint32_t lo = e0 < nvalid ? p16[e0] : 0x8000u;
-            const uint32_t hi = e0 + 1 < nvalid ? p16[e0 + 1] : 0x8000u;
-            return lo | (hi << 16);
-        } else {
-            const int e = c * EPC + (q & 3);
-            return e < nvalid ? gmem((const uint32_t*)rowp)[e] : PAD;
+#define S1_TILE_GEOMETRY                                                             \
+    using T = S1Traits<DT>;                                                          \
+    constexpr int EPC = T::EPC;                                                      \
+    constexpr int BN = T::BN;                                                        \
+    constexpr int CPT = S1_CPT;                                                      \
+    constexpr int NQ = CPT * 4;                                                      \
+    constexpr uint32_t PAD = DT == SS_BF16 ? 0x80008000u : 0x80000000u;              \
+    const int tid = threadIdx.x;                                                     \
+    const int wave = tid / WAVE;                                                     \
+    const int lane = lane_id();                                                      \
+    const int base = tile * BN;                                                      \
+    const int nvalid = min(BN, P.V - base);                                          \
+    const int b = __builtin_amdgcn_readfirstlane(row / P.rows_per_req);              \
+    const bool full = (nvalid == BN);                                                \
+    const bool vec = full && P.aligned16;                                            \
+    const char* rowp = (const char*)P.logits + ((int64_t)row * P.ld + base) * (DT == SS_BF16 ? 2 : 4); \
+    (void)wave; (void)lane; (void)b; (void)vec; (void)NQ; (void)PAD;
+
+// Dword q of this thread's slice (chunk q >> 2, dword q & 3); elements past
+// the end of V read as the smallest signed pattern.
+template <int DT>
+__device__ __forceinline__ uint32_t tile_dword(const char* rowp, bool vec, int nvalid, int q) {
+    constexpr int EPC = S1Traits<DT>::EPC;
+    const int c = (q >> 2) * S1_THREADS + (int)threadIdx.x;
+    if (vec) return gmem((const uint32_t*)rowp)[c * 4 + (q & 3)];
+    if (DT == SS_BF16) {
+        const auto p16 = gmem((const uint16_t*)rowp);
+        const int e0 = c * EPC + 2 * (q & 3);
+        const uint32_t lo = e0 < nvalid ? p16[e0] : 0x8000u;
+        const uint32_t hi = e0 + 1 < nvalid ? p16[e0 + 1] : 0x8000u;
+        return lo | (hi << 16);
+    } else {
+        const int e = c * EPC + (q & 3);
+        return e < nvalid ? gmem((const uint32_t*)rowp)[e] : 0x80000000u;
+    }
+}
+
+// Requests tile `tile` of row `row`: chunk j of thread t is tile chunk
+// j*256 + t (each wave instruction reads 1 KiB of consecutive bytes).
+template <int DT>
+__device__ __forceinline__ void tile_fetch(const Stage1Params& P, int row, int tile, S1In<DT>& in) {
+    S1_TILE_GEOMETRY
+    in.rq_flags = 0;
+    in.rq_lists = 0;
+    if (P.req) {
+        const auto rq = gmem((const uint32_t*)(P.req + b));
+        in.rq_flags = rq[0];
+        in.rq_lists = rq[2] >> 16;   // n_prior, n_bias follow the 16-bit top_k
+    }
+    // wave 0: the first 64 entries of the request's lists
+    in.l_pid = -1;
+    in.l_pct = 0;
+    in.l_bid = -1;
+    if (wave == 0) {
+        if (P.aux.prior_ids && P.aux.prior_cnt && lane < P.aux.prior_stride) {
+            const int64_t o = (int64_t)b * P.aux.prior_stride + lane;
+            in.l_pid = gmem(P.aux.prior_ids)[o];
+            in.l_pct = gmem(P.aux.prior_cnt)[o];
         }
-    };
-    uint32_t raw[NQ];
+        if (P.aux.bias_ids && lane < P.aux.bias_stride)
+            in.l_bid = gmem(P.aux.bias_ids)[(int64_t)b * P.aux.bias_stride + lane];
+    }
     if (vec) {
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
             const vu32x4 v = gmem((const vu32x4*)rowp)[j * S1_THREADS + tid];
-            raw[4 * j + 0] = v.x;
-            raw[4 * j + 1] = v.y;
-            raw[4 * j + 2] = v.z;
-            raw[4 * j + 3] = v.w;
+            in.raw[4 * j + 0] = v.x;
+            in.raw[4 * j + 1] = v.y;
+            in.raw[4 * j + 2] = v.z;
+            in.raw[4 * j + 3] = v.w;
         }
-    } else {
-        // ragged or unaligned tile: whole chunks still load as 16 bytes
-        // where they can
+    } else if (P.aligned16) {
+        // ragged tile: chunks wholly inside V load as 16 bytes, the others
+        // read as PAD; the one chunk that straddles the end is completed by
+        // tile_patch
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
             const int c = j * S1_THREADS + tid;
-            if (P.aligned16 && (c + 1) * EPC <= nvalid) {
-                const vu32x4 v = gmem((const vu32x4*)rowp)[c];
-                raw[4 * j + 0] = v.x;
-                raw[4 * j + 1] = v.y;
-                raw[4 * j + 2] = v.z;
-                raw[4 * j + 3] = v.w;
-            } else {
+            vu32x4 v = {PAD, PAD, PAD, PAD};
+            if ((c + 1) * EPC <= nvalid) v = gmem((const vu32x4*)rowp)[c];
+            in.raw[4 * j + 0] = v.x;
+            in.raw[4 * j + 1] = v.y;
+            in.raw[4 * j + 2] = v.z;
+            in.raw[4 * j + 3] = v.w;
+        }
+    } else {
+        // rows that do not start on a 16-byte boundary: the exact general
+        // path reads the elements itself
 #pragma unroll
-                for (int k = 0; k < 4; ++k) raw[4 * j + k] = load_dword(4 * j + k);
+        for (int q = 0; q < NQ; ++q) in.raw[q] = PAD;
+    }
+    // the tile's grammar bitmask, coalesced: word base/32 + tid + 256k
+    if (P.aux.bitmask) {
+        constexpr int GW = CPT * EPC / 32;
+        const int words = (P.V + 31) / 32;
+        const auto gm = gmem(P.aux.bitmask + (int64_t)row * P.aux.bitmask_stride) + base / 32 + tid;
+#pragma unroll
+        for (int k = 0; k < GW; ++k)
+            in.gw[k] = (full || base / 32 + tid + k * S1_THREADS < words) ? gm[k * S1_THREADS] : 0u;
+    }
+}
+
+// Completes the chunk that straddles the end of V in a ragged tile (its
+// owner thread loads the elements inside V).  Called once the tile's own
+// loads have arrived and before later requests are issued.
+template <int DT>
+__device__ __forceinline__ void tile_patch(const Stage1Params& P, int row, int tile, S1In<DT>& in) {
+    S1_TILE_GEOMETRY
+    if (full || !P.aligned16) return;
+    const int cp = nvalid / EPC;         // first chunk not wholly inside V
+    const int rem = nvalid - cp * EPC;   // its elements inside V
+    if (rem == 0 || (cp & (S1_THREADS - 1)) != tid) return;
+    uint32_t pv[4] = {PAD, PAD, PAD, PAD};
+#pragma unroll
+    for (int k = 0; k < EPC; ++k) {
+        if (k < rem) {
+            if constexpr (DT == SS_BF16) {
+                const uint32_t h = gmem((const uint16_t*)rowp)[cp * EPC + k];
+                const int sft = 16 * (k & 1);
+                pv[k >> 1] = (pv[k >> 1] & ~(0xFFFFu << sft)) | (h << sft);
+            } else {
+                pv[k] = gmem((const uint32_t*)rowp)[cp * EPC + k];
             }
         }
     }
+    const int jp = cp / S1_THREADS;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j)
+        if (j == jp) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) in.raw[4 * j + k] = pv[k];
+        }
+}
 
-    uint32_t flags = 0;
-    int n_prior = 0, n_bias = 0;
-    if (P.req) {
-        const ss_req r = P.req[b];
-        flags = r.flags;
-        // a list longer than its stride makes the row invalid (reported by
-        // Stage 2); the tiles then use no list at all
-        n_prior = (int)r.n_prior <= P.aux.prior_stride ? (int)r.n_prior : 0;
-        n_bias = (int)r.n_bias <= P.aux.bias_stride ? (int)r.n_bias : 0;
-    }
+// The 128 best tokens of tile `tile` of row `row` (whose data `in` holds),
+// sorted best first, left in sh.surv[0..128) (key 0 = no token).  Ends with
+// a barrier.  `next()` is called as soon as the registers of `in` are no
+// longer needed (the candidate chunks are in LDS by then), so that the
+// caller can request its next tile into them while this one is finished.
+template <int DT, typename Next>
+__device__ __forceinline__ void tile_process(const Stage1Params& P, int row, int tile, S1In<DT>& in,
+                                             S1Shared<DT>& sh, Next&& next) {
+    S1_TILE_GEOMETRY
+    using Key = typename T::Key;
+    static_assert(S1_WAVES == 4, "merge tree");
+    uint32_t(&raw)[NQ] = in.raw;
+    auto load_dword = [&](int q) -> uint32_t { return tile_dword<DT>(rowp, vec, nvalid, q); };
+
+    const uint32_t flags = __builtin_amdgcn_readfirstlane(in.rq_flags);
+    const uint32_t lists = __builtin_amdgcn_readfirstlane(in.rq_lists);
+    // a list longer than its stride makes the row invalid (reported by
+    // Stage 2); the tiles then use no list at all
+    const int n_prior = (int)(lists & 0xFFu) <= P.aux.prior_stride ? (int)(lists & 0xFFu) : 0;
+    const int n_bias = (int)(lists >> 8) <= P.aux.bias_stride ? (int)(lists >> 8) : 0;
     const bool use_grammar = (flags & SS_GRAMMAR) && P.aux.bitmask;
     const bool use_prior = (flags & (SS_REP | SS_FREQPRES)) && P.aux.prior_ids && P.aux.prior_cnt && n_prior > 0;
     const bool use_bias = (flags & SS_BIAS) && P.aux.bias_ids && n_bias > 0;
 
-    // grammar bits of each chunk (bit e: element e allowed); one byte of
-    // the row's bitmask covers 8 tokens
-    uint32_t gbits[CPT];
+    // the tile's grammar words go to LDS; each thread then reads the bits
+    // of its own chunks
     if (use_grammar) {
-        const auto gm = gmem((const uint8_t*)(P.aux.bitmask + (int64_t)row * P.aux.bitmask_stride));
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-            const int g0 = base + (j * S1_THREADS + tid) * EPC;
-            uint32_t g = g0 < P.V ? (uint32_t)gm[g0 >> 3] : 0u;
-            if (DT == SS_F32) g >>= (g0 & 4);
-            gbits[j] = g;
+        for (int k = 0; k < CPT * EPC / 32; ++k) sh.gmw[tid + k * S1_THREADS] = in.gw[k];
+        if (DT == SS_BF16) {   // entry tid: bit 2k -> low half of dword k, bit 2k+1 -> high half
+            uint32_t mk[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                mk[k] = (((uint32_t)tid >> (2 * k)) & 1u ? 0x0000FFFFu : 0u) |
+                        (((uint32_t)tid >> (2 * k + 1)) & 1u ? 0xFFFF0000u : 0u);
+            sh.gtab[tid] = make_uint4(mk[0], mk[1], mk[2], mk[3]);
         }
     }
+    const int l_pid = in.l_pid, l_pct = in.l_pct, l_bid = in.l_bid;
 
-    // ---- tokens of this tile named by an active list: ranked in Stage 2,
-    // left out here.  Every wave counts them; wave 0 also records them. ----
-    int nl = 0;
-    if (use_prior) {
-        const auto ids = gmem(P.aux.prior_ids + (int64_t)b * P.aux.prior_stride);
-        const auto cts = gmem(P.aux.prior_cnt + (int64_t)b * P.aux.prior_stride);
-        for (int j0 = 0; j0 < n_prior; j0 += WAVE) {
-            const int j = j0 + lane;
-            bool ok = false;
-            int loc = 0;
-            if (j < n_prior) {
-                const int id = ids[j];
-                loc = id - base;
-                ok = cts[j] >= 1 && id >= 0 && id < P.V && loc >= 0 && loc < nvalid;
-            }
+    // ---- wave 0: tokens of this tile named by an active list (ranked in
+    // Stage 2, left out here) ----
+    if (wave == 0) {
+        int nl = 0;
+        auto record = [&](bool ok, int loc) {
             const uint64_t bal = __ballot(ok);
-            if (wave == 0 && ok) sh.listed[nl + __popcll(bal & lt)] = loc;
+            if (ok) {
+                const int i = nl + lane_prefix(bal);
+                sh.listed[i] = loc;
+                sh.lcb[i] = make_int2(loc / EPC, (int)chunk_bit<DT>(loc % EPC));
+            }
             nl += __popcll(bal);
+        };
+        // entries 0..63 come from the early request (no wait on memory
+        // here: the next tile's loads are in flight); longer lists load the
+        // rest now
+        if (use_prior) {
+            const int loc = l_pid - base;
+            record(lane < n_prior && l_pct >= 1 && l_pid >= 0 && l_pid < P.V && loc >= 0 && loc < nvalid, loc);
+            if (n_prior > WAVE) {
+                const auto ids = gmem(P.aux.prior_ids + (int64_t)b * P.aux.prior_stride);
+                const auto cts = gmem(P.aux.prior_cnt + (int64_t)b * P.aux.prior_stride);
+                for (int j0 = WAVE; j0 < n_prior; j0 += WAVE) {
+                    const int j = j0 + lane;
+                    const int id = j < n_prior ? ids[j] : -1;
+                    const int ct = j < n_prior ? cts[j] : 0;
+                    const int lc = id - base;
+                    record(j < n_prior && ct >= 1 && id >= 0 && id < P.V && lc >= 0 && lc < nvalid, lc);
+                }
+            }
+        }
+        if (use_bias) {
+            const int loc = l_bid - base;
+            record(lane < n_bias && l_bid >= 0 && l_bid < P.V && loc >= 0 && loc < nvalid, loc);
+            if (n_bias > WAVE) {
+                const auto ids = gmem(P.aux.bias_ids + (int64_t)b * P.aux.bias_stride);
+                for (int j0 = WAVE; j0 < n_bias; j0 += WAVE) {
+                    const int j = j0 + lane;
+                    const int id = j < n_bias ? ids[j] : -1;
+                    const int lc = id - base;
+                    record(j < n_bias && id >= 0 && id < P.V && lc >= 0 && lc < nvalid, lc);
+                }
+            }
+        }
+        if (lane == 0) {
+            sh.nl = nl;
+            sh.ovf = 0;
         }
     }
-    if (use_bias) {
-        const auto ids = gmem(P.aux.bias_ids + (int64_t)b * P.aux.bias_stride);
-        for (int j0 = 0; j0 < n_bias; j0 += WAVE) {
-            const int j = j0 + lane;
-            bool ok = false;
-            int loc = 0;
-            if (j < n_bias) {
-                const int id = ids[j];
-                loc = id - base;
-                ok = id >= 0 && id < P.V && loc >= 0 && loc < nvalid;
-            }
-            const uint64_t bal = __ballot(ok);
-            if (wave == 0 && ok) sh.listed[nl + __popcll(bal & lt)] = loc;
-            nl += __popcll(bal);
-        }
-    }
-    if (tid == 0) sh.ovf = 0;
+    __syncthreads();   // listed tokens, grammar table
+    const int nl = sh.nl;
 
     // ---- grammar: masked elements take PAD ----
     if (use_grammar) {
+        // bits of chunk j's elements allowed by the grammar (bit e: element e)
+        uint32_t gbits[CPT];
+        const uint8_t* gb = (const uint8_t*)sh.gmw;
+#pragma unroll
+        for (int j = 0; j < CPT; ++j)
+            gbits[j] = DT == SS_BF16 ? gb[j * S1_THREADS + tid]
+                                     : (uint32_t)gb[(j * S1_THREADS + tid) >> 1] >> ((tid & 1) * 4);
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
-            const uint32_t g = gbits[j];
-            if (DT == SS_BF16) {
-                // bit 2k -> low half of dword k, bit 2k+1 -> high half
-                const s16x2 G = bits_s16x2(g | (g << 16));
+            if constexpr (DT == SS_BF16) {
+                const uint4 M = sh.gtab[gbits[j]];
+                const uint32_t m4[4] = {M.x, M.y, M.z, M.w};
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const s16x2 sh_l = {(short)(15 - 2 * k), (short)(14 - 2 * k)};
-                    const s16x2 sh_r = {15, 15};
-                    const uint32_t M = s16x2_bits((G << sh_l) >> sh_r);
-                    raw[4 * j + k] = (raw[4 * j + k] & M) | (PAD & ~M);
-                }
+                for (int k = 0; k < 4; ++k) raw[4 * j + k] = (raw[4 * j + k] & m4[k]) | (PAD & ~m4[k]);
             } else {
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    const uint32_t M = 0u - ((g >> k) & 1u);
+                    const uint32_t M = 0u - ((gbits[j] >> k) & 1u);
                     raw[4 * j + k] = (raw[4 * j + k] & M) | (PAD & ~M);
                 }
             }
@@ -395,7 +513,7 @@ __device__ __forceinline__ void stage1_tile(const Stage1Params& P, int row, int 
         sh.tau[wave] = tau_w;
         sh.special[wave] = sp != 0ull;
     }
-    __syncthreads();   // tau, listed[], ovf
+    __syncthreads();   // tau
     int tau = sh.tau[0];
     bool any_special = false;
 #pragma unroll
@@ -403,7 +521,7 @@ __device__ __forceinline__ void stage1_tile(const Stage1Params& P, int row, int 
         tau = min(tau, sh.tau[w]);
         any_special |= sh.special[w] != 0;
     }
-    const bool fast = !any_special && tau >= 1 && nl_ok;   // block-uniform
+    const bool fast = !any_special && tau >= 1 && nl_ok && P.aligned16;   // block-uniform
 
     if (fast) {
         // ---- chunks holding a value >= tau go to the wave's LDS area ----
@@ -413,60 +531,60 @@ __device__ __forceinline__ void stage1_tile(const Stage1Params& P, int row, int 
         for (int j = 0; j < CPT; ++j) {
             bool f;
             if constexpr (DT == SS_BF16)
-                f = s16x2_bits(__builtin_elementwise_max(bits_s16x2(cmx[j]), bits_s16x2(T2))) != T2;
+                // the chunk maximum again, folded with tau - 1 (cheaper
+                // than holding the 16 maxima in registers meanwhile)
+                f = s16x2_bits(__builtin_elementwise_max(
+                        __builtin_elementwise_max(bits_s16x2(raw[4 * j]), bits_s16x2(raw[4 * j + 1])),
+                        __builtin_elementwise_max(bits_s16x2(raw[4 * j + 2]),
+                                                  __builtin_elementwise_max(bits_s16x2(raw[4 * j + 3]),
+                                                                            bits_s16x2(T2))))) != T2;
             else
-                f = (int)cmx[j] >= tau;
+                f = max(max((int)raw[4 * j], (int)raw[4 * j + 1]), max((int)raw[4 * j + 2], (int)raw[4 * j + 3])) >= tau;
             const uint64_t bal = __ballot(f);
-            if (f) {
-                const int s = wcnt + __popcll(bal & lt);
-                if (s < S1_CCAP) {
-                    sh.chunks[wave][s] = make_uint4(raw[4 * j], raw[4 * j + 1], raw[4 * j + 2], raw[4 * j + 3]);
-                    sh.cid[wave][s] = j * S1_THREADS + tid;
-                }
+            if (f && wcnt <= S1_CCAP) {   // slots up to S1_CCAP + 63 exist
+                const int s = wcnt + lane_prefix(bal);
+                sh.chunks[wave][s] = make_uint4(raw[4 * j], raw[4 * j + 1], raw[4 * j + 2], raw[4 * j + 3]);
+                sh.cid[wave][s] = j * S1_THREADS + tid;
             }
             wcnt += __popcll(bal);
         }
+        next();   // in.raw is free from here on
         wave_lds_sync();
 
-        // ---- the survivors of those chunks become keys (listed ones dropped) ----
+        // ---- their elements >= tau that are not listed become keys, one
+        // per lane per round ----
         const int nck = min(wcnt, S1_CCAP);
         int nk = 0;
         for (int s0 = 0; s0 < nck; s0 += WAVE) {
             const int s = s0 + lane;
-            uint4 d = make_uint4(PAD, PAD, PAD, PAD);
-            int c = -1;
+            uint32_t sm = 0;
+            int c = 0;
             if (s < nck) {
-                d = sh.chunks[wave][s];
                 c = sh.cid[wave][s];
-            }
-            uint32_t ex = 0;
-            for (int i = 0; i < nl; ++i) {
-                const int loc = sh.listed[i];
-                if (loc / EPC == c) ex |= 1u << (loc % EPC);
-            }
-            const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) {
-                uint32_t h;
-                int v;
-                if constexpr (DT == SS_BF16) {
-                    h = (dw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                    v = (int)(short)h;
-                } else {
-                    h = dw[e];
-                    v = (int)h;
+                sm = chunk_survivors<DT>(sh.chunks[wave][s], tau);
+                for (int i = 0; i < nl; ++i) {
+                    const int2 e = sh.lcb[i];
+                    if (e.x == c) sm &= ~(uint32_t)e.y;
                 }
-                const bool sv = v >= tau && !((ex >> e) & 1u);
-                const uint64_t bal = __ballot(sv);
-                if (sv) {
-                    const int slot = nk + __popcll(bal & lt);
+            }
+            const auto elems = (const uint8_t*)&sh.chunks[wave][s < nck ? s : 0];
+            for (;;) {
+                const bool act = sm != 0;
+                const uint64_t bal = __ballot(act);
+                if (bal == 0ull) break;
+                if (act) {
+                    const int e = chunk_elem<DT>(__builtin_ctz(sm));
+                    sm &= sm - 1u;
+                    const int slot = nk + lane_prefix(bal);
                     const int local = c * EPC + e;
-                    if (slot < S1_KCAP) {
-                        // value > 0 and not NaN here
-                        if constexpr (DT == SS_BF16)
+                    if (slot < S1_KCAP) {   // value > 0 and not NaN here
+                        if constexpr (DT == SS_BF16) {
+                            const uint32_t h = *(const uint16_t*)(elems + 2 * e);
                             sh.keys[wave][slot] = ((h | 0x8000u) << 16) | (0xFFFFu - (uint32_t)local);
-                        else
+                        } else {
+                            const uint32_t h = *(const uint32_t*)(elems + 4 * e);
                             sh.keys[wave][slot] = key_f32(h, local, true, true);
+                        }
                     }
                 }
                 nk += __popcll(bal);
@@ -480,6 +598,8 @@ __device__ __forceinline__ void stage1_tile(const Stage1Params& P, int row, int 
             sh.wl[wave][lane] = mine.lo;
             sh.wl[wave][lane + WAVE] = mine.hi;
         }
+    } else {
+        next();
     }
     __syncthreads();   // wave lists, ovf
 
@@ -506,41 +626,26 @@ __device__ __forceinline__ void stage1_tile(const Stage1Params& P, int row, int 
     }
 
     // ---- general path: exact keys for every element (re-read from cache),
-    // bisection for the 128th key ----
-    const uint32_t all_bits = (1u << EPC) - 1u;
-    uint64_t alw = ~0ull, pres = ~0ull, excl = 0;
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-        const int c0 = (j * S1_THREADS + tid) * EPC;
-        uint32_t pb = all_bits;
-        if (!full) pb = c0 >= nvalid ? 0u : (nvalid - c0 >= EPC ? all_bits : ((1u << (nvalid - c0)) - 1u));
-        pres &= ~((uint64_t)(all_bits & ~pb) << (j * EPC));
-        if (use_grammar && pb) {
-            const int g0 = base + c0;
-            const uint32_t w = gmem(P.aux.bitmask)[(int64_t)row * P.aux.bitmask_stride + (g0 >> 5)];
-            alw &= ~((uint64_t)(all_bits & ~((w >> (g0 & 31)) & all_bits)) << (j * EPC));
-        }
-    }
-    for (int i = 0; i < nl; ++i) {
-        const int loc = sh.listed[i];
-        const int c = loc / EPC;
-        if ((c & (S1_THREADS - 1)) == tid) excl |= 1ull << ((c / S1_THREADS) * EPC + (loc % EPC));
-    }
+    // bisection for the 128th key.  The tile's listed tokens go to a bitmap
+    // in LDS (over the chunk areas, no longer in use). ----
+    uint32_t* lbm = (uint32_t*)&sh.chunks[0][0];
+    static_assert(BN / 32 * 4 <= (int)sizeof(sh.chunks), "listed bitmap");
+    for (int i = tid; i < BN / 32; i += S1_THREADS) lbm[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < nl; i += S1_THREADS) atomicOr(&lbm[sh.listed[i] >> 5], 1u << (sh.listed[i] & 31));
+    __syncthreads();
+    const auto gmask = gmem(P.aux.bitmask + (use_grammar ? (int64_t)row * P.aux.bitmask_stride : 0));
     auto ekey = [&](int q, int h) -> Key {
         const uint32_t d = load_dword(q);
         const int c = (q >> 2) * S1_THREADS + tid;
-        if (DT == SS_BF16) {
-            const int e = 2 * (q & 3) + h;
-            const int bitpos = (q >> 2) * EPC + e;
-            const bool present = ((pres & ~excl) >> bitpos) & 1ull;
-            const bool allowed = (alw >> bitpos) & 1ull;
-            return (Key)key_bf16(h ? (d >> 16) : (d & 0xFFFFu), c * EPC + e, present, allowed);
-        } else {
-            const int bitpos = q;
-            const bool present = ((pres & ~excl) >> bitpos) & 1ull;
-            const bool allowed = (alw >> bitpos) & 1ull;
-            return (Key)key_f32(d, c * EPC + (q & 3), present, allowed);
-        }
+        const int e = DT == SS_BF16 ? 2 * (q & 3) + h : (q & 3);
+        const int loc = c * EPC + e;
+        const bool present = loc < nvalid && !((lbm[loc >> 5] >> (loc & 31)) & 1u);
+        const bool allowed = present && (!use_grammar || ((gmask[(base + loc) >> 5] >> ((base + loc) & 31)) & 1u));
+        if constexpr (DT == SS_BF16)
+            return (Key)key_bf16(h ? (d >> 16) : (d & 0xFFFFu), loc, present, allowed);
+        else
+            return (Key)key_f32(d, loc, present, allowed);
     };
     constexpr int HALVES = DT == SS_BF16 ? 2 : 1;
     constexpr int KB = (int)sizeof(Key) * 8;
@@ -549,7 +654,9 @@ __device__ __forceinline__ void stage1_tile(const Stage1Params& P, int row, int 
     for (int bit = KB - 1; bit >= 0; --bit) {
         const Key cand = res | ((Key)1 << bit);
         int c = 0;
+#pragma nounroll
         for (int q = 0; q < NQ; ++q)
+#pragma unroll
             for (int h = 0; h < HALVES; ++h) c += ekey(q, h) >= cand;
         c = wave_sum(c);
         if (lane == 0) sh.red[parity][wave] = c;
@@ -562,12 +669,16 @@ __device__ __forceinline__ void stage1_tile(const Stage1Params& P, int row, int 
     }
     const Key thr = res > (Key)1 ? res : (Key)1;   // key 0 = no token
     int cnt = 0;
+#pragma nounroll
     for (int q = 0; q < NQ; ++q)
+#pragma unroll
         for (int h = 0; h < HALVES; ++h) cnt += ekey(q, h) >= thr;
     int total;
     int off = block_excl_scan(cnt, sh.scan, &total);   // total <= 128 (keys are unique)
     Key* g = &sh.keys[0][0];
+#pragma nounroll
     for (int q = 0; q < NQ; ++q)
+#pragma unroll
         for (int h = 0; h < HALVES; ++h) {
             const Key k = ekey(q, h);
             if (k >= thr) g[off++] = k;
@@ -580,6 +691,15 @@ __device__ __forceinline__ void stage1_tile(const Stage1Params& P, int row, int 
         sh.surv[lane + WAVE] = l.hi;
     }
     __syncthreads();
+}
+
+// One tile, requested and processed in turn.
+template <int DT>
+__device__ __forceinline__ void stage1_tile(const Stage1Params& P, int row, int tile, S1Shared<DT>& sh) {
+    S1In<DT> in;
+    tile_fetch<DT>(P, row, tile, in);
+    tile_patch<DT>(P, row, tile, in);
+    tile_process<DT>(P, row, tile, in, sh, [] {});
 }
 
 }  // namespace ssd

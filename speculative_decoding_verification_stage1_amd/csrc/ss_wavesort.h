@@ -3,6 +3,12 @@
 // build and merge them with cross-lane exchanges instead of LDS round trips
 // and workgroup barriers.  Keys are unsigned (uint32 or uint64); larger is
 // better.
+//
+// A compare-exchange with lane ^ J keeps the larger key in some lanes and
+// the smaller in the others; which lanes do depends only on J and the stage,
+// so it is a compile-time 64-bit lane mask, turned into a per-lane flag with
+// no vector instruction (inverse ballot).  Each step is then one exchange,
+// one compare and one select.
 #pragma once
 
 #include "ss_device.h"
@@ -25,20 +31,29 @@ __device__ __forceinline__ K kmax(K a, K b) { return a > b ? a : b; }
 template <typename K>
 __device__ __forceinline__ K kmin(K a, K b) { return a < b ? a : b; }
 
-// Compare-exchange with lane ^ J in both halves; the lane keeps the larger
-// key where *_max is set.
-template <int J, typename K>
-__device__ __forceinline__ void cas_step(WList<K>& c, bool lo_max, bool hi_max) {
-    const K plo = xor_key<J>(c.lo), phi = xor_key<J>(c.hi);
-    c.lo = lo_max ? kmax(c.lo, plo) : kmin(c.lo, plo);
-    c.hi = hi_max ? kmax(c.hi, phi) : kmin(c.hi, phi);
+// Lanes l (0..63) of a 64-key block at index offset `off` that keep the
+// larger key at exchange distance J in a stage sorting blocks of KS keys,
+// descending where (index & KS) == 0.
+constexpr uint64_t keep_max_mask(int J, int KS, int off) {
+    uint64_t m = 0;
+    for (int l = 0; l < 64; ++l)
+        if (((l & J) == 0) == (((l + off) & KS) == 0)) m |= 1ull << l;
+    return m;
+}
+
+template <int J, uint64_t KEEP, typename K>
+__device__ __forceinline__ K cas_lane(K a) {
+    const K p = xor_key<J>(a);
+    const bool keep_max = __builtin_amdgcn_inverse_ballot_w64(KEEP);
+    return ((p > a) == keep_max) ? p : a;
 }
 
 // Half-cleaners j = J .. 1 on both halves (descending).
 template <int J = 32, typename K>
 __device__ __forceinline__ void wave_half_clean(WList<K>& c) {
-    const bool lower = (lane_id() & J) == 0;
-    cas_step<J>(c, lower, lower);
+    constexpr uint64_t M = keep_max_mask(J, 128, 0);   // lower lane of each pair keeps the max
+    c.lo = cas_lane<J, M>(c.lo);
+    c.hi = cas_lane<J, M>(c.hi);
     if constexpr (J > 1) wave_half_clean<J / 2>(c);
 }
 
@@ -74,15 +89,12 @@ __device__ __forceinline__ WList<K> wave_merge(const WList<K>& a, const WList<K>
     return c;
 }
 
-// Bitonic sort (descending) of 128 keys.  Stage k sorts blocks of k keys,
-// descending where (index & k) == 0 and ascending otherwise.
+// Bitonic sort (descending) of 128 keys.  Stage KS sorts blocks of KS keys,
+// descending where (index & KS) == 0 and ascending otherwise.
 template <int KS, int J, typename K>
 __device__ __forceinline__ void sort_substeps(WList<K>& c) {
-    const int lane = lane_id();
-    const bool lower = (lane & J) == 0;
-    const bool dlo = (lane & KS) == 0;
-    const bool dhi = ((lane + 64) & KS) == 0;
-    cas_step<J>(c, lower == dlo, lower == dhi);
+    c.lo = cas_lane<J, keep_max_mask(J, KS, 0)>(c.lo);
+    c.hi = cas_lane<J, keep_max_mask(J, KS, 64)>(c.hi);
     if constexpr (J > 1) sort_substeps<KS, J / 2>(c);
 }
 template <int KS = 2, typename K>
@@ -96,6 +108,18 @@ __device__ __forceinline__ WList<K> wave_sort128(WList<K> c) {
     cas_64(c);
     wave_half_clean(c);
     return c;
+}
+
+// Bitonic sort (descending) of 64 keys, one per lane.
+template <int KS, int J, typename K>
+__device__ __forceinline__ void sort64_substeps(K& v) {
+    v = cas_lane<J, keep_max_mask(J, KS, 0)>(v);
+    if constexpr (J > 1) sort64_substeps<KS, J / 2>(v);
+}
+template <int KS = 2, typename K>
+__device__ __forceinline__ void wave_sort64(K& v) {
+    sort64_substeps<KS, KS / 2>(v);
+    if constexpr (KS < 64) wave_sort64<KS * 2>(v);
 }
 
 }  // namespace ssd

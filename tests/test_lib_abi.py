@@ -77,12 +77,13 @@ int main(void) {
 
 
 def test_sizes(L):
-    assert L.ss_tile_size(L.SS_BF16) == 16384
-    assert L.ss_tile_size(L.SS_F32) == 8192
+    assert L.ss_tile_size(L.SS_BF16) == 32768
+    assert L.ss_tile_size(L.SS_F32) == 16384
     assert L.ss_tile_size(9) == 0
-    # 256 rows x 16 tiles x 128 keys x 4 B + per-row records
+    # 256 rows x 8 tiles x 128 keys x 4 B, listed keys 256 x 128 x 8 B,
+    # plus per-row records
     ws = L.ss_workspace_bytes(256, 262144, L.SS_BF16)
-    assert ws >= 256 * 16 * 128 * 4
+    assert ws >= 256 * 8 * 128 * 4 + 256 * 128 * 8
     assert ws % 256 == 0
     assert L.ss_workspace_bytes(-1, 10, 0) == 0
     assert L.ss_workspace_bytes(1, 0, 0) == 0
