@@ -81,18 +81,16 @@ def main():
 
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
-    # one graph holds one step on each input copy (each step: the fused
-    # sampling launch + the device-side offset advance); replays run back to
-    # back, so the timed region is GPU work, not Python launch gaps
+    # one graph holds one step on each input copy (each step advances the
+    # device-side Philox offset itself); replays run back to back, so the
+    # timed region is GPU work, not Python launch gaps
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=stream):
         for i in range(args.copies):
-            L.ss_sample_step(xs[i], dreqs[i], rng, toks, ws=ws, stream=stream)
-            L.ss_rng_advance(rng, 1, stream=stream)
+            L.ss_sample_step(xs[i], dreqs[i], rng, toks, ws=ws, stream=stream, rng_advance=1)
     single = torch.cuda.CUDAGraph()
     with torch.cuda.graph(single, stream=stream):
-        L.ss_sample_step(xs[0], dreqs[0], rng, toks, ws=ws, stream=stream)
-        L.ss_rng_advance(rng, 1, stream=stream)
+        L.ss_sample_step(xs[0], dreqs[0], rng, toks, ws=ws, stream=stream, rng_advance=1)
     torch.cuda.synchronize()
 
     reps = max(1, args.steps // args.copies)
@@ -199,8 +197,8 @@ def main():
         vgraph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(vgraph, stream=stream):
             for i in range(tcopies):
-                L.ss_verify_step(ts[i], vw.B, G, vreq, rng, d, q, vout, vne, None, vws, stream=stream)
-                L.ss_rng_advance(rng, 1, stream=stream)
+                L.ss_verify_step(ts[i], vw.B, G, vreq, rng, d, q, vout, vne, None, vws, stream=stream,
+                                 rng_advance=1)
         torch.cuda.synchronize()
         for i in range(3):
             vgraph.replay()

@@ -109,7 +109,8 @@ typedef struct ss_req {
 } ss_req;
 
 /* Philox seed and offset, in DEVICE memory; the kernels read them at run
- * time, so a captured graph draws new noise after ss_rng_advance. */
+ * time, so a captured graph draws new noise after ss_rng_advance, or on
+ * every replay when the step advances the offset itself (rng_advance). */
 typedef struct ss_rng {
     uint64_t seed;
     uint64_t offset;
@@ -171,9 +172,13 @@ int ss_tile_size(int dtype);
  *   out_tokens [B] int32, out_topk_ids [B,128] int32 (the K candidates, -1
  *   after), out_probs [B,128] float (e_k / Z; greedy rows 1,0,...),
  *   out_kept [B] int32 (kept count), out_mass [B] float (kept mass / Z),
- *   out_status [B] int32 (SS_ROW_*). */
+ *   out_status [B] int32 (SS_ROW_*).
+ * rng_advance: the step copies *rng into its workspace in its first launch
+ * and then adds rng_advance to rng->offset on the device (0 leaves *rng
+ * untouched); its own draws use the copied offset.  A decode loop or a
+ * captured graph thus needs no separate ss_rng_advance. */
 int ss_sample_step(const void* logits, int dtype, int B, int V, int64_t ld,
-                   const ss_req* req, const ss_aux* aux, const ss_rng* rng,
+                   const ss_req* req, const ss_aux* aux, ss_rng* rng, uint64_t rng_advance,
                    int32_t* out_tokens, int32_t* out_topk_ids, float* out_probs,
                    int32_t* out_kept, float* out_mass, int32_t* out_status,
                    void* ws, size_t ws_bytes, void* stream);
@@ -198,9 +203,10 @@ int ss_sample_step(const void* logits, int dtype, int B, int V, int64_t ld,
  * mismatch and stop, and emit the best id of row gamma when all match.
  * Outputs: out_tokens [B, gamma+1] (-1 after the emitted ones), out_n_emit
  * [B], out_status [B] (optional; SS_ROW_ALL_MASKED when a target row that
- * is reached has no finite candidate). */
+ * is reached has no finite candidate).  rng_advance as for
+ * ss_sample_step. */
 int ss_verify_step(const void* target_logits, int dtype, int B, int gamma, int V, int64_t ld,
-                   const ss_req* req, const ss_aux* aux, const ss_rng* rng,
+                   const ss_req* req, const ss_aux* aux, ss_rng* rng, uint64_t rng_advance,
                    const int32_t* draft_ids, const float* draft_probs,
                    int32_t* out_tokens, int32_t* out_n_emit, int32_t* out_status,
                    void* ws, size_t ws_bytes, void* stream);

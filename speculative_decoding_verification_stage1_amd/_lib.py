@@ -72,9 +72,9 @@ def _load():
     L.ss_workspace_bytes.restype = sz
     L.ss_tile_size.argtypes = [i32]
     L.ss_tile_size.restype = i32
-    L.ss_sample_step.argtypes = [P, i32, i32, i32, i64, P, P, P, P, P, P, P, P, P, P, sz, P]
+    L.ss_sample_step.argtypes = [P, i32, i32, i32, i64, P, P, P, u64, P, P, P, P, P, P, P, sz, P]
     L.ss_sample_step.restype = i32
-    L.ss_verify_step.argtypes = [P, i32, i32, i32, i32, i64, P, P, P, P, P, P, P, P, P, sz, P]
+    L.ss_verify_step.argtypes = [P, i32, i32, i32, i32, i64, P, P, P, u64, P, P, P, P, P, P, sz, P]
     L.ss_verify_step.restype = i32
     L.ss_topk_step.argtypes = [P, i32, i32, i32, i64, i32, P, P, P, sz, P]
     L.ss_topk_step.restype = i32
@@ -212,20 +212,22 @@ def dtype_code(t) -> int:
 # ---------------------------------------------------------------------------
 
 def ss_sample_step(logits, dreq: DeviceRequests, rng, out_tokens, out_topk_ids=None, out_probs=None,
-                   out_kept=None, out_mass=None, out_status=None, ws=None, stream=None) -> int:
+                   out_kept=None, out_mass=None, out_status=None, ws=None, stream=None,
+                   rng_advance: int = 0) -> int:
     B, V = logits.shape
     rc = lib.ss_sample_step(ptr(logits), dtype_code(logits), B, V, logits.stride(0), ptr(dreq.req),
-                            ctypes.byref(dreq.aux), ptr(rng), ptr(out_tokens), ptr(out_topk_ids),
+                            ctypes.byref(dreq.aux), ptr(rng), rng_advance, ptr(out_tokens), ptr(out_topk_ids),
                             ptr(out_probs), ptr(out_kept), ptr(out_mass), ptr(out_status), ptr(ws),
                             0 if ws is None else ws.numel(), stream_handle(stream))
     return _check(rc)
 
 
 def ss_verify_step(target, B: int, gamma: int, dreq: DeviceRequests, rng, draft_ids, draft_probs,
-                   out_tokens, out_n_emit, out_status=None, ws=None, stream=None) -> int:
+                   out_tokens, out_n_emit, out_status=None, ws=None, stream=None,
+                   rng_advance: int = 0) -> int:
     rows, V = target.shape
     rc = lib.ss_verify_step(ptr(target), dtype_code(target), B, gamma, V, target.stride(0), ptr(dreq.req),
-                            ctypes.byref(dreq.aux), ptr(rng), ptr(draft_ids), ptr(draft_probs),
+                            ctypes.byref(dreq.aux), ptr(rng), rng_advance, ptr(draft_ids), ptr(draft_probs),
                             ptr(out_tokens), ptr(out_n_emit), ptr(out_status), ptr(ws),
                             0 if ws is None else ws.numel(), stream_handle(stream))
     return _check(rc)

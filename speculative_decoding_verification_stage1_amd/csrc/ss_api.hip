@@ -20,18 +20,21 @@ size_t scratch_bytes(int rows, int V, int dtype) {
 }
 size_t rec_bytes(int rows) { return align256((size_t)rows * sizeof(RowRec)); }
 size_t listed_bytes(int rows) { return align256((size_t)rows * KMAX * sizeof(uint64_t)); }
+constexpr size_t RNG_SNAP_BYTES = 256;
 
-// workspace: [tile keys][listed-token keys][row records]
+// workspace: [tile keys][listed-token keys][row records][rng copy]
 struct WsLayout {
     void* scratch;
     uint64_t* listed;
     RowRec* recs;
+    ss_rng* rng_snap;
 };
 WsLayout ws_layout(void* ws, int rows, int V, int dtype) {
     WsLayout L;
     L.scratch = ws;
     L.listed = (uint64_t*)((char*)ws + scratch_bytes(rows, V, dtype));
     L.recs = (RowRec*)((char*)L.listed + listed_bytes(rows));
+    L.rng_snap = (ss_rng*)((char*)L.recs + rec_bytes(rows));
     return L;
 }
 
@@ -88,7 +91,8 @@ Stage1Params make_s1(const void* logits, int dtype, int rows, int V, int64_t ld,
 }
 
 void launch_stage1(int dtype, const Stage1Params& p, hipStream_t s) {
-    const dim3 grid((unsigned)(p.listed_rows + p.rows * p.Zv)), block(S1_THREADS);
+    const int listed_wgs = (p.listed_rows + S1_WAVES - 1) / S1_WAVES;
+    const dim3 grid((unsigned)(listed_wgs + p.rows * p.Zv)), block(S1_THREADS);
     if (dtype == SS_BF16) hipLaunchKernelGGL(stage1_kernel<SS_BF16>, grid, block, 0, s, p);
     else hipLaunchKernelGGL(stage1_kernel<SS_F32>, grid, block, 0, s, p);
 }
@@ -173,7 +177,7 @@ int ss_tile_size(int dtype) {
 
 size_t ss_workspace_bytes(int rows, int V, int dtype) {
     if (rows < 0 || V < 1 || (dtype != SS_F32 && dtype != SS_BF16)) return 0;
-    return scratch_bytes(rows, V, dtype) + listed_bytes(rows) + rec_bytes(rows);
+    return scratch_bytes(rows, V, dtype) + listed_bytes(rows) + rec_bytes(rows) + RNG_SNAP_BYTES;
 }
 
 const char* ss_status_str(int status) {
@@ -188,7 +192,7 @@ const char* ss_status_str(int status) {
 }
 
 int ss_sample_step(const void* logits, int dtype, int B, int V, int64_t ld, const ss_req* req,
-                   const ss_aux* aux, const ss_rng* rng, int32_t* out_tokens, int32_t* out_topk_ids,
+                   const ss_aux* aux, ss_rng* rng, uint64_t rng_advance, int32_t* out_tokens, int32_t* out_topk_ids,
                    float* out_probs, int32_t* out_kept, float* out_mass, int32_t* out_status, void* ws,
                    size_t ws_bytes, void* stream) {
     int rc = check_logits(logits, dtype, B, V, ld);
@@ -202,8 +206,11 @@ int ss_sample_step(const void* logits, int dtype, int B, int V, int64_t ld, cons
     Stage1Params s1 = make_s1(logits, dtype, B, V, ld, 1, req, aux, W.scratch, nullptr);
     s1.listed = W.listed;
     s1.listed_rows = B;
+    s1.rng = rng;
+    s1.rng_snap = W.rng_snap;
+    s1.rng_advance = rng_advance;
     launch_stage1(dtype, s1, s);
-    Stage2Params f = make_s2(s1, rng, MODE_SAMPLE, W);
+    Stage2Params f = make_s2(s1, W.rng_snap, MODE_SAMPLE, W);
     f.tokens = out_tokens;
     f.topk_ids = out_topk_ids;
     f.probs = out_probs;
@@ -215,7 +222,7 @@ int ss_sample_step(const void* logits, int dtype, int B, int V, int64_t ld, cons
 }
 
 int ss_verify_step(const void* target_logits, int dtype, int B, int gamma, int V, int64_t ld,
-                   const ss_req* req, const ss_aux* aux, const ss_rng* rng, const int32_t* draft_ids,
+                   const ss_req* req, const ss_aux* aux, ss_rng* rng, uint64_t rng_advance, const int32_t* draft_ids,
                    const float* draft_probs, int32_t* out_tokens, int32_t* out_n_emit, int32_t* out_status,
                    void* ws, size_t ws_bytes, void* stream) {
     if (gamma < 1 || gamma > SS_GAMMA_MAX) return SS_ERR_UNSUPPORTED;
@@ -232,8 +239,11 @@ int ss_verify_step(const void* target_logits, int dtype, int B, int gamma, int V
     Stage1Params s1 = make_s1(target_logits, dtype, rows, V, ld, gamma + 1, req, aux, W.scratch, nullptr);
     s1.listed = W.listed;
     s1.listed_rows = rows;
+    s1.rng = rng;
+    s1.rng_snap = W.rng_snap;
+    s1.rng_advance = rng_advance;
     launch_stage1(dtype, s1, s);
-    Stage2Params f = make_s2(s1, rng, MODE_VERIFY, W);
+    Stage2Params f = make_s2(s1, W.rng_snap, MODE_VERIFY, W);
     f.gamma = gamma;
     f.draft_ids = draft_ids;
     f.draft_probs = draft_probs;

@@ -12,23 +12,33 @@ namespace ssd {
 template <int DT>
 union S1KernelShared {
     S1Shared<DT> tile;
-    S2Lists lists;
+    S2Lists lists[S1_WAVES];
 };
 
-// Workgroups 0 .. listed_rows-1 compute each row's listed tokens (ranked in
-// Stage 2); the rest each own one (row, tile).  The listed workgroups come
-// first so they run alongside the streaming, not after it.
+// The first ceil(listed_rows / 4) workgroups compute the rows' listed
+// tokens (ranked in Stage 2), one row per wave; the rest each own one
+// (row, tile).  The listed workgroups come first so they run alongside the
+// streaming, not after it.
 template <int DT>
 __global__ __launch_bounds__(S1_THREADS) void stage1_kernel(Stage1Params P) {
     using Key = typename S1Traits<DT>::Key;
     __shared__ S1KernelShared<DT> shu;
     const int tid = threadIdx.x;
-    if ((int)blockIdx.x < P.listed_rows) {
-        listed_row<DT>(P, P.listed, blockIdx.x, shu.lists);
+    if (blockIdx.x == 0 && tid == 0 && P.rng_snap) {   // the step's copy of the generator state
+        ss_rng r{0ull, 0ull};
+        if (P.rng) r = *P.rng;
+        *P.rng_snap = r;
+        if (P.rng && P.rng_advance) P.rng->offset = r.offset + P.rng_advance;
+    }
+    const int nlw = (P.listed_rows + S1_WAVES - 1) / S1_WAVES;
+    if ((int)blockIdx.x < nlw) {
+        const int wave = tid / WAVE;
+        const int r = (int)blockIdx.x * S1_WAVES + wave;
+        if (r < P.listed_rows) listed_row_wave<DT>(P, P.listed, r, shu.lists[wave]);
         return;
     }
     S1Shared<DT>& sh = shu.tile;
-    const int wg = blockIdx.x - P.listed_rows;
+    const int wg = blockIdx.x - nlw;
     const int row = wg / P.Zv;
     const int tile = wg - row * P.Zv;
     stage1_tile<DT>(P, row, tile, sh);

@@ -75,8 +75,11 @@ struct Stage1Params {
     void* scratch;       // keys [rows][Zv][128]
     int32_t* out_ids;    // optional [rows][Zv][128]
     uint64_t* listed;    // [rows][128] listed tokens' merge keys (sampling / verification)
-    int listed_rows;     // workgroups 0 .. listed_rows-1 compute them
+    int listed_rows;     // rows 0 .. listed_rows-1 need them (one wave per row)
     int aligned16;       // rows start on 16-byte boundaries
+    ss_rng* rng;         // sampling / verification: the caller's generator state
+    ss_rng* rng_snap;    // ... copied here for Stage 2 (workgroup 0)
+    uint64_t rng_advance;   // ... after which rng->offset += rng_advance
 };
 
 // Largest t such that at least k lanes of the wave hold m >= t (signed).

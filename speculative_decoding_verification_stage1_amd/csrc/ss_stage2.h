@@ -111,11 +111,11 @@ __device__ inline RowParams row_params(const Stage1Params& P, int b) {
     if ((f & SS_BIAS) && r.n_bias > 0 && (!P.aux.bias_ids || !P.aux.bias_val)) ok = false;
     if ((f & SS_REP) && !(finitef(r.rep_penalty) && r.rep_penalty > 0.0f)) ok = false;
     if ((f & SS_FREQPRES) && !(finitef(r.freq_penalty) && finitef(r.pres_penalty))) ok = false;
-    if (ok && (f & SS_BIAS)) {
-        const float* bv = P.aux.bias_val + (int64_t)b * P.aux.bias_stride;
-        bool fin = true;
-        for (int j = 0; j < (int)r.n_bias; ++j) fin &= finitef(bv[j]);
-        ok = fin;
+    if (ok && (f & SS_BIAS)) {   // every bias value finite: lanes check in parallel
+        const auto bv = gmem(P.aux.bias_val + (int64_t)b * P.aux.bias_stride);
+        bool bad = false;
+        for (int j = lane_id(); j < (int)r.n_bias; j += WAVE) bad |= !finitef(bv[j]);
+        ok = __ballot(bad) == 0ull;
     }
     bool g = (f & SS_GREEDY) != 0;
     if (!g) {
@@ -306,29 +306,31 @@ __device__ __forceinline__ WL64 listed_list(const Stage1Params& P, const RowPara
 // One workgroup of the Stage-1 launch per row computes the row's listed
 // tokens (wave 0) and stores the best 128 as merge keys; it runs alongside
 // the tile workgroups, so Stage 2 only has to load one more sorted list.
+// One wave computes row `row`'s listed tokens: its lists are staged in the
+// wave's own LDS area, then ranked as exact keys (list order arithmetic).
 template <int DT>
-__device__ __forceinline__ void listed_row(const Stage1Params& P, uint64_t* out, int row, S2Lists& lists) {
-    const int b = row / P.rows_per_req;
+__device__ __forceinline__ void listed_row_wave(const Stage1Params& P, uint64_t* out, int row, S2Lists& lists) {
+    const int b = __builtin_amdgcn_readfirstlane(row / P.rows_per_req);
     const RowParams rp = row_params(P, b);
     const int np = rp.valid ? rp.n_prior : 0;
     const int nb = rp.valid ? rp.n_bias : 0;
-    if (np + nb == 0) return;   // block-uniform; Stage 2 skips rows without lists
-    const int32_t* pid = P.aux.prior_ids + (int64_t)b * P.aux.prior_stride;
-    const int32_t* pct = P.aux.prior_cnt + (int64_t)b * P.aux.prior_stride;
-    const int32_t* bid = P.aux.bias_ids + (int64_t)b * P.aux.bias_stride;
-    const float* bvl = P.aux.bias_val + (int64_t)b * P.aux.bias_stride;
-    for (int u = threadIdx.x; u < np; u += blockDim.x) {
+    if (np + nb == 0) return;   // wave-uniform; Stage 2 skips rows without lists
+    const auto pid = gmem(P.aux.prior_ids + (int64_t)b * P.aux.prior_stride);
+    const auto pct = gmem(P.aux.prior_cnt + (int64_t)b * P.aux.prior_stride);
+    const auto bid = gmem(P.aux.bias_ids + (int64_t)b * P.aux.bias_stride);
+    const auto bvl = gmem(P.aux.bias_val + (int64_t)b * P.aux.bias_stride);
+    const int lane = lane_id();
+    for (int u = lane; u < np; u += WAVE) {
         lists.pid[u] = pid[u];
         lists.pct[u] = pct[u];
     }
-    for (int u = threadIdx.x; u < nb; u += blockDim.x) {
+    for (int u = lane; u < nb; u += WAVE) {
         lists.bid[u] = bid[u];
         lists.bval[u] = bvl[u];
     }
-    __syncthreads();
-    if (threadIdx.x >= WAVE) return;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
     const WL64 l = listed_list<DT>(P, rp, row, np, nb, lists);
-    const int lane = lane_id();
     out[(int64_t)row * KMAX + lane] = l.lo;
     out[(int64_t)row * KMAX + lane + WAVE] = l.hi;
 }
@@ -337,29 +339,45 @@ constexpr int S2_THREADS = 256;
 constexpr int S2_WAVES = S2_THREADS / WAVE;
 constexpr int S2_PREFETCH = 4;   // tile lists per wave requested up front
 
-// The row's 128 best as a wave-0 register list.  Every load is issued
-// before any merging; one workgroup barrier.
+// The row's Stage-1 lists, requested before anything else in Stage 2.
 template <int DT>
-__device__ __forceinline__ WL64 row_merge(const Stage2Params& F, const RowParams& rp, int row, S2Shared& sh) {
+struct RowLoads {
+    typename S1Traits<DT>::Key pre_lo[S2_PREFETCH], pre_hi[S2_PREFETCH];
+    WL64 listed;
+};
+template <int DT>
+__device__ __forceinline__ void row_loads(const Stage2Params& F, int row, RowLoads<DT>& L) {
+    using Key = typename S1Traits<DT>::Key;
+    const Stage1Params& P = F.s1;
+    const int lane = lane_id();
+    const int wave = threadIdx.x / WAVE;
+    const auto sc = gmem((const Key*)P.scratch + (int64_t)row * P.Zv * KMAX);
+#pragma unroll
+    for (int i = 0; i < S2_PREFETCH; ++i) {
+        const int t = wave + S2_WAVES * i;
+        L.pre_lo[i] = t < P.Zv ? sc[(int64_t)t * KMAX + lane] : (Key)0;
+        L.pre_hi[i] = t < P.Zv ? sc[(int64_t)t * KMAX + lane + WAVE] : (Key)0;
+    }
+    L.listed = WL64{0ull, 0ull};
+    if (wave == 0 && F.listed) {   // used only when the row has lists
+        const auto lk = gmem(F.listed + (int64_t)row * KMAX);
+        L.listed = WL64{lk[lane], lk[lane + WAVE]};
+    }
+}
+
+// The row's 128 best as a wave-0 register list; one workgroup barrier.
+template <int DT>
+__device__ __forceinline__ WL64 row_merge(const Stage2Params& F, const RowParams& rp, int row, S2Shared& sh,
+                                          const RowLoads<DT>& L) {
     using Key = typename S1Traits<DT>::Key;
     const Stage1Params& P = F.s1;
     const int lane = lane_id();
     const int wave = threadIdx.x / WAVE;
     const bool has_listed = rp.valid && rp.n_prior + rp.n_bias > 0;
-
     const Key* sc = (const Key*)P.scratch + (int64_t)row * P.Zv * KMAX;
-    Key pre_lo[S2_PREFETCH], pre_hi[S2_PREFETCH];
-#pragma unroll
-    for (int i = 0; i < S2_PREFETCH; ++i) {
-        const int t = wave + S2_WAVES * i;
-        pre_lo[i] = t < P.Zv ? sc[(int64_t)t * KMAX + lane] : (Key)0;
-        pre_hi[i] = t < P.Zv ? sc[(int64_t)t * KMAX + lane + WAVE] : (Key)0;
-    }
-    WL64 listed{0ull, 0ull};
-    if (wave == 0 && has_listed) {
-        const uint64_t* lk = F.listed + (int64_t)row * KMAX;
-        listed = WL64{lk[lane], lk[lane + WAVE]};
-    }
+    const auto& pre_lo = L.pre_lo;
+    const auto& pre_hi = L.pre_hi;
+    const WL64 listed = L.listed;
 
     // fold this wave's tiles: four at a time as a tree
     auto tl = [&](int i) -> WL64 {
@@ -381,24 +399,26 @@ __device__ __forceinline__ WL64 row_merge(const Stage2Params& F, const RowParams
     for (int t = wave + S2_WAVES * S2_PREFETCH; t < P.Zv; t += S2_WAVES)   // long vocabularies
         mine = wave_merge(mine, WL64{merge_key<DT>(sc[(int64_t)t * KMAX + lane], t),
                                      merge_key<DT>(sc[(int64_t)t * KMAX + lane + WAVE], t)});
+    if (wave == 0 && has_listed) mine = wave_merge(mine, listed);
     sh.wl[wave][0][lane] = mine.lo;
     sh.wl[wave][1][lane] = mine.hi;
     __syncthreads();
 
-    WL64 res{0ull, 0ull};
-    if (wave == 0) {
-        const int nw = min(S2_WAVES, P.Zv);
-        auto wl = [&](int w) -> WL64 { return WL64{sh.wl[w][0][lane], sh.wl[w][1][lane]}; };
-        WL64 x = mine;
-        if (has_listed) x = wave_merge(x, listed);
-        WL64 y{0ull, 0ull};
-        if (nw >= 2) y = wl(1);
-        if (nw >= 3) {
+    // cross-wave tree: wave 0 takes wave 1's list while wave 1 merges
+    // waves 2 and 3; then wave 0 merges the two
+    const int nw = min(S2_WAVES, P.Zv);   // block-uniform
+    auto wl = [&](int w) -> WL64 { return WL64{sh.wl[w][0][lane], sh.wl[w][1][lane]}; };
+    WL64 res = mine;
+    if (wave == 0 && nw >= 2) res = wave_merge(res, wl(1));
+    if (nw >= 3) {
+        if (wave == 1) {
             WL64 z = wl(2);
             if (nw >= 4) z = wave_merge(z, wl(3));
-            y = wave_merge(y, z);
+            sh.wl[2][0][lane] = z.lo;
+            sh.wl[2][1][lane] = z.hi;
         }
-        res = nw >= 2 ? wave_merge(x, y) : x;
+        __syncthreads();
+        if (wave == 0) res = wave_merge(res, wl(2));
     }
     return res;
 }
@@ -556,11 +576,13 @@ template <int DT, int MODE>
 __global__ __launch_bounds__(S2_THREADS) void stage2_kernel(Stage2Params F) {
     __shared__ S2Shared sh;
     const int row = blockIdx.x;
-    const int b = row / F.s1.rows_per_req;
+    const int b = __builtin_amdgcn_readfirstlane(row / F.s1.rows_per_req);
+    RowLoads<DT> L;
+    row_loads<DT>(F, row, L);   // the Stage-1 lists first
     ss_rng rg{0ull, 0ull};
-    if (F.rng) rg = *F.rng;   // requested before the merge work
+    if (F.rng) rg = *F.rng;
     const RowParams rp = row_params(F.s1, b);
-    const WL64 best = row_merge<DT>(F, rp, row, sh);
+    const WL64 best = row_merge<DT>(F, rp, row, sh, L);
     if (threadIdx.x >= WAVE) return;
     row_epilogue<DT>(F, rp, row, b, best, rg);
 }

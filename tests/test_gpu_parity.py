@@ -270,7 +270,7 @@ def test_determinism_repeated_runs():
 # verification
 # ---------------------------------------------------------------------------
 
-def run_verify(wl, seed=0, offset=0):
+def run_verify(wl, seed=0, offset=0, rng_advance=0):
     lib = L()
     x = _dev_logits(wl.target, wl.dtype)
     rows, V = x.shape
@@ -285,9 +285,10 @@ def run_verify(wl, seed=0, offset=0):
     ne = torch.full((B,), -7, dtype=torch.int32, device="cuda")
     st = torch.full((B,), -7, dtype=torch.int32, device="cuda")
     ws = lib.workspace(rows, V, wl.dtype)
-    lib.ss_verify_step(x, B, G, dreq, rng, d, q, toks, ne, st, ws)
+    lib.ss_verify_step(x, B, G, dreq, rng, d, q, toks, ne, st, ws, rng_advance=rng_advance)
     torch.cuda.synchronize()
-    return dict(tokens=toks.cpu().numpy(), n_emit=ne.cpu().numpy(), status=st.cpu().numpy())
+    return dict(tokens=toks.cpu().numpy(), n_emit=ne.cpu().numpy(), status=st.cpu().numpy(),
+                offset_after=int(rng.cpu().view(torch.int64)[1]))
 
 
 def verify_parity(wl, seed=0, offset=0):
@@ -418,3 +419,44 @@ def test_graph_replay_matches_eager_offsets():
     for i in range(4):
         o = oracle.sample(wl.logits, wl.dtype, wl.req, seed=42, offset=i, threads=16)
         assert np.array_equal(got[i], o["tokens"]), i
+
+
+def test_step_advances_offset_itself():
+    """rng_advance: each step draws with the offset it finds, then leaves
+    offset + rng_advance behind - eagerly and under graph replay."""
+    lib = L()
+    wl = W.workload_mixed(1, 12, 40000, grammar=False)
+    wl.req.greedy[:] = False
+    x = _dev_logits(wl.logits, wl.dtype)
+    B, V = x.shape
+    dreq = lib.DeviceRequests(wl.req)
+    rng = lib.make_rng(7, 100)
+    ws = lib.workspace(B, V, wl.dtype)
+    toks = torch.zeros(B, dtype=torch.int32, device="cuda")
+    lib.ss_sample_step(x, dreq, rng, toks, ws=ws, rng_advance=5)
+    torch.cuda.synchronize()
+    assert int(rng.cpu().view(torch.int64)[1]) == 105
+    o = oracle.sample(wl.logits, wl.dtype, wl.req, seed=7, offset=100, threads=16)
+    assert np.array_equal(toks.cpu().numpy(), o["tokens"])
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        lib.ss_sample_step(x, dreq, rng, toks, ws=ws, stream=s, rng_advance=3)
+    torch.cuda.synchronize()
+    rng.copy_(lib.make_rng(7, 200))
+    for i in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        o = oracle.sample(wl.logits, wl.dtype, wl.req, seed=7, offset=200 + 3 * i, threads=16)
+        assert np.array_equal(toks.cpu().numpy(), o["tokens"]), i
+        _ = (x.float().sum()).item()
+    assert int(rng.cpu().view(torch.int64)[1]) == 209
+    # verification takes the same argument
+    vw = W.workload_verify(B=4, gamma=3, V=30000)
+    g = run_verify(vw, seed=3, offset=40, rng_advance=2)
+    assert g["offset_after"] == 42
+    o = oracle.verify(vw.target, vw.dtype, vw.B, vw.gamma, vw.req, vw.draft_ids, vw.draft_probs,
+                      seed=3, offset=40, threads=16)
+    for k in ("tokens", "n_emit", "status"):
+        assert np.array_equal(g[k], o[k]), k

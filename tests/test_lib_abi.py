@@ -94,27 +94,27 @@ def test_argument_errors_return_before_launch(L):
     P = None
     fake = ctypes.c_void_p(0x1000)
     # sample: bad dtype, V, ld, missing pointers, workspace
-    assert lib.ss_sample_step(fake, 5, 4, 100, 100, fake, None, fake, fake, P, P, P, P, P, fake, 10**9, P) == L.SS_ERR_UNSUPPORTED
-    assert lib.ss_sample_step(fake, 1, 4, 0, 100, fake, None, fake, fake, P, P, P, P, P, fake, 10**9, P) == L.SS_ERR_INVALID_ARG
-    assert lib.ss_sample_step(fake, 1, 4, 100, 99, fake, None, fake, fake, P, P, P, P, P, fake, 10**9, P) == L.SS_ERR_INVALID_ARG
-    assert lib.ss_sample_step(P, 1, 4, 100, 100, fake, None, fake, fake, P, P, P, P, P, fake, 10**9, P) == L.SS_ERR_INVALID_ARG
-    assert lib.ss_sample_step(fake, 1, 4, 100, 100, P, None, fake, fake, P, P, P, P, P, fake, 10**9, P) == L.SS_ERR_INVALID_ARG
-    assert lib.ss_sample_step(fake, 1, 4, 100, 100, fake, None, fake, fake, P, P, P, P, P, P, 0, P) == L.SS_ERR_WORKSPACE
-    assert lib.ss_sample_step(fake, 1, 4, 100, 100, fake, None, fake, fake, P, P, P, P, P,
+    assert lib.ss_sample_step(fake, 5, 4, 100, 100, fake, None, fake, 0, fake, P, P, P, P, P, fake, 10**9, P) == L.SS_ERR_UNSUPPORTED
+    assert lib.ss_sample_step(fake, 1, 4, 0, 100, fake, None, fake, 0, fake, P, P, P, P, P, fake, 10**9, P) == L.SS_ERR_INVALID_ARG
+    assert lib.ss_sample_step(fake, 1, 4, 100, 99, fake, None, fake, 0, fake, P, P, P, P, P, fake, 10**9, P) == L.SS_ERR_INVALID_ARG
+    assert lib.ss_sample_step(P, 1, 4, 100, 100, fake, None, fake, 0, fake, P, P, P, P, P, fake, 10**9, P) == L.SS_ERR_INVALID_ARG
+    assert lib.ss_sample_step(fake, 1, 4, 100, 100, P, None, fake, 0, fake, P, P, P, P, P, fake, 10**9, P) == L.SS_ERR_INVALID_ARG
+    assert lib.ss_sample_step(fake, 1, 4, 100, 100, fake, None, fake, 0, fake, P, P, P, P, P, P, 0, P) == L.SS_ERR_WORKSPACE
+    assert lib.ss_sample_step(fake, 1, 4, 100, 100, fake, None, fake, 0, fake, P, P, P, P, P,
                               ctypes.c_void_p(0x1010), 10**9, P) == L.SS_ERR_WORKSPACE
-    assert lib.ss_sample_step(fake, 1, 4, 100, 100, fake, None, fake, fake, P, P, P, P, P, fake, 16, P) == L.SS_ERR_WORKSPACE
-    assert lib.ss_sample_step(fake, 1, 4, (1 << 24) + 1, (1 << 24) + 1, fake, None, fake, fake, P, P, P, P, P,
+    assert lib.ss_sample_step(fake, 1, 4, 100, 100, fake, None, fake, 0, fake, P, P, P, P, P, fake, 16, P) == L.SS_ERR_WORKSPACE
+    assert lib.ss_sample_step(fake, 1, 4, (1 << 24) + 1, (1 << 24) + 1, fake, None, fake, 0, fake, P, P, P, P, P,
                               fake, 10**12, P) == L.SS_ERR_UNSUPPORTED
     # bitmask stride shorter than ceil(V/32)
     aux = L.SsAux(None, None, 0, None, None, 0, 0x2000, 3)
-    assert lib.ss_sample_step(fake, 1, 4, 100, 100, fake, ctypes.byref(aux), fake, fake, P, P, P, P, P,
+    assert lib.ss_sample_step(fake, 1, 4, 100, 100, fake, ctypes.byref(aux), fake, 0, fake, P, P, P, P, P,
                               fake, 10**9, P) == L.SS_ERR_INVALID_ARG
     # B = 0 is a no-op
-    assert lib.ss_sample_step(fake, 1, 0, 100, 100, P, None, P, P, P, P, P, P, P, P, 0, P) == L.SS_OK
+    assert lib.ss_sample_step(fake, 1, 0, 100, 100, P, None, P, 0, P, P, P, P, P, P, P, 0, P) == L.SS_OK
     # verify: gamma range
-    assert lib.ss_verify_step(fake, 1, 2, 0, 100, 100, fake, None, fake, fake, fake, fake, fake, P, fake, 10**9, P) == L.SS_ERR_UNSUPPORTED
-    assert lib.ss_verify_step(fake, 1, 2, 17, 100, 100, fake, None, fake, fake, fake, fake, fake, P, fake, 10**9, P) == L.SS_ERR_UNSUPPORTED
-    assert lib.ss_verify_step(fake, 1, 2, 4, 100, 100, fake, None, fake, P, fake, fake, fake, P, fake, 10**9, P) == L.SS_ERR_INVALID_ARG
+    assert lib.ss_verify_step(fake, 1, 2, 0, 100, 100, fake, None, fake, 0, fake, fake, fake, fake, P, fake, 10**9, P) == L.SS_ERR_UNSUPPORTED
+    assert lib.ss_verify_step(fake, 1, 2, 17, 100, 100, fake, None, fake, 0, fake, fake, fake, fake, P, fake, 10**9, P) == L.SS_ERR_UNSUPPORTED
+    assert lib.ss_verify_step(fake, 1, 2, 4, 100, 100, fake, None, fake, 0, P, fake, fake, fake, P, fake, 10**9, P) == L.SS_ERR_INVALID_ARG
     # top-k: k range
     assert lib.ss_topk_step(fake, 0, 2, 100, 100, 0, fake, P, fake, 10**9, P) == L.SS_ERR_UNSUPPORTED
     assert lib.ss_topk_step(fake, 0, 2, 100, 100, 129, fake, P, fake, 10**9, P) == L.SS_ERR_UNSUPPORTED
