@@ -43,6 +43,111 @@ def stage1_bytes_per_row(V, prior, nbias, grammar=True, dtype_bytes=2):
     return alg_bytes_per_row(V, prior, nbias, grammar, dtype_bytes) - 4
 
 
+PROFILE_MD = os.path.join(ROOT, "profiles", "stage1_bf16_c2.md")
+PROFILE_CMDS = [
+    "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/p3/trace -o c2 -- "
+    "python3 bench.py --steps 40 --warmup 8 --no-cpu",
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/p3/FETCH_SIZE -o c2 -- "
+    "python3 bench.py --steps 8 --warmup 2 --no-cpu --no-verify --copy-calibration",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/p3/WRITE_SIZE -o c2 -- "
+    "python3 bench.py --steps 8 --warmup 2 --no-cpu --no-verify --copy-calibration",
+]
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the HIP sources and the C header: recorded HBM counters
+    apply only to the kernels they were taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "speculative_decoding_verification_stage1_amd", "csrc")
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc)) + [os.path.join(ROOT, "include", "ss.h")]
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per Stage-1 launch from the committed counter summary, or
+    None when the kernels changed since it was taken."""
+    try:
+        with open(PROFILE_MD) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        if line.startswith("traffic_bytes_per_launch:") or line.startswith("source_sha256:"):
+            k, v = line.split(":", 1)
+            vals[k] = v.strip()
+    if vals.get("source_sha256") != kernel_source_hash() or "traffic_bytes_per_launch" not in vals:
+        return None
+    return int(vals["traffic_bytes_per_launch"])
+
+
+def summarize_rocprof(d: str, out: str) -> None:
+    """Writes the short summary kept under profiles/ from the three rocprofv3
+    runs in PROFILE_CMDS (output directory d)."""
+    import csv
+    import statistics
+
+    def rows(path):
+        with open(path) as fh:
+            return list(csv.DictReader(fh))
+
+    B, V = B_HEAD, V_HEAD
+    tile_grid = B * ((V + 32767) // 32768) * 256      # ss_tile_topk: one workgroup per tile
+    lines = ["# Stage 1 (bf16), c2 workload: B=256, V=262144, rotating input copies", ""]
+    lines += ["Commands (run from the repository root with TMPDIR=/tmp):", ""]
+    lines += ["    " + c for c in PROFILE_CMDS] + [""]
+    lines += ["## rocprofv3 --kernel-trace --stats (kernel_stats.csv, ssd kernels)", "",
+              "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for r in rows(os.path.join(d, "trace", "c2_kernel_stats.csv")):
+        if "ssd::" in r["Name"]:
+            lines.append(f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    tr = rows(os.path.join(d, "trace", "c2_kernel_trace.csv"))
+    per = {}
+    for r in tr:
+        if "ssd::" not in r["Kernel_Name"]:
+            continue
+        k = (r["Kernel_Name"], int(r["Grid_Size_X"]))
+        per.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines += ["", "## per launch shape (kernel_trace.csv)", "",
+              "| kernel | grid (threads) | calls | avg us | median us |", "|---|---|---|---|---|"]
+    for (name, grid), v in sorted(per.items()):
+        lines.append(f"| {name} | {grid} | {len(v)} | {sum(v) / len(v):.2f} | {statistics.median(v):.2f} |")
+    s1 = per.get(("void ssd::stage1_kernel<1>(ssd::Stage1Params)", tile_grid), [])
+
+    def counter(name):
+        rr = rows(os.path.join(d, name, "c2_counter_collection.csv"))
+        st = [float(r["Counter_Value"]) for r in rr
+              if "stage1_kernel<1>" in r["Kernel_Name"] and int(r["Grid_Size"]) == tile_grid]
+        cp = [float(r["Counter_Value"]) for r in rr if "neg_kernel" in r["Kernel_Name"]]
+        return sum(st) / len(st), sum(cp) / len(cp)
+
+    f_s1, f_cp = counter("FETCH_SIZE")
+    w_s1, w_cp = counter("WRITE_SIZE")
+    copy_kib = (64 << 20) * 2 / 1024.0          # bytes read (and written) by one copy launch, KiB
+    ff, fw = copy_kib / f_cp, copy_kib / w_cp
+    traffic = (f_s1 * ff + w_s1 * fw) * 1024.0
+    alg = stage1_bytes_per_row(V, PRIOR, NBIAS) * B
+    lines += ["", "## HBM bytes (rocprofv3 --pmc, KiB per dispatch)", "",
+              f"- calibration: torch.neg over 64 Mi bf16 (128 MiB read, 128 MiB written): FETCH_SIZE "
+              f"{f_cp:.1f}, WRITE_SIZE {w_cp:.1f} -> scale factors {ff:.4f} (fetch), {fw:.4f} (write)",
+              f"- stage1_kernel<bf16>, grid {tile_grid}: FETCH_SIZE {f_s1:.1f}, WRITE_SIZE {w_s1:.1f}",
+              f"- scaled: {f_s1 * ff / 1024:.2f} MiB read, {w_s1 * fw / 1024:.2f} MiB written per launch; "
+              f"algorithmic {alg / 2**20:.2f} MiB (ratio {traffic / alg:.3f})",
+              f"- Stage-1 average over {len(s1)} launches of that shape: "
+              f"{(sum(s1) / len(s1) if s1 else float('nan')):.2f} us", "",
+              f"traffic_bytes_per_launch: {int(round(traffic))}",
+              f"source_sha256: {kernel_source_hash()}", ""]
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -52,7 +157,14 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-verify", action="store_true", help="skip the verification latency")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 128 MiB device copy (scales HBM byte counters)")
+    ap.add_argument("--summarize-rocprof", metavar="DIR",
+                    help="write the profiles/ summary from the rocprofv3 runs in DIR and exit")
     args = ap.parse_args()
+    if args.summarize_rocprof:
+        summarize_rocprof(args.summarize_rocprof, PROFILE_MD)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the sampling path runs on a single MI355X "
               "(rows shard across GPUs with no communication); use --gpus 1", file=sys.stderr)
@@ -176,7 +288,10 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(s1_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            # HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE,
+            # scaled by a plain copy (profiles/stage1_bf16_c2.md); None once
+            # the kernel sources differ from the ones measured there
+            "traffic": recorded_traffic(),
         },
         "input_gen_s": round(gen_s, 2),
     }
@@ -235,6 +350,15 @@ def main():
             "sample": f"{passes} passes over all 256 rows of the same workload (oracle.sample, "
                       f"{cores} threads), {cpu_s:.1f} s",
         }
+
+    if args.copy_calibration:
+        # a plain read-once / write-once kernel of known size: 64 Mi bf16
+        # elements read and 64 Mi written per launch
+        src = torch.ones(64 << 20, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
 
     print(json.dumps(result))
 
