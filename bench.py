@@ -157,6 +157,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-verify", action="store_true", help="skip the verification latency")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-extra", action="store_true", help="skip the c0, c1, c4 and copy figures")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 128 MiB device copy (scales HBM byte counters)")
     ap.add_argument("--summarize-rocprof", metavar="DIR",
@@ -300,7 +301,7 @@ def main():
     if not args.no_verify:
         vw = W.workload_verify()
         G = vw.gamma
-        tcopies = 3
+        tcopies = 7   # 7 x 80 MiB of target logits: more than the 256 MB last-level cache
         t0d = torch.from_numpy(vw.target.view(np.int16)).to(dev).view(torch.bfloat16)
         ts = [t0d] + [t0d.clone() for _ in range(tcopies - 1)]
         vreq = L.DeviceRequests(vw.req)
@@ -327,6 +328,10 @@ def main():
         result["verify_us"] = round(v_us, 2)
         result["verify_config"] = "c3: B=64 gamma=4 V=131072 bf16 target, fp32 draft probs (gathered)"
         result["verify_mean_emitted"] = round(float(vne.float().mean().item()), 3)
+        result["verify_acceptance_rate"] = round(float((vne.float() - 1).sum().item()) / (vw.B * G), 4)
+
+    if not args.no_extra:
+        result.update(extra_measurements(args, dev, L, W, stream))
 
     # ---- CPU oracle on a bounded sample of the same workload ----
     if not args.no_cpu:
@@ -350,6 +355,18 @@ def main():
             "sample": f"{passes} passes over all 256 rows of the same workload (oracle.sample, "
                       f"{cores} threads), {cpu_s:.1f} s",
         }
+        # one thread, on the first 32 rows (bounded)
+        sub = W.SampleWorkload(wl.name, wl.dtype, wl.logits[:32], _subset(wl.req, 32))
+        t0 = time.perf_counter()
+        n1p = 0
+        while True:
+            oracle.sample(sub.logits, sub.dtype, sub.req, threads=1)
+            n1p += 1
+            c1s = time.perf_counter() - t0
+            if c1s >= min(3.0, args.cpu_seconds) or n1p >= 50:
+                break
+        result["cpu_baseline_1thread"] = {"value": round(n1p * 32 / c1s, 2), "unit": "tokens/s", "cores": 1,
+                                          "sample": f"{n1p} passes over rows 0-31 of c2, {c1s:.1f} s"}
 
     if args.copy_calibration:
         # a plain read-once / write-once kernel of known size: 64 Mi bf16
@@ -361,6 +378,108 @@ def main():
         torch.cuda.synchronize()
 
     print(json.dumps(result))
+
+
+def _events_us(fn, n, stream=None):
+    """Mean GPU time per call of fn() over n back-to-back calls (HIP events
+    on the stream the work runs on)."""
+    import torch
+    st = stream if stream is not None else torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(st)
+    for i in range(n):
+        fn(i)
+    b.record(st)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1000.0 / n
+
+
+def extra_measurements(args, dev, L, W, stream):
+    """The other workloads' figures: c0 latency, c1 throughput (cold: 34
+    rotating copies > 512 MB), c4 two-stage vs single-pass top-k per regime
+    (torch.topk as context), and a plain device copy as the bandwidth
+    reference."""
+    import torch
+    out = {}
+    # ---- c0: one fp32 row, graph latency (greedy and stochastic) ----
+    c0 = {}
+    for greedy in (True, False):
+        wl = W.workload_c0(greedy)
+        x = torch.from_numpy(wl.logits).to(dev)
+        dreq = L.DeviceRequests(wl.req)
+        rng = L.make_rng(0, 0)
+        tok = torch.zeros(1, dtype=torch.int32, device=dev)
+        ws = L.workspace(1, wl.V, L.SS_F32)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            L.ss_sample_step(x, dreq, rng, tok, ws=ws, stream=stream, rng_advance=1)
+        for _ in range(5):
+            g.replay()
+        torch.cuda.synchronize()
+        gpu_us = _events_us(lambda i: g.replay(), 50)
+        t0 = time.perf_counter()
+        for _ in range(50):
+            g.replay()
+            torch.cuda.synchronize()
+        sync_us = (time.perf_counter() - t0) / 50 * 1e6
+        c0["greedy" if greedy else "stochastic"] = {"graph_replay_us": round(gpu_us, 2),
+                                                    "replay_and_sync_us": round(sync_us, 2)}
+    out["c0_latency"] = c0
+    # ---- c1: 64 x 131072 bf16, mixed settings ----
+    wl = W.workload_c1()
+    B1, V1 = wl.B, wl.V
+    ncp = 34
+    x1 = torch.from_numpy(wl.logits.view(np.int16)).to(dev).view(torch.bfloat16)
+    x1s = [x1] + [x1.clone() for _ in range(ncp - 1)]
+    d1 = L.DeviceRequests(wl.req)
+    rng = L.make_rng(0, 0)
+    tok1 = torch.zeros(B1, dtype=torch.int32, device=dev)
+    ws1 = L.workspace(B1, V1, L.SS_BF16)
+    g1 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g1, stream=stream):
+        for i in range(ncp):
+            L.ss_sample_step(x1s[i], d1, rng, tok1, ws=ws1, stream=stream, rng_advance=1)
+    g1.replay()
+    torch.cuda.synchronize()
+    us1 = _events_us(lambda i: g1.replay(), 5) / ncp
+    b1 = alg_bytes_per_row(V1, PRIOR, NBIAS, grammar=False) * B1
+    out["c1"] = {"step_us": round(us1, 2), "tokens_per_s": round(B1 / (us1 * 1e-6), 1),
+                 "alg_GBps": round(b1 / (us1 * 1e-6) / 1e9, 1),
+                 "inputs": f"{ncp} rotating copies ({ncp * B1 * V1 * 2 / 2**20:.0f} MiB)"}
+    del x1s
+    # ---- c4: top-k of 512 x 262144 fp32, two regimes ----
+    c4 = {}
+    for regime in ("peaked", "flat"):
+        tw = W.workload_c4(regime)
+        Bk, Vk = tw.logits.shape
+        xk = [torch.from_numpy(tw.logits).to(dev)]
+        xk.append(xk[0].clone())
+        ids = torch.zeros((Bk, tw.k), dtype=torch.int32, device=dev)
+        wsk = L.workspace(Bk, Vk, L.SS_F32)
+        nbytes = Bk * Vk * 4
+        L.ss_topk_step(xk[0], tw.k, ids, ws=wsk)
+        two = _events_us(lambda i: L.ss_topk_step(xk[i % 2], tw.k, ids, ws=wsk), 10)
+        ids1 = torch.zeros_like(ids)
+        L.ss_topk_single_pass(xk[0], tw.k, ids1)
+        one = _events_us(lambda i: L.ss_topk_single_pass(xk[i % 2], tw.k, ids1), 3)
+        same = bool(torch.equal(ids, ids1))
+        tt = _events_us(lambda i: torch.topk(xk[i % 2], tw.k, dim=1), 3)
+        c4[regime] = {"two_stage_us": round(two, 1), "two_stage_GBps": round(nbytes / (two * 1e-6) / 1e9, 1),
+                      "single_pass_us": round(one, 1),
+                      "single_pass_GBps": round(nbytes / (one * 1e-6) / 1e9, 1),
+                      "ids_equal": same, "torch_topk_us": round(tt, 1)}
+        del xk
+    out["c4_topk"] = c4
+    # ---- bandwidth reference: a plain device copy, 128 MiB read + 128 MiB written ----
+    src = torch.ones(64 << 20, dtype=torch.bfloat16, device=dev)
+    dst = [torch.empty_like(src) for _ in range(2)]
+    torch.neg(src, out=dst[0])
+    cu = _events_us(lambda i: torch.neg(src, out=dst[i % 2]), 10)
+    out["copy_reference"] = {"us": round(cu, 2), "GBps_read_plus_write": round(2 * (128 << 20) / (cu * 1e-6) / 1e9, 1),
+                             "kernel": "torch.neg over 64 Mi bf16"}
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
 
 
 def _subset(req, n):

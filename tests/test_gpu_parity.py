@@ -106,7 +106,7 @@ def test_sample_c0_both_runs():
         sample_parity(W.workload_c0(greedy))
 
 
-@pytest.mark.parametrize("V", [1, 5, 127, 128, 129, 16383, 16385, 32767, 32769, 50001, 98311])
+@pytest.mark.parametrize("V", [1, 5, 127, 128, 129, 16383, 16385, 32767, 32769, 50001, 65537, 98311])
 def test_sample_small_shapes(V):
     rng = np.random.default_rng(V)
     for dtype in (W.DTYPE_BF16, W.DTYPE_F32):
