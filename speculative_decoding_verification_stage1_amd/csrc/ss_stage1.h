@@ -450,6 +450,18 @@ __device__ __forceinline__ void tile_process(const Stage1Params& P, int row, int
     }
     __syncthreads();   // listed tokens, grammar table
     const int nl = sh.nl;
+    // grammar rows: the tile's listed tokens are cleared from its grammar
+    // words, so the mask leaves them out like any disallowed token and the
+    // threshold and survivor steps need not know about them
+    const bool fold = use_grammar && nl > 0;   // block-uniform
+    if (fold) {
+        for (int i = tid; i < nl; i += S1_THREADS) {
+            const int loc = sh.listed[i];
+            atomicAnd(&sh.gmw[loc >> 5], ~(1u << (loc & 31)));
+        }
+        __syncthreads();
+    }
+    const int nl_data = fold ? 0 : nl;   // listed tokens still present in the data
 
     // ---- grammar: masked elements take PAD ----
     if (use_grammar) {
@@ -508,8 +520,8 @@ __device__ __forceinline__ void tile_process(const Stage1Params& P, int row, int
     if (DT == SS_F32) m = min(m, (int)F32_MAX_BITS);
     // at least 128 + nl tokens at or above tau, so that 128 remain once the
     // listed ones are set aside
-    const bool nl_ok = nl <= S1_NL_FAST;
-    const int kw = KMAX / S1_WAVES + (nl_ok ? (nl + S1_WAVES - 1) / S1_WAVES : 0);
+    const bool nl_ok = nl_data <= S1_NL_FAST;
+    const int kw = KMAX / S1_WAVES + (nl_ok ? (nl_data + S1_WAVES - 1) / S1_WAVES : 0);
     const int tau_w = wave_kth_largest<T::VAL_BITS>(m, kw);
     const uint64_t sp = __ballot(special);
     if (lane == 0) {
@@ -534,15 +546,9 @@ __device__ __forceinline__ void tile_process(const Stage1Params& P, int row, int
         for (int j = 0; j < CPT; ++j) {
             bool f;
             if constexpr (DT == SS_BF16)
-                // the chunk maximum again, folded with tau - 1 (cheaper
-                // than holding the 16 maxima in registers meanwhile)
-                f = s16x2_bits(__builtin_elementwise_max(
-                        __builtin_elementwise_max(bits_s16x2(raw[4 * j]), bits_s16x2(raw[4 * j + 1])),
-                        __builtin_elementwise_max(bits_s16x2(raw[4 * j + 2]),
-                                                  __builtin_elementwise_max(bits_s16x2(raw[4 * j + 3]),
-                                                                            bits_s16x2(T2))))) != T2;
+                f = s16x2_bits(__builtin_elementwise_max(bits_s16x2(cmx[j]), bits_s16x2(T2))) != T2;
             else
-                f = max(max((int)raw[4 * j], (int)raw[4 * j + 1]), max((int)raw[4 * j + 2], (int)raw[4 * j + 3])) >= tau;
+                f = (int)cmx[j] >= tau;
             const uint64_t bal = __ballot(f);
             if (f && wcnt <= S1_CCAP) {   // slots up to S1_CCAP + 63 exist
                 const int s = wcnt + lane_prefix(bal);
@@ -565,7 +571,7 @@ __device__ __forceinline__ void tile_process(const Stage1Params& P, int row, int
             if (s < nck) {
                 c = sh.cid[wave][s];
                 sm = chunk_survivors<DT>(sh.chunks[wave][s], tau);
-                for (int i = 0; i < nl; ++i) {
+                for (int i = 0; i < nl_data; ++i) {
                     const int2 e = sh.lcb[i];
                     if (e.x == c) sm &= ~(uint32_t)e.y;
                 }
