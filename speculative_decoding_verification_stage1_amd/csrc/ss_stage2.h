@@ -87,7 +87,9 @@ __device__ __forceinline__ bool finitef(float x) { return x == x && x - x == 0.0
 
 // Row validation and parameters; every thread computes the same values from
 // the (uniform) request record.
-__device__ inline RowParams row_params(const Stage1Params& P, int b) {
+// bias_head: this lane's entry lane of the request's bias values when the
+// caller requested it early (NaN-free check), else read here.
+__device__ inline RowParams row_params(const Stage1Params& P, int b, const float* bias_head = nullptr) {
     RowParams rp{};
     if (!P.req) {   // plain top-k: no processing
         rp.valid = 1;
@@ -114,7 +116,12 @@ __device__ inline RowParams row_params(const Stage1Params& P, int b) {
     if (ok && (f & SS_BIAS)) {   // every bias value finite: lanes check in parallel
         const auto bv = gmem(P.aux.bias_val + (int64_t)b * P.aux.bias_stride);
         bool bad = false;
-        for (int j = lane_id(); j < (int)r.n_bias; j += WAVE) bad |= !finitef(bv[j]);
+        int j0 = 0;
+        if (bias_head) {
+            bad = lane_id() < (int)r.n_bias && !finitef(*bias_head);
+            j0 = WAVE;
+        }
+        for (int j = j0 + lane_id(); j < (int)r.n_bias; j += WAVE) bad |= !finitef(bv[j]);
         ok = __ballot(bad) == 0ull;
     }
     bool g = (f & SS_GREEDY) != 0;
@@ -344,6 +351,7 @@ template <int DT>
 struct RowLoads {
     typename S1Traits<DT>::Key pre_lo[S2_PREFETCH], pre_hi[S2_PREFETCH];
     WL64 listed;
+    float bias_head;   // bias value `lane` of the request (validation)
 };
 template <int DT>
 __device__ __forceinline__ void row_loads(const Stage2Params& F, int row, RowLoads<DT>& L) {
@@ -362,6 +370,11 @@ __device__ __forceinline__ void row_loads(const Stage2Params& F, int row, RowLoa
     if (wave == 0 && F.listed) {   // used only when the row has lists
         const auto lk = gmem(F.listed + (int64_t)row * KMAX);
         L.listed = WL64{lk[lane], lk[lane + WAVE]};
+    }
+    L.bias_head = 0.0f;
+    if (P.aux.bias_val && lane < P.aux.bias_stride) {
+        const int b = row / P.rows_per_req;
+        L.bias_head = gmem(P.aux.bias_val)[(int64_t)b * P.aux.bias_stride + lane];
     }
 }
 
@@ -427,7 +440,7 @@ __device__ __forceinline__ WL64 row_merge(const Stage2Params& F, const RowParams
 // outputs for the row.  Uses no barrier.
 template <int DT>
 __device__ __forceinline__ void row_epilogue(const Stage2Params& F, const RowParams& rp, int row, int b, const WL64& best,
-                             const ss_rng rg) {
+                             const ss_rng rg, S2Shared& sh) {
     const Stage1Params& P = F.s1;
     const int lane = lane_id();
     const uint64_t k_lo = best.lo, k_hi = best.hi;
@@ -484,21 +497,45 @@ __device__ __forceinline__ void row_epilogue(const Stage2Params& F, const RowPar
             v_hi = vscale(z_hi);
             e_hi = exp_fixed(v_hi - m);
         }
-        // running sums E_k = e_0 + ... + e_{k-1}, left to right (ranks past
-        // K hold e = 0, which leaves E unchanged)
-        float E = 0.0f, E_lo = 0.0f, E_hi = 0.0f;
-#pragma unroll
-        for (int k = 0; k < WAVE; ++k) {
-            E_lo = lane == k ? E : E_lo;
-            E = E + readlane_f(e_lo, k);
+        uint32_t c1, c2;
+        if (F.mode == MODE_VERIFY) {
+            c1 = (uint32_t)b;
+            c2 = (uint32_t)(row - b * P.rows_per_req);
+        } else {
+            c1 = (uint32_t)row;
+            c2 = 0u;
         }
-        if (K > WAVE) {
+        // Gumbel noise of every candidate, independent of the sums below
+        float g_lo = 0.0f, g_hi = 0.0f;
+        if (lane < K) g_lo = gumbel_noise(rg.seed, rg.offset, (uint32_t)id_lo, c1, c2);
+        if (lane + 64 < K) g_hi = gumbel_noise(rg.seed, rg.offset, (uint32_t)id_hi, c1, c2);
+        // running sums E_k = e_0 + ... + e_{k-1}, left to right: the e's go
+        // to LDS and every lane runs the same dependent chain on broadcast
+        // reads (ranks past K hold e = 0, which leaves E unchanged)
+        float* es = (float*)&sh.wl[0][0][0];   // waves 1-3 are done with sh
+        float* Es = es + KMAX;
+        es[lane] = e_lo;
+        es[lane + WAVE] = e_hi;
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        float E = 0.0f;
 #pragma unroll
-            for (int k = 0; k < WAVE; ++k) {
-                E_hi = lane == k ? E : E_hi;
-                E = E + readlane_f(e_hi, k);
-            }
+        for (int k0 = 0; k0 < KMAX; k0 += 4) {
+            const float4 q = *(const float4*)&es[k0];
+            float4 o;
+            o.x = E;
+            E = E + q.x;
+            o.y = E;
+            E = E + q.y;
+            o.z = E;
+            E = E + q.z;
+            o.w = E;
+            E = E + q.w;
+            if (lane == 0) *(float4*)&Es[k0] = o;
         }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        const float E_lo = Es[lane], E_hi = Es[lane + WAVE];
         Z = E;
         int n_p = K, n_m = K;
         if ((rp.flags & SS_TOPP) && rp.top_p < 1.0f) {
@@ -515,18 +552,10 @@ __device__ __forceinline__ void row_epilogue(const Stage2Params& F, const RowPar
         if (n >= K) En = Z;
         else if (n < 64) En = readlane_f(E_lo, n);
         else En = readlane_f(E_hi, n - 64);
-        uint32_t c1, c2;
-        if (F.mode == MODE_VERIFY) {
-            c1 = (uint32_t)b;
-            c2 = (uint32_t)(row - b * P.rows_per_req);
-        } else {
-            c1 = (uint32_t)row;
-            c2 = 0u;
-        }
         float s_lo = 0.0f, s_hi = 0.0f;
         const bool c_lo = lane < n, c_hi = lane + 64 < n;
-        if (c_lo) s_lo = v_lo + gumbel_noise(rg.seed, rg.offset, (uint32_t)id_lo, c1, c2);
-        if (c_hi) s_hi = v_hi + gumbel_noise(rg.seed, rg.offset, (uint32_t)id_hi, c1, c2);
+        if (c_lo) s_lo = v_lo + g_lo;
+        if (c_hi) s_hi = v_hi + g_hi;
         // best of the lane's two, then across the wave
         float s = s_lo;
         int id = c_lo ? id_lo : -1;
@@ -581,10 +610,10 @@ __global__ __launch_bounds__(S2_THREADS) void stage2_kernel(Stage2Params F) {
     row_loads<DT>(F, row, L);   // the Stage-1 lists first
     ss_rng rg{0ull, 0ull};
     if (F.rng) rg = *F.rng;
-    const RowParams rp = row_params(F.s1, b);
+    const RowParams rp = row_params(F.s1, b, &L.bias_head);
     const WL64 best = row_merge<DT>(F, rp, row, sh, L);
     if (threadIdx.x >= WAVE) return;
-    row_epilogue<DT>(F, rp, row, b, best, rg);
+    row_epilogue<DT>(F, rp, row, b, best, rg, sh);
 }
 
 }  // namespace ssd
