@@ -187,18 +187,27 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 }
 
 // ---------------------------------------------------------------------------
-// lane exchange v(lane ^ J) without LDS traffic where the ISA allows:
-// DPP quad permutes for J = 1, 2; ds_swizzle (bit mode) for J = 4, 8;
-// the gfx950 row-swap permutes for J = 16, 32.
+// lane exchange v(lane ^ J) with no LDS traffic: DPP quad permutes for J =
+// 1, 2; two DPP mirrors for J = 4 (quad reversal, then the 8-lane mirror:
+// l ^ 3 ^ 7 = l ^ 4) and J = 8 (8-lane mirror, then the 16-lane mirror:
+// l ^ 7 ^ 15 = l ^ 8); the gfx950 row-swap permutes for J = 16, 32.
 // ---------------------------------------------------------------------------
+constexpr int DPP_QUAD_REV = 0x1B;      // quad_perm [3,2,1,0]
+constexpr int DPP_ROW_MIRROR = 0x140;
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+
 template <int J>
 __device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
     if constexpr (J == 1) {
         return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
     } else if constexpr (J == 2) {
         return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
-    } else if constexpr (J == 4 || J == 8) {
-        return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (J << 10) | 0x1F);
+    } else if constexpr (J == 4) {
+        const int a = __builtin_amdgcn_mov_dpp((int)v, DPP_QUAD_REV, 0xF, 0xF, false);
+        return (uint32_t)__builtin_amdgcn_mov_dpp(a, DPP_ROW_HALF_MIRROR, 0xF, 0xF, false);
+    } else if constexpr (J == 8) {
+        const int a = __builtin_amdgcn_mov_dpp((int)v, DPP_ROW_HALF_MIRROR, 0xF, 0xF, false);
+        return (uint32_t)__builtin_amdgcn_mov_dpp(a, DPP_ROW_MIRROR, 0xF, 0xF, false);
     } else if constexpr (J == 16) {
         const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
         return (lane_id() & 16) ? r[0] : r[1];

@@ -41,19 +41,21 @@ __global__ __launch_bounds__(S1_THREADS) void stage1_kernel(Stage1Params P) {
     const int wg = blockIdx.x - nlw;
     const int row = wg / P.Zv;
     const int tile = wg - row * P.Zv;
-    stage1_tile<DT>(P, row, tile, sh);
-    if (tid < KMAX) {
+    WList<Key> res{0, 0};
+    stage1_tile<DT>(P, row, tile, sh, &res);
+    if (tid < WAVE) {   // wave 0 holds the tile's sorted 128 keys
         const int64_t o = ((int64_t)row * P.Zv + tile) * KMAX + tid;
-        const Key k = sh.surv[tid];
-        ((Key*)P.scratch)[o] = k;
+        ((Key*)P.scratch)[o] = res.lo;
+        ((Key*)P.scratch)[o + WAVE] = res.hi;
         if (P.out_ids) {
-            int id = -1;
-            if (k != 0) {
+            auto id_of = [&](Key k) -> int {
+                if (k == 0) return -1;
                 const uint32_t lo = DT == SS_BF16 ? (0xFFFFu - ((uint32_t)k & 0xFFFFu))
                                                   : (0xFFFFFFFFu - (uint32_t)k);
-                id = tile * S1Traits<DT>::BN + (int)lo;
-            }
-            P.out_ids[o] = id;
+                return tile * S1Traits<DT>::BN + (int)lo;
+            };
+            P.out_ids[o] = id_of(res.lo);
+            P.out_ids[o + WAVE] = id_of(res.hi);
         }
     }
 }

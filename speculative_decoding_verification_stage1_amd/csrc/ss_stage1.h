@@ -366,7 +366,8 @@ __device__ __forceinline__ void tile_patch(const Stage1Params& P, int row, int t
 // caller can request its next tile into them while this one is finished.
 template <int DT, typename Next>
 __device__ __forceinline__ void tile_process(const Stage1Params& P, int row, int tile, S1In<DT>& in,
-                                             S1Shared<DT>& sh, Next&& next) {
+                                             S1Shared<DT>& sh, Next&& next,
+                                             WList<typename S1Traits<DT>::Key>* to_regs = nullptr) {
     S1_TILE_GEOMETRY
     using Key = typename T::Key;
     static_assert(S1_WAVES == 4, "merge tree");
@@ -627,9 +628,14 @@ __device__ __forceinline__ void tile_process(const Stage1Params& P, int row, int
         __syncthreads();
         if (wave == 0) {
             r = wave_merge(r, WList<Key>{sh.wl[2][lane], sh.wl[2][lane + WAVE]});
+            if (to_regs) {   // the caller takes wave 0's registers
+                *to_regs = r;
+                return;
+            }
             sh.surv[lane] = r.lo;
             sh.surv[lane + WAVE] = r.hi;
         }
+        if (to_regs) return;
         __syncthreads();
         return;
     }
@@ -696,19 +702,27 @@ __device__ __forceinline__ void tile_process(const Stage1Params& P, int row, int
     if (wave == 0) {
         WList<Key> l{lane < total ? g[lane] : (Key)0, lane + WAVE < total ? g[lane + WAVE] : (Key)0};
         l = wave_sort128(l);
+        if (to_regs) {
+            *to_regs = l;
+            return;
+        }
         sh.surv[lane] = l.lo;
         sh.surv[lane + WAVE] = l.hi;
     }
+    if (to_regs) return;
     __syncthreads();
 }
 
-// One tile, requested and processed in turn.
+// One tile, requested and processed in turn.  Without `to_regs` the sorted
+// result is left in sh.surv behind a barrier; with it, wave 0 receives the
+// result in registers and no wave waits at the end.
 template <int DT>
-__device__ __forceinline__ void stage1_tile(const Stage1Params& P, int row, int tile, S1Shared<DT>& sh) {
+__device__ __forceinline__ void stage1_tile(const Stage1Params& P, int row, int tile, S1Shared<DT>& sh,
+                                            WList<typename S1Traits<DT>::Key>* to_regs = nullptr) {
     S1In<DT> in;
     tile_fetch<DT>(P, row, tile, in);
     tile_patch<DT>(P, row, tile, in);
-    tile_process<DT>(P, row, tile, in, sh, [] {});
+    tile_process<DT>(P, row, tile, in, sh, [] {}, to_regs);
 }
 
 }  // namespace ssd

@@ -65,15 +65,20 @@ __device__ __forceinline__ void cas_64(WList<K>& c) {
     c.lo = t;
 }
 
+// v(63 - lane): the 16-lane mirror (l ^ 15), then rows swapped by the
+// row-swap permutes (l ^ 48).
+__device__ __forceinline__ uint32_t reverse_lanes32(uint32_t v) {
+    const uint32_t m = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, DPP_ROW_MIRROR, 0xF, 0xF, false);
+    return xor_lane<16>(xor_lane<32>(m));
+}
 template <typename K>
 __device__ __forceinline__ K reverse_lanes(K v) {
-    const int r = (WAVE - 1 - lane_id()) * 4;
     if constexpr (sizeof(K) == 8) {
-        const uint32_t x = (uint32_t)__builtin_amdgcn_ds_bpermute(r, (int)(uint32_t)v);
-        const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute(r, (int)(uint32_t)((uint64_t)v >> 32));
+        const uint32_t x = reverse_lanes32((uint32_t)v);
+        const uint32_t y = reverse_lanes32((uint32_t)((uint64_t)v >> 32));
         return (K)(((uint64_t)y << 32) | x);
     } else {
-        return (K)(uint32_t)__builtin_amdgcn_ds_bpermute(r, (int)(uint32_t)v);
+        return (K)reverse_lanes32((uint32_t)v);
     }
 }
 
