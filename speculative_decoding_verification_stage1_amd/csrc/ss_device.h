@@ -66,6 +66,9 @@ __device__ __forceinline__ float widen_bf16(uint32_t h) { return bitsf((h & 0xFF
 // Global-memory view of a pointer: loads through it are global_load (vector
 // memory only) instead of flat loads, which also hold the LDS counter.
 typedef uint32_t vu32x4 __attribute__((ext_vector_type(4)));   // 16-byte load unit
+// Fourth word of a raw buffer resource on this chip family: 32-bit data
+// format, no swizzle, no per-lane index.
+constexpr int BUF_DWORD3 = 0x00020000;
 
 template <typename T>
 __device__ __forceinline__ const __attribute__((address_space(1))) T* gmem(const T* p) {

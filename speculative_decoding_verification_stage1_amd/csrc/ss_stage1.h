@@ -287,36 +287,8 @@ __device__ __forceinline__ void tile_fetch(const Stage1Params& P, int row, int t
         if (P.aux.bias_ids && lane < P.aux.bias_stride)
             in.l_bid = gmem(P.aux.bias_ids)[(int64_t)b * P.aux.bias_stride + lane];
     }
-    if (vec) {
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-            const vu32x4 v = gmem((const vu32x4*)rowp)[j * S1_THREADS + tid];
-            in.raw[4 * j + 0] = v.x;
-            in.raw[4 * j + 1] = v.y;
-            in.raw[4 * j + 2] = v.z;
-            in.raw[4 * j + 3] = v.w;
-        }
-    } else if (P.aligned16) {
-        // ragged tile: chunks wholly inside V load as 16 bytes, the others
-        // read as PAD; the one chunk that straddles the end is completed by
-        // tile_patch
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-            const int c = j * S1_THREADS + tid;
-            vu32x4 v = {PAD, PAD, PAD, PAD};
-            if ((c + 1) * EPC <= nvalid) v = gmem((const vu32x4*)rowp)[c];
-            in.raw[4 * j + 0] = v.x;
-            in.raw[4 * j + 1] = v.y;
-            in.raw[4 * j + 2] = v.z;
-            in.raw[4 * j + 3] = v.w;
-        }
-    } else {
-        // rows that do not start on a 16-byte boundary: the exact general
-        // path reads the elements itself
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) in.raw[q] = PAD;
-    }
     // the tile's grammar bitmask, coalesced: word base/32 + tid + 256k
+    // (requested before the logits, so that it can be used while they arrive)
     if (P.aux.bitmask) {
         constexpr int GW = CPT * EPC / 32;
         const int words = (P.V + 31) / 32;
@@ -325,16 +297,42 @@ __device__ __forceinline__ void tile_fetch(const Stage1Params& P, int row, int t
         for (int k = 0; k < GW; ++k)
             in.gw[k] = (full || base / 32 + tid + k * S1_THREADS < words) ? gm[k * S1_THREADS] : 0u;
     }
+    // the logits, as one buffer view over the tile's whole 16-byte chunks:
+    // the same 16 loads for every tile, with nothing between them, so that
+    // each chunk can be used as soon as it has arrived.  Chunks past V (and
+    // every chunk of a row that does not start on a 16-byte boundary) read
+    // as zero without touching memory; tile_patch sets them.  The whole
+    // offset is in the lane's offset, which the range check covers.
+    const int nbytes = P.aligned16 ? (nvalid / EPC) * 16 : 0;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)rowp, (short)0, nbytes, BUF_DWORD3);
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        const vu32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, (tid + j * S1_THREADS) * 16, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);   // keep the issue order: chunk j is used j-th
+        in.raw[4 * j + 0] = v.x;
+        in.raw[4 * j + 1] = v.y;
+        in.raw[4 * j + 2] = v.z;
+        in.raw[4 * j + 3] = v.w;
+    }
 }
 
-// Completes the chunk that straddles the end of V in a ragged tile (its
-// owner thread loads the elements inside V).  Called once the tile's own
-// loads have arrived and before later requests are issued.
+// Tiles that are not whole 16-byte chunks of an aligned row: chunks not
+// wholly inside V become PAD, and the one that straddles the end is
+// completed by its owner thread from the elements inside V (rows that do
+// not start on a 16-byte boundary are all PAD: the exact general path reads
+// their elements itself).  Waits for the tile's loads, so full tiles skip it.
 template <int DT>
 __device__ __forceinline__ void tile_patch(const Stage1Params& P, int row, int tile, S1In<DT>& in) {
     S1_TILE_GEOMETRY
-    if (full || !P.aligned16) return;
-    const int cp = nvalid / EPC;         // first chunk not wholly inside V
+    if (vec) return;
+    const int cp = P.aligned16 ? nvalid / EPC : 0;   // first chunk not wholly inside V
+#pragma unroll
+    for (int j = 0; j < CPT; ++j)
+        if (j * S1_THREADS + tid >= cp) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) in.raw[4 * j + k] = PAD;
+        }
+    if (!P.aligned16) return;
     const int rem = nvalid - cp * EPC;   // its elements inside V
     if (rem == 0 || (cp & (S1_THREADS - 1)) != tid) return;
     uint32_t pv[4] = {PAD, PAD, PAD, PAD};
@@ -464,15 +462,29 @@ __device__ __forceinline__ void tile_process(const Stage1Params& P, int row, int
     }
     const int nl_data = fold ? 0 : nl;   // listed tokens still present in the data
 
-    // ---- grammar: masked elements take PAD ----
+    // ---- grammar mask (masked elements take PAD) and maxima per chunk and
+    // per lane (raw patterns read as signed), chunk by chunk in the order
+    // the loads were issued, so that each waits only for its own data ----
+    uint32_t gbits[CPT];   // bits of chunk j's elements allowed by the grammar (bit e: element e)
     if (use_grammar) {
-        // bits of chunk j's elements allowed by the grammar (bit e: element e)
-        uint32_t gbits[CPT];
         const uint8_t* gb = (const uint8_t*)sh.gmw;
 #pragma unroll
         for (int j = 0; j < CPT; ++j)
             gbits[j] = DT == SS_BF16 ? gb[j * S1_THREADS + tid]
                                      : (uint32_t)gb[(j * S1_THREADS + tid) >> 1] >> ((tid & 1) * 4);
+    }
+    uint32_t cmx[CPT];
+    auto chunk_max = [&](int j) {
+        if constexpr (DT == SS_BF16) {
+            const s16x2 a = __builtin_elementwise_max(bits_s16x2(raw[4 * j]), bits_s16x2(raw[4 * j + 1]));
+            const s16x2 c = __builtin_elementwise_max(bits_s16x2(raw[4 * j + 2]), bits_s16x2(raw[4 * j + 3]));
+            cmx[j] = s16x2_bits(__builtin_elementwise_max(a, c));
+        } else {
+            cmx[j] = (uint32_t)max(max((int)raw[4 * j], (int)raw[4 * j + 1]),
+                                   max((int)raw[4 * j + 2], (int)raw[4 * j + 3]));
+        }
+    };
+    if (use_grammar) {
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
             if constexpr (DT == SS_BF16) {
@@ -487,28 +499,23 @@ __device__ __forceinline__ void tile_process(const Stage1Params& P, int row, int
                     raw[4 * j + k] = (raw[4 * j + k] & M) | (PAD & ~M);
                 }
             }
+            chunk_max(j);
+            __builtin_amdgcn_sched_barrier(0);   // chunks in arrival order
         }
-    }
-
-    // ---- maxima per chunk and per lane (raw patterns read as signed) ----
-    uint32_t cmx[CPT];
-    int m;
-    if constexpr (DT == SS_BF16) {
+    } else {
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
-            const s16x2 a = __builtin_elementwise_max(bits_s16x2(raw[4 * j]), bits_s16x2(raw[4 * j + 1]));
-            const s16x2 c = __builtin_elementwise_max(bits_s16x2(raw[4 * j + 2]), bits_s16x2(raw[4 * j + 3]));
-            cmx[j] = s16x2_bits(__builtin_elementwise_max(a, c));
+            chunk_max(j);
+            __builtin_amdgcn_sched_barrier(0);
         }
+    }
+    int m;
+    if constexpr (DT == SS_BF16) {
         s16x2 mm = bits_s16x2(cmx[0]);
 #pragma unroll
         for (int j = 1; j < CPT; ++j) mm = __builtin_elementwise_max(mm, bits_s16x2(cmx[j]));
         m = max((int)mm.x, (int)mm.y);
     } else {
-#pragma unroll
-        for (int j = 0; j < CPT; ++j)
-            cmx[j] = (uint32_t)max(max((int)raw[4 * j], (int)raw[4 * j + 1]),
-                                   max((int)raw[4 * j + 2], (int)raw[4 * j + 3]));
         m = (int)cmx[0];
 #pragma unroll
         for (int j = 1; j < CPT; ++j) m = max(m, (int)cmx[j]);
