@@ -70,6 +70,20 @@ typedef uint32_t vu32x4 __attribute__((ext_vector_type(4)));   // 16-byte load u
 // format, no swizzle, no per-lane index.
 constexpr int BUF_DWORD3 = 0x00020000;
 
+// A buffer view of `bytes` bytes at `base` (uniform).  Loads at offsets
+// past the end return zero and touch no memory, so a fixed run of loads
+// needs no branch around the ones that fall outside.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_view(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, BUF_DWORD3);
+}
+__device__ __forceinline__ uint32_t buf_u32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint64_t buf_u64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+    return (uint64_t)v[0] | ((uint64_t)v[1] << 32);
+}
+
 template <typename T>
 __device__ __forceinline__ const __attribute__((address_space(1))) T* gmem(const T* p) {
     return (const __attribute__((address_space(1))) T*)p;

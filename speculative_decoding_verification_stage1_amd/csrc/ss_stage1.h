@@ -304,7 +304,7 @@ __device__ __forceinline__ void tile_fetch(const Stage1Params& P, int row, int t
     // as zero without touching memory; tile_patch sets them.  The whole
     // offset is in the lane's offset, which the range check covers.
     const int nbytes = P.aligned16 ? (nvalid / EPC) * 16 : 0;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)rowp, (short)0, nbytes, BUF_DWORD3);
+    const __amdgpu_buffer_rsrc_t rs = buf_view(rowp, (uint32_t)nbytes);
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
         const vu32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, (tid + j * S1_THREADS) * 16, 0, 0);

@@ -89,7 +89,10 @@ __device__ __forceinline__ bool finitef(float x) { return x == x && x - x == 0.0
 // the (uniform) request record.
 // bias_head: this lane's entry lane of the request's bias values when the
 // caller requested it early (NaN-free check), else read here.
-__device__ inline RowParams row_params(const Stage1Params& P, int b, const float* bias_head = nullptr) {
+// rq_pre: the request record's eight words when the caller requested them
+// early, else read here.
+__device__ inline RowParams row_params(const Stage1Params& P, int b, const float* bias_head = nullptr,
+                                       const uint32_t* rq_pre = nullptr) {
     RowParams rp{};
     if (!P.req) {   // plain top-k: no processing
         rp.valid = 1;
@@ -97,7 +100,13 @@ __device__ inline RowParams row_params(const Stage1Params& P, int b, const float
         rp.K = min(KMAX, P.V);
         return rp;
     }
-    const ss_req r = P.req[b];
+    ss_req r;
+    if (rq_pre) {
+        static_assert(sizeof(ss_req) == 8 * sizeof(uint32_t), "request record");
+        __builtin_memcpy(&r, rq_pre, sizeof(r));
+    } else {
+        r = P.req[b];
+    }
     const uint32_t f = r.flags;
     rp.flags = f;
     rp.temperature = r.temperature;
@@ -352,6 +361,7 @@ struct RowLoads {
     typename S1Traits<DT>::Key pre_lo[S2_PREFETCH], pre_hi[S2_PREFETCH];
     WL64 listed;
     float bias_head;   // bias value `lane` of the request (validation)
+    uint32_t rq[8];    // the request record
 };
 template <int DT>
 __device__ __forceinline__ void row_loads(const Stage2Params& F, int row, RowLoads<DT>& L) {
@@ -359,23 +369,39 @@ __device__ __forceinline__ void row_loads(const Stage2Params& F, int row, RowLoa
     const Stage1Params& P = F.s1;
     const int lane = lane_id();
     const int wave = threadIdx.x / WAVE;
-    const auto sc = gmem((const Key*)P.scratch + (int64_t)row * P.Zv * KMAX);
+    // the request record and the bias values first: the row's parameters
+    // are worked out while the lists arrive
+    if (P.req) {
+        const auto rq = gmem((const uint32_t*)(P.req + row / P.rows_per_req));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) L.rq[i] = rq[i];
+    }
+    // bias value `lane` (zero past the stride or without values)
+    {
+        const int b = row / P.rows_per_req;
+        const auto bv = buf_view(P.aux.bias_val + (P.aux.bias_val ? (int64_t)b * P.aux.bias_stride : 0),
+                                 P.aux.bias_val ? (uint32_t)P.aux.bias_stride * 4u : 0u);
+        L.bias_head = __uint_as_float(buf_u32(bv, (uint32_t)lane * 4u));
+    }
+    // the tile lists: a fixed run of loads over the row's lists (tiles past
+    // Zv read as key 0, no token)
+    const auto sv = buf_view((const Key*)P.scratch + (int64_t)row * P.Zv * KMAX,
+                             (uint32_t)(P.Zv * KMAX * (int)sizeof(Key)));
 #pragma unroll
     for (int i = 0; i < S2_PREFETCH; ++i) {
-        const int t = wave + S2_WAVES * i;
-        L.pre_lo[i] = t < P.Zv ? sc[(int64_t)t * KMAX + lane] : (Key)0;
-        L.pre_hi[i] = t < P.Zv ? sc[(int64_t)t * KMAX + lane + WAVE] : (Key)0;
+        const uint32_t o = (uint32_t)((wave + S2_WAVES * i) * KMAX + lane) * (uint32_t)sizeof(Key);
+        if constexpr (sizeof(Key) == 4) {
+            L.pre_lo[i] = buf_u32(sv, o);
+            L.pre_hi[i] = buf_u32(sv, o + WAVE * 4u);
+        } else {
+            L.pre_lo[i] = buf_u64(sv, o);
+            L.pre_hi[i] = buf_u64(sv, o + WAVE * 8u);
+        }
     }
-    L.listed = WL64{0ull, 0ull};
-    if (wave == 0 && F.listed) {   // used only when the row has lists
-        const auto lk = gmem(F.listed + (int64_t)row * KMAX);
-        L.listed = WL64{lk[lane], lk[lane + WAVE]};
-    }
-    L.bias_head = 0.0f;
-    if (P.aux.bias_val && lane < P.aux.bias_stride) {
-        const int b = row / P.rows_per_req;
-        L.bias_head = gmem(P.aux.bias_val)[(int64_t)b * P.aux.bias_stride + lane];
-    }
+    // wave 0: the listed tokens' list (used only when the row has lists)
+    const auto lv = buf_view(F.listed ? F.listed + (int64_t)row * KMAX : nullptr,
+                             (F.listed && wave == 0) ? (uint32_t)(KMAX * 8) : 0u);
+    L.listed = WL64{buf_u64(lv, (uint32_t)lane * 8u), buf_u64(lv, (uint32_t)(lane + WAVE) * 8u)};
 }
 
 // The row's 128 best as a wave-0 register list; one workgroup barrier.
@@ -518,10 +544,16 @@ __device__ __forceinline__ void row_epilogue(const Stage2Params& F, const RowPar
         es[lane + WAVE] = e_hi;
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
+        // every e is requested before the chain starts (the chain then
+        // waits on no LDS read)
+        float4 eq[KMAX / 4];
+#pragma unroll
+        for (int i = 0; i < KMAX / 4; ++i) eq[i] = *(const float4*)&es[4 * i];
+        __builtin_amdgcn_sched_barrier(0);
         float E = 0.0f;
 #pragma unroll
         for (int k0 = 0; k0 < KMAX; k0 += 4) {
-            const float4 q = *(const float4*)&es[k0];
+            const float4 q = eq[k0 / 4];
             float4 o;
             o.x = E;
             E = E + q.x;
@@ -610,7 +642,7 @@ __global__ __launch_bounds__(S2_THREADS) void stage2_kernel(Stage2Params F) {
     row_loads<DT>(F, row, L);   // the Stage-1 lists first
     ss_rng rg{0ull, 0ull};
     if (F.rng) rg = *F.rng;
-    const RowParams rp = row_params(F.s1, b, &L.bias_head);
+    const RowParams rp = row_params(F.s1, b, &L.bias_head, L.rq);
     const WL64 best = row_merge<DT>(F, rp, row, sh, L);
     if (threadIdx.x >= WAVE) return;
     row_epilogue<DT>(F, rp, row, b, best, rg, sh);
