@@ -515,13 +515,16 @@ __device__ __forceinline__ void row_epilogue(const Stage2Params& F, const RowPar
             return v;
         };
         const float m = vscale(z0);
-        if (lane < K) {
-            v_lo = vscale(z_lo);
-            e_lo = exp_fixed(v_lo - m);
-        }
-        if (lane + 64 < K) {
-            v_hi = vscale(z_hi);
-            e_hi = exp_fixed(v_hi - m);
+        // ranks past K keep v = -inf, e = 0 (selected, so that the code
+        // below has no branch)
+        const bool in_lo = lane < K, in_hi = lane + 64 < K;
+        {
+            const float vl = vscale(z_lo), vh = vscale(z_hi);
+            const float el = exp_fixed(vl - m), eh = exp_fixed(vh - m);
+            v_lo = in_lo ? vl : NINF;
+            v_hi = in_hi ? vh : NINF;
+            e_lo = in_lo ? el : 0.0f;
+            e_hi = in_hi ? eh : 0.0f;
         }
         uint32_t c1, c2;
         if (F.mode == MODE_VERIFY) {
@@ -531,43 +534,33 @@ __device__ __forceinline__ void row_epilogue(const Stage2Params& F, const RowPar
             c1 = (uint32_t)row;
             c2 = 0u;
         }
-        // Gumbel noise of every candidate, independent of the sums below
-        float g_lo = 0.0f, g_hi = 0.0f;
-        if (lane < K) g_lo = gumbel_noise(rg.seed, rg.offset, (uint32_t)id_lo, c1, c2);
-        if (lane + 64 < K) g_hi = gumbel_noise(rg.seed, rg.offset, (uint32_t)id_hi, c1, c2);
         // running sums E_k = e_0 + ... + e_{k-1}, left to right: the e's go
         // to LDS and every lane runs the same dependent chain on broadcast
-        // reads (ranks past K hold e = 0, which leaves E unchanged)
+        // reads (ranks past K hold e = 0, which leaves E unchanged); lane k
+        // keeps E_k and E_{k+64}.  The Gumbel noise of both candidates is
+        // worked out in the same straight-line block, so that its dependent
+        // chains and the sum's fill each other's latency.
         float* es = (float*)&sh.wl[0][0][0];   // waves 1-3 are done with sh
-        float* Es = es + KMAX;
         es[lane] = e_lo;
         es[lane + WAVE] = e_hi;
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
-        // every e is requested before the chain starts (the chain then
-        // waits on no LDS read)
         float4 eq[KMAX / 4];
 #pragma unroll
         for (int i = 0; i < KMAX / 4; ++i) eq[i] = *(const float4*)&es[4 * i];
-        __builtin_amdgcn_sched_barrier(0);
-        float E = 0.0f;
+        const float gl = gumbel_noise(rg.seed, rg.offset, (uint32_t)id_lo, c1, c2);
+        const float gh = gumbel_noise(rg.seed, rg.offset, (uint32_t)id_hi, c1, c2);
+        float E = 0.0f, E_lo = 0.0f, E_hi = 0.0f;
 #pragma unroll
-        for (int k0 = 0; k0 < KMAX; k0 += 4) {
-            const float4 q = eq[k0 / 4];
-            float4 o;
-            o.x = E;
-            E = E + q.x;
-            o.y = E;
-            E = E + q.y;
-            o.z = E;
-            E = E + q.z;
-            o.w = E;
-            E = E + q.w;
-            if (lane == 0) *(float4*)&Es[k0] = o;
+        for (int k = 0; k < KMAX; ++k) {
+            const float4 q = eq[k / 4];
+            const float ek = (k & 3) == 0 ? q.x : (k & 3) == 1 ? q.y : (k & 3) == 2 ? q.z : q.w;
+            const bool mine = __builtin_amdgcn_inverse_ballot_w64(1ull << (k & 63));   // lane == k mod 64
+            if (k < WAVE) E_lo = mine ? E : E_lo;
+            else E_hi = mine ? E : E_hi;
+            E = E + ek;
         }
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        const float E_lo = Es[lane], E_hi = Es[lane + WAVE];
+        const float g_lo = in_lo ? gl : 0.0f, g_hi = in_hi ? gh : 0.0f;
         Z = E;
         int n_p = K, n_m = K;
         if ((rp.flags & SS_TOPP) && rp.top_p < 1.0f) {
