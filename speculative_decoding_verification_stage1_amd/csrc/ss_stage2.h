@@ -426,7 +426,20 @@ __device__ __forceinline__ WL64 row_merge(const Stage2Params& F, const RowParams
     const int mine_n = wave < P.Zv ? (P.Zv - wave + S2_WAVES - 1) / S2_WAVES : 0;
     WL64 mine{0ull, 0ull};
     if (mine_n >= 1) mine = tl(0);
-    if (mine_n >= 2) {
+    if (DT == SS_BF16 && mine_n == 2) {
+        // two bf16 tiles merge on their 32-bit keys: bit 15 of the low half
+        // is always set (local < 2^15) and is cleared on the second tile's
+        // keys, so that equal values rank the first tile (lower ids) first;
+        // a valid key's high half is never 0, so no key becomes "no token"
+        const WList<uint32_t> a{(uint32_t)pre_lo[0], (uint32_t)pre_hi[0]};
+        const WList<uint32_t> c{(uint32_t)pre_lo[1] & ~0x8000u, (uint32_t)pre_hi[1] & ~0x8000u};
+        const WList<uint32_t> m = wave_merge(a, c);
+        auto widen = [&](uint32_t k) -> uint64_t {   // the tile comes back from bit 15
+            return k ? merge_key<DT>((typename S1Traits<DT>::Key)(k | 0x8000u), (k & 0x8000u) ? wave : wave + S2_WAVES)
+                     : 0ull;
+        };
+        mine = WL64{widen(m.lo), widen(m.hi)};
+    } else if (mine_n >= 2) {
         WL64 a = tl(1);
         if (mine_n >= 3) {
             WL64 c = tl(2);
