@@ -43,8 +43,8 @@ __global__ __launch_bounds__(S1_THREADS) void stage1_kernel(Stage1Params P) {
     const int tile = wg - row * P.Zv;
     WList<Key> res{0, 0};
     stage1_tile<DT>(P, row, tile, sh, &res);
-    if (tid < WAVE) {   // wave 0 holds the tile's sorted 128 keys
-        const int64_t o = ((int64_t)row * P.Zv + tile) * KMAX + tid;
+    if (tid / WAVE == s1_lead_wave()) {   // the lead wave holds the tile's sorted 128 keys
+        const int64_t o = ((int64_t)row * P.Zv + tile) * KMAX + (tid & (WAVE - 1));
         ((Key*)P.scratch)[o] = res.lo;
         ((Key*)P.scratch)[o + WAVE] = res.hi;
         if (P.out_ids) {

@@ -225,6 +225,8 @@ struct S1In {
     uint32_t rq_flags, rq_lists; // the request's flags and its n_prior | n_bias << 8
 };
 
+__device__ __forceinline__ int s1_lead_wave() { return (int)((blockIdx.x >> 3) & (S1_WAVES - 1)); }
+
 #define S1_TILE_GEOMETRY                                                             \
     using T = S1Traits<DT>;                                                          \
     constexpr int EPC = T::EPC;                                                      \
@@ -234,6 +236,10 @@ struct S1In {
     constexpr uint32_t PAD = DT == SS_BF16 ? 0x80008000u : 0x80000000u;              \
     const int tid = threadIdx.x;                                                     \
     const int wave = tid / WAVE;                                                     \
+    /* the wave that reads the lists, merges last and holds the result: it   \
+       rotates with the workgroup index, so that the workgroups sharing a    \
+       compute unit put this extra work on different SIMDs */                \
+    const int lead = s1_lead_wave();                                                 \
     const int lane = lane_id();                                                      \
     const int base = tile * BN;                                                      \
     const int nvalid = min(BN, P.V - base);                                          \
@@ -241,7 +247,7 @@ struct S1In {
     const bool full = (nvalid == BN);                                                \
     const bool vec = full && P.aligned16;                                            \
     const char* rowp = (const char*)P.logits + ((int64_t)row * P.ld + base) * (DT == SS_BF16 ? 2 : 4); \
-    (void)wave; (void)lane; (void)b; (void)vec; (void)NQ; (void)PAD;
+    (void)wave; (void)lead; (void)lane; (void)b; (void)vec; (void)NQ; (void)PAD;
 
 // Dword q of this thread's slice (chunk q >> 2, dword q & 3); elements past
 // the end of V read as the smallest signed pattern.
@@ -278,7 +284,7 @@ __device__ __forceinline__ void tile_fetch(const Stage1Params& P, int row, int t
     in.l_pid = -1;
     in.l_pct = 0;
     in.l_bid = -1;
-    if (wave == 0) {
+    if (wave == lead) {
         if (P.aux.prior_ids && P.aux.prior_cnt && lane < P.aux.prior_stride) {
             const int64_t o = (int64_t)b * P.aux.prior_stride + lane;
             in.l_pid = gmem(P.aux.prior_ids)[o];
@@ -398,9 +404,9 @@ __device__ __forceinline__ void tile_process(const Stage1Params& P, int row, int
     }
     const int l_pid = in.l_pid, l_pct = in.l_pct, l_bid = in.l_bid;
 
-    // ---- wave 0: tokens of this tile named by an active list (ranked in
+    // ---- the lead wave: tokens of this tile named by an active list (ranked in
     // Stage 2, left out here) ----
-    if (wave == 0) {
+    if (wave == lead) {
         int nl = 0;
         auto record = [&](bool ok, int loc) {
             const uint64_t bal = __ballot(ok);
@@ -621,21 +627,26 @@ __device__ __forceinline__ void tile_process(const Stage1Params& P, int row, int
     __syncthreads();   // wave lists, ovf
 
     if (fast && sh.ovf == 0) {
-        // ---- merge tree: (0+1) on wave 0 and (2+3) on wave 1, then both ----
+        // ---- merge tree over the wave lists, in the lead wave's order
+        // (lw = 0 is the lead): (0+1) on lw 0 and (2+3) on lw 1, then both ----
+        const int lw = (wave - lead) & (S1_WAVES - 1);
+        auto wl_of = [&](int l) -> WList<Key> {
+            const int w = (l + lead) & (S1_WAVES - 1);
+            return WList<Key>{sh.wl[w][lane], sh.wl[w][lane + WAVE]};
+        };
+        const int w2 = (lead + 2) & (S1_WAVES - 1);
         WList<Key> r{0, 0};
-        if (wave < 2) {
-            const int a = 2 * wave;
-            r = wave_merge(WList<Key>{sh.wl[a][lane], sh.wl[a][lane + WAVE]},
-                           WList<Key>{sh.wl[a + 1][lane], sh.wl[a + 1][lane + WAVE]});
-            if (wave == 1) {
-                sh.wl[2][lane] = r.lo;
-                sh.wl[2][lane + WAVE] = r.hi;
+        if (lw < 2) {
+            r = wave_merge(wl_of(2 * lw), wl_of(2 * lw + 1));
+            if (lw == 1) {
+                sh.wl[w2][lane] = r.lo;
+                sh.wl[w2][lane + WAVE] = r.hi;
             }
         }
         __syncthreads();
-        if (wave == 0) {
-            r = wave_merge(r, WList<Key>{sh.wl[2][lane], sh.wl[2][lane + WAVE]});
-            if (to_regs) {   // the caller takes wave 0's registers
+        if (lw == 0) {
+            r = wave_merge(r, WList<Key>{sh.wl[w2][lane], sh.wl[w2][lane + WAVE]});
+            if (to_regs) {   // the caller takes the lead wave's registers
                 *to_regs = r;
                 return;
             }
@@ -706,7 +717,7 @@ __device__ __forceinline__ void tile_process(const Stage1Params& P, int row, int
             if (k >= thr) g[off++] = k;
         }
     __syncthreads();
-    if (wave == 0) {
+    if (wave == lead) {
         WList<Key> l{lane < total ? g[lane] : (Key)0, lane + WAVE < total ? g[lane + WAVE] : (Key)0};
         l = wave_sort128(l);
         if (to_regs) {
@@ -721,8 +732,9 @@ __device__ __forceinline__ void tile_process(const Stage1Params& P, int row, int
 }
 
 // One tile, requested and processed in turn.  Without `to_regs` the sorted
-// result is left in sh.surv behind a barrier; with it, wave 0 receives the
-// result in registers and no wave waits at the end.
+// result is left in sh.surv behind a barrier; with it, the lead wave
+// (s1_lead_wave) receives the result in registers and no wave waits at the
+// end.
 template <int DT>
 __device__ __forceinline__ void stage1_tile(const Stage1Params& P, int row, int tile, S1Shared<DT>& sh,
                                             WList<typename S1Traits<DT>::Key>* to_regs = nullptr) {
