@@ -176,6 +176,14 @@ __device__ __forceinline__ float gumbel_noise(uint64_t seed, uint64_t offset, ui
     return -log_fixed(-log_fixed(u));
 }
 
+// n / d for uniform d > 0: d = 1 and powers of two (the usual tile counts and
+// rows per request) skip the integer division sequence.
+__device__ __forceinline__ int div_uniform(int n, int d) {
+    if (d == 1) return n;
+    if ((d & (d - 1)) == 0) return n >> __builtin_ctz((unsigned)d);
+    return n / d;
+}
+
 // ---------------------------------------------------------------------------
 // wave helpers (wave64)
 // ---------------------------------------------------------------------------

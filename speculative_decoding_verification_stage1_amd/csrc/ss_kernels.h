@@ -39,7 +39,7 @@ __global__ __launch_bounds__(S1_THREADS) void stage1_kernel(Stage1Params P) {
     }
     S1Shared<DT>& sh = shu.tile;
     const int wg = blockIdx.x - nlw;
-    const int row = wg / P.Zv;
+    const int row = div_uniform(wg, P.Zv);
     const int tile = wg - row * P.Zv;
     WList<Key> res{0, 0};
     stage1_tile<DT>(P, row, tile, sh, &res);

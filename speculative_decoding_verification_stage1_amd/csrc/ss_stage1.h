@@ -243,7 +243,7 @@ __device__ __forceinline__ int s1_lead_wave() { return (int)((blockIdx.x >> 3) &
     const int lane = lane_id();                                                      \
     const int base = tile * BN;                                                      \
     const int nvalid = min(BN, P.V - base);                                          \
-    const int b = __builtin_amdgcn_readfirstlane(row / P.rows_per_req);              \
+    const int b = __builtin_amdgcn_readfirstlane(div_uniform(row, P.rows_per_req));  \
     const bool full = (nvalid == BN);                                                \
     const bool vec = full && P.aligned16;                                            \
     const char* rowp = (const char*)P.logits + ((int64_t)row * P.ld + base) * (DT == SS_BF16 ? 2 : 4); \
@@ -273,13 +273,6 @@ __device__ __forceinline__ uint32_t tile_dword(const char* rowp, bool vec, int n
 template <int DT>
 __device__ __forceinline__ void tile_fetch(const Stage1Params& P, int row, int tile, S1In<DT>& in) {
     S1_TILE_GEOMETRY
-    in.rq_flags = 0;
-    in.rq_lists = 0;
-    if (P.req) {
-        const auto rq = gmem((const uint32_t*)(P.req + b));
-        in.rq_flags = rq[0];
-        in.rq_lists = rq[2] >> 16;   // n_prior, n_bias follow the 16-bit top_k
-    }
     // wave 0: the first 64 entries of the request's lists
     in.l_pid = -1;
     in.l_pct = 0;
@@ -319,6 +312,16 @@ __device__ __forceinline__ void tile_fetch(const Stage1Params& P, int row, int t
         in.raw[4 * j + 1] = v.y;
         in.raw[4 * j + 2] = v.z;
         in.raw[4 * j + 3] = v.w;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // the request's flags and list lengths last, through the scalar cache:
+    // nothing above waits for them
+    in.rq_flags = 0;
+    in.rq_lists = 0;
+    if (P.req) {
+        const auto rq = (const uint32_t*)(P.req + b);
+        in.rq_flags = rq[0];
+        in.rq_lists = rq[2] >> 16;   // n_prior, n_bias follow the 16-bit top_k
     }
 }
 

@@ -326,7 +326,7 @@ __device__ __forceinline__ WL64 listed_list(const Stage1Params& P, const RowPara
 // wave's own LDS area, then ranked as exact keys (list order arithmetic).
 template <int DT>
 __device__ __forceinline__ void listed_row_wave(const Stage1Params& P, uint64_t* out, int row, S2Lists& lists) {
-    const int b = __builtin_amdgcn_readfirstlane(row / P.rows_per_req);
+    const int b = __builtin_amdgcn_readfirstlane(div_uniform(row, P.rows_per_req));
     const RowParams rp = row_params(P, b);
     const int np = rp.valid ? rp.n_prior : 0;
     const int nb = rp.valid ? rp.n_bias : 0;
@@ -372,13 +372,13 @@ __device__ __forceinline__ void row_loads(const Stage2Params& F, int row, RowLoa
     // the request record and the bias values first: the row's parameters
     // are worked out while the lists arrive
     if (P.req) {
-        const auto rq = gmem((const uint32_t*)(P.req + row / P.rows_per_req));
+        const auto rq = gmem((const uint32_t*)(P.req + div_uniform(row, P.rows_per_req)));
 #pragma unroll
         for (int i = 0; i < 8; ++i) L.rq[i] = rq[i];
     }
     // bias value `lane` (zero past the stride or without values)
     {
-        const int b = row / P.rows_per_req;
+        const int b = div_uniform(row, P.rows_per_req);
         const auto bv = buf_view(P.aux.bias_val + (P.aux.bias_val ? (int64_t)b * P.aux.bias_stride : 0),
                                  P.aux.bias_val ? (uint32_t)P.aux.bias_stride * 4u : 0u);
         L.bias_head = __uint_as_float(buf_u32(bv, (uint32_t)lane * 4u));
@@ -643,7 +643,7 @@ template <int DT, int MODE>
 __global__ __launch_bounds__(S2_THREADS) void stage2_kernel(Stage2Params F) {
     __shared__ S2Shared sh;
     const int row = blockIdx.x;
-    const int b = __builtin_amdgcn_readfirstlane(row / F.s1.rows_per_req);
+    const int b = __builtin_amdgcn_readfirstlane(div_uniform(row, F.s1.rows_per_req));
     RowLoads<DT> L;
     row_loads<DT>(F, row, L);   // the Stage-1 lists first
     ss_rng rg{0ull, 0ull};
