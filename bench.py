@@ -4,9 +4,12 @@ penalties, logit bias, mixed per-request settings) on one MI355X.
 One step = one full pass of the hot path over the batch: Stage 1 (per-tile
 prelude + top-128) and Stage 2 (merge, temperature, top-p / min-p,
 Gumbel-max) for all 256 rows, replayed from a hipGraph with the Philox
-offset advanced on the device.  Inputs are resident in HBM; four copies of
-the logits and bitmask are rotated so the 256 MB last-level cache cannot
-serve a step from the previous one.
+offset advanced on the device.  Inputs are resident in HBM; sixteen copies
+of the logits and bitmask are rotated so the 256 MB last-level cache cannot
+serve a step from the previous one, and one graph holds one step per copy,
+so that the host's replay call (a few microseconds between replays) is
+spread over sixteen steps, as when the sampler's kernels run back to back
+inside a decode step's graph.
 
 Printed: one JSON line with the headline rate (sampled tokens/s), the
 Stage-1 roofline (algorithmic bytes / measured kernel time against the 8
@@ -153,7 +156,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--copies", type=int, default=16)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-verify", action="store_true", help="skip the verification latency")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -273,7 +276,8 @@ def main():
         "config": {
             "workload": "c2: B=256 V=262144 bf16 logits 2*N(0,1)+10 on 8 ids, grammar bitmask 5% allowed, "
                         "repetition/frequency/presence over 64 prior ids, 16 bias ids, mixed greedy/top-k/"
-                        "top-p/min-p; hipGraph replays of 4 steps over 4 rotating input copies",
+                        "top-p/min-p; hipGraph replays of one step per rotating input copy",
+            "input_copies": args.copies,
             "global_batch": B, "vocab": V, "tile": L.ss_tile_size(L.SS_BF16), "parallelism": "single-gpu",
         },
         "logits_GBps": round(logits_gbps, 1),
