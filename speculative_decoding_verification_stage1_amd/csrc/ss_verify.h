@@ -33,27 +33,39 @@ __global__ __launch_bounds__(VF_THREADS) void verify_kernel(Stage2Params F) {
 
     for (int j = wave; j <= G; j += VF_WAVES) {
         const RowRec* rec = r0 + j;
+        // every record field and draft value this position may use is
+        // requested at once (no load waits on a branch), then the draft
+        // probabilities at the candidates and at the draft token
         const int status = rec->status;
+        const int greedy = rec->greedy;
+        const int n = rec->n;
+        const int rtoken = rec->token;
+        const int best = rec->ids[0];
+        const int d = j < G ? F.draft_ids[(int64_t)b * G + j] : -1;
+        const int id_lo_r = rec->ids[lane], id_hi_r = rec->ids[lane + 64];
+        const float p_lo_r = rec->p[lane], p_hi_r = rec->p[lane + 64];
+        const float v_lo = rec->v[lane], v_hi = rec->v[lane + 64];
+        const float* q = F.draft_probs + ((int64_t)b * G + (j < G ? j : G - 1)) * V;   // any row for j = G
+        auto in_v = [&](int id) { return (unsigned)id < (unsigned)V; };
+        const float q_lo_r = q[in_v(id_lo_r) ? id_lo_r : 0];
+        const float q_hi_r = q[in_v(id_hi_r) ? id_hi_r : 0];
+        const float q_d_r = q[in_v(d) ? d : 0];
         int accept = 0, token = -1;
         const bool live = status == SS_ROW_OK || status == SS_ROW_TOPK_CLAMPED;
         if (live && j == G) {          // bonus token
-            token = rec->token;
+            token = rtoken;
             accept = 1;
-        } else if (live && rec->greedy) {
-            const int d = F.draft_ids[(int64_t)b * G + j];
-            token = rec->ids[0];
+        } else if (live && greedy) {
+            token = best;
             accept = d == token;
         } else if (live) {
-            const int d = F.draft_ids[(int64_t)b * G + j];
-            const int n = rec->n;
-            const float* q = F.draft_probs + ((int64_t)b * G + j) * V;
-            const int id_lo = lane < n ? rec->ids[lane] : -1;
-            const int id_hi = lane + 64 < n ? rec->ids[lane + 64] : -1;
-            const float p_lo = lane < n ? rec->p[lane] : 0.0f;
-            const float p_hi = lane + 64 < n ? rec->p[lane + 64] : 0.0f;
-            const float q_lo = id_lo >= 0 ? q[id_lo] : 0.0f;
-            const float q_hi = id_hi >= 0 ? q[id_hi] : 0.0f;
-            const float qd = (d >= 0 && d < V) ? q[d] : 0.0f;
+            const int id_lo = lane < n ? id_lo_r : -1;
+            const int id_hi = lane + 64 < n ? id_hi_r : -1;
+            const float p_lo = lane < n ? p_lo_r : 0.0f;
+            const float p_hi = lane + 64 < n ? p_hi_r : 0.0f;
+            const float q_lo = id_lo >= 0 ? q_lo_r : 0.0f;
+            const float q_hi = id_hi >= 0 ? q_hi_r : 0.0f;
+            const float qd = (d >= 0 && d < V) ? q_d_r : 0.0f;
             // p_j(d): the kept candidate equal to d, if any (ids are unique)
             float pd = 0.0f;
             const uint64_t m_lo = __ballot(id_lo == d && id_lo >= 0);
@@ -83,10 +95,10 @@ __global__ __launch_bounds__(VF_THREADS) void verify_kernel(Stage2Params F) {
                 }
                 token = wave_argmax(s, id, id >= 0);
                 if (token < 0) {   // p <= q on every kept candidate: draw from p
-                    float s2 = id_lo >= 0 ? rec->v[lane] + g_lo : 0.0f;
+                    float s2 = id_lo >= 0 ? v_lo + g_lo : 0.0f;
                     int i2 = id_lo;
                     if (id_hi >= 0) {
-                        const float sh = rec->v[lane + 64] + g_hi;
+                        const float sh = v_hi + g_hi;
                         if (i2 < 0 || sh > s2 || (sh == s2 && id_hi < i2)) {
                             s2 = sh;
                             i2 = id_hi;
