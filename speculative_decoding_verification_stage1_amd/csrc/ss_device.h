@@ -170,10 +170,31 @@ __device__ __forceinline__ float log_fixed(float x) {
     return __builtin_fmaf(ef, 0x1.62e4p-1f, __builtin_fmaf(ef, 0x1.7f7d1cp-20f, h + h));
 }
 
+// log_fixed for a positive, normal, finite x (its special cases and the
+// subnormal scaling never apply): the same operations, with no branch.
+__device__ __forceinline__ float log_fixed_normal(float x) {
+    const uint32_t b = fbits(x);
+    int e = (int)(b >> 23) - 127;
+    float m = bitsf((b & 0x007FFFFFu) | 0x3F800000u);
+    const bool big = m > 0x1.6a09e6p+0f;
+    m = big ? m * 0.5f : m;
+    e += big ? 1 : 0;
+    const float s = (m - 1.0f) / (m + 1.0f);
+    const float s2 = s * s;
+    float q = __builtin_fmaf(0x1.c71c72p-4f, s2, 0x1.24924ap-3f);
+    q = __builtin_fmaf(q, s2, 0x1.99999ap-3f);
+    q = __builtin_fmaf(q, s2, 0x1.555556p-2f);
+    const float h = __builtin_fmaf(s * s2, q, s);
+    const float ef = (float)e;
+    return __builtin_fmaf(ef, 0x1.62e4p-1f, __builtin_fmaf(ef, 0x1.7f7d1cp-20f, h + h));
+}
+
+// u lies in [2^-24, 1 - 2^-24], so -ln u is positive and normal: both
+// logarithms take the branch-free form.
 __device__ __forceinline__ float gumbel_noise(uint64_t seed, uint64_t offset, uint32_t c0,
                                               uint32_t c1, uint32_t c2) {
     const float u = unit_open(philox_w0(seed, offset, c0, c1, c2));
-    return -log_fixed(-log_fixed(u));
+    return -log_fixed_normal(-log_fixed_normal(u));
 }
 
 // n / d for uniform d > 0: d = 1 and powers of two (the usual tile counts and
