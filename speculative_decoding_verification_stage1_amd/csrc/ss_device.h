@@ -127,12 +127,12 @@ __device__ __forceinline__ float unit_open(uint32_t w) {
 // give 0.  log: x = 2^e m, m in (sqrt(1/2), sqrt(2)], ln m = 2 atanh((m-1)/
 // (m+1)) by its odd series to the 9th power.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float exp_fixed(float x) {
-    if (x != x) return x;
-    if (x < -86.0f) return 0.0f;
-    if (x > 88.0f) return bitsf(F32_PINF_BITS);
-    const float n = __builtin_rintf(x * 0x1.715476p+0f);
-    float r = __builtin_fmaf(-n, 0x1.62e4p-1f, x);
+// exp for x <= 0 or -inf (never NaN), the only arguments the epilogue has
+// (x = v - max v); the cut below -86 is a select, not a branch.
+__device__ __forceinline__ float exp_fixed_nonpos(float x) {
+    const float xc = x < -86.0f ? -86.0f : x;
+    const float n = __builtin_rintf(xc * 0x1.715476p+0f);
+    float r = __builtin_fmaf(-n, 0x1.62e4p-1f, xc);
     r = __builtin_fmaf(-n, 0x1.7f7d1cp-20f, r);
     float p = __builtin_fmaf(0x1.a01a02p-13f, r, 0x1.6c16c2p-10f);
     p = __builtin_fmaf(p, r, 0x1.111112p-7f);
@@ -141,7 +141,7 @@ __device__ __forceinline__ float exp_fixed(float x) {
     p = __builtin_fmaf(p, r, 0.5f);
     p = __builtin_fmaf(p, r, 1.0f);
     p = __builtin_fmaf(p, r, 1.0f);
-    return __builtin_ldexpf(p, (int)n);
+    return x < -86.0f ? 0.0f : __builtin_ldexpf(p, (int)n);
 }
 
 __device__ __forceinline__ float log_fixed(float x) {

@@ -533,7 +533,8 @@ __device__ __forceinline__ void row_epilogue(const Stage2Params& F, const RowPar
         const bool in_lo = lane < K, in_hi = lane + 64 < K;
         {
             const float vl = vscale(z_lo), vh = vscale(z_hi);
-            const float el = exp_fixed(vl - m), eh = exp_fixed(vh - m);
+            // v - m <= 0 (m is the best value; a live row's m is finite)
+            const float el = exp_fixed_nonpos(vl - m), eh = exp_fixed_nonpos(vh - m);
             v_lo = in_lo ? vl : NINF;
             v_hi = in_hi ? vh : NINF;
             e_lo = in_lo ? el : 0.0f;
