@@ -221,7 +221,7 @@ template <int DT>
 struct S1In {
     uint32_t raw[S1_CPT * 4];   // dword q: dword (q & 3) of this thread's chunk (q >> 2)
     uint32_t gw[S1_CPT * S1Traits<DT>::EPC / 32];   // the tile's bitmask words tid + 256k
-    int l_pid, l_pct, l_bid;    // wave 0: first 64 entries of the request's lists
+    int l_pid, l_pct, l_bid;    // lead wave: first 64 entries of the request's lists
     uint32_t rq_flags, rq_lists; // the request's flags and its n_prior | n_bias << 8
 };
 
@@ -273,7 +273,7 @@ __device__ __forceinline__ uint32_t tile_dword(const char* rowp, bool vec, int n
 template <int DT>
 __device__ __forceinline__ void tile_fetch(const Stage1Params& P, int row, int tile, S1In<DT>& in) {
     S1_TILE_GEOMETRY
-    // wave 0: the first 64 entries of the request's lists
+    // the lead wave: the first 64 entries of the request's lists
     in.l_pid = -1;
     in.l_pct = 0;
     in.l_bid = -1;
@@ -367,10 +367,11 @@ __device__ __forceinline__ void tile_patch(const Stage1Params& P, int row, int t
 }
 
 // The 128 best tokens of tile `tile` of row `row` (whose data `in` holds),
-// sorted best first, left in sh.surv[0..128) (key 0 = no token).  Ends with
-// a barrier.  `next()` is called as soon as the registers of `in` are no
-// longer needed (the candidate chunks are in LDS by then), so that the
-// caller can request its next tile into them while this one is finished.
+// sorted best first (key 0 = no token): left in sh.surv[0..128) behind a
+// final barrier, or, with `to_regs`, handed to the lead wave's registers
+// with no final barrier (the other waves return early).  `next()` is called
+// as soon as the registers of `in` are no longer needed (the candidate
+// chunks are in LDS by then).
 template <int DT, typename Next>
 __device__ __forceinline__ void tile_process(const Stage1Params& P, int row, int tile, S1In<DT>& in,
                                              S1Shared<DT>& sh, Next&& next,
@@ -420,8 +421,7 @@ __device__ __forceinline__ void tile_process(const Stage1Params& P, int row, int
             }
             nl += __popcll(bal);
         };
-        // entries 0..63 come from the early request (no wait on memory
-        // here: the next tile's loads are in flight); longer lists load the
+        // entries 0..63 come from the early request; longer lists load the
         // rest now
         if (use_prior) {
             const int loc = l_pid - base;
