@@ -233,7 +233,9 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 }
 
 // ---------------------------------------------------------------------------
-// lane exchange v(lane ^ J) with no LDS traffic: DPP quad permutes for J =
+// lane exchange v(lane ^ J) with no LDS traffic (every DPP pattern here is a
+// full permutation, so bound_ctrl, which lets the compiler fold the move
+// into the instruction that uses it, changes no value): DPP quad permutes for J =
 // 1, 2; two DPP mirrors for J = 4 (quad reversal, then the 8-lane mirror:
 // l ^ 3 ^ 7 = l ^ 4) and J = 8 (8-lane mirror, then the 16-lane mirror:
 // l ^ 7 ^ 15 = l ^ 8); the gfx950 row-swap permutes for J = 16, 32.
@@ -245,15 +247,15 @@ constexpr int DPP_ROW_HALF_MIRROR = 0x141;
 template <int J>
 __device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
     if constexpr (J == 1) {
-        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
     } else if constexpr (J == 2) {
-        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
     } else if constexpr (J == 4) {
-        const int a = __builtin_amdgcn_mov_dpp((int)v, DPP_QUAD_REV, 0xF, 0xF, false);
-        return (uint32_t)__builtin_amdgcn_mov_dpp(a, DPP_ROW_HALF_MIRROR, 0xF, 0xF, false);
+        const int a = __builtin_amdgcn_mov_dpp((int)v, DPP_QUAD_REV, 0xF, 0xF, true);
+        return (uint32_t)__builtin_amdgcn_mov_dpp(a, DPP_ROW_HALF_MIRROR, 0xF, 0xF, true);
     } else if constexpr (J == 8) {
-        const int a = __builtin_amdgcn_mov_dpp((int)v, DPP_ROW_HALF_MIRROR, 0xF, 0xF, false);
-        return (uint32_t)__builtin_amdgcn_mov_dpp(a, DPP_ROW_MIRROR, 0xF, 0xF, false);
+        const int a = __builtin_amdgcn_mov_dpp((int)v, DPP_ROW_HALF_MIRROR, 0xF, 0xF, true);
+        return (uint32_t)__builtin_amdgcn_mov_dpp(a, DPP_ROW_MIRROR, 0xF, 0xF, true);
     } else if constexpr (J == 16) {
         const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
         return (lane_id() & 16) ? r[0] : r[1];

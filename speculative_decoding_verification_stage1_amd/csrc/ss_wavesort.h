@@ -7,8 +7,9 @@
 // A compare-exchange with lane ^ J keeps the larger key in some lanes and
 // the smaller in the others; which lanes do depends only on J and the stage,
 // so it is a compile-time 64-bit lane mask, turned into a per-lane flag with
-// no vector instruction (inverse ballot).  Each step is then one exchange,
-// one compare and one select.
+// no vector instruction (inverse ballot).  For 32-bit keys within a row of
+// 16 lanes a step is a max and a min that read the exchanged value through
+// DPP, and one select; otherwise one exchange, one compare and one select.
 #pragma once
 
 #include "ss_device.h"
@@ -45,7 +46,13 @@ template <int J, uint64_t KEEP, typename K>
 __device__ __forceinline__ K cas_lane(K a) {
     const K p = xor_key<J>(a);
     const bool keep_max = __builtin_amdgcn_inverse_ballot_w64(KEEP);
-    return ((p > a) == keep_max) ? p : a;
+    if constexpr (sizeof(K) == 4 && J <= 8) {
+        // 32-bit keys within a row of 16 lanes: max and min take the lane
+        // exchange as an operand, and the lane mask picks one (no compare)
+        return keep_max ? kmax(a, p) : kmin(a, p);
+    } else {
+        return ((p > a) == keep_max) ? p : a;
+    }
 }
 
 // Half-cleaners j = J .. 1 on both halves (descending).
@@ -68,7 +75,7 @@ __device__ __forceinline__ void cas_64(WList<K>& c) {
 // v(63 - lane): the 16-lane mirror (l ^ 15), then rows swapped by the
 // row-swap permutes (l ^ 48).
 __device__ __forceinline__ uint32_t reverse_lanes32(uint32_t v) {
-    const uint32_t m = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, DPP_ROW_MIRROR, 0xF, 0xF, false);
+    const uint32_t m = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, DPP_ROW_MIRROR, 0xF, 0xF, true);
     return xor_lane<16>(xor_lane<32>(m));
 }
 template <typename K>
