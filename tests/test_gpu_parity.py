@@ -120,6 +120,43 @@ def test_sample_small_shapes(V):
         sample_parity(W.SampleWorkload(f"small-V{V}-dt{dtype}", dtype, logits, req), seed=5, offset=77)
 
 
+def run_sample_strided(logits_np, dtype, req, ld, seed=0, offset=0):
+    """Like run_sample, but the rows lie `ld` elements apart in a wider
+    buffer (the columns past V hold large values the step must not read)."""
+    lib = L()
+    B, V = logits_np.shape
+    wide = np.zeros((B, ld), dtype=logits_np.dtype)
+    wide[:, :V] = logits_np
+    wide[:, V:] = W.to_bf16_bits(np.full((B, ld - V), 1e4, np.float32)) if dtype == W.DTYPE_BF16 else 1e4
+    xw = _dev_logits(wide, dtype)
+    x = xw[:, :V]
+    assert x.stride(0) == ld
+    dreq = lib.DeviceRequests(req)
+    rng = lib.make_rng(seed, offset)
+    out = dict(tokens=torch.full((B,), -7, dtype=torch.int32, device="cuda"),
+               topk_ids=torch.full((B, 128), -7, dtype=torch.int32, device="cuda"),
+               probs=torch.full((B, 128), -7.0, dtype=torch.float32, device="cuda"),
+               kept=torch.full((B,), -7, dtype=torch.int32, device="cuda"),
+               mass=torch.full((B,), -7.0, dtype=torch.float32, device="cuda"),
+               status=torch.full((B,), -7, dtype=torch.int32, device="cuda"))
+    ws = lib.workspace(B, V, dtype)
+    lib.ss_sample_step(x, dreq, rng, out["tokens"], out["topk_ids"], out["probs"], out["kept"],
+                       out["mass"], out["status"], ws)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+@pytest.mark.parametrize("dtype,pad", [(W.DTYPE_BF16, 8), (W.DTYPE_BF16, 3), (W.DTYPE_F32, 4), (W.DTYPE_F32, 1)])
+def test_sample_strided_rows(dtype, pad):
+    # row stride above V: 16-byte aligned rows (fast path) and rows that are
+    # not (every element read by the exact path)
+    wl = W.workload_mixed(1, 6, 40000, grammar=False)
+    logits = wl.logits if dtype == W.DTYPE_BF16 else W.bf16_bits_to_f32(wl.logits)
+    g = run_sample_strided(logits, dtype, wl.req, 40000 + pad, seed=3, offset=9)
+    o = oracle.sample(logits, dtype, wl.req, seed=3, offset=9, threads=16)
+    compare_sample(g, o, tag=f"strided dt{dtype} pad{pad}")
+
+
 def test_sample_mixed_small_with_grammar_and_lists():
     for cfg, grammar in [(1, False), (2, True)]:
         wl = W.workload_mixed(cfg, 12, 90000, grammar=grammar)
