@@ -79,7 +79,7 @@ def lib():
                                     u64, u64, P, P, P, P, P, P, i32]
         L.oracle_sample.restype = i32
         L.oracle_verify.argtypes = [P, i32, i32, i32, i32, i64, P, P, P, i32, P, P, i32, P, i64,
-                                    P, P, u64, u64, P, P, P, i32]
+                                    P, P, P, u64, u64, P, P, P, i32]
         L.oracle_verify.restype = i32
         L.oracle_topk.argtypes = [P, i32, i32, i32, i64, i32, P, P, i32]
         L.oracle_topk.restype = i32
@@ -230,8 +230,10 @@ def sample(logits, dtype: int, req, seed: int = 0, offset: int = 0, threads: int
 
 
 def verify(target, dtype: int, B: int, gamma: int, req, draft_ids, draft_probs, bitmask=None,
-           seed: int = 0, offset: int = 0, threads: int = 1, flags=None, packed=None):
-    """Speculative verification of gamma drafts for B requests.  Returns a
+           seed: int = 0, offset: int = 0, threads: int = 1, flags=None, packed=None, cu_num_draft=None):
+    """Speculative verification of gamma drafts for B requests (or of
+    n_b = cu[b] - cu[b-1] <= gamma drafts each, with the inclusive cumulative
+    counts `cu_num_draft`; tensors keep their gamma-wide layout).  Returns a
     dict with tokens [B, gamma+1] (-1 padded), n_emit [B], status [B]."""
     x = np.ascontiguousarray(target)
     rows, V = x.shape
@@ -241,11 +243,13 @@ def verify(target, dtype: int, B: int, gamma: int, req, draft_ids, draft_probs, 
     bm = None if bitmask is None else np.ascontiguousarray(bitmask, np.uint32)
     d = np.ascontiguousarray(draft_ids, np.int32)
     q = np.ascontiguousarray(draft_probs, np.float32)
+    cu = None if cu_num_draft is None else np.ascontiguousarray(cu_num_draft, np.int32)
+    assert cu is None or cu.shape == (B,)
     out = dict(tokens=np.zeros((B, gamma + 1), np.int32), n_emit=np.zeros(B, np.int32),
                status=np.zeros(B, np.int32))
     rc = lib().oracle_verify(
         _p(x), dtype, B, gamma, V, V, _p(r), _p(pid), _p(pc), pid.shape[1], _p(bid), _p(bv),
-        bid.shape[1], _p(bm), 0 if bm is None else bm.shape[1], _p(d), _p(q), seed, offset,
+        bid.shape[1], _p(bm), 0 if bm is None else bm.shape[1], _p(d), _p(q), _p(cu), seed, offset,
         _p(out["tokens"]), _p(out["n_emit"]), _p(out["status"]), threads)
     if rc != 0:
         raise ValueError("oracle_verify rejected its arguments")

@@ -539,6 +539,12 @@ int oracle_sample(const void* logits, int dtype, int B, int V, int64_t ld, const
  * Noise counters (c0, c1, c2): Gumbel for position j (0 / token id, b,
  * j), acceptance uniform (0, b, (1<<24)|j), residual Gumbel (id, b,
  * (2<<24)|j).
+ * Variable drafts per request [DN "Rejection Sampler": per-request draft
+ * counts from cumulative offsets]: with cu_num_draft (inclusive cumulative
+ * counts, n_b = cu[b] - cu[b-1]) request b has n_b <= gamma drafts at
+ * positions 0..n_b-1 of its (still gamma+1) rows, and its bonus position
+ * is n_b; the rows past n_b take no part.  n_b outside [0, gamma] makes
+ * the request invalid.
  * ====================================================================== */
 typedef struct {
     const void* target; int dtype; int B; int gamma; int V; int64_t ld;
@@ -547,6 +553,7 @@ typedef struct {
     const int32_t* bias_ids; const float* bias_val; int bias_stride;
     const uint32_t* bitmask; int64_t bitmask_stride;
     const int32_t* draft_ids; const float* draft_probs;
+    const int32_t* cu_num_draft;
     uint64_t seed, offset;
     int32_t* out_tokens; int32_t* n_emit; int32_t* status;
     int row_begin, row_end;
@@ -584,16 +591,24 @@ static void* verify_worker(void* arg)
               r->n_bias >= 0 && r->n_bias <= J->bias_stride) || !arrays_ok(r, &S)) {
             st = OST_INVALID;
         }
-        for (int j = 0; j <= G && st != OST_INVALID; ++j) {
+        /* this request's draft count: gamma, or from the cumulative offsets */
+        int Gb = G;
+        if (J->cu_num_draft) {
+            const int64_t hi = J->cu_num_draft[b];
+            const int64_t lo = b > 0 ? J->cu_num_draft[b - 1] : 0;
+            if (hi - lo < 0 || hi - lo > G) st = OST_INVALID;
+            else Gb = (int)(hi - lo);
+        }
+        for (int j = 0; j <= Gb && st != OST_INVALID; ++j) {
             int64_t row = (int64_t)b * (G + 1) + j;
             prelude_for(&S, r, row, b, z);
             decide_row(r, z, V, J->prior_stride, J->bias_stride, bv, work, d);
             if (d->status == OST_INVALID) { st = OST_INVALID; emitted = 0; break; }
             if (d->status == OST_TOPK_CLAMPED) st = OST_TOPK_CLAMPED;
             if (d->status == OST_ALL_MASKED) { st = OST_ALL_MASKED; break; }
-            if (j == G) {    /* bonus token */
+            if (j == Gb) {   /* bonus token */
                 out[emitted++] = d->greedy ? d->cand[0].id
-                                           : gumbel_pick(d, d->n, J->seed, J->offset, (uint32_t)b, (uint32_t)G);
+                                           : gumbel_pick(d, d->n, J->seed, J->offset, (uint32_t)b, (uint32_t)Gb);
                 break;
             }
             int32_t dj = J->draft_ids[(int64_t)b * G + j];
@@ -640,7 +655,7 @@ int oracle_verify(const void* target, int dtype, int B, int gamma, int V, int64_
                   const int32_t* prior_ids, const int32_t* prior_cnt, int prior_stride,
                   const int32_t* bias_ids, const float* bias_val, int bias_stride,
                   const uint32_t* bitmask, int64_t bitmask_stride,
-                  const int32_t* draft_ids, const float* draft_probs,
+                  const int32_t* draft_ids, const float* draft_probs, const int32_t* cu_num_draft,
                   uint64_t seed, uint64_t offset,
                   int32_t* out_tokens, int32_t* n_emit, int32_t* status, int threads)
 {
@@ -655,7 +670,7 @@ int oracle_verify(const void* target, int dtype, int B, int gamma, int V, int64_
         J->prior_ids = prior_ids; J->prior_cnt = prior_cnt; J->prior_stride = prior_stride;
         J->bias_ids = bias_ids; J->bias_val = bias_val; J->bias_stride = bias_stride;
         J->bitmask = bitmask; J->bitmask_stride = bitmask_stride;
-        J->draft_ids = draft_ids; J->draft_probs = draft_probs;
+        J->draft_ids = draft_ids; J->draft_probs = draft_probs; J->cu_num_draft = cu_num_draft;
         J->seed = seed; J->offset = offset;
         J->out_tokens = out_tokens; J->n_emit = n_emit; J->status = status;
     }

@@ -140,3 +140,98 @@ def test_verify_workload_shapes_and_determinism():
     for r in range(4):
         n = a["n_emit"][r]
         assert np.all(a["tokens"][r, :n] >= 0) and np.all(a["tokens"][r, n:] == -1)
+
+
+# ---------------------------------------------------------------------------
+# per-request draft counts (inclusive cumulative offsets, as in the rejection
+# kernel on the notes page): request b checks n_b = cu[b] - cu[b-1] drafts
+# and draws its bonus at position n_b
+# ---------------------------------------------------------------------------
+
+def _cu(counts):
+    return np.cumsum(np.asarray(counts, np.int64)).astype(np.int32)
+
+
+def test_variable_drafts_greedy_control_flow():
+    V, gamma, B = 40, 4, 8
+    rng = np.random.default_rng(21)
+    target = (rng.standard_normal((B * (gamma + 1), V)) * 3).astype(np.float32)
+    am = target.argmax(1).reshape(B, gamma + 1)
+    counts = [0, 1, 2, 3, 4, 2, 0, 3]
+    mismatch_at = [None, None, 1, None, 0, None, None, 2]
+    d = am[:, :gamma].copy().astype(np.int32)
+    for b, j in enumerate(mismatch_at):
+        if j is not None:
+            d[b, j] = (am[b, j] + 1) % V
+    qp = np.full((B, gamma, V), 1.0 / V, np.float32)
+    out = oracle.verify(target, W.DTYPE_F32, B, gamma, W.plain_requests(B, greedy=True), d, qp,
+                        cu_num_draft=_cu(counts))
+    for b in range(B):
+        n, j = counts[b], mismatch_at[b]
+        if j is None or j >= n:   # every checked draft matches: n drafts, then the bonus at n
+            assert out["n_emit"][b] == n + 1
+            assert list(out["tokens"][b, :n]) == list(d[b, :n])
+            assert out["tokens"][b, n] == am[b, n]
+        else:
+            assert out["n_emit"][b] == j + 1
+            assert out["tokens"][b, j] == am[b, j]
+        assert np.all(out["tokens"][b, out["n_emit"][b]:] == -1)
+
+
+def test_variable_drafts_bonus_follows_its_position():
+    # q = the target's own fp32 probabilities: every draft is accepted and the
+    # bonus comes from row n_b, whatever that is
+    rng = np.random.default_rng(22)
+    V, N, gamma = 5, 60000, 2
+    zs = [(rng.standard_normal(V) * 1.0).astype(np.float32) for _ in range(gamma + 1)]
+    target = np.stack([np.stack(zs)] * N).reshape(N * (gamma + 1), V)
+    qrows = []
+    for j in range(gamma):
+        o = oracle.sample(zs[j][None], W.DTYPE_F32, W.plain_requests(1, temperature=1.0))
+        qq = np.zeros(V, np.float32)
+        qq[o["topk_ids"][0, :V]] = o["probs"][0, :V]
+        qrows.append(qq)
+    qp = np.tile(np.stack(qrows), (N, 1, 1))
+    d = np.stack([np.searchsorted(np.cumsum(qrows[j].astype(np.float64)), rng.random(N) * qrows[j].sum(),
+                                  side="right").clip(0, V - 1) for j in range(gamma)], 1).astype(np.int32)
+    counts = rng.integers(0, gamma + 1, N)
+    out = oracle.verify(target, W.DTYPE_F32, N, gamma, W.plain_requests(N, temperature=1.0), d, qp,
+                        threads=8, cu_num_draft=_cu(counts))
+    assert np.array_equal(out["n_emit"], counts + 1)
+    for n in range(gamma + 1):
+        sel = counts == n
+        assert np.array_equal(out["tokens"][sel, :n], d[sel, :n])
+        bonus = out["tokens"][sel, n]
+        pv = stats.chisquare([(bonus == i).sum() for i in range(V)], _p_of(zs[n]) * sel.sum()).pvalue
+        assert pv > 1e-3, (n, pv)
+
+
+def test_variable_drafts_ignore_unused_positions():
+    wl = W.workload_verify(B=6, gamma=4, V=4096)
+    counts = [4, 0, 2, 1, 3, 4]
+    cu = _cu(counts)
+    a = oracle.verify(wl.target, wl.dtype, wl.B, wl.gamma, wl.req, wl.draft_ids, wl.draft_probs, cu_num_draft=cu)
+    d2 = wl.draft_ids.copy()
+    q2 = wl.draft_probs.copy()
+    t2 = wl.target.copy().reshape(wl.B, wl.gamma + 1, -1)
+    rng = np.random.default_rng(23)
+    for b, n in enumerate(counts):
+        d2[b, n:] = rng.integers(0, 4096, wl.gamma - n)
+        q2[b, n:] = rng.random((wl.gamma - n, 4096)).astype(np.float32)
+        t2[b, n + 1:] = t2[b, n + 1:][:, ::-1]   # rows past the bonus position changed too
+    b_ = oracle.verify(t2.reshape(wl.target.shape), wl.dtype, wl.B, wl.gamma, wl.req, d2, q2, cu_num_draft=cu)
+    assert np.array_equal(a["tokens"], b_["tokens"]) and np.array_equal(a["n_emit"], b_["n_emit"])
+    # counts equal to gamma everywhere: the fixed-gamma result
+    full = oracle.verify(wl.target, wl.dtype, wl.B, wl.gamma, wl.req, wl.draft_ids, wl.draft_probs,
+                         cu_num_draft=_cu([wl.gamma] * wl.B))
+    ref = oracle.verify(wl.target, wl.dtype, wl.B, wl.gamma, wl.req, wl.draft_ids, wl.draft_probs)
+    assert np.array_equal(full["tokens"], ref["tokens"]) and np.array_equal(full["n_emit"], ref["n_emit"])
+
+
+def test_variable_drafts_out_of_range_counts_are_invalid():
+    wl = W.workload_verify(B=3, gamma=2, V=512)
+    cu = np.array([3, 2, 4], np.int32)   # counts 3 (> gamma), -1, 2
+    out = oracle.verify(wl.target, wl.dtype, wl.B, wl.gamma, wl.req, wl.draft_ids, wl.draft_probs, cu_num_draft=cu)
+    assert list(out["status"][:2]) == [oracle.STATUS_INVALID] * 2
+    assert list(out["n_emit"][:2]) == [0, 0] and np.all(out["tokens"][:2] == -1)
+    assert out["status"][2] != oracle.STATUS_INVALID and out["n_emit"][2] >= 1
