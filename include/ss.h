@@ -211,6 +211,25 @@ int ss_verify_step(const void* target_logits, int dtype, int B, int gamma, int V
                    int32_t* out_tokens, int32_t* out_n_emit, int32_t* out_status,
                    void* ws, size_t ws_bytes, void* stream);
 
+/* ss_verify_step with a per-request number of drafts (the decoding notes,
+ * "Rejection Sampler": the verification kernel takes each request's draft
+ * range from cumulative offsets, cu_num_draft_tokens).  cu_num_draft
+ * [B] int32 in device memory holds inclusive cumulative counts, so request
+ * b has n_b = cu[b] - cu[b-1] (cu[-1] = 0) drafts.  The tensors keep the
+ * gamma-wide layout of ss_verify_step (gamma is the largest count): request
+ * b's drafts are draft_ids[b, 0..n_b-1] and draft_probs[b, 0..n_b-1], its
+ * target rows are b*(gamma+1) + 0..n_b, and row n_b gives its bonus token;
+ * rows, drafts and probabilities past n_b are not used (they are still read
+ * by the tile stage, so keep them finite or masked).  A count outside
+ * [0, gamma] makes the request SS_ROW_INVALID (no token emitted).  The
+ * counts are read on the device, so the call stays graph-capturable.
+ * cu_num_draft = NULL is ss_verify_step. */
+int ss_verify_step_var(const void* target_logits, int dtype, int B, int gamma, int V, int64_t ld,
+                       const ss_req* req, const ss_aux* aux, ss_rng* rng, uint64_t rng_advance,
+                       const int32_t* cu_num_draft, const int32_t* draft_ids, const float* draft_probs,
+                       int32_t* out_tokens, int32_t* out_n_emit, int32_t* out_status,
+                       void* ws, size_t ws_bytes, void* stream);
+
 /* Two-stage top-k of raw logits (no processing beyond NaN -> -inf, +inf ->
  * FLT_MAX, -0 -> +0): out_ids [B, k] in order (value descending, id
  * ascending) and out_vals [B, k] (optional) their values; positions past V

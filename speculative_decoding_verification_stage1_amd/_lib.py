@@ -76,6 +76,8 @@ def _load():
     L.ss_sample_step.restype = i32
     L.ss_verify_step.argtypes = [P, i32, i32, i32, i32, i64, P, P, P, u64, P, P, P, P, P, P, sz, P]
     L.ss_verify_step.restype = i32
+    L.ss_verify_step_var.argtypes = [P, i32, i32, i32, i32, i64, P, P, P, u64, P, P, P, P, P, P, P, sz, P]
+    L.ss_verify_step_var.restype = i32
     L.ss_topk_step.argtypes = [P, i32, i32, i32, i64, i32, P, P, P, sz, P]
     L.ss_topk_step.restype = i32
     L.ss_topk_single_pass.argtypes = [P, i32, i32, i32, i64, i32, P, P, P]
@@ -91,8 +93,8 @@ def _load():
 
 lib = _load()
 
-EXPORTS = ["ss_workspace_bytes", "ss_tile_size", "ss_sample_step", "ss_verify_step", "ss_topk_step",
-           "ss_topk_single_pass", "ss_tile_topk", "ss_rng_advance", "ss_status_str"]
+EXPORTS = ["ss_workspace_bytes", "ss_tile_size", "ss_sample_step", "ss_verify_step", "ss_verify_step_var",
+           "ss_topk_step", "ss_topk_single_pass", "ss_tile_topk", "ss_rng_advance", "ss_status_str"]
 
 
 class SsError(RuntimeError):
@@ -230,6 +232,17 @@ def ss_verify_step(target, B: int, gamma: int, dreq: DeviceRequests, rng, draft_
                             ctypes.byref(dreq.aux), ptr(rng), rng_advance, ptr(draft_ids), ptr(draft_probs),
                             ptr(out_tokens), ptr(out_n_emit), ptr(out_status), ptr(ws),
                             0 if ws is None else ws.numel(), stream_handle(stream))
+    return _check(rc)
+
+
+def ss_verify_step_var(target, B: int, gamma: int, dreq: DeviceRequests, rng, cu_num_draft, draft_ids,
+                       draft_probs, out_tokens, out_n_emit, out_status=None, ws=None, stream=None,
+                       rng_advance: int = 0) -> int:
+    rows, V = target.shape
+    rc = lib.ss_verify_step_var(ptr(target), dtype_code(target), B, gamma, V, target.stride(0), ptr(dreq.req),
+                                ctypes.byref(dreq.aux), ptr(rng), rng_advance, ptr(cu_num_draft), ptr(draft_ids),
+                                ptr(draft_probs), ptr(out_tokens), ptr(out_n_emit), ptr(out_status), ptr(ws),
+                                0 if ws is None else ws.numel(), stream_handle(stream))
     return _check(rc)
 
 

@@ -225,6 +225,15 @@ int ss_verify_step(const void* target_logits, int dtype, int B, int gamma, int V
                    const ss_req* req, const ss_aux* aux, ss_rng* rng, uint64_t rng_advance, const int32_t* draft_ids,
                    const float* draft_probs, int32_t* out_tokens, int32_t* out_n_emit, int32_t* out_status,
                    void* ws, size_t ws_bytes, void* stream) {
+    return ss_verify_step_var(target_logits, dtype, B, gamma, V, ld, req, aux, rng, rng_advance, nullptr, draft_ids,
+                              draft_probs, out_tokens, out_n_emit, out_status, ws, ws_bytes, stream);
+}
+
+int ss_verify_step_var(const void* target_logits, int dtype, int B, int gamma, int V, int64_t ld,
+                       const ss_req* req, const ss_aux* aux, ss_rng* rng, uint64_t rng_advance,
+                       const int32_t* cu_num_draft, const int32_t* draft_ids, const float* draft_probs,
+                       int32_t* out_tokens, int32_t* out_n_emit, int32_t* out_status,
+                       void* ws, size_t ws_bytes, void* stream) {
     if (gamma < 1 || gamma > SS_GAMMA_MAX) return SS_ERR_UNSUPPORTED;
     if (B < 0 || (int64_t)B * (gamma + 1) > KERNEL_ROWS_MAX) return B < 0 ? SS_ERR_INVALID_ARG : SS_ERR_UNSUPPORTED;
     const int rows = B * (gamma + 1);
@@ -247,6 +256,7 @@ int ss_verify_step(const void* target_logits, int dtype, int B, int gamma, int V
     f.gamma = gamma;
     f.draft_ids = draft_ids;
     f.draft_probs = draft_probs;
+    f.cu_num_draft = cu_num_draft;
     f.v_tokens = out_tokens;
     f.v_n_emit = out_n_emit;
     f.v_status = out_status;

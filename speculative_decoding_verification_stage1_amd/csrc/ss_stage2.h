@@ -56,6 +56,7 @@ struct Stage2Params {
     int gamma;
     const int32_t* draft_ids;
     const float* draft_probs;
+    const int32_t* cu_num_draft;   // optional [B] inclusive cumulative draft counts
     int32_t* v_tokens;
     int32_t* v_n_emit;
     int32_t* v_status;

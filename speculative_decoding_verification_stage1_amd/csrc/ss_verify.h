@@ -10,6 +10,12 @@
 // waves evaluate all positions at once; one lane then walks the positions
 // in order to emit the accepted prefix and the first rejection's draw (or
 // the bonus token).
+//
+// With per-request draft counts (inclusive cumulative offsets, as the
+// notes' rejection kernel reads its range from cu_num_draft_tokens),
+// request b checks n_b = cu[b] - cu[b-1] drafts, at positions 0..n_b-1 of
+// its gamma + 1 rows, and its bonus position is n_b; rows past n_b take no
+// part.  A count outside [0, gamma] makes the request invalid.
 #pragma once
 
 #include "ss_stage2.h"
@@ -30,8 +36,16 @@ __global__ __launch_bounds__(VF_THREADS) void verify_kernel(Stage2Params F) {
     const int V = F.s1.V;
     const ss_rng rg = *F.rng;
     const RowRec* r0 = F.recs + (int64_t)b * (G + 1);
+    int Gb = G;   // this request's draft count (uniform)
+    bool count_ok = true;
+    if (F.cu_num_draft) {
+        const int hi = F.cu_num_draft[b];
+        const int lo = b > 0 ? F.cu_num_draft[b - 1] : 0;
+        count_ok = hi - lo >= 0 && hi - lo <= G;
+        Gb = count_ok ? hi - lo : 0;
+    }
 
-    for (int j = wave; j <= G; j += VF_WAVES) {
+    for (int j = wave; j <= Gb; j += VF_WAVES) {
         const RowRec* rec = r0 + j;
         // every record field and draft value this position may use is
         // requested at once (no load waits on a branch), then the draft
@@ -41,7 +55,7 @@ __global__ __launch_bounds__(VF_THREADS) void verify_kernel(Stage2Params F) {
         const int n = rec->n;
         const int rtoken = rec->token;
         const int best = rec->ids[0];
-        const int d = j < G ? F.draft_ids[(int64_t)b * G + j] : -1;
+        const int d = j < Gb ? F.draft_ids[(int64_t)b * G + j] : -1;
         const int id_lo_r = rec->ids[lane], id_hi_r = rec->ids[lane + 64];
         const float p_lo_r = rec->p[lane], p_hi_r = rec->p[lane + 64];
         const float v_lo = rec->v[lane], v_hi = rec->v[lane + 64];
@@ -52,7 +66,7 @@ __global__ __launch_bounds__(VF_THREADS) void verify_kernel(Stage2Params F) {
         const float q_d_r = q[in_v(d) ? d : 0];
         int accept = 0, token = -1;
         const bool live = status == SS_ROW_OK || status == SS_ROW_TOPK_CLAMPED;
-        if (live && j == G) {          // bonus token
+        if (live && j == Gb) {         // bonus token
             token = rtoken;
             accept = 1;
         } else if (live && greedy) {
@@ -120,16 +134,16 @@ __global__ __launch_bounds__(VF_THREADS) void verify_kernel(Stage2Params F) {
         int32_t* out = F.v_tokens + (int64_t)b * (G + 1);
         int emitted = 0;
         int st;
-        if (s_status[0] == SS_ROW_INVALID) {
+        if (!count_ok || s_status[0] == SS_ROW_INVALID) {
             st = SS_ROW_INVALID;
         } else {
             st = s_status[0] == SS_ROW_TOPK_CLAMPED ? SS_ROW_TOPK_CLAMPED : SS_ROW_OK;
-            for (int j = 0; j <= G; ++j) {
+            for (int j = 0; j <= Gb; ++j) {
                 if (s_status[j] == SS_ROW_ALL_MASKED) {
                     st = SS_ROW_ALL_MASKED;
                     break;
                 }
-                if (j < G && s_accept[j]) {
+                if (j < Gb && s_accept[j]) {
                     out[emitted++] = F.draft_ids[(int64_t)b * G + j];
                     continue;
                 }

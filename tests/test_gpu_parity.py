@@ -307,7 +307,7 @@ def test_determinism_repeated_runs():
 # verification
 # ---------------------------------------------------------------------------
 
-def run_verify(wl, seed=0, offset=0, rng_advance=0):
+def run_verify(wl, seed=0, offset=0, rng_advance=0, cu_num_draft=None):
     lib = L()
     x = _dev_logits(wl.target, wl.dtype)
     rows, V = x.shape
@@ -322,16 +322,21 @@ def run_verify(wl, seed=0, offset=0, rng_advance=0):
     ne = torch.full((B,), -7, dtype=torch.int32, device="cuda")
     st = torch.full((B,), -7, dtype=torch.int32, device="cuda")
     ws = lib.workspace(rows, V, wl.dtype)
-    lib.ss_verify_step(x, B, G, dreq, rng, d, q, toks, ne, st, ws, rng_advance=rng_advance)
+    if cu_num_draft is None:
+        lib.ss_verify_step(x, B, G, dreq, rng, d, q, toks, ne, st, ws, rng_advance=rng_advance)
+    else:
+        cu = torch.from_numpy(np.ascontiguousarray(cu_num_draft, np.int32)).cuda()
+        lib.ss_verify_step_var(x, B, G, dreq, rng, cu, d, q, toks, ne, st, ws, rng_advance=rng_advance)
     torch.cuda.synchronize()
     return dict(tokens=toks.cpu().numpy(), n_emit=ne.cpu().numpy(), status=st.cpu().numpy(),
                 offset_after=int(rng.cpu().view(torch.int64)[1]))
 
 
-def verify_parity(wl, seed=0, offset=0):
-    g = run_verify(wl, seed, offset)
+def verify_parity(wl, seed=0, offset=0, cu_num_draft=None):
+    g = run_verify(wl, seed, offset, cu_num_draft=cu_num_draft)
     o = oracle.verify(wl.target, wl.dtype, wl.B, wl.gamma, wl.req, wl.draft_ids, wl.draft_probs,
-                      bitmask=getattr(wl, "bitmask", None), seed=seed, offset=offset, threads=16)
+                      bitmask=getattr(wl, "bitmask", None), seed=seed, offset=offset, threads=16,
+                      cu_num_draft=cu_num_draft)
     for k in ("tokens", "n_emit", "status"):
         assert np.array_equal(g[k], o[k]), (k, np.nonzero((g[k] != o[k]).reshape(wl.B, -1).any(1))[0][:10])
     return g
@@ -345,6 +350,34 @@ def test_verify_small():
 def test_verify_c3_full():
     g = verify_parity(W.workload_verify())
     assert g["n_emit"].min() >= 1
+
+
+def _counts_cu(counts):
+    return np.cumsum(np.asarray(counts, np.int64)).astype(np.int32)
+
+
+def test_verify_variable_draft_counts():
+    # per-request counts 0..gamma, including requests that check no draft
+    # (bonus only) and two with counts outside [0, gamma] (invalid)
+    wl = W.workload_verify(B=16, gamma=4, V=20000)
+    counts = np.random.default_rng(31).integers(0, 5, 16)
+    counts[0], counts[1] = 0, 4
+    cu = _counts_cu(counts)
+    g = verify_parity(wl, seed=2, offset=3, cu_num_draft=cu)
+    assert np.array_equal(g["n_emit"] <= counts + 1, np.ones(16, bool))
+    bad = cu.copy()
+    bad[5] = bad[4] + 5    # count 5 > gamma
+    bad[6] = bad[5] - 1    # count -1
+    bad[7:] = bad[7:] - counts[5] - counts[6] + 5 - 1
+    g = verify_parity(wl, seed=2, offset=3, cu_num_draft=bad)
+    assert g["status"][5] == 2 and g["status"][6] == 2
+
+
+def test_verify_variable_draft_counts_c3_full():
+    wl = W.workload_verify()
+    counts = np.random.default_rng(32).integers(0, wl.gamma + 1, wl.B)
+    g = verify_parity(wl, cu_num_draft=_counts_cu(counts))
+    assert np.all(g["n_emit"] >= 1) and np.all(g["n_emit"] <= counts + 1)
 
 
 def test_verify_accept_all_and_mixed_settings():
