@@ -334,6 +334,29 @@ def main():
         result["verify_mean_emitted"] = round(float(vne.float().mean().item()), 3)
         result["verify_acceptance_rate"] = round(float((vne.float() - 1).sum().item()) / (vw.B * G), 4)
 
+        # the same requests with per-request draft counts (seeded, uniform in
+        # 0..gamma), passed as inclusive cumulative offsets
+        counts = np.random.default_rng(1003).integers(0, G + 1, vw.B)
+        cu = torch.from_numpy(np.cumsum(counts).astype(np.int32)).to(dev)
+        vgraph2 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(vgraph2, stream=stream):
+            for i in range(tcopies):
+                L.ss_verify_step_var(ts[i], vw.B, G, vreq, rng, cu, d, q, vout, vne, None, vws, stream=stream,
+                                     rng_advance=1)
+        torch.cuda.synchronize()
+        for i in range(3):
+            vgraph2.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(vreps):
+            vgraph2.replay()
+        torch.cuda.synchronize()
+        result["verify_var"] = {
+            "us": round((time.perf_counter() - t0) / (vreps * tcopies) * 1e6, 2),
+            "draft_counts": "uniform 0..4 per request (seeded), mean %.2f" % float(counts.mean()),
+            "mean_emitted": round(float(vne.float().mean().item()), 3),
+        }
+
     if not args.no_extra:
         result.update(extra_measurements(args, dev, L, W, stream))
 

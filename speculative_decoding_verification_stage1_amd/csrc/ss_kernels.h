@@ -34,13 +34,14 @@ __global__ __launch_bounds__(S1_THREADS) void stage1_kernel(Stage1Params P) {
     if ((int)blockIdx.x < nlw) {
         const int wave = tid / WAVE;
         const int r = (int)blockIdx.x * S1_WAVES + wave;
-        if (r < P.listed_rows) listed_row_wave<DT>(P, P.listed, r, shu.lists[wave]);
+        if (r < P.listed_rows && row_used(P, r)) listed_row_wave<DT>(P, P.listed, r, shu.lists[wave]);
         return;
     }
     S1Shared<DT>& sh = shu.tile;
     const int wg = blockIdx.x - nlw;
     const int row = div_uniform(wg, P.Zv);
     const int tile = wg - row * P.Zv;
+    if (!row_used(P, row)) return;   // no loads for a row past its request's bonus position
     WList<Key> res{0, 0};
     stage1_tile<DT>(P, row, tile, sh, &res);
     if (tid / WAVE == s1_lead_wave()) {   // the lead wave holds the tile's sorted 128 keys

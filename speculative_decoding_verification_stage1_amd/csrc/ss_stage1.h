@@ -80,7 +80,20 @@ struct Stage1Params {
     ss_rng* rng;         // sampling / verification: the caller's generator state
     ss_rng* rng_snap;    // ... copied here for Stage 2 (workgroup 0)
     uint64_t rng_advance;   // ... after which rng->offset += rng_advance
+    const int32_t* cu_num_draft;   // verification with per-request draft counts (or null)
 };
+
+// Whether row `row` takes part: always, except in verification with
+// per-request draft counts, where request b's rows past its bonus position
+// n_b are not used (a count outside [0, rows_per_req - 1] leaves every row
+// in: the request is reported invalid).  Uniform per workgroup.
+__device__ __forceinline__ bool row_used(const Stage1Params& P, int row) {
+    if (!P.cu_num_draft) return true;
+    const int b = div_uniform(row, P.rows_per_req);
+    const int j = row - b * P.rows_per_req;
+    const int n = P.cu_num_draft[b] - (b > 0 ? P.cu_num_draft[b - 1] : 0);
+    return n < 0 || n >= P.rows_per_req || j <= n;
+}
 
 // Largest t such that at least k lanes of the wave hold m >= t (signed).
 // Bisection on the biased value, one ballot per bit.

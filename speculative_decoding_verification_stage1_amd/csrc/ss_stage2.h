@@ -645,6 +645,7 @@ template <int DT, int MODE>
 __global__ __launch_bounds__(S2_THREADS) void stage2_kernel(Stage2Params F) {
     __shared__ S2Shared sh;
     const int row = blockIdx.x;
+    if (!row_used(F.s1, row)) return;
     const int b = __builtin_amdgcn_readfirstlane(div_uniform(row, F.s1.rows_per_req));
     RowLoads<DT> L;
     row_loads<DT>(F, row, L);   // the Stage-1 lists first
