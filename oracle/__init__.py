@@ -26,6 +26,7 @@ FLAG_BIAS = 1 << 4
 FLAG_TOPK = 1 << 5
 FLAG_TOPP = 1 << 6
 FLAG_MINP = 1 << 7
+FLAG_DRAFT_HIST = 1 << 8   # verification: earlier drafts join the penalty history
 
 KMAX = 128
 

@@ -48,6 +48,7 @@
 #define OF_TOPK     (1u << 5)
 #define OF_TOPP     (1u << 6)
 #define OF_MINP     (1u << 7)
+#define OF_DRAFT_HIST (1u << 8)
 
 #define OK_MAX 128           /* bounded candidate set, [SS] section 3.3 */
 
@@ -545,6 +546,13 @@ int oracle_sample(const void* logits, int dtype, int B, int V, int64_t ld, const
  * positions 0..n_b-1 of its (still gamma+1) rows, and its bonus position
  * is n_b; the rows past n_b take no part.  n_b outside [0, gamma] makes
  * the request invalid.
+ * Penalty history with the earlier drafts [DN "Repetition penalty",
+ * "Frequency and presence penalties": the penalised history is every token
+ * generated so far]: for a request with OF_DRAFT_HIST, position j's
+ * history is the request's prior list with d_0..d_{j-1} added, each draft
+ * (an id in [0, V)) adding one occurrence: to the count of the first prior
+ * entry with its id and a count >= 1, else to an entry appended for it
+ * (one per distinct id, in order of first appearance).
  * ====================================================================== */
 typedef struct {
     const void* target; int dtype; int B; int gamma; int V; int64_t ld;
@@ -573,6 +581,8 @@ static void* verify_worker(void* arg)
     float* z = (float*)malloc(sizeof(float) * (size_t)V);
     zid* work = (zid*)malloc(sizeof(zid) * (size_t)V);
     rowdec* d = (rowdec*)malloc(sizeof(rowdec));
+    int32_t* hist_ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)(J->prior_stride + G + 1));
+    int32_t* hist_cnt = (int32_t*)malloc(sizeof(int32_t) * (size_t)(J->prior_stride + G + 1));
     sample_job S;            /* reuse the prelude helper */
     memset(&S, 0, sizeof(S));
     S.logits = J->target; S.dtype = J->dtype; S.V = V; S.ld = J->ld;
@@ -601,7 +611,34 @@ static void* verify_worker(void* arg)
         }
         for (int j = 0; j <= Gb && st != OST_INVALID; ++j) {
             int64_t row = (int64_t)b * (G + 1) + j;
-            prelude_for(&S, r, row, b, z);
+            if ((r->flags & OF_DRAFT_HIST) && (r->flags & (OF_REP | OF_FREQPRES)) && j > 0) {
+                /* the prior entries, then the drafts before position j */
+                const int np = r->n_prior;
+                for (int k = 0; k < np; ++k) {
+                    hist_ids[k] = J->prior_ids[(int64_t)b * J->prior_stride + k];
+                    hist_cnt[k] = J->prior_cnt[(int64_t)b * J->prior_stride + k];
+                }
+                int nh = np;
+                for (int i = 0; i < j; ++i) {
+                    const int32_t dv = J->draft_ids[(int64_t)b * G + i];
+                    if (dv < 0 || dv >= V) continue;
+                    int k = 0;
+                    while (k < nh && !(hist_ids[k] == dv && hist_cnt[k] >= 1)) ++k;
+                    if (k < nh) { hist_cnt[k] += 1; continue; }
+                    hist_ids[nh] = dv;
+                    hist_cnt[nh] = 1;
+                    ++nh;
+                }
+                oracle_prelude_row(row_ptr(S.logits, S.dtype, S.ld, row), S.dtype, V, r->flags,
+                                   S.bitmask ? S.bitmask + row * S.bitmask_stride : NULL,
+                                   hist_ids, hist_cnt, nh,
+                                   S.bias_ids ? S.bias_ids + (int64_t)b * S.bias_stride : NULL,
+                                   S.bias_val ? S.bias_val + (int64_t)b * S.bias_stride : NULL,
+                                   (r->flags & OF_BIAS) ? r->n_bias : 0,
+                                   r->rep, r->freq, r->pres, z);
+            } else {
+                prelude_for(&S, r, row, b, z);
+            }
             decide_row(r, z, V, J->prior_stride, J->bias_stride, bv, work, d);
             if (d->status == OST_INVALID) { st = OST_INVALID; emitted = 0; break; }
             if (d->status == OST_TOPK_CLAMPED) st = OST_TOPK_CLAMPED;
@@ -647,7 +684,7 @@ static void* verify_worker(void* arg)
         J->n_emit[b] = emitted;
         if (J->status) J->status[b] = st;
     }
-    free(z); free(work); free(d);
+    free(z); free(work); free(d); free(hist_ids); free(hist_cnt);
     return NULL;
 }
 

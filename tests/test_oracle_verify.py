@@ -235,3 +235,142 @@ def test_variable_drafts_out_of_range_counts_are_invalid():
     assert list(out["status"][:2]) == [oracle.STATUS_INVALID] * 2
     assert list(out["n_emit"][:2]) == [0, 0] and np.all(out["tokens"][:2] == -1)
     assert out["status"][2] != oracle.STATUS_INVALID and out["n_emit"][2] >= 1
+
+
+# ---------------------------------------------------------------------------
+# penalty history with the earlier drafts (decoding notes, "Repetition
+# penalty" / "Frequency and presence penalties": the history is every token
+# generated so far): with FLAG_DRAFT_HIST, position j is processed with the
+# prior list plus d_0..d_{j-1}, each draft adding one occurrence to the first
+# prior entry with its id and a count >= 1, else to an entry appended for it
+# ---------------------------------------------------------------------------
+
+def _hist_lists(prior_ids, prior_cnt, n_prior, drafts, V):
+    """The rule above, written out on Python lists."""
+    ids = list(prior_ids[:n_prior])
+    cnt = list(prior_cnt[:n_prior])
+    for dv in drafts:
+        if not (0 <= dv < V):
+            continue
+        for k in range(len(ids)):
+            if ids[k] == dv and cnt[k] >= 1:
+                cnt[k] += 1
+                break
+        else:
+            ids.append(int(dv))
+            cnt.append(1)
+    return ids, cnt
+
+
+def _req_with_list(req, b, ids, cnt):
+    import copy
+    r = copy.deepcopy(req)
+    P = max(r.prior_ids.shape[1], len(ids))
+    pid = np.full((r.batch, P), -1, np.int32)
+    pc = np.zeros((r.batch, P), np.int32)
+    pid[:, :r.prior_ids.shape[1]] = r.prior_ids
+    pc[:, :r.prior_cnt.shape[1]] = r.prior_cnt
+    pid[b, :len(ids)] = ids
+    pc[b, :len(ids)] = cnt
+    r.prior_ids, r.prior_cnt = pid, pc
+    r.n_prior = r.n_prior.copy()
+    r.n_prior[b] = len(ids)
+    return r
+
+
+def test_draft_history_penalties():
+    V, gamma, B = 48, 4, 5
+    rng = np.random.default_rng(41)
+    target = (rng.standard_normal((B * (gamma + 1), V)) * 1.5).astype(np.float32)
+    req = W.plain_requests(B, greedy=True)
+    req.use_penalties[:] = True
+    req.rep_penalty[:] = 2.5
+    req.freq_penalty[:] = 0.7
+    req.pres_penalty[:] = 0.4
+    P = 6
+    req.prior_ids = rng.choice(V, (B, P)).astype(np.int32)
+    req.prior_cnt = rng.integers(1, 4, (B, P)).astype(np.int32)
+    req.prior_cnt[1, 2] = 0            # an ignored entry: a draft of that id gets a new entry
+    req.n_prior = np.array([P, P, 3, 0, P], np.int32)
+    flags = [oracle.flags_of(req, b) | oracle.FLAG_DRAFT_HIST for b in range(B)]
+    # drafts chosen as the argmax of each position processed with its history,
+    # so that every draft is accepted; drafts repeat and hit prior ids
+    d = np.zeros((B, gamma), np.int32)
+    expect = np.zeros((B, gamma + 1), np.int32)
+    for b in range(B):
+        for j in range(gamma + 1):
+            ids, cnt = _hist_lists(req.prior_ids[b], req.prior_cnt[b], req.n_prior[b], d[b, :j], V)
+            z = oracle.prelude_row(target[b * (gamma + 1) + j], W.DTYPE_F32, flags[b], _req_with_list(req, b, ids, cnt), b)
+            best = int(np.argmax(z))   # first index of the maximum: ties go to the lower id
+            expect[b, j] = best
+            if j < gamma:
+                d[b, j] = best
+                if b == 2 and j == 1:
+                    d[b, j] = d[b, 0]     # a repeated draft (still accepted only if it is the argmax)
+                    expect[b, j] = best
+    out = oracle.verify(target, W.DTYPE_F32, B, gamma, req, d, np.full((B, gamma, V), 1.0 / V, np.float32),
+                        flags=np.array(flags, np.uint32))
+    for b in range(B):
+        n = out["n_emit"][b]
+        if b == 2 and d[2, 1] != expect[2, 1]:
+            assert n == 2 and out["tokens"][2, 1] == expect[2, 1]
+        else:
+            assert n == gamma + 1, b
+            assert list(out["tokens"][b]) == list(expect[b]), b
+    # without the flag the history is the prior list alone at every position
+    plain = oracle.verify(target, W.DTYPE_F32, B, gamma, req, d, np.full((B, gamma, V), 1.0 / V, np.float32))
+    for b in range(B):
+        ref = []
+        for j in range(gamma + 1):
+            z = oracle.prelude_row(target[b * (gamma + 1) + j], W.DTYPE_F32, oracle.flags_of(req, b), req, b)
+            ref.append(int(np.argmax(z)))
+        n = plain["n_emit"][b]
+        for j in range(n - 1):
+            assert plain["tokens"][b, j] == d[b, j] == ref[j]
+        assert plain["tokens"][b, n - 1] == ref[n - 1]
+
+
+def test_history_rule_cases():
+    # the merge rule on its own: prior hit, ignored entry, repeats, out-of-range
+    ids, cnt = _hist_lists(np.array([5, 7, 9]), np.array([2, 0, 1]), 3, [7, 5, 5, 11, -1, 60, 11], 50)
+    assert ids == [5, 7, 9, 7, 11] and cnt == [4, 0, 1, 1, 2]
+
+
+def test_draft_history_hand_cases():
+    # worked by hand from the penalty definitions: one row repeated at every
+    # position, greedy, token 0 best
+    V, gamma = 6, 3
+    row = np.array([5.0, 4.5, 3.0, 2.0, 1.0, 0.0], np.float32)
+    target = np.tile(row, (gamma + 1, 1))
+    qp = np.full((1, gamma, V), 1.0 / V, np.float32)
+    d = np.zeros((1, gamma), np.int32)          # drafts 0, 0, 0
+
+    def run(rep, freq, pres, hist):
+        req = W.plain_requests(1, greedy=True)
+        req.use_penalties[:] = True
+        req.rep_penalty[:] = rep
+        req.freq_penalty[:] = freq
+        req.pres_penalty[:] = pres
+        req.n_prior[:] = 0
+        f = oracle.flags_of(req, 0) | (oracle.FLAG_DRAFT_HIST if hist else 0)
+        return oracle.verify(target, W.DTYPE_F32, 1, gamma, req, d, qp, flags=np.array([f], np.uint32))
+
+    # repetition 10: after one occurrence token 0 scores 0.5 < 4.5, so the
+    # second draft is rejected and token 1 is emitted
+    o = run(10.0, 0.0, 0.0, True)
+    assert o["n_emit"][0] == 2 and list(o["tokens"][0, :2]) == [0, 1]
+    # without the history every draft matches and the bonus is token 0
+    o = run(10.0, 0.0, 0.0, False)
+    assert o["n_emit"][0] == 4 and list(o["tokens"][0]) == [0, 0, 0, 0]
+    # frequency 0.3 per occurrence: 5 - 0.3 = 4.7 > 4.5 keeps token 0 after one
+    # draft; after two, 5 - 0.6 = 4.4 < 4.5 gives token 1 at position 2
+    o = run(1.0, 0.3, 0.0, True)
+    assert o["n_emit"][0] == 3 and list(o["tokens"][0, :3]) == [0, 0, 1]
+    # presence 0.1 once: 5 - 0.3 - 0.1 = 4.6 after one draft, 5 - 0.6 - 0.1 =
+    # 4.3 after two: the same outcome, the presence term not growing
+    o = run(1.0, 0.3, 0.1, True)
+    assert o["n_emit"][0] == 3 and list(o["tokens"][0, :3]) == [0, 0, 1]
+    # presence 0.2 with frequency 0.1: 4.7 after one, 4.6 after two, 4.5 after
+    # three (a tie with token 1 goes to the lower id): every draft passes
+    o = run(1.0, 0.1, 0.2, True)
+    assert o["n_emit"][0] == 4 and list(o["tokens"][0]) == [0, 0, 0, 0]
