@@ -79,7 +79,13 @@ enum {
     SS_BIAS = 1u << 4,      /* additive logit bias list */
     SS_TOPK = 1u << 5,      /* keep the top_k best candidates */
     SS_TOPP = 1u << 6,      /* nucleus truncation at top_p */
-    SS_MINP = 1u << 7       /* keep p_i >= min_p * p_max */
+    SS_MINP = 1u << 7,      /* keep p_i >= min_p * p_max */
+    /* verification only: target position j's penalty history (SS_REP,
+     * SS_FREQPRES) is the prior list plus the request's drafts
+     * d_0..d_{j-1}, each adding one occurrence to the first prior entry of
+     * its id with a count >= 1, else to an entry appended for it (the
+     * decoding notes' penalties act on every token generated so far) */
+    SS_DRAFT_HIST = 1u << 8
 };
 
 /* One request, 32 bytes, in device memory (so a captured graph can be

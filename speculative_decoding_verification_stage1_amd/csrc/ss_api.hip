@@ -249,6 +249,7 @@ int ss_verify_step_var(const void* target_logits, int dtype, int B, int gamma, i
     s1.listed = W.listed;
     s1.listed_rows = rows;
     s1.cu_num_draft = cu_num_draft;
+    s1.draft_ids = draft_ids;
     s1.rng = rng;
     s1.rng_snap = W.rng_snap;
     s1.rng_advance = rng_advance;

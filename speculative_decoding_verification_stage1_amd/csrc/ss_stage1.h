@@ -46,7 +46,7 @@ constexpr int S1_WAVES = S1_THREADS / WAVE;
 constexpr int S1_CPT = 16;            // 16-byte chunks per thread
 constexpr int S1_CCAP = 128;          // flagged chunks held per wave (fast path)
 constexpr int S1_KCAP = 256;          // survivors held per wave (fast path)
-constexpr int S1_LIST_CAP = 512;      // >= 255 prior + 255 bias entries
+constexpr int S1_LIST_CAP = 528;      // >= 255 prior + 255 bias entries + SS_GAMMA_MAX drafts
 constexpr int S1_NL_FAST = 128;       // listed tokens per tile the fast path absorbs
 
 template <int DT> struct S1Traits;
@@ -81,7 +81,17 @@ struct Stage1Params {
     ss_rng* rng_snap;    // ... copied here for Stage 2 (workgroup 0)
     uint64_t rng_advance;   // ... after which rng->offset += rng_advance
     const int32_t* cu_num_draft;   // verification with per-request draft counts (or null)
+    const int32_t* draft_ids;      // verification: [requests, rows_per_req - 1] drafts (or null)
 };
+
+// Number of earlier drafts in row `row`'s penalty history: its position j
+// when the request asks for the draft history and applies penalties, else
+// 0.  Uniform per row.
+__device__ __forceinline__ int draft_hist_len(const Stage1Params& P, uint32_t flags, int row) {
+    if (!P.draft_ids || !(flags & SS_DRAFT_HIST) || !(flags & (SS_REP | SS_FREQPRES))) return 0;
+    const int b = div_uniform(row, P.rows_per_req);
+    return row - b * P.rows_per_req;
+}
 
 // Whether row `row` takes part: always, except in verification with
 // per-request draft counts, where request b's rows past its bonus position
@@ -235,6 +245,7 @@ struct S1In {
     uint32_t raw[S1_CPT * 4];   // dword q: dword (q & 3) of this thread's chunk (q >> 2)
     uint32_t gw[S1_CPT * S1Traits<DT>::EPC / 32];   // the tile's bitmask words tid + 256k
     int l_pid, l_pct, l_bid;    // lead wave: first 64 entries of the request's lists
+    int l_did;                  // lead wave: draft `lane` of the request (verification), or -1
     uint32_t rq_flags, rq_lists; // the request's flags and its n_prior | n_bias << 8
 };
 
@@ -298,6 +309,11 @@ __device__ __forceinline__ void tile_fetch(const Stage1Params& P, int row, int t
         }
         if (P.aux.bias_ids && lane < P.aux.bias_stride)
             in.l_bid = gmem(P.aux.bias_ids)[(int64_t)b * P.aux.bias_stride + lane];
+    }
+    in.l_did = -1;
+    if (wave == lead && P.draft_ids) {   // drafts before this row's position (read if the flag asks)
+        const int j = row - b * P.rows_per_req;
+        if (lane < j) in.l_did = gmem(P.draft_ids)[(int64_t)b * (P.rows_per_req - 1) + lane];
     }
     // the tile's grammar bitmask, coalesced: word base/32 + tid + 256k
     // (requested before the logits, so that it can be used while they arrive)
@@ -463,6 +479,12 @@ __device__ __forceinline__ void tile_process(const Stage1Params& P, int row, int
                     record(j < n_bias && id >= 0 && id < P.V && lc >= 0 && lc < nvalid, lc);
                 }
             }
+        }
+        // earlier drafts in the penalty history (verification)
+        const int nh = draft_hist_len(P, flags, row);
+        if (nh > 0) {
+            const int loc = in.l_did - base;
+            record(lane < nh && in.l_did >= 0 && in.l_did < P.V && loc >= 0 && loc < nvalid, loc);
         }
         if (lane == 0) {
             sh.nl = nl;

@@ -204,8 +204,8 @@ using WL64 = WList<uint64_t>;
 
 // The row's side lists, staged in LDS by the listed-token workgroup.
 struct S2Lists {
-    int32_t pid[256];
-    int32_t pct[256];
+    int32_t pid[256 + SS_GAMMA_MAX];   // prior entries, then entries for earlier drafts
+    int32_t pct[256 + SS_GAMMA_MAX];
     int32_t bid[256];
     float bval[256];
 };
@@ -329,9 +329,10 @@ template <int DT>
 __device__ __forceinline__ void listed_row_wave(const Stage1Params& P, uint64_t* out, int row, S2Lists& lists) {
     const int b = __builtin_amdgcn_readfirstlane(div_uniform(row, P.rows_per_req));
     const RowParams rp = row_params(P, b);
-    const int np = rp.valid ? rp.n_prior : 0;
+    int np = rp.valid ? rp.n_prior : 0;
     const int nb = rp.valid ? rp.n_bias : 0;
-    if (np + nb == 0) return;   // wave-uniform; Stage 2 skips rows without lists
+    const int nh = rp.valid ? draft_hist_len(P, rp.flags, row) : 0;
+    if (np + nb + nh == 0) return;   // wave-uniform; Stage 2 skips rows without lists
     const auto pid = gmem(P.aux.prior_ids + (int64_t)b * P.aux.prior_stride);
     const auto pct = gmem(P.aux.prior_cnt + (int64_t)b * P.aux.prior_stride);
     const auto bid = gmem(P.aux.bias_ids + (int64_t)b * P.aux.bias_stride);
@@ -347,6 +348,33 @@ __device__ __forceinline__ void listed_row_wave(const Stage1Params& P, uint64_t*
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
+    if (nh > 0) {
+        // the drafts before this position join the history in order: one
+        // more occurrence on the first live entry of the id, else a new
+        // entry for it
+        const int dl = lane < nh ? gmem(P.draft_ids)[(int64_t)b * (P.rows_per_req - 1) + lane] : -1;
+        for (int i = 0; i < nh; ++i) {   // uniform
+            const int dv = __builtin_amdgcn_readlane(dl, i);
+            if (dv < 0 || dv >= P.V) continue;
+            int hit = -1;
+            for (int k0 = 0; k0 < np && hit < 0; k0 += WAVE) {
+                const int k = k0 + lane;
+                const uint64_t m = __ballot(k < np && lists.pid[k] == dv && lists.pct[k] >= 1);
+                if (m) hit = k0 + __builtin_ctzll(m);
+            }
+            if (lane == 0) {
+                if (hit >= 0) {
+                    lists.pct[hit] += 1;
+                } else {
+                    lists.pid[np] = dv;
+                    lists.pct[np] = 1;
+                }
+            }
+            if (hit < 0) ++np;
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
     const WL64 l = listed_list<DT>(P, rp, row, np, nb, lists);
     out[(int64_t)row * KMAX + lane] = l.lo;
     out[(int64_t)row * KMAX + lane + WAVE] = l.hi;
@@ -413,7 +441,7 @@ __device__ __forceinline__ WL64 row_merge(const Stage2Params& F, const RowParams
     const Stage1Params& P = F.s1;
     const int lane = lane_id();
     const int wave = threadIdx.x / WAVE;
-    const bool has_listed = rp.valid && rp.n_prior + rp.n_bias > 0;
+    const bool has_listed = rp.valid && rp.n_prior + rp.n_bias + draft_hist_len(P, rp.flags, row) > 0;
     const Key* sc = (const Key*)P.scratch + (int64_t)row * P.Zv * KMAX;
     const auto& pre_lo = L.pre_lo;
     const auto& pre_hi = L.pre_hi;

@@ -307,12 +307,12 @@ def test_determinism_repeated_runs():
 # verification
 # ---------------------------------------------------------------------------
 
-def run_verify(wl, seed=0, offset=0, rng_advance=0, cu_num_draft=None):
+def run_verify(wl, seed=0, offset=0, rng_advance=0, cu_num_draft=None, flags=None):
     lib = L()
     x = _dev_logits(wl.target, wl.dtype)
     rows, V = x.shape
     B, G = wl.B, wl.gamma
-    dreq = lib.DeviceRequests(wl.req)
+    dreq = lib.DeviceRequests(wl.req, flags=flags)
     if getattr(wl, "bitmask", None) is not None:
         dreq.with_bitmask(torch.from_numpy(wl.bitmask.view(np.int32)).cuda())
     rng = lib.make_rng(seed, offset)
@@ -332,11 +332,11 @@ def run_verify(wl, seed=0, offset=0, rng_advance=0, cu_num_draft=None):
                 offset_after=int(rng.cpu().view(torch.int64)[1]))
 
 
-def verify_parity(wl, seed=0, offset=0, cu_num_draft=None):
-    g = run_verify(wl, seed, offset, cu_num_draft=cu_num_draft)
+def verify_parity(wl, seed=0, offset=0, cu_num_draft=None, flags=None):
+    g = run_verify(wl, seed, offset, cu_num_draft=cu_num_draft, flags=flags)
     o = oracle.verify(wl.target, wl.dtype, wl.B, wl.gamma, wl.req, wl.draft_ids, wl.draft_probs,
                       bitmask=getattr(wl, "bitmask", None), seed=seed, offset=offset, threads=16,
-                      cu_num_draft=cu_num_draft)
+                      cu_num_draft=cu_num_draft, flags=None if flags is None else np.asarray(flags, np.uint32))
     for k in ("tokens", "n_emit", "status"):
         assert np.array_equal(g[k], o[k]), (k, np.nonzero((g[k] != o[k]).reshape(wl.B, -1).any(1))[0][:10])
     return g
@@ -378,6 +378,47 @@ def test_verify_variable_draft_counts_c3_full():
     counts = np.random.default_rng(32).integers(0, wl.gamma + 1, wl.B)
     g = verify_parity(wl, cu_num_draft=_counts_cu(counts))
     assert np.all(g["n_emit"] >= 1) and np.all(g["n_emit"] <= counts + 1)
+
+
+def test_verify_draft_history():
+    # penalties whose history includes the earlier drafts, on half the
+    # requests; prior lists that contain some of the drafts (count hits),
+    # repeated drafts, bias lists, and per-request draft counts
+    wl = W.workload_verify(B=16, gamma=4, V=20000)
+    req = wl.req
+    rng = np.random.default_rng(51)
+    P, NB = 64, 16
+    # even requests: greedy, every position the same row and every draft its
+    # best token, so that the history decides where a request stops
+    t = wl.target.reshape(16, 5, -1)
+    for b in range(0, 16, 2):
+        t[b, 1:] = t[b, 0]
+        wl.draft_ids[b, :] = int(np.argmax(W.bf16_bits_to_f32(t[b, 0])))
+    req.greedy[:] = False
+    req.greedy[::2] = True
+    req.use_penalties[:] = True
+    req.rep_penalty[:] = 1.3
+    req.freq_penalty[:] = 0.3
+    req.pres_penalty[:] = 0.2
+    req.prior_ids = rng.integers(0, 20000, (16, P)).astype(np.int32)
+    req.prior_ids[1::2, :2] = wl.draft_ids[1::2, :2]     # drafts already in the history
+    req.prior_cnt = rng.integers(1, 6, (16, P)).astype(np.int32)
+    req.prior_cnt[3, 0] = 0                               # an ignored entry hit by a draft
+    req.n_prior = np.full(16, P, np.int32)
+    req.n_prior[5] = 0                                    # history made of drafts only
+    req.use_bias[::3] = True
+    req.bias_ids = rng.integers(0, 20000, (16, NB)).astype(np.int32)
+    req.bias_val = rng.uniform(-2, 2, (16, NB)).astype(np.float32)
+    req.n_bias = np.full(16, NB, np.int32)
+    wl.draft_ids[7, 2] = wl.draft_ids[7, 0]               # a repeated draft
+    import oracle as O
+    flags = [O.flags_of(req, b) | (O.FLAG_DRAFT_HIST if b % 2 == 0 or b == 5 else 0) for b in range(16)]
+    g = verify_parity(wl, seed=4, offset=2, flags=flags)
+    plain = oracle.verify(wl.target, wl.dtype, 16, 4, req, wl.draft_ids, wl.draft_probs, seed=4, offset=2,
+                          flags=np.array([O.flags_of(req, b) for b in range(16)], np.uint32))
+    assert not np.array_equal(g["n_emit"], plain["n_emit"])   # the history changes where requests stop
+    counts = rng.integers(0, 5, 16)
+    verify_parity(wl, seed=4, offset=2, flags=flags, cu_num_draft=_counts_cu(counts))
 
 
 def test_verify_accept_all_and_mixed_settings():
