@@ -423,7 +423,8 @@ def _events_us(fn, n, stream=None):
 
 def extra_measurements(args, dev, L, W, stream):
     """The other workloads' figures: c0 latency, c1 throughput (cold: 34
-    rotating copies > 512 MB), c4 two-stage vs single-pass top-k per regime
+    rotating copies > 512 MB), c4 two-stage (threshold and radix-bitonic tile
+    selects) vs single-pass top-k per regime
     (torch.topk as context), and a plain device copy as the bandwidth
     reference."""
     import torch
@@ -490,8 +491,14 @@ def extra_measurements(args, dev, L, W, stream):
         L.ss_topk_single_pass(xk[0], tw.k, ids1)
         one = _events_us(lambda i: L.ss_topk_single_pass(xk[i % 2], tw.k, ids1), 3)
         same = bool(torch.equal(ids, ids1))
+        idsr = torch.zeros_like(ids)
+        L.ss_topk_step_radix(xk[0], tw.k, idsr, ws=wsk)
+        rad = _events_us(lambda i: L.ss_topk_step_radix(xk[i % 2], tw.k, idsr, ws=wsk), 10)
+        same = same and bool(torch.equal(ids, idsr))
         tt = _events_us(lambda i: torch.topk(xk[i % 2], tw.k, dim=1), 3)
         c4[regime] = {"two_stage_us": round(two, 1), "two_stage_GBps": round(nbytes / (two * 1e-6) / 1e9, 1),
+                      "radix_bitonic_us": round(rad, 1),
+                      "radix_bitonic_GBps": round(nbytes / (rad * 1e-6) / 1e9, 1),
                       "single_pass_us": round(one, 1),
                       "single_pass_GBps": round(nbytes / (one * 1e-6) / 1e9, 1),
                       "ids_equal": same, "torch_topk_us": round(tt, 1)}

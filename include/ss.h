@@ -243,6 +243,16 @@ int ss_verify_step_var(const void* target_logits, int dtype, int B, int gamma, i
 int ss_topk_step(const void* logits, int dtype, int B, int V, int64_t ld, int k,
                  int32_t* out_ids, float* out_vals, void* ws, size_t ws_bytes, void* stream);
 
+/* The same result as ss_topk_step (same arguments, workspace and errors),
+ * with the tile stage selecting by the adaptive radix-bitonic strategy of
+ * the SonicSampler paper (Fig. 1, right panel): a 6-bit screen of the
+ * 16-bit order key, then either the bitonic select of the survivors at once
+ * or a radix pass over the next 10 bits first (more than 256 elements tied
+ * at 16-bit precision take the threshold path, so the result is exact for
+ * every input).  For comparison with ss_topk_step's threshold select. */
+int ss_topk_step_radix(const void* logits, int dtype, int B, int V, int64_t ld, int k,
+                       int32_t* out_ids, float* out_vals, void* ws, size_t ws_bytes, void* stream);
+
 /* The same result from a single-program-per-row streaming kernel (one
  * workgroup walks the whole vocabulary; the design the two-stage method
  * replaces, SonicSampler section 3.2).  Needs no workspace. */

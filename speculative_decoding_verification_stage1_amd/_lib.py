@@ -80,6 +80,8 @@ def _load():
     L.ss_verify_step_var.restype = i32
     L.ss_topk_step.argtypes = [P, i32, i32, i32, i64, i32, P, P, P, sz, P]
     L.ss_topk_step.restype = i32
+    L.ss_topk_step_radix.argtypes = [P, i32, i32, i32, i64, i32, P, P, P, sz, P]
+    L.ss_topk_step_radix.restype = i32
     L.ss_topk_single_pass.argtypes = [P, i32, i32, i32, i64, i32, P, P, P]
     L.ss_topk_single_pass.restype = i32
     L.ss_tile_topk.argtypes = [P, i32, i32, i32, i64, i32, P, P, P, P, sz, P]
@@ -94,7 +96,8 @@ def _load():
 lib = _load()
 
 EXPORTS = ["ss_workspace_bytes", "ss_tile_size", "ss_sample_step", "ss_verify_step", "ss_verify_step_var",
-           "ss_topk_step", "ss_topk_single_pass", "ss_tile_topk", "ss_rng_advance", "ss_status_str"]
+           "ss_topk_step", "ss_topk_step_radix", "ss_topk_single_pass", "ss_tile_topk", "ss_rng_advance",
+           "ss_status_str"]
 
 
 class SsError(RuntimeError):
@@ -250,6 +253,13 @@ def ss_topk_step(logits, k: int, out_ids, out_vals=None, ws=None, stream=None) -
     B, V = logits.shape
     rc = lib.ss_topk_step(ptr(logits), dtype_code(logits), B, V, logits.stride(0), k, ptr(out_ids),
                           ptr(out_vals), ptr(ws), 0 if ws is None else ws.numel(), stream_handle(stream))
+    return _check(rc)
+
+
+def ss_topk_step_radix(logits, k: int, out_ids, out_vals=None, ws=None, stream=None) -> int:
+    B, V = logits.shape
+    rc = lib.ss_topk_step_radix(ptr(logits), dtype_code(logits), B, V, logits.stride(0), k, ptr(out_ids),
+                                ptr(out_vals), ptr(ws), 0 if ws is None else ws.numel(), stream_handle(stream))
     return _check(rc)
 
 

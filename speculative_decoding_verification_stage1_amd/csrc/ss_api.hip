@@ -2,6 +2,7 @@
 // the arguments, carves the caller's workspace and queues fixed-grid
 // kernels on the caller's stream; it never allocates or synchronises.
 #include "ss_kernels.h"
+#include "ss_radix.h"
 
 using namespace ssd;
 
@@ -279,6 +280,28 @@ int ss_topk_step(const void* logits, int dtype, int B, int V, int64_t ld, int k,
     const WsLayout W = ws_layout(ws, B, V, dtype);
     Stage1Params s1 = make_s1(logits, dtype, B, V, ld, 1, nullptr, nullptr, W.scratch, nullptr);
     launch_stage1(dtype, s1, s);
+    Stage2Params f = make_s2(s1, nullptr, MODE_TOPK, W);
+    f.topk_k = k;
+    f.topk_ids = out_ids;
+    f.topk_vals = out_vals;
+    launch_stage2<MODE_TOPK>(dtype, f, s);
+    return launched();
+}
+
+int ss_topk_step_radix(const void* logits, int dtype, int B, int V, int64_t ld, int k, int32_t* out_ids,
+                       float* out_vals, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_logits(logits, dtype, B, V, ld);
+    if (rc) return rc;
+    if (k < 1 || k > KMAX) return SS_ERR_UNSUPPORTED;
+    if (B == 0) return SS_OK;
+    if (!out_ids) return SS_ERR_INVALID_ARG;
+    if ((rc = check_ws(ws, ws_bytes, ss_workspace_bytes(B, V, dtype)))) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    const WsLayout W = ws_layout(ws, B, V, dtype);
+    Stage1Params s1 = make_s1(logits, dtype, B, V, ld, 1, nullptr, nullptr, W.scratch, nullptr);
+    const dim3 grid((unsigned)(B * s1.Zv)), block(S1_THREADS);
+    if (dtype == SS_BF16) hipLaunchKernelGGL(stage1_radix_kernel<SS_BF16>, grid, block, 0, s, s1);
+    else hipLaunchKernelGGL(stage1_radix_kernel<SS_F32>, grid, block, 0, s, s1);
     Stage2Params f = make_s2(s1, nullptr, MODE_TOPK, W);
     f.topk_k = k;
     f.topk_ids = out_ids;

@@ -497,6 +497,117 @@ def test_topk_small_k_and_bf16(k):
     assert np.array_equal(ids.cpu().numpy(), ref_ids)
 
 
+def _radix_vs_oracle(x_np, dtype, k, pad=0, tag=""):
+    """ss_topk_step_radix on rows `pad` elements wider than V (the columns
+    past V hold values above every logit, which must not be read) against
+    the oracle's top-k."""
+    lib = L()
+    B, V = x_np.shape
+    ref_ids, ref_vals = oracle.topk(x_np, dtype, k, threads=16)
+    if pad:
+        wide = np.zeros((B, V + pad), dtype=x_np.dtype)
+        wide[:, :V] = x_np
+        wide[:, V:] = W.to_bf16_bits(np.full((B, pad), 1e4, np.float32)) if dtype == W.DTYPE_BF16 else 1e4
+        x = _dev_logits(wide, dtype)[:, :V]
+    else:
+        x = _dev_logits(x_np, dtype)
+    ids = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
+    vals = torch.zeros((B, k), dtype=torch.float32, device="cuda")
+    lib.ss_topk_step_radix(x, k, ids, vals, lib.workspace(B, V, dtype))
+    torch.cuda.synchronize()
+    gi, gv = ids.cpu().numpy(), vals.cpu().numpy()
+    for r in range(B):
+        assert np.array_equal(gi[r], ref_ids[r]), f"{tag} row {r} ids"
+        assert np.array_equal(gv[r], ref_vals[r]), f"{tag} row {r} vals"
+
+
+@pytest.mark.parametrize("regime", ["peaked", "flat"])
+def test_topk_radix_c4_rows(regime):
+    wl = W.workload_c4(regime, rows=24)
+    _radix_vs_oracle(wl.logits, wl.dtype, 128, tag=regime)
+
+
+@pytest.mark.parametrize("k", [1, 7, 128])
+@pytest.mark.parametrize("dtype", [W.DTYPE_BF16, W.DTYPE_F32])
+def test_topk_radix_small_k_ragged(k, dtype):
+    rng = np.random.default_rng(100 + k)
+    x = (rng.standard_normal((5, 30001)) * 3).astype(np.float32)
+    _radix_vs_oracle(W.to_bf16_bits(x) if dtype == W.DTYPE_BF16 else x, dtype, k, tag=f"k{k}")
+
+
+@pytest.mark.parametrize("dtype,pad", [(W.DTYPE_BF16, 8), (W.DTYPE_BF16, 3), (W.DTYPE_F32, 4), (W.DTYPE_F32, 1)])
+def test_topk_radix_strided_rows(dtype, pad):
+    rng = np.random.default_rng(pad)
+    x = (rng.standard_normal((4, 40000)) * 2).astype(np.float32)
+    _radix_vs_oracle(W.to_bf16_bits(x) if dtype == W.DTYPE_BF16 else x, dtype, 128, pad=pad,
+                     tag=f"pad{pad}")
+
+
+def test_topk_radix_ties():
+    # ties at 16-bit precision: fewer survivors than the bitonic finish takes
+    # (rows 1, 4) and more (rows 0, 2, 3, 5: the exact threshold path)
+    V = 40000
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal((6, V))).astype(np.float32)
+    x[0, :] = 1.0                                  # all equal
+    x[1, rng.choice(V, 200, replace=False)] = 6.0  # 200 equal maxima
+    x[2, rng.choice(V, 300, replace=False)] = 6.0  # 300 equal maxima
+    x[3, ::7] = 5.0
+    # fp32 values that agree in their upper 16 bits (one bf16 value) and
+    # differ below: 200 of them, then 3000
+    base = np.float32(6.0).view(np.uint32)
+    i4 = rng.choice(V, 200, replace=False)
+    x[4, i4] = (base + rng.integers(0, 1 << 16, 200).astype(np.uint32)).view(np.float32)
+    i5 = rng.choice(V, 3000, replace=False)
+    x[5, i5] = (base + rng.integers(0, 1 << 16, 3000).astype(np.uint32)).view(np.float32)
+    _radix_vs_oracle(x, W.DTYPE_F32, 128, tag="ties-f32")
+    _radix_vs_oracle(W.to_bf16_bits(x), W.DTYPE_BF16, 128, tag="ties-bf16")
+    q = W.to_bf16_bits(np.round(rng.standard_normal((3, V)) * 4) / 4)   # few distinct values
+    _radix_vs_oracle(q, W.DTYPE_BF16, 128, tag="quantised")
+
+
+def test_topk_radix_special_values_and_short_rows():
+    V = 20000
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal((6, V)) * 2).astype(np.float32)
+    x[0, 5] = np.nan
+    x[0, 17000] = np.inf
+    x[1, :] = -0.0
+    x[1, 100] = 0.0
+    x[2, ::3] = np.nan
+    x[3, :] = -np.inf
+    x[3, 12345] = -1e30
+    x[4, 1:] = np.nan
+    x[5, 7] = -np.nan
+    x[5, 9] = np.float32(3.0e38)
+    for dtype in (W.DTYPE_F32, W.DTYPE_BF16):
+        xd = x if dtype == W.DTYPE_F32 else W.to_bf16_bits(x)
+        _radix_vs_oracle(xd, dtype, 128, tag=f"special dt{dtype}")
+    # rows shorter than k, and a row of one element
+    for V in (1, 100, 127, 129, 300):
+        y = (rng.standard_normal((3, V)) * 2).astype(np.float32)
+        _radix_vs_oracle(y, W.DTYPE_F32, 128, tag=f"V{V}")
+        _radix_vs_oracle(W.to_bf16_bits(y), W.DTYPE_BF16, 128, tag=f"V{V} bf16")
+
+
+def test_topk_radix_c4_full_sampled():
+    # the full stress shape in the launch the benchmark times; the oracle
+    # ranks a sample of the rows
+    lib = L()
+    for regime in ("peaked", "flat"):
+        wl = W.workload_c4(regime)
+        x = _dev_logits(wl.logits, wl.dtype)
+        B, V = x.shape
+        ids = torch.full((B, 128), -7, dtype=torch.int32, device="cuda")
+        vals = torch.zeros((B, 128), dtype=torch.float32, device="cuda")
+        lib.ss_topk_step_radix(x, 128, ids, vals, lib.workspace(B, V, wl.dtype))
+        torch.cuda.synchronize()
+        rows = np.random.default_rng(11).choice(B, 24, replace=False)
+        ref_ids, ref_vals = oracle.topk(wl.logits[rows], wl.dtype, 128, threads=16)
+        assert np.array_equal(ids.cpu().numpy()[rows], ref_ids), regime
+        assert np.array_equal(vals.cpu().numpy()[rows], ref_vals), regime
+
+
 # ---------------------------------------------------------------------------
 # graph capture: replays with a device-side offset equal eager calls
 # ---------------------------------------------------------------------------

@@ -124,6 +124,11 @@ def test_argument_errors_return_before_launch(L):
     # top-k: k range
     assert lib.ss_topk_step(fake, 0, 2, 100, 100, 0, fake, P, fake, 10**9, P) == L.SS_ERR_UNSUPPORTED
     assert lib.ss_topk_step(fake, 0, 2, 100, 100, 129, fake, P, fake, 10**9, P) == L.SS_ERR_UNSUPPORTED
+    assert lib.ss_topk_step_radix(fake, 0, 2, 100, 100, 0, fake, P, fake, 10**9, P) == L.SS_ERR_UNSUPPORTED
+    assert lib.ss_topk_step_radix(fake, 0, 2, 100, 100, 129, fake, P, fake, 10**9, P) == L.SS_ERR_UNSUPPORTED
+    assert lib.ss_topk_step_radix(fake, 0, 2, 100, 100, 8, P, P, fake, 10**9, P) == L.SS_ERR_INVALID_ARG
+    assert lib.ss_topk_step_radix(fake, 0, 2, 100, 100, 8, fake, P, fake, 16, P) == L.SS_ERR_WORKSPACE
+    assert lib.ss_topk_step_radix(fake, 0, 0, 100, 100, 8, P, P, P, 0, P) == L.SS_OK
     assert lib.ss_topk_single_pass(fake, 0, 2, 100, 100, 129, fake, P, P) == L.SS_ERR_UNSUPPORTED
     assert lib.ss_tile_topk(fake, 0, 2, 100, 100, 0, P, None, P, fake, 10**9, P) == L.SS_ERR_INVALID_ARG
     assert lib.ss_rng_advance(P, 1, P) == L.SS_ERR_INVALID_ARG
