@@ -82,6 +82,9 @@ def lib():
         L.oracle_verify.argtypes = [P, i32, i32, i32, i32, i64, P, P, P, i32, P, P, i32, P, i64,
                                     P, P, P, u64, u64, P, P, P, i32]
         L.oracle_verify.restype = i32
+        L.oracle_verify_dense.argtypes = [P, i32, i32, i32, i32, i64, P, P, P, P, u64, u64,
+                                          ctypes.c_double, P, P, P, P, i32]
+        L.oracle_verify_dense.restype = i32
         L.oracle_topk.argtypes = [P, i32, i32, i32, i64, i32, P, P, i32]
         L.oracle_topk.restype = i32
         L.oracle_tile_topk.argtypes = [P, i32, i32, i32, i64, i32, i32, P, P, P, i32, P, P, i32,
@@ -254,6 +257,31 @@ def verify(target, dtype: int, B: int, gamma: int, req, draft_ids, draft_probs, 
         _p(out["tokens"]), _p(out["n_emit"]), _p(out["status"]), threads)
     if rc != 0:
         raise ValueError("oracle_verify rejected its arguments")
+    return out
+
+
+def verify_dense(target, dtype: int, B: int, gamma: int, req, draft_ids, draft_probs=None, seed: int = 0,
+                 offset: int = 0, threads: int = 1, flags=None, packed=None, cu_num_draft=None,
+                 zslack: float = 1e-5):
+    """Dense verification (full-vocabulary p; draft_probs None: no draft
+    probabilities).  Returns tokens [B, gamma+1] (-1 padded), n_emit [B],
+    status [B] and fragile [B] (1 where the tokens depend on Z to within a
+    relative `zslack`)."""
+    x = np.ascontiguousarray(target)
+    rows, V = x.shape
+    assert rows == B * (gamma + 1)
+    r = pack_requests(req, flags) if packed is None else packed
+    d = np.ascontiguousarray(draft_ids, np.int32)
+    q = None if draft_probs is None else np.ascontiguousarray(draft_probs, np.float32)
+    cu = None if cu_num_draft is None else np.ascontiguousarray(cu_num_draft, np.int32)
+    assert cu is None or cu.shape == (B,)
+    out = dict(tokens=np.zeros((B, gamma + 1), np.int32), n_emit=np.zeros(B, np.int32),
+               status=np.zeros(B, np.int32), fragile=np.zeros(B, np.int32))
+    rc = lib().oracle_verify_dense(
+        _p(x), dtype, B, gamma, V, V, _p(r), _p(d), _p(q), _p(cu), seed, offset, zslack,
+        _p(out["tokens"]), _p(out["n_emit"]), _p(out["status"]), _p(out["fragile"]), threads)
+    if rc != 0:
+        raise ValueError("oracle_verify_dense rejected its arguments")
     return out
 
 

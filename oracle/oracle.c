@@ -49,6 +49,7 @@
 #define OF_TOPP     (1u << 6)
 #define OF_MINP     (1u << 7)
 #define OF_DRAFT_HIST (1u << 8)
+#define SS_ORACLE_GMAX 16   /* largest number of drafts per request */
 
 #define OK_MAX 128           /* bounded candidate set, [SS] section 3.3 */
 
@@ -712,6 +713,198 @@ int oracle_verify(const void* target, int dtype, int B, int gamma, int V, int64_
         J->out_tokens = out_tokens; J->n_emit = n_emit; J->status = status;
     }
     if (B > 0) run_rows(verify_worker, jobs, sizeof(verify_job), B, threads, verify_set_range);
+    free(jobs);
+    return 0;
+}
+
+/* ======================================================================
+ * Dense verification [DN "Rejection Sampler": the notes' rejection and
+ * recovery kernels take full-vocabulary target probabilities (and draft
+ * probabilities, or none: then the draft probability counts as 1 and the
+ * recovered token is drawn from the target distribution with the draft
+ * token left out); the recovered token is the argmax of the residual over
+ * an exponential race, i.e. a Gumbel-max on its logarithm].
+ * p_j is the softmax of v = z/T over the whole vocabulary, z the canonical
+ * logits: no truncation (top-k, top-p and min-p settings do not apply) and
+ * no other processing, so a request that asks for a grammar mask, penalties
+ * or a bias list is invalid here.  Greedy: SS_GREEDY or T <= 0; otherwise
+ * T must be finite.  v_i = z_i * (1/T) clamped to the finite range (-inf
+ * stays -inf), m = max_i v_i, e_i = exp(v_i - m) with the written exp,
+ * Z = sum_i e_i (double, rounded once to float), p_i = e_i / Z.
+ *   accept d_j:   q_j(d_j) > 0 and u_j q_j(d_j) <= p_j(d_j)
+ *   recovered:    argmax over r_i = p_i - q_j(i) > 0 (no draft
+ *                 probabilities: r_i = p_i, with r = 0 at d_j) of
+ *                 ln r_i + g(i, b, (2<<24)|j); no such i: argmax of
+ *                 v_i + g(i, b, (2<<24)|j)
+ *   bonus:        argmax of v_i + g(i, b, n_b) over the whole vocabulary
+ *   greedy rows:  accept iff d_j is the best id; emit the best id
+ *   a row whose every value is -inf: status ALL_MASKED, stop.
+ * Noise counters as in the bounded verification.  `fragile[b]` is set when
+ * the emitted tokens change if Z is taken as Z (1 - zslack) or Z (1 + zslack)
+ * instead: a sum of V terms in another order may differ from this one by
+ * about that much, and only such requests may legitimately differ.
+ * ====================================================================== */
+typedef struct {
+    const void* target; int dtype; int B; int gamma; int V; int64_t ld;
+    const oreq* req;
+    const int32_t* draft_ids; const float* draft_probs; const int32_t* cu_num_draft;
+    uint64_t seed, offset;
+    double zslack;
+    int32_t* out_tokens; int32_t* n_emit; int32_t* status; int32_t* fragile;
+    int row_begin, row_end;
+} dense_job;
+
+static void dense_set_range(void* j, int lo, int hi)
+{
+    ((dense_job*)j)->row_begin = lo;
+    ((dense_job*)j)->row_end = hi;
+}
+
+/* One request's tokens with Z scaled by zscale; returns the status. */
+static int dense_request(const dense_job* J, int b, int greedy, int Gb, double zscale,
+                         float* z, float* v, float* e, int32_t* out, int* emitted)
+{
+    const int G = J->gamma, V = J->V;
+    const oreq* r = &J->req[b];
+    *emitted = 0;
+    for (int j = 0; j <= Gb; ++j) {
+        const int64_t row = (int64_t)b * (G + 1) + j;
+        const void* rp = row_ptr(J->target, J->dtype, J->ld, row);
+        for (int i = 0; i < V; ++i) z[i] = canon(widen(rp, J->dtype, i));
+        const int32_t d = j < Gb ? J->draft_ids[(int64_t)b * G + j] : -1;
+        if (greedy) {
+            int best = 0;
+            for (int i = 1; i < V; ++i)
+                if (z[i] > z[best]) best = i;
+            if (z[best] == -INFINITY) return OST_ALL_MASKED;
+            out[(*emitted)++] = (j == Gb || d != best) ? best : d;
+            if (j == Gb || d != best) return OST_OK;
+            continue;
+        }
+        const float invT = 1.0f / r->temperature;
+        float m = -INFINITY;
+        for (int i = 0; i < V; ++i) {
+            float vi;
+            if (z[i] == -INFINITY) vi = -INFINITY;
+            else {
+                vi = z[i] * invT;
+                if (vi > FLT_MAX) vi = FLT_MAX;
+                if (vi < -FLT_MAX) vi = -FLT_MAX;
+            }
+            v[i] = vi;
+            if (vi > m) m = vi;
+        }
+        if (m == -INFINITY) return OST_ALL_MASKED;
+        double Zd = 0.0;
+        for (int i = 0; i < V; ++i) {
+            e[i] = oracle_exp_spec(v[i] - m);
+            Zd += (double)e[i];
+        }
+        const float Z = (float)(Zd * zscale);
+        if (j == Gb) {   /* bonus: the untruncated target distribution */
+            int32_t best = -1;
+            float bs = 0.0f;
+            for (int i = 0; i < V; ++i) {
+                float s = v[i] + oracle_gumbel(J->seed, J->offset, (uint32_t)i, (uint32_t)b, (uint32_t)Gb);
+                if (best < 0 || s > bs) { best = i; bs = s; }
+            }
+            out[(*emitted)++] = best;
+            return OST_OK;
+        }
+        const float* q = J->draft_probs ? J->draft_probs + ((int64_t)b * G + j) * V : NULL;
+        const int din = d >= 0 && d < V;
+        const float q_d = din ? (q ? q[d] : 1.0f) : 0.0f;
+        const float p_d = din ? e[d] / Z : 0.0f;
+        const float u = oracle_uniform(oracle_philox_word(J->seed, J->offset, 0u, (uint32_t)b,
+                                                          (1u << 24) | (uint32_t)j));
+        if (q_d > 0.0f && u * q_d <= p_d) { out[(*emitted)++] = d; continue; }
+        const uint32_t c2 = (2u << 24) | (uint32_t)j;
+        int32_t best = -1;
+        float bs = 0.0f;
+        for (int i = 0; i < V; ++i) {
+            const float pi = e[i] / Z;
+            const float rho = q ? pi - q[i] : (i == d ? 0.0f : pi);
+            if (!(rho > 0.0f)) continue;
+            const float s = oracle_log_spec(rho) + oracle_gumbel(J->seed, J->offset, (uint32_t)i, (uint32_t)b, c2);
+            if (best < 0 || s > bs) { best = i; bs = s; }
+        }
+        if (best < 0) {   /* p <= q everywhere: draw from p */
+            for (int i = 0; i < V; ++i) {
+                const float s = v[i] + oracle_gumbel(J->seed, J->offset, (uint32_t)i, (uint32_t)b, c2);
+                if (best < 0 || s > bs) { best = i; bs = s; }
+            }
+        }
+        out[(*emitted)++] = best;
+        return OST_OK;
+    }
+    return OST_OK;
+}
+
+static void* dense_worker(void* arg)
+{
+    const dense_job* J = (const dense_job*)arg;
+    const int G = J->gamma, V = J->V;
+    float* z = (float*)malloc(sizeof(float) * (size_t)V);
+    float* v = (float*)malloc(sizeof(float) * (size_t)V);
+    float* e = (float*)malloc(sizeof(float) * (size_t)V);
+    int32_t alt[2][SS_ORACLE_GMAX + 1];
+    for (int b = J->row_begin; b < J->row_end; ++b) {
+        const oreq* r = &J->req[b];
+        int32_t* out = J->out_tokens + (int64_t)b * (G + 1);
+        for (int j = 0; j <= G; ++j) out[j] = -1;
+        int st = OST_OK, emitted = 0, fragile = 0;
+        int greedy = (r->flags & OF_GREEDY) != 0;
+        if (r->flags & (OF_GRAMMAR | OF_REP | OF_FREQPRES | OF_BIAS | OF_DRAFT_HIST)) st = OST_INVALID;
+        if (!greedy) {
+            if (isnan(r->temperature)) st = OST_INVALID;
+            else if (r->temperature <= 0.0f) greedy = 1;
+            else if (!finite_f(r->temperature)) st = OST_INVALID;
+        }
+        int Gb = G;
+        if (J->cu_num_draft) {
+            const int64_t hi = J->cu_num_draft[b];
+            const int64_t lo = b > 0 ? J->cu_num_draft[b - 1] : 0;
+            if (hi - lo < 0 || hi - lo > G) st = OST_INVALID;
+            else Gb = (int)(hi - lo);
+        }
+        if (st != OST_INVALID) {
+            st = dense_request(J, b, greedy, Gb, 1.0, z, v, e, out, &emitted);
+            if (!greedy && J->zslack > 0.0) {
+                for (int s = 0; s < 2; ++s) {
+                    int em2 = 0;
+                    for (int j = 0; j <= G; ++j) alt[s][j] = -1;
+                    int st2 = dense_request(J, b, 0, Gb, s ? 1.0 + J->zslack : 1.0 - J->zslack, z, v, e, alt[s], &em2);
+                    if (st2 != st || em2 != emitted || memcmp(alt[s], out, sizeof(int32_t) * (size_t)(G + 1)) != 0)
+                        fragile = 1;
+                }
+            }
+        }
+        if (st == OST_INVALID) { for (int j = 0; j <= G; ++j) out[j] = -1; emitted = 0; }
+        J->n_emit[b] = emitted;
+        if (J->status) J->status[b] = st;
+        if (J->fragile) J->fragile[b] = fragile;
+    }
+    free(z); free(v); free(e);
+    return NULL;
+}
+
+int oracle_verify_dense(const void* target, int dtype, int B, int gamma, int V, int64_t ld, const oreq* req,
+                        const int32_t* draft_ids, const float* draft_probs, const int32_t* cu_num_draft,
+                        uint64_t seed, uint64_t offset, double zslack,
+                        int32_t* out_tokens, int32_t* n_emit, int32_t* status, int32_t* fragile, int threads)
+{
+    if (!target || !req || !draft_ids || !out_tokens || !n_emit) return -1;
+    if (B < 0 || gamma < 1 || gamma > SS_ORACLE_GMAX || V < 1 || ld < V) return -1;
+    if (threads < 1) threads = 1;
+    dense_job* jobs = (dense_job*)calloc((size_t)threads, sizeof(dense_job));
+    for (int t = 0; t < threads; ++t) {
+        dense_job* J = &jobs[t];
+        J->target = target; J->dtype = dtype; J->B = B; J->gamma = gamma; J->V = V; J->ld = ld;
+        J->req = req; J->draft_ids = draft_ids; J->draft_probs = draft_probs; J->cu_num_draft = cu_num_draft;
+        J->seed = seed; J->offset = offset; J->zslack = zslack;
+        J->out_tokens = out_tokens; J->n_emit = n_emit; J->status = status; J->fragile = fragile;
+    }
+    if (B > 0) run_rows(dense_worker, jobs, sizeof(dense_job), B, threads, dense_set_range);
     free(jobs);
     return 0;
 }

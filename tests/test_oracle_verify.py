@@ -374,3 +374,132 @@ def test_draft_history_hand_cases():
     # three (a tie with token 1 goes to the lower id): every draft passes
     o = run(1.0, 0.1, 0.2, True)
     assert o["n_emit"][0] == 4 and list(o["tokens"][0]) == [0, 0, 0, 0]
+
+
+# ---------------------------------------------------------------------------
+# dense verification: full-vocabulary p, q read densely or absent
+# (decoding notes, "Rejection Sampler": rejection and recovery kernels over
+# whole target and draft rows; without draft probabilities q counts as 1 and
+# the recovery draws from p with the draft token left out)
+# ---------------------------------------------------------------------------
+
+def test_dense_output_follows_target_acceptance_and_residual():
+    # the emitted token ~ p whatever q is; acceptance rate sum min(p, q);
+    # rejected positions ~ norm(max(0, p - q)) -- every quantity from float64
+    # numpy on the definitions, not from the oracle
+    rng = np.random.default_rng(31)
+    V, N, gamma = 7, 60000, 1
+    z = (rng.standard_normal(V) * 1.1).astype(np.float32)
+    T = 0.8
+    q = rng.dirichlet(np.ones(V))
+    target, qp, d = _setup(N, gamma, z, q, rng)
+    req = W.plain_requests(N, temperature=T)
+    out = oracle.verify_dense(target, W.DTYPE_F32, N, gamma, req, d, qp, seed=5, offset=3, threads=8)
+    p = _p_of(z.astype(np.float64) / T)
+    first = out["tokens"][:, 0]
+    pv = stats.chisquare([(first == i).sum() for i in range(V)], p * N).pvalue
+    assert pv > 1e-3, pv
+    accepted = out["n_emit"] == gamma + 1
+    expect = np.minimum(p, q).sum()
+    se = np.sqrt(expect * (1 - expect) / N)
+    assert abs(accepted.mean() - expect) < 4 * se, (accepted.mean(), expect)
+    res = np.maximum(0.0, p - q)
+    res /= res.sum()
+    rej = first[~accepted]
+    pv = stats.chisquare([(rej == i).sum() for i in range(V)], res * len(rej) + 1e-12).pvalue
+    assert pv > 1e-3, pv
+    assert np.all(out["status"] == 0)
+
+
+def test_dense_without_draft_probabilities():
+    # q counts as 1 at the draft: accept with probability p(d); a rejection
+    # draws from p without d -- so the emitted token is still ~ p
+    rng = np.random.default_rng(32)
+    V, N, gamma = 6, 60000, 1
+    z = (rng.standard_normal(V) * 0.9).astype(np.float32)
+    target = np.tile(z, (N * (gamma + 1), 1))
+    d = rng.integers(0, V, (N, gamma)).astype(np.int32)
+    out = oracle.verify_dense(target, W.DTYPE_F32, N, gamma, W.plain_requests(N, temperature=1.0), d, None,
+                              seed=2, offset=0, threads=8)
+    p = _p_of(z)
+    first = out["tokens"][:, 0]
+    pv = stats.chisquare([(first == i).sum() for i in range(V)], p * N).pvalue
+    assert pv > 1e-3, pv
+    accepted = out["n_emit"] == gamma + 1
+    for i in range(V):   # acceptance of draft i ~ p(i)
+        sel = d[:, 0] == i
+        se = np.sqrt(p[i] * (1 - p[i]) / sel.sum())
+        assert abs(accepted[sel].mean() - p[i]) < 4.5 * se, (i, accepted[sel].mean(), p[i])
+    # a rejected draft never comes back as the recovered token
+    assert not np.any((first == d[:, 0]) & ~accepted)
+
+
+def test_dense_bonus_follows_the_bonus_row():
+    rng = np.random.default_rng(33)
+    V, N, gamma = 5, 50000, 2
+    zs = [(rng.standard_normal(V)).astype(np.float32) for _ in range(gamma + 1)]
+    target = np.stack([np.stack(zs)] * N).reshape(N * (gamma + 1), V)
+    d = rng.integers(0, V, (N, gamma)).astype(np.int32)
+    # a tiny draft probability at every token: u q <= p always, so every
+    # draft is accepted and the bonus comes from row gamma
+    qp = np.full((N, gamma, V), 1e-30, np.float32)
+    out = oracle.verify_dense(target, W.DTYPE_F32, N, gamma, W.plain_requests(N, temperature=1.3), d, qp,
+                              seed=7, offset=11, threads=8)
+    assert np.all(out["n_emit"] == gamma + 1)
+    assert np.array_equal(out["tokens"][:, :gamma], d)
+    p = _p_of(zs[gamma].astype(np.float64) / 1.3)
+    bonus = out["tokens"][:, gamma]
+    pv = stats.chisquare([(bonus == i).sum() for i in range(V)], p * N).pvalue
+    assert pv > 1e-3, pv
+
+
+def test_dense_greedy_masks_counts_and_invalid_requests():
+    V, gamma = 9, 3
+    z = np.array([0.5, 2.0, -1.0, 2.0, 1.0, -np.inf, 0.0, 1.5, np.nan], np.float32)   # argmax: id 1 (tie with 3)
+    B = 6
+    target = np.tile(z, (B * (gamma + 1), 1))
+    target[5 * (gamma + 1) + 1, :] = -np.inf           # request 5, position 1: every value -inf
+    d = np.array([[1, 1, 3], [1, 3, 1], [0, 1, 1], [1, 1, 1], [1, 1, 1], [1, 1, 1]], np.int32)
+    req = W.plain_requests(B, temperature=0.0)          # T <= 0: greedy
+    req.temperature[4] = np.nan                          # invalid
+    cu = np.array([3, 5, 6, 6, 9, 12], np.int32)        # counts 3, 2, 1, 0, 3, 3
+    out = oracle.verify_dense(target, W.DTYPE_F32, B, gamma, req, d, None, cu_num_draft=cu)
+    t, n, st = out["tokens"], out["n_emit"], out["status"]
+    assert list(t[0]) == [1, 1, 1, -1] and n[0] == 3      # third draft 3 != 1: emit 1
+    assert list(t[1]) == [1, 1, -1, -1] and n[1] == 2     # second draft rejected
+    assert list(t[2]) == [1, -1, -1, -1] and n[2] == 1    # one draft (0) rejected
+    assert list(t[3]) == [1, -1, -1, -1] and n[3] == 1    # no drafts: the bonus
+    assert st[4] == 2 and n[4] == 0 and np.all(t[4] == -1)
+    assert st[5] == 1 and n[5] == 1 and t[5, 0] == 1      # masked at position 1 after one acceptance
+    # processing flags are not part of the dense variant: invalid
+    for f in (2, 4, 8, 16, 256):   # grammar, repetition, frequency/presence, bias, draft history
+        o = oracle.verify_dense(target[: gamma + 1], W.DTYPE_F32, 1, gamma, W.plain_requests(1, temperature=1.0),
+                                d[:1], None, flags=np.array([f], np.uint32))
+        assert o["status"][0] == 2 and o["n_emit"][0] == 0
+    # a draft probability of 0 at the draft token always rejects
+    N = 200
+    tz = np.tile(np.zeros(4, np.float32), (N * 2, 1))
+    qp = np.tile(np.array([0.0, 1 / 3, 1 / 3, 1 / 3], np.float32), (N, 1, 1))
+    o = oracle.verify_dense(tz, W.DTYPE_F32, N, 1, W.plain_requests(N, temperature=1.0), np.zeros((N, 1), np.int32),
+                            qp, threads=4)
+    assert np.all(o["n_emit"] == 1)
+    assert np.all(o["tokens"][:, 0] == 0)   # residual max(0, p - q) lives on id 0 alone
+
+
+def test_dense_equals_bounded_when_nothing_is_truncated():
+    # V <= 128 and no truncation: the bounded candidate set is the whole
+    # vocabulary, so both variants follow the same definitions; they may
+    # differ only where the sum Z, taken in another order, decides
+    rng = np.random.default_rng(34)
+    B, gamma, V = 300, 4, 100
+    z = (rng.standard_normal((B * (gamma + 1), V)) * 2).astype(np.float32)
+    q = rng.dirichlet(np.ones(V), size=(B, gamma)).astype(np.float32)
+    d = np.stack([[rng.choice(V, p=q[b, j] / q[b, j].sum()) for j in range(gamma)] for b in range(B)]).astype(np.int32)
+    req = W.plain_requests(B, temperature=0.9)
+    req.greedy[::5] = True
+    dense = oracle.verify_dense(z, W.DTYPE_F32, B, gamma, req, d, q, seed=3, offset=4, threads=8)
+    bounded = oracle.verify(z, W.DTYPE_F32, B, gamma, req, d, q, seed=3, offset=4, threads=8)
+    ok = dense["fragile"] == 0
+    assert ok.sum() >= B - 3
+    assert np.array_equal(dense["tokens"][ok], bounded["tokens"][ok])
+    assert np.array_equal(dense["n_emit"][ok], bounded["n_emit"][ok])
