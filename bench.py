@@ -357,6 +357,31 @@ def main():
             "mean_emitted": round(float(vne.float().mean().item()), 3),
         }
 
+        # dense variant: whole-vocabulary p, the residual over whole q rows
+        # (q rotated too: 7 x 128 MiB), and with no draft probabilities
+        qs = [q] + [q.clone() for _ in range(tcopies - 1)]
+        dws = L.dense_workspace(vw.B, G, vw.V)
+        dense = {}
+        for tag, with_q in (("with_q", True), ("no_draft_probs", False)):
+            vgraph3 = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(vgraph3, stream=stream):
+                for i in range(tcopies):
+                    L.ss_verify_step_dense(ts[i], vw.B, G, vreq, rng, d, qs[i] if with_q else None, vout, vne,
+                                           None, dws, stream=stream, rng_advance=1)
+            torch.cuda.synchronize()
+            for i in range(3):
+                vgraph3.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(vreps):
+                vgraph3.replay()
+            torch.cuda.synchronize()
+            dense[tag] = {"us": round((time.perf_counter() - t0) / (vreps * tcopies) * 1e6, 2),
+                          "mean_emitted": round(float(vne.float().mean().item()), 3)}
+            del vgraph3
+        result["verify_dense"] = dense
+        del qs
+
     if not args.no_extra:
         result.update(extra_measurements(args, dev, L, W, stream))
 

@@ -236,6 +236,33 @@ int ss_verify_step_var(const void* target_logits, int dtype, int B, int gamma, i
                        int32_t* out_tokens, int32_t* out_n_emit, int32_t* out_status,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* Dense verification (decoding notes, "Rejection Sampler": the rejection
+ * and recovery kernels read whole target and draft probability rows).
+ * p_j is the softmax of v = z/T over the WHOLE vocabulary: z the canonical
+ * target logits, no candidate bound and no truncation (top_k, top_p, min_p
+ * do not apply); T as in ss_req (SS_GREEDY or T <= 0: greedy).  A request
+ * that asks for a grammar mask, penalties, bias or SS_DRAFT_HIST is
+ * SS_ROW_INVALID here (no logits processing in this variant).
+ *   target_logits [B*(gamma+1), ld] as in ss_verify_step.
+ *   draft_probs   [B, gamma, V] fp32 rows, or NULL: no draft probabilities
+ *                 (q counts as 1 at the draft token; a rejection draws from
+ *                 p with the draft token left out).
+ *   cu_num_draft  NULL or the inclusive cumulative draft counts, as in
+ *                 ss_verify_step_var.
+ * Draft d_j is accepted when q_j(d_j) > 0 and u_j q_j(d_j) <= p_j(d_j); at
+ * the first rejection the token is the Gumbel-max of ln max(0, p_j - q_j)
+ * over the vocabulary (p where q >= p everywhere); when every draft is
+ * accepted the bonus is the Gumbel-max of v over row n_b.  Greedy requests
+ * accept a draft equal to the row's best id.  Outputs, statuses, noise
+ * counters, rng and rng_advance as in ss_verify_step.  ws: at least
+ * ss_verify_dense_workspace_bytes(B, gamma, V) bytes, 256-byte aligned. */
+size_t ss_verify_dense_workspace_bytes(int B, int gamma, int V);
+int ss_verify_step_dense(const void* target_logits, int dtype, int B, int gamma, int V, int64_t ld,
+                         const ss_req* req, ss_rng* rng, uint64_t rng_advance,
+                         const int32_t* cu_num_draft, const int32_t* draft_ids, const float* draft_probs,
+                         int32_t* out_tokens, int32_t* out_n_emit, int32_t* out_status,
+                         void* ws, size_t ws_bytes, void* stream);
+
 /* Two-stage top-k of raw logits (no processing beyond NaN -> -inf, +inf ->
  * FLT_MAX, -0 -> +0): out_ids [B, k] in order (value descending, id
  * ascending) and out_vals [B, k] (optional) their values; positions past V

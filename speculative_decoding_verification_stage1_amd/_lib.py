@@ -78,6 +78,10 @@ def _load():
     L.ss_verify_step.restype = i32
     L.ss_verify_step_var.argtypes = [P, i32, i32, i32, i32, i64, P, P, P, u64, P, P, P, P, P, P, P, sz, P]
     L.ss_verify_step_var.restype = i32
+    L.ss_verify_dense_workspace_bytes.argtypes = [i32, i32, i32]
+    L.ss_verify_dense_workspace_bytes.restype = sz
+    L.ss_verify_step_dense.argtypes = [P, i32, i32, i32, i32, i64, P, P, u64, P, P, P, P, P, P, P, sz, P]
+    L.ss_verify_step_dense.restype = i32
     L.ss_topk_step.argtypes = [P, i32, i32, i32, i64, i32, P, P, P, sz, P]
     L.ss_topk_step.restype = i32
     L.ss_topk_step_radix.argtypes = [P, i32, i32, i32, i64, i32, P, P, P, sz, P]
@@ -96,7 +100,7 @@ def _load():
 lib = _load()
 
 EXPORTS = ["ss_workspace_bytes", "ss_tile_size", "ss_sample_step", "ss_verify_step", "ss_verify_step_var",
-           "ss_topk_step", "ss_topk_step_radix", "ss_topk_single_pass", "ss_tile_topk", "ss_rng_advance",
+           "ss_verify_dense_workspace_bytes", "ss_verify_step_dense", "ss_topk_step", "ss_topk_step_radix", "ss_topk_single_pass", "ss_tile_topk", "ss_rng_advance",
            "ss_status_str"]
 
 
@@ -246,6 +250,24 @@ def ss_verify_step_var(target, B: int, gamma: int, dreq: DeviceRequests, rng, cu
                                 ctypes.byref(dreq.aux), ptr(rng), rng_advance, ptr(cu_num_draft), ptr(draft_ids),
                                 ptr(draft_probs), ptr(out_tokens), ptr(out_n_emit), ptr(out_status), ptr(ws),
                                 0 if ws is None else ws.numel(), stream_handle(stream))
+    return _check(rc)
+
+
+def dense_workspace(B: int, gamma: int, V: int, device="cuda"):
+    """Workspace of ss_verify_step_dense (256-byte aligned torch allocation)."""
+    import torch
+    n = int(lib.ss_verify_dense_workspace_bytes(B, gamma, V))
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def ss_verify_step_dense(target, B: int, gamma: int, dreq: DeviceRequests, rng, draft_ids, draft_probs,
+                         out_tokens, out_n_emit, out_status=None, ws=None, cu_num_draft=None, stream=None,
+                         rng_advance: int = 0) -> int:
+    rows, V = target.shape
+    rc = lib.ss_verify_step_dense(ptr(target), dtype_code(target), B, gamma, V, target.stride(0), ptr(dreq.req),
+                                  ptr(rng), rng_advance, ptr(cu_num_draft), ptr(draft_ids), ptr(draft_probs),
+                                  ptr(out_tokens), ptr(out_n_emit), ptr(out_status), ptr(ws),
+                                  0 if ws is None else ws.numel(), stream_handle(stream))
     return _check(rc)
 
 

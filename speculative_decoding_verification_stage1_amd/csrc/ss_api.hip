@@ -2,6 +2,7 @@
 // the arguments, carves the caller's workspace and queues fixed-grid
 // kernels on the caller's stream; it never allocates or synchronises.
 #include "ss_kernels.h"
+#include "ss_dense.h"
 #include "ss_radix.h"
 
 using namespace ssd;
@@ -265,6 +266,96 @@ int ss_verify_step_var(const void* target_logits, int dtype, int B, int gamma, i
     f.v_status = out_status;
     launch_stage2<MODE_VERIFY>(dtype, f, s);
     hipLaunchKernelGGL(verify_kernel, dim3((unsigned)B), dim3(VF_THREADS), 0, s, f);
+    return launched();
+}
+
+namespace {
+
+int dense_tiles(int V) { return (V + DN_TILE - 1) / DN_TILE; }
+
+// dense workspace: [tile keys][tile sums][draw keys][decisions][rng copy]
+struct DenseWs {
+    uint64_t* part_k;
+    float* part_s;
+    uint64_t* draw_k;
+    DenseDec* dec;
+    ss_rng* rng_snap;
+    size_t bytes;
+};
+DenseWs dense_ws(void* ws, int B, int gamma, int V) {
+    const size_t rz = (size_t)B * (gamma + 1) * dense_tiles(V), bz = (size_t)B * dense_tiles(V);
+    DenseWs L;
+    char* p = (char*)ws;
+    size_t o = 0;
+    L.part_k = (uint64_t*)(p + o);
+    o += align256(rz * sizeof(uint64_t));
+    L.part_s = (float*)(p + o);
+    o += align256(rz * sizeof(float));
+    L.draw_k = (uint64_t*)(p + o);
+    o += align256(bz * sizeof(uint64_t));
+    L.dec = (DenseDec*)(p + o);
+    o += align256((size_t)B * sizeof(DenseDec));
+    L.rng_snap = (ss_rng*)(p + o);
+    o += RNG_SNAP_BYTES;
+    L.bytes = o;
+    return L;
+}
+
+}  // namespace
+
+size_t ss_verify_dense_workspace_bytes(int B, int gamma, int V) {
+    if (B < 0 || gamma < 1 || gamma > SS_GAMMA_MAX || V < 1 || V > SS_V_MAX) return 0;
+    return dense_ws(nullptr, B, gamma, V).bytes;
+}
+
+int ss_verify_step_dense(const void* target_logits, int dtype, int B, int gamma, int V, int64_t ld,
+                         const ss_req* req, ss_rng* rng, uint64_t rng_advance, const int32_t* cu_num_draft,
+                         const int32_t* draft_ids, const float* draft_probs, int32_t* out_tokens,
+                         int32_t* out_n_emit, int32_t* out_status, void* ws, size_t ws_bytes, void* stream) {
+    if (gamma < 1 || gamma > SS_GAMMA_MAX) return SS_ERR_UNSUPPORTED;
+    if (B < 0 || (int64_t)B * (gamma + 1) > KERNEL_ROWS_MAX) return B < 0 ? SS_ERR_INVALID_ARG : SS_ERR_UNSUPPORTED;
+    const int rows = B * (gamma + 1);
+    int rc = check_logits(target_logits, dtype, rows, V, ld);
+    if (rc) return rc;
+    if ((int64_t)rows * dense_tiles(V) > 0x7FFFFFFFLL) return SS_ERR_UNSUPPORTED;
+    if (B == 0) return SS_OK;
+    if (!req || !rng || !draft_ids || !out_tokens || !out_n_emit) return SS_ERR_INVALID_ARG;
+    if ((rc = check_ws(ws, ws_bytes, ss_verify_dense_workspace_bytes(B, gamma, V)))) return rc;
+    const DenseWs L = dense_ws(ws, B, gamma, V);
+    DenseParams D{};
+    D.target = target_logits;
+    D.dtype = dtype;
+    D.B = B;
+    D.G = gamma;
+    D.V = V;
+    D.Zt = dense_tiles(V);
+    D.ld = ld;
+    D.aligned16 = aligned16(target_logits, dtype, ld);
+    D.req = req;
+    D.rng = rng;
+    D.rng_snap = L.rng_snap;
+    D.rng_advance = rng_advance;
+    D.cu_num_draft = cu_num_draft;
+    D.draft_ids = draft_ids;
+    D.draft_probs = draft_probs;
+    D.part_k = L.part_k;
+    D.part_s = L.part_s;
+    D.draw_k = L.draw_k;
+    D.dec = L.dec;
+    D.out_tokens = out_tokens;
+    D.out_n_emit = out_n_emit;
+    D.out_status = out_status;
+    hipStream_t s = (hipStream_t)stream;
+    const dim3 blk(DN_THREADS);
+    if (dtype == SS_BF16) {
+        hipLaunchKernelGGL(dense_stats_kernel<SS_BF16>, dim3((unsigned)(rows * D.Zt)), blk, 0, s, D);
+        hipLaunchKernelGGL(dense_draw_kernel<SS_BF16>, dim3((unsigned)(B * D.Zt)), blk, 0, s, D);
+        hipLaunchKernelGGL(dense_finish_kernel<SS_BF16>, dim3((unsigned)B), dim3(WAVE), 0, s, D);
+    } else {
+        hipLaunchKernelGGL(dense_stats_kernel<SS_F32>, dim3((unsigned)(rows * D.Zt)), blk, 0, s, D);
+        hipLaunchKernelGGL(dense_draw_kernel<SS_F32>, dim3((unsigned)(B * D.Zt)), blk, 0, s, D);
+        hipLaunchKernelGGL(dense_finish_kernel<SS_F32>, dim3((unsigned)B), dim3(WAVE), 0, s, D);
+    }
     return launched();
 }
 

@@ -497,6 +497,110 @@ def test_topk_small_k_and_bf16(k):
     assert np.array_equal(ids.cpu().numpy(), ref_ids)
 
 
+# ---------------------------------------------------------------------------
+# dense verification: whole-vocabulary p, q rows read densely or absent
+# ---------------------------------------------------------------------------
+
+def run_verify_dense(target_np, dtype, B, G, req, draft_ids, draft_probs, seed=0, offset=0, cu_num_draft=None,
+                     flags=None, pad=0, rng_advance=0):
+    lib = L()
+    rows, V = target_np.shape
+    if pad:
+        wide = np.zeros((rows, V + pad), dtype=target_np.dtype)
+        wide[:, :V] = target_np
+        wide[:, V:] = W.to_bf16_bits(np.full((rows, pad), 1e4, np.float32)) if dtype == W.DTYPE_BF16 else 1e4
+        x = _dev_logits(wide, dtype)[:, :V]
+    else:
+        x = _dev_logits(target_np, dtype)
+    dreq = lib.DeviceRequests(req, flags=flags)
+    rng = lib.make_rng(seed, offset)
+    d = torch.from_numpy(np.ascontiguousarray(draft_ids, np.int32)).cuda()
+    q = None if draft_probs is None else torch.from_numpy(np.ascontiguousarray(draft_probs, np.float32)).cuda()
+    cu = None if cu_num_draft is None else torch.from_numpy(np.ascontiguousarray(cu_num_draft, np.int32)).cuda()
+    toks = torch.full((B, G + 1), -7, dtype=torch.int32, device="cuda")
+    ne = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    st = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    ws = lib.dense_workspace(B, G, V)
+    lib.ss_verify_step_dense(x, B, G, dreq, rng, d, q, toks, ne, st, ws, cu_num_draft=cu, rng_advance=rng_advance)
+    torch.cuda.synchronize()
+    return dict(tokens=toks.cpu().numpy(), n_emit=ne.cpu().numpy(), status=st.cpu().numpy(),
+                offset_after=int(rng.cpu().view(torch.int64)[1]))
+
+
+def dense_parity(target_np, dtype, B, G, req, draft_ids, draft_probs, seed=0, offset=0, cu_num_draft=None,
+                 flags=None, pad=0, max_fragile=2):
+    """Tokens, counts and statuses equal the oracle's for every request
+    whose tokens do not hinge on the rounding of the sum Z (the oracle
+    flags those: another summation order may move Z by ~1e-7 relative)."""
+    g = run_verify_dense(target_np, dtype, B, G, req, draft_ids, draft_probs, seed, offset, cu_num_draft, flags, pad)
+    o = oracle.verify_dense(target_np, dtype, B, G, req, draft_ids, draft_probs, seed=seed, offset=offset,
+                            threads=16, cu_num_draft=cu_num_draft,
+                            flags=None if flags is None else np.asarray(flags, np.uint32))
+    ok = o["fragile"] == 0
+    assert (~ok).sum() <= max_fragile, (~ok).sum()
+    for k in ("tokens", "n_emit", "status"):
+        bad = np.nonzero((g[k][ok] != o[k][ok]).reshape(ok.sum(), -1).any(1))[0]
+        assert len(bad) == 0, (k, np.nonzero(ok)[0][bad][:10])
+    return g, o
+
+
+@pytest.mark.parametrize("with_q", [True, False])
+@pytest.mark.parametrize("dtype", [W.DTYPE_BF16, W.DTYPE_F32])
+def test_verify_dense_small(dtype, with_q):
+    wl = W.workload_verify(B=24, gamma=4, V=30001)   # 4 tiles, the last one ragged
+    t = wl.target if dtype == W.DTYPE_BF16 else W.bf16_bits_to_f32(wl.target)
+    g, o = dense_parity(t, dtype, wl.B, wl.gamma, wl.req, wl.draft_ids, wl.draft_probs if with_q else None,
+                        seed=4, offset=6)
+    assert g["n_emit"].min() >= 1
+
+
+def test_verify_dense_c3_full():
+    wl = W.workload_verify()
+    g, o = dense_parity(wl.target, wl.dtype, wl.B, wl.gamma, wl.req, wl.draft_ids, wl.draft_probs)
+    assert g["n_emit"].min() >= 1
+    g, o = dense_parity(wl.target, wl.dtype, wl.B, wl.gamma, wl.req, wl.draft_ids, None, seed=3)
+
+
+def test_verify_dense_counts_strides_and_statuses():
+    rng = np.random.default_rng(41)
+    B, G, V = 12, 3, 9000
+    z = (rng.standard_normal((B * (G + 1), V)) * 2).astype(np.float32)
+    z[5 * (G + 1), :] = -np.inf                   # request 5, position 0: every value -inf
+    z[6 * (G + 1), ::2] = np.nan                  # NaN reads as -inf
+    z[6 * (G + 1), 7] = np.inf                    # +inf reads as the largest float
+    q = rng.dirichlet(np.ones(V), size=(B, G)).astype(np.float32)
+    q[7] = 0.0
+    q[7, :, :] = 1.0                              # q >= p everywhere: a rejection draws from p
+    d = rng.integers(0, V, (B, G)).astype(np.int32)
+    d[8, 0] = V + 5                               # outside the vocabulary: rejected
+    req = W.plain_requests(B, temperature=0.7)
+    req.greedy[[2, 9]] = True
+    req.temperature[10] = np.nan                  # invalid
+    flags = oracle.pack_requests(req)["flags"].copy()
+    flags[11] |= 4                                # a penalty flag: invalid in the dense variant
+    counts = np.array([3, 0, 2, 1, 3, 3, 3, 3, 3, 2, 3, 3])
+    cu = np.cumsum(counts).astype(np.int32)
+    for pad in (0, 3):
+        for qq in (q, None):
+            g, o = dense_parity(z, W.DTYPE_F32, B, G, req, d, qq, seed=8, offset=2, cu_num_draft=cu, flags=flags,
+                                pad=pad)
+            assert g["status"][5] == 1 and g["status"][10] == 2 and g["status"][11] == 2
+    zb = W.to_bf16_bits(z)
+    dense_parity(zb, W.DTYPE_BF16, B, G, req, d, q, seed=8, offset=2, cu_num_draft=cu, flags=flags, pad=5)
+
+
+def test_verify_dense_advances_offset_and_tiny_vocab():
+    rng = np.random.default_rng(42)
+    B, G, V = 40, 2, 100                          # one partial tile
+    z = (rng.standard_normal((B * (G + 1), V)) * 1.5).astype(np.float32)
+    q = rng.dirichlet(np.ones(V), size=(B, G)).astype(np.float32)
+    d = rng.integers(0, V, (B, G)).astype(np.int32)
+    req = W.plain_requests(B, temperature=1.0)
+    dense_parity(z, W.DTYPE_F32, B, G, req, d, q, seed=1, offset=9)
+    g = run_verify_dense(z, W.DTYPE_F32, B, G, req, d, q, seed=1, offset=9, rng_advance=3)
+    assert g["offset_after"] == 12
+
+
 def _radix_vs_oracle(x_np, dtype, k, pad=0, tag=""):
     """ss_topk_step_radix on rows `pad` elements wider than V (the columns
     past V hold values above every logit, which must not be read) against

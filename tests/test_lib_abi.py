@@ -121,6 +121,18 @@ def test_argument_errors_return_before_launch(L):
     assert lib.ss_verify_step_var(fake, 1, 2, 4, 100, 100, fake, None, fake, 0, fake, P, fake, fake, fake, P, fake,
                                   10**9, P) == L.SS_ERR_INVALID_ARG
     assert lib.ss_verify_step_var(fake, 1, 0, 4, 100, 100, P, None, P, 0, P, P, P, P, P, P, P, 0, P) == L.SS_OK
+    # dense verification: gamma range, required pointers, workspace, B = 0
+    assert lib.ss_verify_dense_workspace_bytes(2, 0, 100) == 0
+    assert lib.ss_verify_dense_workspace_bytes(2, 4, 100) > 0
+    assert lib.ss_verify_step_dense(fake, 1, 2, 0, 100, 100, fake, fake, 0, P, fake, P, fake, fake, P, fake,
+                                    10**9, P) == L.SS_ERR_UNSUPPORTED
+    assert lib.ss_verify_step_dense(fake, 1, 2, 4, 100, 100, fake, P, 0, P, fake, P, fake, fake, P, fake,
+                                    10**9, P) == L.SS_ERR_INVALID_ARG
+    assert lib.ss_verify_step_dense(fake, 1, 2, 4, 100, 100, fake, fake, 0, P, fake, P, fake, fake, P, fake,
+                                    16, P) == L.SS_ERR_WORKSPACE
+    assert lib.ss_verify_step_dense(fake, 7, 2, 4, 100, 100, fake, fake, 0, P, fake, P, fake, fake, P, fake,
+                                    10**9, P) == L.SS_ERR_UNSUPPORTED
+    assert lib.ss_verify_step_dense(fake, 1, 0, 4, 100, 100, P, P, 0, P, P, P, P, P, P, P, 0, P) == L.SS_OK
     # top-k: k range
     assert lib.ss_topk_step(fake, 0, 2, 100, 100, 0, fake, P, fake, 10**9, P) == L.SS_ERR_UNSUPPORTED
     assert lib.ss_topk_step(fake, 0, 2, 100, 100, 129, fake, P, fake, 10**9, P) == L.SS_ERR_UNSUPPORTED
