@@ -188,30 +188,49 @@ __global__ __launch_bounds__(DN_THREADS) void dense_stats_kernel(DenseParams D) 
     int Gb;
     const int mode = dense_request(D, b, Gb);
     if (mode < 0 || j > Gb) return;   // block-uniform
+    const float NINF = bitsf(F32_NINF_BITS), FMAX = bitsf(F32_MAX_BITS);
     float z[DN_EPT];
-    dense_load<DT>(D, row, tile, z);
-    // best (value, lower id) of the tile
-    uint64_t key = 0;
+    dense_load<DT>(D, row, tile, z);   // canonical, absent tokens -inf
+    // the thread's best canonical value (the max of the canonical values)
+    float zt = NINF;
 #pragma unroll
-    for (int i = 0; i < DN_EPT; ++i) {
-        const uint64_t k = dense_key(z[i], dense_id<DT>(tile, i));
-        key = k > key ? k : key;
+    for (int i = 0; i < DN_EPT; ++i) zt = fmaxf(zt, z[i]);
+    uint64_t key;
+    if (mode == 1) {
+        // greedy: the lowest id holding it (ids grow with i within a thread)
+        int first = DN_EPT - 1;
+#pragma unroll
+        for (int i = DN_EPT - 1; i >= 0; --i) first = z[i] == zt ? i : first;
+        int id = 0;
+#pragma unroll
+        for (int i = 0; i < DN_EPT; ++i) id = i == first ? dense_id<DT>(tile, i) : id;
+        key = dense_key(zt, id);
+    } else {
+        key = dense_key(zt, 0);   // stochastic rows need the value only
     }
     key = wave_max_u64(key);
-    // stochastic rows: sum exp(v - m) at this thread's maximum, rescaled to
-    // the tile's below
-    float m = bitsf(F32_NINF_BITS), s = 0.0f;
+    // stochastic rows: sum exp(v - m) at this thread's maximum m, rescaled to
+    // the tile's below.  The terms only feed the sum Z, so they take the
+    // hardware exp2 on z (a/ln 2) - m/ln 2 whenever no z/T leaves the
+    // finite range and m is far from -FLT_MAX (then the clamps of v change
+    // no term); otherwise the exact form.
+    float m = NINF, s = 0.0f;
     if (mode == 0) {
         const float invT = 1.0f / D.req[b].temperature;
+        m = dense_v(zt, invT);
+        if (m != NINF) {
+            const float big = zt * invT;
+            if (big <= FMAX && m > -0x1p127f) {
+                const float a = invT * 0x1.715476p+0f, c = m * 0x1.715476p+0f;
 #pragma unroll
-        for (int i = 0; i < DN_EPT; ++i) m = fmaxf(m, dense_v(z[i], invT));
-        if (m != bitsf(F32_NINF_BITS)) {
+                for (int i = 0; i < DN_EPT; ++i) s += __builtin_amdgcn_exp2f(__builtin_fmaf(z[i], a, -c));
+            } else {
 #pragma unroll
-            for (int i = 0; i < DN_EPT; ++i) s += exp_fixed_nonpos(dense_v(z[i], invT) - m);
+                for (int i = 0; i < DN_EPT; ++i) s += exp_fixed_nonpos(dense_v(z[i], invT) - m);
+            }
         }
         const float wm = wave_max_f(m);
-        s = wm == bitsf(F32_NINF_BITS) ? 0.0f : s * exp_fixed_nonpos(m - wm);
-        s = m == bitsf(F32_NINF_BITS) ? 0.0f : s;
+        s = (wm == NINF || m == NINF) ? 0.0f : s * exp_fixed_nonpos(m - wm);
         s = wave_sum_f(s);
         m = wm;
     }
@@ -229,9 +248,9 @@ __global__ __launch_bounds__(DN_THREADS) void dense_stats_kernel(DenseParams D) 
             mt = fmaxf(mt, s_m[w]);
         }
         float st = 0.0f;
-        if (mt != bitsf(F32_NINF_BITS))
+        if (mt != NINF)
             for (int w = 0; w < DN_WAVES; ++w)
-                st += s_m[w] == bitsf(F32_NINF_BITS) ? 0.0f : s_s[w] * exp_fixed_nonpos(s_m[w] - mt);
+                st += s_m[w] == NINF ? 0.0f : s_s[w] * exp_fixed_nonpos(s_m[w] - mt);
         D.part_k[(int64_t)row * D.Zt + tile] = k;
         D.part_s[(int64_t)row * D.Zt + tile] = st;
     }
@@ -276,62 +295,73 @@ __global__ __launch_bounds__(DN_THREADS) void dense_draw_kernel(DenseParams D) {
     const int mode = dense_request(D, b, Gb);
     const float T = D.req[b].temperature;
     const float invT = mode == 0 ? 1.0f / T : 1.0f;
-    if (wave == 0) {
-        // walk the positions in order (every workgroup of the request does,
-        // and finds the same)
+    // every position's outcome in parallel (wave w: positions w, w + 4, ..),
+    // then one thread walks them in order; every workgroup of the request
+    // finds the same
+    __shared__ int s_acc[SS_GAMMA_MAX + 1], s_top[SS_GAMMA_MAX + 1], s_masked[SS_GAMMA_MAX + 1];
+    __shared__ float s_pm[SS_GAMMA_MAX + 1], s_pz[SS_GAMMA_MAX + 1];
+    for (int j = wave; mode >= 0 && j <= Gb; j += DN_WAVES) {
+        const int64_t row = (int64_t)b * (D.G + 1) + j;
+        // the draft's logit and probability are requested with the partials
+        const int d = j < Gb ? D.draft_ids[(int64_t)b * D.G + j] : -1;
+        const bool din = (unsigned)d < (unsigned)D.V;
+        const void* rp = (const char*)D.target + row * D.ld * (DT == SS_BF16 ? 2 : 4);
+        float zd = 0.0f, qd = 0.0f;
+        if (din && mode == 0) {
+            if constexpr (DT == SS_BF16) zd = canon(bitsf((uint32_t)((const uint16_t*)rp)[d] << 16));
+            else zd = canon(((const float*)rp)[d]);
+            qd = D.draft_probs ? D.draft_probs[((int64_t)b * D.G + j) * D.V + d] : 1.0f;
+        }
+        uint64_t best;
+        float m, Z;
+        dense_row_stats(D, row, invT, mode == 0, best, m, Z);
+        const int top = dense_key_id(best);
+        const bool masked = dense_key_val(best) == bitsf(F32_NINF_BITS);
+        int acc;
+        if (mode == 1) {
+            acc = j < Gb && d == top;
+        } else if (j < Gb) {
+            const float pd = din ? exp_fixed_nonpos(dense_v(zd, invT) - m) / Z : 0.0f;
+            const float u = unit_open(philox_w0(rg.seed, rg.offset, 0u, (uint32_t)b, (1u << 24) | (uint32_t)j));
+            acc = qd > 0.0f && u * qd <= pd;
+        } else {
+            acc = 0;
+        }
+        if (lane == 0) {
+            s_acc[j] = acc;
+            s_top[j] = top;
+            s_masked[j] = masked;
+            s_pm[j] = m;
+            s_pz[j] = Z;
+        }
+    }
+    __syncthreads();
+    if (tid == 0) {
         DenseDec dc{0, -1, SS_ROW_OK, -1, 0, {0, 0, 0}};
         float mdraw = 0.0f, Zdraw = 1.0f;
         if (mode < 0) dc.status = SS_ROW_INVALID;
         for (int j = 0; mode >= 0 && j <= Gb; ++j) {
-            const int64_t row = (int64_t)b * (D.G + 1) + j;
-            uint64_t best;
-            float m, Z;
-            dense_row_stats(D, row, invT, mode == 0, best, m, Z);
-            if (dense_key_val(best) == bitsf(F32_NINF_BITS)) {
+            if (s_masked[j]) {
                 dc.status = SS_ROW_ALL_MASKED;
                 break;
             }
-            const int top = dense_key_id(best);
-            if (mode == 1) {   // greedy
-                const int d = j < Gb ? D.draft_ids[(int64_t)b * D.G + j] : -1;
-                if (j < Gb && d == top) {
-                    ++dc.emitted;
-                    continue;
-                }
-                dc.token = top;
-                break;
-            }
-            if (j == Gb) {   // every draft accepted: the bonus is drawn from row Gb
-                dc.jdraw = j;
-                dc.mode = 2;
-                break;
-            }
-            const int d = D.draft_ids[(int64_t)b * D.G + j];
-            const bool din = (unsigned)d < (unsigned)D.V;
-            const void* rp = (const char*)D.target + row * D.ld * (DT == SS_BF16 ? 2 : 4);
-            float zd = 0.0f, qd = 0.0f;
-            if (din) {
-                if constexpr (DT == SS_BF16) zd = canon(bitsf((uint32_t)((const uint16_t*)rp)[d] << 16));
-                else zd = canon(((const float*)rp)[d]);
-                qd = D.draft_probs ? D.draft_probs[((int64_t)b * D.G + j) * D.V + d] : 1.0f;
-            }
-            const float pd = din ? exp_fixed_nonpos(dense_v(zd, invT) - m) / Z : 0.0f;
-            const float u = unit_open(philox_w0(rg.seed, rg.offset, 0u, (uint32_t)b, (1u << 24) | (uint32_t)j));
-            if (qd > 0.0f && u * qd <= pd) {
+            if (s_acc[j]) {
                 ++dc.emitted;
                 continue;
             }
-            dc.jdraw = j;
-            dc.mode = 1;
-            mdraw = m;
-            Zdraw = Z;
+            if (mode == 1) {
+                dc.token = s_top[j];
+            } else {
+                dc.jdraw = j;
+                dc.mode = j == Gb ? 2 : 1;   // every draft accepted: the bonus from row Gb
+                mdraw = s_pm[j];
+                Zdraw = s_pz[j];
+            }
             break;
         }
-        if (lane == 0) {
-            s_dec = dc;
-            s_mz[0] = mdraw;
-            s_mz[1] = Zdraw;
-        }
+        s_dec = dc;
+        s_mz[0] = mdraw;
+        s_mz[1] = Zdraw;
     }
     __syncthreads();
     const DenseDec dc = s_dec;
