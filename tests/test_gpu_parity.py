@@ -747,6 +747,53 @@ def test_graph_replay_matches_eager_offsets():
         assert np.array_equal(got[i], o["tokens"]), i
 
 
+def test_graph_replay_dense_verify_and_radix_topk():
+    """Graph replays of the dense verification (advancing its own offset)
+    and of the radix-bitonic top-k equal the oracle at each replay, with
+    eager work and synchronisation between the replays."""
+    lib = L()
+    rng_np = np.random.default_rng(43)
+    B, G, V = 16, 3, 20000
+    z = (rng_np.standard_normal((B * (G + 1), V)) * 2).astype(np.float32)
+    q = rng_np.dirichlet(np.ones(V), size=(B, G)).astype(np.float32)
+    d = rng_np.integers(0, V, (B, G)).astype(np.int32)
+    req = W.plain_requests(B, temperature=0.8)
+    req.greedy[::4] = True
+    x = _dev_logits(z, W.DTYPE_F32)
+    dreq = lib.DeviceRequests(req)
+    rng = lib.make_rng(5, 0)
+    dd = torch.from_numpy(d).cuda()
+    qq = torch.from_numpy(q).cuda()
+    toks = torch.full((B, G + 1), -7, dtype=torch.int32, device="cuda")
+    ne = torch.zeros(B, dtype=torch.int32, device="cuda")
+    st = torch.zeros(B, dtype=torch.int32, device="cuda")
+    ws = lib.dense_workspace(B, G, V)
+    xk = _dev_logits(z[:B], W.DTYPE_F32)
+    ids = torch.full((B, 128), -7, dtype=torch.int32, device="cuda")
+    wsk = lib.workspace(B, V, W.DTYPE_F32)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        lib.ss_verify_step_dense(x, B, G, dreq, rng, dd, qq, toks, ne, st, ws, stream=s, rng_advance=1)
+        lib.ss_topk_step_radix(xk, 128, ids, ws=wsk, stream=s)
+    torch.cuda.synchronize()
+    rng.copy_(lib.make_rng(5, 0))
+    ref_ids, _ = oracle.topk(z[:B], W.DTYPE_F32, 128)
+    for i in range(3):
+        toks.fill_(-7)
+        ids.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        o = oracle.verify_dense(z, W.DTYPE_F32, B, G, req, d, q, seed=5, offset=i, threads=16)
+        ok = o["fragile"] == 0
+        assert np.array_equal(toks.cpu().numpy()[ok], o["tokens"][ok]), i
+        assert np.array_equal(ne.cpu().numpy()[ok], o["n_emit"][ok]), i
+        assert np.array_equal(ids.cpu().numpy(), ref_ids), i
+        _ = (x.sum()).item()   # eager work between replays
+    assert int(rng.cpu().view(torch.int64)[1]) == 3
+
+
 def test_step_advances_offset_itself():
     """rng_advance: each step draws with the offset it finds, then leaves
     offset + rng_advance behind - eagerly and under graph replay."""
