@@ -149,6 +149,31 @@ def summarize_rocprof(d: str, out: str) -> None:
     with open(out, "w") as fh:
         fh.write("\n".join(lines))
     print("\n".join(lines))
+    # the same trace, per kernel family of the other workloads
+    stats = rows(os.path.join(d, "trace", "c2_kernel_stats.csv"))
+    for fname, title, keys in (
+            ("dense_verify_c3.md", "Dense verification, c3 workload (B=64, gamma=4, V=131072 bf16 target, "
+             "fp32 draft rows rotated with the target; with and without draft probabilities)",
+             ("dense_stats_kernel", "dense_draw_kernel", "dense_finish_kernel", "verify_kernel")),
+            ("radix_bitonic_topk_c4.md", "Top-k stress, c4 workload (512 x 262144 fp32, peaked and flat "
+             "regimes): radix-bitonic and threshold tile selects, single-pass kernel",
+             ("stage1_radix_kernel", "topk_single_pass_kernel"))):
+        sel = [r for r in stats if any(k in r["Name"] for k in keys)]
+        shapes = [(n, g, v) for (n, g), v in sorted(per.items()) if any(k in n for k in keys)]
+        if "radix" in fname:   # the threshold select of the same shape
+            shapes += [(n, g, v) for (n, g), v in sorted(per.items()) if "stage1_kernel<0>" in n and g == 2097152]
+        ll = [f"# {title}", "", "Command (run from the repository root with TMPDIR=/tmp):", "",
+              "    " + PROFILE_CMDS[0], "", "## rocprofv3 --kernel-trace --stats (kernel_stats.csv)", "",
+              "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+        for r in sel:
+            ll.append(f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+        ll += ["", "## per launch shape (kernel_trace.csv)", "",
+               "| kernel | grid (threads) | calls | avg us | median us |", "|---|---|---|---|---|"]
+        for n, g, v in shapes:
+            ll.append(f"| {n} | {g} | {len(v)} | {sum(v) / len(v):.2f} | {statistics.median(v):.2f} |")
+        with open(os.path.join(os.path.dirname(out), fname), "w") as fh:
+            fh.write("\n".join(ll) + "\n")
 
 
 def main():
