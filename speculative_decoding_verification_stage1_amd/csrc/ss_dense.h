@@ -99,8 +99,15 @@ __device__ __forceinline__ float dense_v(float zc, float invT) {
 
 using dn_u32x4 = uint32_t __attribute__((ext_vector_type(4)));
 
-// Canonical logits of this thread's 32 tokens of tile `tile` (absent
-// tokens read as NaN, i.e. -inf): element i is token dense_id(tile, i).
+// NaN -> -inf, +inf -> FLT_MAX (two min/max); -0 stays -0, which equals +0
+// in every comparison, sum and exp here (only a key built from the value
+// must add +0 first).
+__device__ __forceinline__ float dense_canon(float x) {
+    return fminf(fmaxf(x, bitsf(F32_NINF_BITS)), bitsf(F32_MAX_BITS));
+}
+
+// Canonical logits (dense_canon) of this thread's 32 tokens of tile `tile`
+// (absent tokens read as -inf): element i is token dense_id(tile, i).
 template <int DT>
 __device__ __forceinline__ void dense_load(const DenseParams& D, int64_t row, int tile, float (&z)[DN_EPT]) {
     constexpr int EPC = DT == SS_BF16 ? 8 : 4;   // tokens per 16-byte chunk
@@ -117,10 +124,10 @@ __device__ __forceinline__ void dense_load(const DenseParams& D, int64_t row, in
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 if constexpr (DT == SS_BF16) {
-                    z[c * EPC + 2 * k] = canon(bitsf(d[k] << 16));
-                    z[c * EPC + 2 * k + 1] = canon(bitsf(d[k] & 0xFFFF0000u));
+                    z[c * EPC + 2 * k] = dense_canon(bitsf(d[k] << 16));
+                    z[c * EPC + 2 * k + 1] = dense_canon(bitsf(d[k] & 0xFFFF0000u));
                 } else {
-                    z[c * EPC + k] = canon(bitsf(d[k]));
+                    z[c * EPC + k] = dense_canon(bitsf(d[k]));
                 }
             }
         }
@@ -135,7 +142,7 @@ __device__ __forceinline__ void dense_load(const DenseParams& D, int64_t row, in
                     if constexpr (DT == SS_BF16) x = bitsf((uint32_t)gmem((const uint16_t*)rowp)[e] << 16);
                     else x = gmem((const float*)rowp)[e];
                 }
-                z[c * EPC + k] = canon(x);
+                z[c * EPC + k] = dense_canon(x);
             }
     }
 }
@@ -147,8 +154,9 @@ __device__ __forceinline__ int dense_id(int tile, int i) {
     return tile * DN_TILE + ((i / EPC) * DN_THREADS + (int)threadIdx.x) * EPC + (i % EPC);
 }
 
+// (value, lower id first) key; -0 counts as +0 (s is never NaN)
 __device__ __forceinline__ uint64_t dense_key(float s, int id) {
-    return ((uint64_t)ord32(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id);
+    return ((uint64_t)ord32(s + 0.0f) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id);
 }
 __device__ __forceinline__ int dense_key_id(uint64_t k) { return (int)(0xFFFFFFFFu - (uint32_t)k); }
 __device__ __forceinline__ float dense_key_val(uint64_t k) { return unord32((uint32_t)(k >> 32)); }
