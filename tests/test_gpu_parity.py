@@ -794,6 +794,61 @@ def test_graph_replay_dense_verify_and_radix_topk():
     assert int(rng.cpu().view(torch.int64)[1]) == 3
 
 
+# ---------------------------------------------------------------------------
+# the largest vocabulary the library takes (V = 2^24): many tiles per row
+# ---------------------------------------------------------------------------
+
+VMAX = 1 << 24
+
+
+def _vmax_rows(rows, seed, dtype):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((rows, VMAX), dtype=np.float32) * 2).astype(np.float32)
+    x[:, rng.integers(0, VMAX, 8)] += 10.0   # a few peaks, as in the workloads
+    return W.to_bf16_bits(x) if dtype == W.DTYPE_BF16 else x
+
+
+@pytest.mark.parametrize("dtype", [W.DTYPE_BF16, W.DTYPE_F32])
+def test_max_vocab_sample_and_topk(dtype):
+    x = _vmax_rows(2, 51 + dtype, dtype)
+    req = W.plain_requests(2, temperature=0.9, top_p=0.95)
+    req.greedy[0] = True
+    sample_parity(W.SampleWorkload(f"vmax-dt{dtype}", dtype, x, req), seed=6, offset=1)
+    lib = L()
+    xd = _dev_logits(x, dtype)
+    ref_ids, ref_vals = oracle.topk(x, dtype, 128, threads=2)
+    ws = lib.workspace(2, VMAX, dtype)
+    for fn in (lambda i, v: lib.ss_topk_step(xd, 128, i, v, ws), lambda i, v: lib.ss_topk_step_radix(xd, 128, i, v, ws),
+               lambda i, v: lib.ss_topk_single_pass(xd, 128, i, v)):
+        ids = torch.full((2, 128), -7, dtype=torch.int32, device="cuda")
+        vals = torch.zeros((2, 128), dtype=torch.float32, device="cuda")
+        fn(ids, vals)
+        torch.cuda.synchronize()
+        assert np.array_equal(ids.cpu().numpy(), ref_ids)
+        assert np.array_equal(vals.cpu().numpy(), ref_vals)
+
+
+def test_max_vocab_verify_bounded_and_dense():
+    B, G = 1, 2
+    z = _vmax_rows(B * (G + 1), 53, W.DTYPE_BF16)
+    zf = W.bf16_bits_to_f32(z).astype(np.float64)
+    # draft probabilities: the target's softmax with noise, drafts drawn from them
+    rng = np.random.default_rng(54)
+    q = np.zeros((B, G, VMAX), np.float32)
+    d = np.zeros((B, G), np.int32)
+    for j in range(G):
+        e = np.exp(zf[j] + rng.standard_normal(VMAX) * 0.5 - zf[j].max())
+        qq = (e / e.sum()).astype(np.float32)
+        q[0, j] = qq
+        d[0, j] = min(int(np.searchsorted(np.cumsum(qq, dtype=np.float64), rng.random() * qq.sum(dtype=np.float64))),
+                      VMAX - 1)
+    req = W.plain_requests(B, temperature=1.0)
+    wl = W.VerifyWorkload("vmax", W.DTYPE_BF16, z, q, d, req, G)
+    verify_parity(wl, seed=2, offset=3)
+    dense_parity(z, W.DTYPE_BF16, B, G, req, d, q, seed=2, offset=3)
+    dense_parity(z, W.DTYPE_BF16, B, G, req, d, None, seed=2, offset=4)
+
+
 def test_step_advances_offset_itself():
     """rng_advance: each step draws with the offset it finds, then leaves
     offset + rng_advance behind - eagerly and under graph replay."""
