@@ -409,6 +409,10 @@ def main():
 
     if not args.no_extra:
         result.update(extra_measurements(args, dev, L, W, stream))
+        rr = result.get("read_reference")
+        if rr:   # Stage 1 and the whole step against the measured streaming read
+            result["stage1_frac_of_read_reference"] = round(result["roofline"]["achieved"] / rr["GBps"], 4)
+            result["e2e_frac_of_read_reference"] = round(result["e2e_alg_GBps"] / rr["GBps"], 4)
 
     # ---- CPU oracle on a bounded sample of the same workload ----
     if not args.no_cpu:
@@ -554,6 +558,15 @@ def extra_measurements(args, dev, L, W, stream):
                       "ids_equal": same, "torch_topk_us": round(tt, 1)}
         del xk
     out["c4_topk"] = c4
+    # ---- bandwidth reference: the library's streaming read of 1 GiB (four
+    # times the last-level cache), HIP events around each launch ----
+    rbuf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    rout = torch.zeros(2048, dtype=torch.int32, device=dev)
+    L.ss_stream_read(rbuf, rout)
+    r_us = _events_us(lambda i: L.ss_stream_read(rbuf, rout), 5)
+    out["read_reference"] = {"us": round(r_us, 1), "GBps": round((1 << 30) / (r_us * 1e-6) / 1e9, 1),
+                             "bytes": 1 << 30, "kernel": "ss_stream_read (2048 workgroups, 16-byte loads)"}
+    del rbuf
     # ---- bandwidth reference: a plain device copy, 128 MiB read + 128 MiB written ----
     src = torch.ones(64 << 20, dtype=torch.bfloat16, device=dev)
     dst = [torch.empty_like(src) for _ in range(2)]

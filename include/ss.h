@@ -296,6 +296,14 @@ int ss_tile_topk(const void* logits, int dtype, int rows, int V, int64_t ld, int
                  const ss_req* req, const ss_aux* aux, int32_t* out_ids,
                  void* ws, size_t ws_bytes, void* stream);
 
+/* The bandwidth reference of the measurements: reads every byte of the
+ * device buffer [p, p + bytes) once with 16-byte loads (p 16-byte aligned,
+ * bytes a multiple of 16) on `nblocks` workgroups of 256 threads, and
+ * writes out[b] (device, [nblocks] uint32) = the xor of every 32-bit word of
+ * the 16-byte words i with (i mod 256*nblocks) / 256 == b.  No other
+ * effect. */
+int ss_stream_read(const void* p, size_t bytes, int nblocks, uint32_t* out, void* stream);
+
 /* rng->offset += delta on the device (one tiny kernel; capturable). */
 int ss_rng_advance(ss_rng* rng, uint64_t delta, void* stream);
 

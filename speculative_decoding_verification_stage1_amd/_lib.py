@@ -82,6 +82,8 @@ def _load():
     L.ss_verify_dense_workspace_bytes.restype = sz
     L.ss_verify_step_dense.argtypes = [P, i32, i32, i32, i32, i64, P, P, u64, P, P, P, P, P, P, P, sz, P]
     L.ss_verify_step_dense.restype = i32
+    L.ss_stream_read.argtypes = [P, sz, i32, P, P]
+    L.ss_stream_read.restype = i32
     L.ss_topk_step.argtypes = [P, i32, i32, i32, i64, i32, P, P, P, sz, P]
     L.ss_topk_step.restype = i32
     L.ss_topk_step_radix.argtypes = [P, i32, i32, i32, i64, i32, P, P, P, sz, P]
@@ -100,8 +102,8 @@ def _load():
 lib = _load()
 
 EXPORTS = ["ss_workspace_bytes", "ss_tile_size", "ss_sample_step", "ss_verify_step", "ss_verify_step_var",
-           "ss_verify_dense_workspace_bytes", "ss_verify_step_dense", "ss_topk_step", "ss_topk_step_radix", "ss_topk_single_pass", "ss_tile_topk", "ss_rng_advance",
-           "ss_status_str"]
+           "ss_verify_dense_workspace_bytes", "ss_verify_step_dense", "ss_topk_step", "ss_topk_step_radix",
+           "ss_topk_single_pass", "ss_tile_topk", "ss_rng_advance", "ss_stream_read", "ss_status_str"]
 
 
 class SsError(RuntimeError):
@@ -268,6 +270,13 @@ def ss_verify_step_dense(target, B: int, gamma: int, dreq: DeviceRequests, rng, 
                                   ptr(rng), rng_advance, ptr(cu_num_draft), ptr(draft_ids), ptr(draft_probs),
                                   ptr(out_tokens), ptr(out_n_emit), ptr(out_status), ptr(ws),
                                   0 if ws is None else ws.numel(), stream_handle(stream))
+    return _check(rc)
+
+
+def ss_stream_read(buf, out, stream=None) -> int:
+    """Streaming read of the whole tensor `buf` (the bandwidth reference);
+    out: int32/uint32 tensor with one word per workgroup."""
+    rc = lib.ss_stream_read(ptr(buf), buf.numel() * buf.element_size(), out.numel(), ptr(out), stream_handle(stream))
     return _check(rc)
 
 

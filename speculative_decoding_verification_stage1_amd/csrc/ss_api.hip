@@ -165,6 +165,33 @@ __global__ void rng_advance_kernel(ss_rng* rng, uint64_t delta) {
     if (threadIdx.x == 0 && blockIdx.x == 0) rng->offset += delta;
 }
 
+// A plain streaming read, the bandwidth reference of the measurements:
+// 16-byte loads over the buffer (word i goes to workgroup (i mod
+// 256*gridDim) / 256), four in flight per thread; each workgroup xors what
+// it read into out[blockIdx.x], so that no load can be dropped.
+using sr_u32x4 = uint32_t __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void stream_read_kernel(const sr_u32x4* p, uint64_t n16, uint32_t* out) {
+    __shared__ uint32_t s[4];
+    const auto g = gmem(p);
+    const uint64_t stride = (uint64_t)gridDim.x * 256u;
+    uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const sr_u32x4 a = g[i], b = g[i + stride], c = g[i + 2 * stride], d = g[i + 3 * stride];
+        const sr_u32x4 x = a ^ b ^ c ^ d;
+        acc ^= x[0] ^ x[1] ^ x[2] ^ x[3];
+    }
+    for (; i < n16; i += stride) {
+        const sr_u32x4 a = g[i];
+        acc ^= a[0] ^ a[1] ^ a[2] ^ a[3];
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o, WAVE);
+    if ((threadIdx.x & (WAVE - 1)) == 0) s[threadIdx.x / WAVE] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) out[blockIdx.x] = s[0] ^ s[1] ^ s[2] ^ s[3];
+}
+
 }  // namespace ssd
 
 // ---------------------------------------------------------------------------
@@ -431,6 +458,14 @@ int ss_tile_topk(const void* logits, int dtype, int rows, int V, int64_t ld, int
     const WsLayout W = ws_layout(ws, rows, V, dtype);
     Stage1Params s1 = make_s1(logits, dtype, rows, V, ld, rows_per_req, req, aux, W.scratch, out_ids);
     launch_stage1(dtype, s1, s);
+    return launched();
+}
+
+int ss_stream_read(const void* p, size_t bytes, int nblocks, uint32_t* out, void* stream) {
+    if (nblocks < 1 || nblocks > (1 << 20)) return SS_ERR_UNSUPPORTED;
+    if (!out || (bytes && !p) || ((uintptr_t)p & 15u) || (bytes & 15u)) return SS_ERR_INVALID_ARG;
+    hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)nblocks), dim3(256), 0, (hipStream_t)stream,
+                       (const sr_u32x4*)p, (uint64_t)(bytes / 16), out);
     return launched();
 }
 

@@ -849,6 +849,23 @@ def test_max_vocab_verify_bounded_and_dense():
     dense_parity(z, W.DTYPE_BF16, B, G, req, d, None, seed=2, offset=4)
 
 
+@pytest.mark.parametrize("nwords,nblocks", [(1, 1), (5000, 3), (262144 + 17, 64), (1 << 22, 1024)])
+def test_stream_read_reference(nwords, nblocks):
+    """The bandwidth reference reads every 16-byte word once: its per-block
+    xors equal numpy's over the same word-to-block assignment."""
+    lib = L()
+    a = np.random.default_rng(nwords).integers(0, 2**32, (nwords, 4), dtype=np.uint64).astype(np.uint32)
+    x = torch.from_numpy(a.view(np.int32)).cuda()
+    out = torch.full((nblocks,), -7, dtype=torch.int32, device="cuda")
+    lib.ss_stream_read(x, out)
+    torch.cuda.synchronize()
+    w = np.bitwise_xor.reduce(a, axis=1)
+    blk = (np.arange(nwords) % (256 * nblocks)) // 256
+    ref = np.zeros(nblocks, np.uint32)
+    np.bitwise_xor.at(ref, blk, w)
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), ref)
+
+
 def test_step_advances_offset_itself():
     """rng_advance: each step draws with the offset it finds, then leaves
     offset + rng_advance behind - eagerly and under graph replay."""

@@ -144,6 +144,11 @@ def test_argument_errors_return_before_launch(L):
     assert lib.ss_topk_single_pass(fake, 0, 2, 100, 100, 129, fake, P, P) == L.SS_ERR_UNSUPPORTED
     assert lib.ss_tile_topk(fake, 0, 2, 100, 100, 0, P, None, P, fake, 10**9, P) == L.SS_ERR_INVALID_ARG
     assert lib.ss_rng_advance(P, 1, P) == L.SS_ERR_INVALID_ARG
+    # streaming read: alignment, size and block-count checks
+    assert lib.ss_stream_read(fake, 32, 0, fake, P) == L.SS_ERR_UNSUPPORTED
+    assert lib.ss_stream_read(fake, 32, 4, P, P) == L.SS_ERR_INVALID_ARG
+    assert lib.ss_stream_read(fake, 24, 4, fake, P) == L.SS_ERR_INVALID_ARG
+    assert lib.ss_stream_read(ctypes.c_void_p(0x1008), 32, 4, fake, P) == L.SS_ERR_INVALID_ARG
     assert lib.ss_status_str(L.SS_ERR_WORKSPACE).startswith(b"workspace")
 
 
