@@ -167,7 +167,8 @@ __global__ void rng_advance_kernel(ss_rng* rng, uint64_t delta) {
 
 // A plain streaming read, the bandwidth reference of the measurements:
 // 16-byte loads over the buffer (word i goes to workgroup (i mod
-// 256*gridDim) / 256), four in flight per thread; each workgroup xors what
+// 256*gridDim) / 256), four in flight per thread, with the streaming
+// (nontemporal) policy of the logits loads; each workgroup xors what
 // it read into out[blockIdx.x], so that no load can be dropped.
 using sr_u32x4 = uint32_t __attribute__((ext_vector_type(4)));
 __global__ __launch_bounds__(256) void stream_read_kernel(const sr_u32x4* p, uint64_t n16, uint32_t* out) {
@@ -177,12 +178,13 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const sr_u32x4* p, uin
     uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x;
     uint32_t acc = 0;
     for (; i + 3 * stride < n16; i += 4 * stride) {
-        const sr_u32x4 a = g[i], b = g[i + stride], c = g[i + 2 * stride], d = g[i + 3 * stride];
+        const sr_u32x4 a = __builtin_nontemporal_load(g + i), b = __builtin_nontemporal_load(g + i + stride),
+                      c = __builtin_nontemporal_load(g + i + 2 * stride), d = __builtin_nontemporal_load(g + i + 3 * stride);
         const sr_u32x4 x = a ^ b ^ c ^ d;
         acc ^= x[0] ^ x[1] ^ x[2] ^ x[3];
     }
     for (; i < n16; i += stride) {
-        const sr_u32x4 a = g[i];
+        const sr_u32x4 a = __builtin_nontemporal_load(g + i);
         acc ^= a[0] ^ a[1] ^ a[2] ^ a[3];
     }
 #pragma unroll

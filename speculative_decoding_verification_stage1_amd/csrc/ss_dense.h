@@ -119,7 +119,7 @@ __device__ __forceinline__ void dense_load(const DenseParams& D, int64_t row, in
     if (nvalid == DN_TILE && D.aligned16) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            const dn_u32x4 w = gmem((const dn_u32x4*)rowp)[c * DN_THREADS + tid];
+            const dn_u32x4 w = __builtin_nontemporal_load(gmem((const dn_u32x4*)rowp) + c * DN_THREADS + tid);
             const uint32_t d[4] = {w[0], w[1], w[2], w[3]};
 #pragma unroll
             for (int k = 0; k < 4; ++k) {

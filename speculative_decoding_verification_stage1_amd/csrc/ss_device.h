@@ -70,6 +70,12 @@ typedef uint32_t vu32x4 __attribute__((ext_vector_type(4)));   // 16-byte load u
 // format, no swizzle, no per-lane index.
 constexpr int BUF_DWORD3 = 0x00020000;
 
+// Cache policy for data read exactly once (the logits and grammar words):
+// the nt bit, so that the stream is not kept in the caches in place of data
+// that are read again (tile lists, request records).  Measured on a cold
+// 128 MiB read in 64 KiB workgroups: 24.3 us with it, 26.9 us without.
+constexpr int LD_STREAM = 2;
+
 // A buffer view of `bytes` bytes at `base` (uniform).  Loads at offsets
 // past the end return zero and touch no memory, so a fixed run of loads
 // needs no branch around the ones that fall outside.

@@ -323,7 +323,7 @@ __device__ __forceinline__ void tile_fetch(const Stage1Params& P, int row, int t
         const auto gm = gmem(P.aux.bitmask + (int64_t)row * P.aux.bitmask_stride) + base / 32 + tid;
 #pragma unroll
         for (int k = 0; k < GW; ++k)
-            in.gw[k] = (full || base / 32 + tid + k * S1_THREADS < words) ? gm[k * S1_THREADS] : 0u;
+            in.gw[k] = (full || base / 32 + tid + k * S1_THREADS < words) ? __builtin_nontemporal_load(gm + k * S1_THREADS) : 0u;
     }
     // the logits, as one buffer view over the tile's whole 16-byte chunks:
     // the same 16 loads for every tile, with nothing between them, so that
@@ -335,7 +335,7 @@ __device__ __forceinline__ void tile_fetch(const Stage1Params& P, int row, int t
     const __amdgpu_buffer_rsrc_t rs = buf_view(rowp, (uint32_t)nbytes);
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
-        const vu32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, (tid + j * S1_THREADS) * 16, 0, 0);
+        const vu32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, (tid + j * S1_THREADS) * 16, 0, LD_STREAM);
         __builtin_amdgcn_sched_barrier(0);   // keep the issue order: chunk j is used j-th
         in.raw[4 * j + 0] = v.x;
         in.raw[4 * j + 1] = v.y;
