@@ -294,6 +294,12 @@ def test_workspace_reuse_alternating_inputs():
         assert np.array_equal(ids.cpu().numpy(), refs[k]["topk_ids"]), i
 
 
+def test_sample_many_rows():
+    """More than a thousand rows in one step (every option in play)."""
+    wl = W.workload_mixed(2, 1100, 3000, grammar=True)
+    sample_parity(wl, seed=5, offset=9, tag="B=1100")
+
+
 def test_determinism_repeated_runs():
     wl = W.workload_mixed(2, 32, 131072, grammar=True)
     a = run_sample(wl.logits, wl.dtype, wl.req, 1, 2)
