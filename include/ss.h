@@ -153,8 +153,13 @@ typedef struct ss_aux {
 
 /* Bytes of workspace a call over `rows` logits rows of width V needs (rows
  * = B for sampling and top-k, B*(gamma+1) for verification).  Pure host
- * function; the workspace must be 256-byte aligned.  Its contents need no
- * initialisation; calls that share a workspace must not overlap in time. */
+ * function; the workspace must be 256-byte aligned.  Its first 4096 bytes
+ * hold per-request arrival counters of verification (used when B <= 1024)
+ * and must be zero before the workspace's first use, e.g. a zero-filled
+ * allocation; every entry point leaves them zero (also under graph
+ * replay), so one workspace can serve any sequence of calls.  The rest
+ * needs no initialisation.  Calls that share a workspace must not overlap
+ * in time. */
 size_t ss_workspace_bytes(int rows, int V, int dtype);
 
 /* Vocabulary tile width used for `dtype` (B_N of the two-stage top-k). */
@@ -255,7 +260,9 @@ int ss_verify_step_var(const void* target_logits, int dtype, int B, int gamma, i
  * accepted the bonus is the Gumbel-max of v over row n_b.  Greedy requests
  * accept a draft equal to the row's best id.  Outputs, statuses, noise
  * counters, rng and rng_advance as in ss_verify_step.  ws: at least
- * ss_verify_dense_workspace_bytes(B, gamma, V) bytes, 256-byte aligned. */
+ * ss_verify_dense_workspace_bytes(B, gamma, V) bytes, 256-byte aligned;
+ * its first 4096 bytes are not touched (they may hold the counters of a
+ * workspace shared with ss_workspace_bytes users). */
 size_t ss_verify_dense_workspace_bytes(int B, int gamma, int V);
 int ss_verify_step_dense(const void* target_logits, int dtype, int B, int gamma, int V, int64_t ld,
                          const ss_req* req, ss_rng* rng, uint64_t rng_advance,

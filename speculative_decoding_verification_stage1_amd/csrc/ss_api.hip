@@ -23,9 +23,17 @@ size_t scratch_bytes(int rows, int V, int dtype) {
 size_t rec_bytes(int rows) { return align256((size_t)rows * sizeof(RowRec)); }
 size_t listed_bytes(int rows) { return align256((size_t)rows * KMAX * sizeof(uint64_t)); }
 constexpr size_t RNG_SNAP_BYTES = 256;
+// Arrival counters of verification (one per request), at the start of
+// every workspace layout - the same bytes whatever the call - so that a
+// workspace shared by several entry points keeps them at zero: only
+// verification writes them, and every launch leaves them zero.
+constexpr size_t ARRIVE_BYTES = 4096;
+constexpr int ARRIVE_REQUESTS_MAX = (int)(ARRIVE_BYTES / sizeof(uint32_t));
 
-// workspace: [tile keys][listed-token keys][row records][rng copy]
+// workspace: [arrival counters][tile keys][listed-token keys][row records
+// or decisions][rng copy]
 struct WsLayout {
+    uint32_t* arrive;
     void* scratch;
     uint64_t* listed;
     RowRec* recs;
@@ -33,8 +41,9 @@ struct WsLayout {
 };
 WsLayout ws_layout(void* ws, int rows, int V, int dtype) {
     WsLayout L;
-    L.scratch = ws;
-    L.listed = (uint64_t*)((char*)ws + scratch_bytes(rows, V, dtype));
+    L.arrive = (uint32_t*)ws;
+    L.scratch = (char*)ws + ARRIVE_BYTES;
+    L.listed = (uint64_t*)((char*)L.scratch + scratch_bytes(rows, V, dtype));
     L.recs = (RowRec*)((char*)L.listed + listed_bytes(rows));
     L.rng_snap = (ss_rng*)((char*)L.recs + rec_bytes(rows));
     return L;
@@ -208,7 +217,7 @@ int ss_tile_size(int dtype) {
 
 size_t ss_workspace_bytes(int rows, int V, int dtype) {
     if (rows < 0 || V < 1 || (dtype != SS_F32 && dtype != SS_BF16)) return 0;
-    return scratch_bytes(rows, V, dtype) + listed_bytes(rows) + rec_bytes(rows) + RNG_SNAP_BYTES;
+    return ARRIVE_BYTES + scratch_bytes(rows, V, dtype) + listed_bytes(rows) + rec_bytes(rows) + RNG_SNAP_BYTES;
 }
 
 const char* ss_status_str(int status) {
@@ -293,6 +302,13 @@ int ss_verify_step_var(const void* target_logits, int dtype, int B, int gamma, i
     f.v_tokens = out_tokens;
     f.v_n_emit = out_n_emit;
     f.v_status = out_status;
+    if (B <= ARRIVE_REQUESTS_MAX) {   // Stage 2 decides and emits: two launches
+        static_assert(sizeof(RowRec) >= 4 * sizeof(int32_t), "decisions live in the record area");
+        f.arrive = W.arrive;
+        f.dec = (int32_t*)W.recs;
+        launch_stage2<MODE_VERIFY>(dtype, f, s);
+        return launched();
+    }
     launch_stage2<MODE_VERIFY>(dtype, f, s);
     hipLaunchKernelGGL(verify_kernel, dim3((unsigned)B), dim3(VF_THREADS), 0, s, f);
     return launched();
@@ -315,7 +331,7 @@ DenseWs dense_ws(void* ws, int B, int gamma, int V) {
     const size_t rz = (size_t)B * (gamma + 1) * dense_tiles(V), bz = (size_t)B * dense_tiles(V);
     DenseWs L;
     char* p = (char*)ws;
-    size_t o = 0;
+    size_t o = ARRIVE_BYTES;   // left alone: a workspace shared with the bounded path keeps its counters
     L.part_k = (uint64_t*)(p + o);
     o += align256(rz * sizeof(uint64_t));
     L.part_s = (float*)(p + o);

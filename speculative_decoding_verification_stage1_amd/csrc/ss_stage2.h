@@ -60,6 +60,8 @@ struct Stage2Params {
     int32_t* v_tokens;
     int32_t* v_n_emit;
     int32_t* v_status;
+    uint32_t* arrive;   // verification decided in Stage 2: arrival counters [requests] (else null)
+    int32_t* dec;       // ... per-row decisions [rows][4]: accept, token, status
     // top-k
     float* topk_vals;
 };
@@ -504,9 +506,140 @@ __device__ __forceinline__ WL64 row_merge(const Stage2Params& F, const RowParams
     return res;
 }
 
+// ---------------------------------------------------------------------------
+// Verification rules (SonicSampler section 3.1 "Speculative verification";
+// the decoding notes' "Rejection Sampler"), shared by the two places that
+// apply them: Stage 2 itself (each target row decides its own position) and
+// verify_kernel (one workgroup per request, for batches above the counter
+// area).
+// ---------------------------------------------------------------------------
+
+// Request b's draft count: gamma, or n_b = cu[b] - cu[b-1] with per-request
+// counts (a count outside [0, gamma] makes the request invalid).  Uniform.
+struct DraftCount {
+    int n;
+    bool ok;
+};
+__device__ __forceinline__ DraftCount draft_count(const Stage2Params& F, int b) {
+    if (!F.cu_num_draft) return DraftCount{F.gamma, true};
+    const int hi = F.cu_num_draft[b];
+    const int lo = b > 0 ? F.cu_num_draft[b - 1] : 0;
+    const bool ok = hi - lo >= 0 && hi - lo <= F.gamma;
+    return DraftCount{ok ? hi - lo : 0, ok};
+}
+
+// Position j of request b (whole wave; ranks lane and lane + 64): the row's
+// status, greedy flag, kept count n, Gumbel-max token and best id, the
+// draft d, the candidates (id -1 past the row's K), their p (0 past n) and
+// v, and q gathered at the candidates and at d.  Bonus position (j = n_b):
+// the row's token.  Greedy: accept iff d is the best id, else emit the best
+// id.  Otherwise accept iff q(d) > 0 and u q(d) <= p(d), u from Philox
+// counter {0, b, (1 << 24) | j}; on rejection the Gumbel-max of ln(rho) +
+// g over rho = max(0, p - q) > 0 with g from counter {id, b, (2 << 24) | j},
+// or of v + g when rho vanishes on every kept candidate.
+struct PosDecision {
+    int accept;
+    int token;
+};
+__device__ __forceinline__ PosDecision decide_position(const ss_rng rg, int b, int j, int n_b, int status,
+                                                       int greedy, int n, int rtoken, int best, int d, int id_lo_r,
+                                                       int id_hi_r, float p_lo_r, float p_hi_r, float v_lo,
+                                                       float v_hi, float q_lo_r, float q_hi_r, float q_d_r, int V) {
+    const int lane = lane_id();
+    int accept = 0, token = -1;
+    const bool live = status == SS_ROW_OK || status == SS_ROW_TOPK_CLAMPED;
+    if (live && j == n_b) {   // bonus token
+        token = rtoken;
+        accept = 1;
+    } else if (live && greedy) {
+        token = best;
+        accept = d == token;
+    } else if (live) {
+        const int id_lo = lane < n ? id_lo_r : -1;
+        const int id_hi = lane + 64 < n ? id_hi_r : -1;
+        const float p_lo = lane < n ? p_lo_r : 0.0f;
+        const float p_hi = lane + 64 < n ? p_hi_r : 0.0f;
+        const float q_lo = id_lo >= 0 ? q_lo_r : 0.0f;
+        const float q_hi = id_hi >= 0 ? q_hi_r : 0.0f;
+        const float qd = (d >= 0 && d < V) ? q_d_r : 0.0f;
+        // p_j(d): the kept candidate equal to d, if any (ids are unique)
+        float pd = 0.0f;
+        const uint64_t m_lo = __ballot(id_lo == d && id_lo >= 0);
+        const uint64_t m_hi = __ballot(id_hi == d && id_hi >= 0);
+        if (m_lo) pd = readlane_f(p_lo, __builtin_ctzll(m_lo));
+        else if (m_hi) pd = readlane_f(p_hi, __builtin_ctzll(m_hi));
+        const float u = unit_open(philox_w0(rg.seed, rg.offset, 0u, (uint32_t)b, (1u << 24) | (uint32_t)j));
+        accept = qd > 0.0f && u * qd <= pd;
+        if (!accept) {
+            // draw from norm(max(0, p - q)) by Gumbel-max on ln(rho)
+            const uint32_t c2 = (2u << 24) | (uint32_t)j;
+            const float g_lo = id_lo >= 0 ? gumbel_noise(rg.seed, rg.offset, (uint32_t)id_lo, (uint32_t)b, c2) : 0.0f;
+            const float g_hi = id_hi >= 0 ? gumbel_noise(rg.seed, rg.offset, (uint32_t)id_hi, (uint32_t)b, c2) : 0.0f;
+            const float rho_lo = p_lo - q_lo, rho_hi = p_hi - q_hi;
+            const bool ok_lo = id_lo >= 0 && rho_lo > 0.0f;
+            const bool ok_hi = id_hi >= 0 && rho_hi > 0.0f;
+            float s = ok_lo ? log_fixed(rho_lo) + g_lo : 0.0f;
+            int id = ok_lo ? id_lo : -1;
+            if (ok_hi) {
+                const float sh = log_fixed(rho_hi) + g_hi;
+                if (id < 0 || sh > s || (sh == s && id_hi < id)) {
+                    s = sh;
+                    id = id_hi;
+                }
+            }
+            token = wave_argmax(s, id, id >= 0);
+            if (token < 0) {   // p <= q on every kept candidate: draw from p
+                float s2 = id_lo >= 0 ? v_lo + g_lo : 0.0f;
+                int i2 = id_lo;
+                if (id_hi >= 0) {
+                    const float sh = v_hi + g_hi;
+                    if (i2 < 0 || sh > s2 || (sh == s2 && id_hi < i2)) {
+                        s2 = sh;
+                        i2 = id_hi;
+                    }
+                }
+                token = wave_argmax(s2, i2, i2 >= 0);
+            }
+        }
+    }
+    return PosDecision{accept, token};
+}
+
+// Request b's output from its positions' decisions (one lane): the accepted
+// drafts in order, then the first rejection's draw or the bonus token; -1
+// after; a request whose first row is invalid (or whose count is) emits
+// nothing, and one whose emitted path meets an all-masked row stops there.
+__device__ __forceinline__ void emit_request(const Stage2Params& F, int b, const DraftCount& dc, const int* acc,
+                                             const int* tok, const int* st) {
+    const int G = F.gamma;
+    int32_t* out = F.v_tokens + (int64_t)b * (G + 1);
+    int emitted = 0;
+    int status;
+    if (!dc.ok || st[0] == SS_ROW_INVALID) {
+        status = SS_ROW_INVALID;
+    } else {
+        status = st[0] == SS_ROW_TOPK_CLAMPED ? SS_ROW_TOPK_CLAMPED : SS_ROW_OK;
+        for (int j = 0; j <= dc.n; ++j) {
+            if (st[j] == SS_ROW_ALL_MASKED) {
+                status = SS_ROW_ALL_MASKED;
+                break;
+            }
+            if (j < dc.n && acc[j]) {
+                out[emitted++] = F.draft_ids[(int64_t)b * G + j];
+                continue;
+            }
+            out[emitted++] = tok[j];   // first rejection's draw, or the bonus
+            break;
+        }
+    }
+    for (int j = emitted; j <= G; ++j) out[j] = -1;
+    F.v_n_emit[b] = emitted;
+    if (F.v_status) F.v_status[b] = status;
+}
+
 // Epilogue on wave 0 (ranks k = lane and lane + 64).  Writes the mode's
 // outputs for the row.  Uses no barrier.
-template <int DT>
+template <int DT, int MODE>
 __device__ __forceinline__ void row_epilogue(const Stage2Params& F, const RowParams& rp, int row, int b, const WL64& best,
                              const ss_rng rg, S2Shared& sh) {
     const Stage1Params& P = F.s1;
@@ -519,8 +652,26 @@ __device__ __forceinline__ void row_epilogue(const Stage2Params& F, const RowPar
     const int id0 = key_id(k0);
     const float z0 = key_z(k0);
     const float NINF = bitsf(F32_NINF_BITS);
+    // verification decided in this launch: the draft and the draft
+    // probabilities at it and at the candidates are requested first, so
+    // that they arrive while the epilogue runs
+    int vj = 0, vd = -1;
+    DraftCount dc{0, true};
+    float q_lo_r = 0.0f, q_hi_r = 0.0f, q_d_r = 0.0f;
+    if constexpr (MODE == MODE_VERIFY) {
+        if (F.arrive) {
+            vj = row - b * P.rows_per_req;
+            dc = draft_count(F, b);
+            vd = vj < dc.n ? F.draft_ids[(int64_t)b * F.gamma + vj] : -1;
+            const float* q = F.draft_probs + ((int64_t)b * F.gamma + (vj < F.gamma ? vj : F.gamma - 1)) * P.V;
+            auto in_v = [&](int id) { return (unsigned)id < (unsigned)P.V; };
+            q_lo_r = q[in_v(id_lo) ? id_lo : 0];
+            q_hi_r = q[in_v(id_hi) ? id_hi : 0];
+            q_d_r = q[in_v(vd) ? vd : 0];
+        }
+    }
 
-    if (F.mode == MODE_TOPK) {
+    if constexpr (MODE == MODE_TOPK) {
         const int kk = F.topk_k;
         for (int h = 0; h < 2; ++h) {
             const int k = lane + 64 * h;
@@ -570,7 +721,7 @@ __device__ __forceinline__ void row_epilogue(const Stage2Params& F, const RowPar
             e_hi = in_hi ? eh : 0.0f;
         }
         uint32_t c1, c2;
-        if (F.mode == MODE_VERIFY) {
+        if constexpr (MODE == MODE_VERIFY) {
             c1 = (uint32_t)b;
             c2 = (uint32_t)(row - b * P.rows_per_req);
         } else {
@@ -634,7 +785,7 @@ __device__ __forceinline__ void row_epilogue(const Stage2Params& F, const RowPar
         token = wave_argmax(s, id, id >= 0);
     }
 
-    if (F.mode == MODE_SAMPLE) {
+    if constexpr (MODE == MODE_SAMPLE) {
         if (lane == 0) {
             F.tokens[row] = token;
             if (F.status) F.status[row] = status;
@@ -651,7 +802,38 @@ __device__ __forceinline__ void row_epilogue(const Stage2Params& F, const RowPar
                 F.probs[(int64_t)row * KMAX + k] = pk;
             }
         }
-    } else {   // MODE_VERIFY
+    } else if (F.arrive) {   // MODE_VERIFY, decided here
+        const int n_r = live ? n : 0;
+        const int idl = (status != SS_ROW_INVALID && lane < K) ? id_lo : -1;
+        const int idh = (status != SS_ROW_INVALID && lane + 64 < K) ? id_hi : -1;
+        const float pl = (live && !rp.greedy && lane < n) ? e_lo / En : 0.0f;
+        const float ph = (live && !rp.greedy && lane + 64 < n) ? e_hi / En : 0.0f;
+        const int best_id = __builtin_amdgcn_readfirstlane(idl);
+        const PosDecision pd = decide_position(rg, b, vj, dc.n, status, rp.greedy, n_r, token, best_id, vd, idl, idh,
+                                               pl, ph, v_lo, v_hi, q_lo_r, q_hi_r, q_d_r, P.V);
+        // hand the decision to the request's last row: device-coherent
+        // stores, completed before the arrival is counted
+        if (lane == 0) {
+            int32_t* dr = F.dec + (int64_t)row * 4;
+            store_coherent(dr, pd.accept);
+            store_coherent(dr + 1, pd.token);
+            store_coherent(dr + 2, (int32_t)status);
+        }
+        wait_memory();
+        if (lane == 0 && arrive_last(F.arrive + b, (uint32_t)((dc.ok ? dc.n : F.gamma) + 1))) {
+            int acc[SS_GAMMA_MAX + 1], tok[SS_GAMMA_MAX + 1], st[SS_GAMMA_MAX + 1];
+            const int32_t* d0 = F.dec + (int64_t)b * P.rows_per_req * 4;
+#pragma unroll
+            for (int j = 0; j <= SS_GAMMA_MAX; ++j) {
+                if (j <= dc.n) {
+                    acc[j] = load_coherent(d0 + 4 * j);
+                    tok[j] = load_coherent(d0 + 4 * j + 1);
+                    st[j] = load_coherent(d0 + 4 * j + 2);
+                }
+            }
+            emit_request(F, b, dc, acc, tok, st);
+        }
+    } else {   // MODE_VERIFY, records for verify_kernel
         RowRec* rec = F.recs + row;
         for (int h = 0; h < 2; ++h) {
             const int k = lane + 64 * h;
@@ -682,7 +864,7 @@ __global__ __launch_bounds__(S2_THREADS) void stage2_kernel(Stage2Params F) {
     const RowParams rp = row_params(F.s1, b, &L.bias_head, L.rq);
     const WL64 best = row_merge<DT>(F, rp, row, sh, L);
     if (threadIdx.x >= WAVE) return;
-    row_epilogue<DT>(F, rp, row, b, best, rg, sh);
+    row_epilogue<DT, MODE>(F, rp, row, b, best, rg, sh);
 }
 
 }  // namespace ssd

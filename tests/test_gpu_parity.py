@@ -353,6 +353,92 @@ def test_verify_small():
     verify_parity(wl, seed=1, offset=5)
 
 
+@pytest.mark.parametrize("B", [1024, 1030])
+def test_verify_request_count_limit(B):
+    """Up to 1024 requests Stage 2 decides and emits (two launches); above
+    that a third launch does, from the rows' records.  Both match the
+    oracle, with variable draft counts in play."""
+    wl = W.workload_verify(B=B, gamma=2, V=1500)
+    cu = np.cumsum(np.random.default_rng(B).integers(0, 3, size=B)).astype(np.int32)
+    verify_parity(wl, seed=2, offset=7)
+    verify_parity(wl, seed=2, offset=8, cu_num_draft=cu)
+
+
+def test_verify_graph_replays():
+    """Bounded verification captured once and replayed: every replay uses
+    the offset it finds and matches the oracle (the per-request arrival
+    counters are back at zero after each launch)."""
+    lib = L()
+    wl = W.workload_verify(B=12, gamma=3, V=30000)
+    x = _dev_logits(wl.target, wl.dtype)
+    rows, V = x.shape
+    dreq = lib.DeviceRequests(wl.req)
+    d = torch.from_numpy(np.ascontiguousarray(wl.draft_ids, np.int32)).cuda()
+    q = torch.from_numpy(np.ascontiguousarray(wl.draft_probs, np.float32)).cuda()
+    toks = torch.zeros((wl.B, wl.gamma + 1), dtype=torch.int32, device="cuda")
+    ne = torch.zeros(wl.B, dtype=torch.int32, device="cuda")
+    ws = lib.workspace(rows, V, wl.dtype)
+    rng = lib.make_rng(9, 0)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        lib.ss_verify_step(x, wl.B, wl.gamma, dreq, rng, d, q, toks, ne, None, ws, stream=s, rng_advance=1)
+    torch.cuda.synchronize()
+    rng.copy_(lib.make_rng(9, 20))
+    for i in range(4):
+        g.replay()
+        torch.cuda.synchronize()
+        o = oracle.verify(wl.target, wl.dtype, wl.B, wl.gamma, wl.req, wl.draft_ids, wl.draft_probs,
+                          seed=9, offset=20 + i, threads=16)
+        assert np.array_equal(toks.cpu().numpy(), o["tokens"]), i
+        assert np.array_equal(ne.cpu().numpy(), o["n_emit"]), i
+        assert int(ws[:4096].count_nonzero()) == 0, i
+        _ = (x.float().sum()).item()
+
+
+def test_workspace_shared_across_entry_points():
+    """One zero-filled workspace serves verification, top-k and sampling in
+    turn: the arrival counters at its start are zero after every call, and
+    every call matches the oracle."""
+    lib = L()
+    sw = W.workload_mixed(2, 24, 70000, grammar=True)
+    vw = W.workload_verify(B=6, gamma=4, V=70000)
+    rows_v = vw.B * (vw.gamma + 1)
+    n = max(int(lib.lib.ss_workspace_bytes(rows_v, 70000, W.DTYPE_F32)),
+            int(lib.lib.ss_workspace_bytes(sw.logits.shape[0], 70000, sw.dtype)))
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    xs = _dev_logits(sw.logits, sw.dtype)
+    dreq = lib.DeviceRequests(sw.req)
+    ref = oracle.sample(sw.logits, sw.dtype, sw.req, seed=11, offset=3, threads=16)
+    toks = torch.zeros(sw.logits.shape[0], dtype=torch.int32, device="cuda")
+    xv = _dev_logits(vw.target, vw.dtype)
+    vreq = lib.DeviceRequests(vw.req)
+    d = torch.from_numpy(np.ascontiguousarray(vw.draft_ids, np.int32)).cuda()
+    q = torch.from_numpy(np.ascontiguousarray(vw.draft_probs, np.float32)).cuda()
+    vt = torch.zeros((vw.B, vw.gamma + 1), dtype=torch.int32, device="cuda")
+    ve = torch.zeros(vw.B, dtype=torch.int32, device="cuda")
+    vref = oracle.verify(vw.target, vw.dtype, vw.B, vw.gamma, vw.req, vw.draft_ids, vw.draft_probs,
+                         seed=1, offset=1, threads=16)
+    kx = torch.randn(rows_v, 70000, generator=torch.Generator().manual_seed(4))
+    kref = torch.sort(kx, dim=1, descending=True, stable=True).indices[:, :128].numpy()
+    kx = kx.cuda()
+    kid = torch.zeros((rows_v, 128), dtype=torch.int32, device="cuda")
+    for i in range(3):
+        lib.ss_verify_step(xv, vw.B, vw.gamma, vreq, lib.make_rng(1, 1), d, q, vt, ve, None, ws)
+        torch.cuda.synchronize()
+        assert int(ws[:4096].count_nonzero()) == 0, ("after verify", i)
+        assert np.array_equal(vt.cpu().numpy(), vref["tokens"]), i
+        lib.ss_topk_step(kx, 128, kid, ws=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:4096].count_nonzero()) == 0, ("after top-k", i)
+        assert np.array_equal(kid.cpu().numpy(), kref), i
+        lib.ss_sample_step(xs, dreq, lib.make_rng(11, 3), toks, ws=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:4096].count_nonzero()) == 0, ("after sample", i)
+        assert np.array_equal(toks.cpu().numpy(), ref["tokens"]), i
+
+
 def test_verify_c3_full():
     g = verify_parity(W.workload_verify())
     assert g["n_emit"].min() >= 1
