@@ -637,11 +637,30 @@ __device__ __forceinline__ void emit_request(const Stage2Params& F, int b, const
     if (F.v_status) F.v_status[b] = status;
 }
 
+// What verification in Stage 2 can request before the merge: the request's
+// draft count and position j's draft (any value past the count: not used).
+// They depend only on (request, position), so they are requested at the
+// start of the workgroup and arrive during the merge; q at the draft waits
+// for the epilogue, with q at the candidates, so no wave waits for the
+// draft early.
+struct VerifyPre {
+    DraftCount dc;
+    int d;
+};
+__device__ __forceinline__ VerifyPre verify_pre(const Stage2Params& F, int row, int b) {
+    const int G = F.gamma;
+    const int j = row - b * F.s1.rows_per_req;
+    VerifyPre vp;
+    vp.d = j < G ? F.draft_ids[(int64_t)b * G + j] : -1;
+    vp.dc = draft_count(F, b);
+    return vp;
+}
+
 // Epilogue on wave 0 (ranks k = lane and lane + 64).  Writes the mode's
 // outputs for the row.  Uses no barrier.
 template <int DT, int MODE>
 __device__ __forceinline__ void row_epilogue(const Stage2Params& F, const RowParams& rp, int row, int b, const WL64& best,
-                             const ss_rng rg, S2Shared& sh) {
+                             const ss_rng rg, S2Shared& sh, const VerifyPre& vp) {
     const Stage1Params& P = F.s1;
     const int lane = lane_id();
     const uint64_t k_lo = best.lo, k_hi = best.hi;
@@ -652,17 +671,15 @@ __device__ __forceinline__ void row_epilogue(const Stage2Params& F, const RowPar
     const int id0 = key_id(k0);
     const float z0 = key_z(k0);
     const float NINF = bitsf(F32_NINF_BITS);
-    // verification decided in this launch: the draft and the draft
-    // probabilities at it and at the candidates are requested first, so
-    // that they arrive while the epilogue runs
-    int vj = 0, vd = -1;
-    DraftCount dc{0, true};
+    // verification decided in this launch: the draft probabilities at the
+    // candidates and at the draft (requested with the lists) are requested
+    // first, so that they arrive while the epilogue runs
+    const int vj = row - b * P.rows_per_req;
+    const DraftCount dc = vp.dc;
+    const int vd = vj < dc.n ? vp.d : -1;
     float q_lo_r = 0.0f, q_hi_r = 0.0f, q_d_r = 0.0f;
     if constexpr (MODE == MODE_VERIFY) {
         if (F.arrive) {
-            vj = row - b * P.rows_per_req;
-            dc = draft_count(F, b);
-            vd = vj < dc.n ? F.draft_ids[(int64_t)b * F.gamma + vj] : -1;
             const float* q = F.draft_probs + ((int64_t)b * F.gamma + (vj < F.gamma ? vj : F.gamma - 1)) * P.V;
             auto in_v = [&](int id) { return (unsigned)id < (unsigned)P.V; };
             q_lo_r = q[in_v(id_lo) ? id_lo : 0];
@@ -859,12 +876,15 @@ __global__ __launch_bounds__(S2_THREADS) void stage2_kernel(Stage2Params F) {
     const int b = __builtin_amdgcn_readfirstlane(div_uniform(row, F.s1.rows_per_req));
     RowLoads<DT> L;
     row_loads<DT>(F, row, L);   // the Stage-1 lists first
+    VerifyPre vp{DraftCount{0, true}, -1};
+    if constexpr (MODE == MODE_VERIFY)
+        if (F.arrive) vp = verify_pre(F, row, b);
     ss_rng rg{0ull, 0ull};
     if (F.rng) rg = *F.rng;
     const RowParams rp = row_params(F.s1, b, &L.bias_head, L.rq);
     const WL64 best = row_merge<DT>(F, rp, row, sh, L);
     if (threadIdx.x >= WAVE) return;
-    row_epilogue<DT, MODE>(F, rp, row, b, best, rg, sh);
+    row_epilogue<DT, MODE>(F, rp, row, b, best, rg, sh, vp);
 }
 
 }  // namespace ssd
