@@ -130,8 +130,10 @@ struct u32x4 { uint32_t x, y, z, w; };
 __device__ __forceinline__ u32x4 philox10(u32x4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
     for (int i = 0; i < 10; ++i) {
-        const uint32_t a = 0xD2511F53u * c.x, ah = __umulhi(0xD2511F53u, c.x);
-        const uint32_t b = 0xCD9E8D57u * c.z, bh = __umulhi(0xCD9E8D57u, c.z);
+        // each 32 x 32 -> 64 product as one multiply-add (both halves)
+        const uint64_t pa = (uint64_t)0xD2511F53u * c.x, pb = (uint64_t)0xCD9E8D57u * c.z;
+        const uint32_t a = (uint32_t)pa, ah = (uint32_t)(pa >> 32);
+        const uint32_t b = (uint32_t)pb, bh = (uint32_t)(pb >> 32);
         c = u32x4{bh ^ c.y ^ k0, b, ah ^ c.w ^ k1, a};
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;
