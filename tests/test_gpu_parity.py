@@ -465,6 +465,19 @@ def test_verify_variable_draft_counts():
     assert g["status"][5] == 2 and g["status"][6] == 2
 
 
+@pytest.mark.parametrize("B,G,V", [(3, 16, 5000), (1, 1, 700), (5, 16, 40000)])
+def test_verify_gamma_extremes(B, G, V):
+    """The largest draft count (16) and the smallest (1, one request), with
+    all drafts checked and with per-request counts including 0 and gamma."""
+    wl = W.workload_verify(B=B, gamma=G, V=V, greedy_frac=0.34)
+    verify_parity(wl, seed=6, offset=1)
+    counts = np.random.default_rng(B * 100 + G).integers(0, G + 1, B)
+    counts[0] = G
+    if B > 1:
+        counts[1] = 0
+    verify_parity(wl, seed=6, offset=1, cu_num_draft=_counts_cu(counts))
+
+
 def test_verify_variable_draft_counts_c3_full():
     wl = W.workload_verify()
     counts = np.random.default_rng(32).integers(0, wl.gamma + 1, wl.B)
