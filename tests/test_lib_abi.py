@@ -85,6 +85,10 @@ def test_sizes(L):
     ws = L.ss_workspace_bytes(256, 262144, L.SS_BF16)
     assert ws >= 256 * 8 * 128 * 4 + 256 * 128 * 8
     assert ws % 256 == 0
+    # the 4 KiB of arrival counters lead every layout, so the smallest
+    # workspace holds them too, and so does the dense one
+    assert L.ss_workspace_bytes(1, 1, L.SS_F32) >= 4096 + 128 * 8
+    assert L.lib.ss_verify_dense_workspace_bytes(1, 1, 1) >= 4096
     assert L.ss_workspace_bytes(-1, 10, 0) == 0
     assert L.ss_workspace_bytes(1, 0, 0) == 0
 
