@@ -384,22 +384,63 @@ __global__ __launch_bounds__(DN_THREADS) void dense_draw_kernel(DenseParams D) {
     const int d = dc.mode == 1 ? D.draft_ids[(int64_t)b * D.G + jd] : -1;
     const float* q = (dc.mode == 1 && D.draft_probs) ? D.draft_probs + ((int64_t)b * D.G + jd) * D.V : nullptr;
     uint64_t key = 0;
+    if (q) {
+        // With draft probabilities about half the tokens have rho = p - q
+        // > 0: those are queued per wave in LDS, and the logarithm and the
+        // Gumbel noise are worked out over the queue in full rounds of 64
+        // lanes.  Each candidate's arithmetic is the direct path's and the
+        // keys are unique, so the maximum does not depend on the order.
+        // (Without q every token but the draft is a candidate, and the
+        // queue would only add work.)
+        constexpr int QSLOTS = 8;   // token slots per queue fill
+        __shared__ int s_qid[DN_WAVES][QSLOTS * WAVE];
+        __shared__ float s_qx[DN_WAVES][QSLOTS * WAVE];
 #pragma unroll
-    for (int i = 0; i < DN_EPT; ++i) {
-        const int id = dense_id<DT>(tile, i);
-        if (id >= D.V) continue;
-        const float v = dense_v(z[i], invT);
-        float s;
-        if (dc.mode == 2) {
-            s = v + gumbel_noise(rg.seed, rg.offset, (uint32_t)id, (uint32_t)b, c2);
-        } else {
-            const float pi = exp_fixed_nonpos(v - m) / Z;
-            const float rho = q ? pi - q[id] : (id == d ? 0.0f : pi);
-            if (!(rho > 0.0f)) continue;
-            s = log_fixed(rho) + gumbel_noise(rg.seed, rg.offset, (uint32_t)id, (uint32_t)b, c2);
+        for (int g = 0; g < DN_EPT; g += QSLOTS) {
+            int n = 0;   // queue length (uniform)
+#pragma unroll
+            for (int i = g; i < g + QSLOTS; ++i) {
+                const int id = dense_id<DT>(tile, i);
+                float rho = 0.0f;
+                if (id < D.V) rho = exp_fixed_nonpos(dense_v(z[i], invT) - m) / Z - q[id];
+                const bool cand = rho > 0.0f;
+                const uint64_t bal = __ballot(cand);
+                if (cand) {
+                    const int slot = n + lane_prefix(bal);
+                    s_qid[wave][slot] = id;
+                    s_qx[wave][slot] = rho;
+                }
+                n += __popcll(bal);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            for (int k = lane; k < n; k += WAVE) {
+                const int id = s_qid[wave][k];
+                const float sc = log_fixed(s_qx[wave][k]) +
+                                 gumbel_noise(rg.seed, rg.offset, (uint32_t)id, (uint32_t)b, c2);
+                const uint64_t kk = dense_key(sc, id);   // > 0 for every candidate
+                key = kk > key ? kk : key;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // read before the next fill
+            __builtin_amdgcn_wave_barrier();
         }
-        const uint64_t k = dense_key(s, id);   // > 0 for every candidate (s is never NaN)
-        key = k > key ? k : key;
+    } else {
+#pragma unroll
+        for (int i = 0; i < DN_EPT; ++i) {
+            const int id = dense_id<DT>(tile, i);
+            if (id >= D.V) continue;
+            const float v = dense_v(z[i], invT);
+            float sc;
+            if (dc.mode == 2) {
+                sc = v + gumbel_noise(rg.seed, rg.offset, (uint32_t)id, (uint32_t)b, c2);
+            } else {
+                const float rho = id == d ? 0.0f : exp_fixed_nonpos(v - m) / Z;
+                if (!(rho > 0.0f)) continue;
+                sc = log_fixed(rho) + gumbel_noise(rg.seed, rg.offset, (uint32_t)id, (uint32_t)b, c2);
+            }
+            const uint64_t kk = dense_key(sc, id);   // > 0 for every candidate (sc is never NaN)
+            key = kk > key ? kk : key;
+        }
     }
     key = wave_max_u64(key);
     if (lane == 0) s_best[wave] = key;
