@@ -154,7 +154,7 @@ typedef struct ss_aux {
 /* Bytes of workspace a call over `rows` logits rows of width V needs (rows
  * = B for sampling and top-k, B*(gamma+1) for verification).  Pure host
  * function; the workspace must be 256-byte aligned.  Its first 4096 bytes
- * hold per-request arrival counters of verification (used when B <= 1024)
+ * hold per-request decision words of verification (used when B <= 512)
  * and must be zero before the workspace's first use, e.g. a zero-filled
  * allocation; every entry point leaves them zero (also under graph
  * replay), so one workspace can serve any sequence of calls.  The rest

@@ -23,12 +23,13 @@ size_t scratch_bytes(int rows, int V, int dtype) {
 size_t rec_bytes(int rows) { return align256((size_t)rows * sizeof(RowRec)); }
 size_t listed_bytes(int rows) { return align256((size_t)rows * KMAX * sizeof(uint64_t)); }
 constexpr size_t RNG_SNAP_BYTES = 256;
-// Arrival counters of verification (one per request), at the start of
-// every workspace layout - the same bytes whatever the call - so that a
-// workspace shared by several entry points keeps them at zero: only
-// verification writes them, and every launch leaves them zero.
+// Verification's per-request decision words (64 bits: arrivals and
+// per-position bits), at the start of every workspace layout - the same
+// bytes whatever the call - so that a workspace shared by several entry
+// points keeps them at zero: only verification writes them, and every
+// launch leaves them zero.
 constexpr size_t ARRIVE_BYTES = 4096;
-constexpr int ARRIVE_REQUESTS_MAX = (int)(ARRIVE_BYTES / sizeof(uint32_t));
+constexpr int ARRIVE_REQUESTS_MAX = (int)(ARRIVE_BYTES / sizeof(uint64_t));
 
 // workspace: [arrival counters][tile keys][listed-token keys][row records
 // or decisions][rng copy]
@@ -303,9 +304,7 @@ int ss_verify_step_var(const void* target_logits, int dtype, int B, int gamma, i
     f.v_n_emit = out_n_emit;
     f.v_status = out_status;
     if (B <= ARRIVE_REQUESTS_MAX) {   // Stage 2 decides and emits: two launches
-        static_assert(sizeof(RowRec) >= 4 * sizeof(int32_t), "decisions live in the record area");
         f.arrive = W.arrive;
-        f.dec = (int32_t*)W.recs;
         launch_stage2<MODE_VERIFY>(dtype, f, s);
         return launched();
     }

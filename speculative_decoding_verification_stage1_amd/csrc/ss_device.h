@@ -94,26 +94,17 @@ __device__ __forceinline__ uint64_t buf_u64(__amdgpu_buffer_rsrc_t r, uint32_t o
 // and a device-scope fence writes back or invalidates a whole L2 (µs each,
 // serialised per XCD), so none is used: the producer writes with
 // device-coherent stores (sc1: through to memory), waits until they have
-// completed, then counts its arrival with a device-scope atomic; the
-// consumer, having seen the count, reads with device-coherent loads (sc1:
-// never served from a stale cache line).
+// completed, then counts its arrival with a device-scope atomic (whose
+// return value can carry the earlier producers' data as well); whoever sees
+// the final count writes with device-coherent stores where earlier
+// producers wrote, so that no cached copy is written back over its own.
 template <typename T>
 __device__ __forceinline__ void store_coherent(T* p, T v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-template <typename T>
-__device__ __forceinline__ T load_coherent(const T* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 // Wait until this wave's memory operations have completed (a compiler
 // barrier as well).
 __device__ __forceinline__ void wait_memory() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// Counts an arrival at a counter that expects n of them per launch; true
-// for the last one.  The counter wraps back to 0 on that arrival, so it is
-// 0 again for the next launch.
-__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t n) {
-    return __builtin_amdgcn_atomic_inc32(counter, n - 1u, __ATOMIC_RELAXED, "agent") == n - 1u;
-}
 
 template <typename T>
 __device__ __forceinline__ const __attribute__((address_space(1))) T* gmem(const T* p) {

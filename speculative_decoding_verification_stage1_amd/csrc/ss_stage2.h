@@ -60,8 +60,7 @@ struct Stage2Params {
     int32_t* v_tokens;
     int32_t* v_n_emit;
     int32_t* v_status;
-    uint32_t* arrive;   // verification decided in Stage 2: arrival counters [requests] (else null)
-    int32_t* dec;       // ... per-row decisions [rows][4]: accept, token, status
+    uint32_t* arrive;   // verification decided in Stage 2: one 64-bit word per request (else null)
     // top-k
     float* topk_vals;
 };
@@ -508,10 +507,11 @@ __device__ __forceinline__ WL64 row_merge(const Stage2Params& F, const RowParams
 
 // ---------------------------------------------------------------------------
 // Verification rules (SonicSampler section 3.1 "Speculative verification";
-// the decoding notes' "Rejection Sampler"), shared by the two places that
-// apply them: Stage 2 itself (each target row decides its own position) and
-// verify_kernel (one workgroup per request, for batches above the counter
-// area).
+// the decoding notes' "Rejection Sampler"), applied in two places: Stage 2
+// itself (each target row decides its own position; the request's last row
+// to arrive finds where it stops from the positions' accept and all-masked
+// bits) and verify_kernel (one workgroup per request, from the rows'
+// records, for batches above the workspace's word area; emit_request).
 // ---------------------------------------------------------------------------
 
 // Request b's draft count: gamma, or n_b = cu[b] - cu[b-1] with per-request
@@ -527,6 +527,12 @@ __device__ __forceinline__ DraftCount draft_count(const Stage2Params& F, int b) 
     const bool ok = hi - lo >= 0 && hi - lo <= F.gamma;
     return DraftCount{ok ? hi - lo : 0, ok};
 }
+
+// The request's 64-bit word while its rows decide in Stage 2: accept bits
+// 0..gamma, all-masked bits 17..17+gamma, the arrival count from bit 48.
+constexpr int VF_MASKED_SHIFT = SS_GAMMA_MAX + 1;
+constexpr int VF_COUNT_SHIFT = 48;
+static_assert(VF_MASKED_SHIFT + SS_GAMMA_MAX + 1 <= VF_COUNT_SHIFT, "decision word layout");
 
 // Position j of request b (whole wave; ranks lane and lane + 64): the row's
 // status, greedy flag, kept count n, Gumbel-max token and best id, the
@@ -828,27 +834,45 @@ __device__ __forceinline__ void row_epilogue(const Stage2Params& F, const RowPar
         const int best_id = __builtin_amdgcn_readfirstlane(idl);
         const PosDecision pd = decide_position(rg, b, vj, dc.n, status, rp.greedy, n_r, token, best_id, vd, idl, idh,
                                                pl, ph, v_lo, v_hi, q_lo_r, q_hi_r, q_d_r, P.V);
-        // hand the decision to the request's last row: device-coherent
-        // stores, completed before the arrival is counted
+        // Position j's output slot holds the draft if it was accepted, else
+        // this row's draw: what the request emits there whenever every
+        // earlier draft is accepted.  The row writes it (device-coherent,
+        // completed before the arrival), then adds its arrival, its accept
+        // bit (bit j) and its all-masked bit (bit 17 + j) to the request's
+        // 64-bit word; the last arrival has every position's bits from the
+        // add's return value, finds where the request stops, and writes -1
+        // past it (also device-coherent, so that it lands after the rows'
+        // writes), the count and the status, and clears the word.
         if (lane == 0) {
-            int32_t* dr = F.dec + (int64_t)row * 4;
-            store_coherent(dr, pd.accept);
-            store_coherent(dr + 1, pd.token);
-            store_coherent(dr + 2, (int32_t)status);
-        }
-        wait_memory();
-        if (lane == 0 && arrive_last(F.arrive + b, (uint32_t)((dc.ok ? dc.n : F.gamma) + 1))) {
-            int acc[SS_GAMMA_MAX + 1], tok[SS_GAMMA_MAX + 1], st[SS_GAMMA_MAX + 1];
-            const int32_t* d0 = F.dec + (int64_t)b * P.rows_per_req * 4;
-#pragma unroll
-            for (int j = 0; j <= SS_GAMMA_MAX; ++j) {
-                if (j <= dc.n) {
-                    acc[j] = load_coherent(d0 + 4 * j);
-                    tok[j] = load_coherent(d0 + 4 * j + 1);
-                    st[j] = load_coherent(d0 + 4 * j + 2);
+            const int G = F.gamma;
+            int32_t* out = F.v_tokens + (int64_t)b * (G + 1);
+            const bool acc = vj < dc.n && pd.accept;
+            store_coherent(out + vj, acc ? vd : pd.token);
+            wait_memory();
+            const uint64_t mine = (1ull << VF_COUNT_SHIFT) | ((uint64_t)acc << vj) |
+                                  ((uint64_t)(status == SS_ROW_ALL_MASKED) << (VF_MASKED_SHIFT + vj));
+            uint64_t* word = (uint64_t*)F.arrive + b;
+            const uint64_t old = __hip_atomic_fetch_add(word, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int arrivals = (dc.ok ? dc.n : G) + 1;
+            if ((int)(old >> VF_COUNT_SHIFT) + 1 == arrivals) {
+                const uint64_t all = old + mine;
+                int emitted = 0, st = SS_ROW_INVALID;
+                if (dc.ok && status != SS_ROW_INVALID) {   // validity is per request
+                    st = rp.clamped ? SS_ROW_TOPK_CLAMPED : SS_ROW_OK;
+                    for (int j = 0; j <= dc.n; ++j) {
+                        if ((all >> (VF_MASKED_SHIFT + j)) & 1ull) {
+                            st = SS_ROW_ALL_MASKED;   // nothing emitted here (the row wrote -1)
+                            break;
+                        }
+                        emitted = j + 1;
+                        if (j == dc.n || !((all >> j) & 1ull)) break;
+                    }
                 }
+                for (int j = emitted; j <= G; ++j) store_coherent(out + j, -1);
+                F.v_n_emit[b] = emitted;
+                if (F.v_status) F.v_status[b] = st;
+                store_coherent(word, (uint64_t)0);
             }
-            emit_request(F, b, dc, acc, tok, st);
         }
     } else {   // MODE_VERIFY, records for verify_kernel
         RowRec* rec = F.recs + row;

@@ -8,11 +8,11 @@
 // What happens at position j depends only on position j's data (accept or
 // not, and the residual draw if not), so all positions are evaluated at
 // once; one lane then walks them in order to emit the accepted prefix and
-// the first rejection's draw (or the bonus token).  Up to 1024 requests,
+// the first rejection's draw (or the bonus token).  Up to 512 requests,
 // Stage 2 does this itself (decide_position in each target row's
-// workgroup, emit_request in the request's last row to finish); above
-// that, verify_kernel does it with one workgroup per request from the rows'
-// records.
+// workgroup; the request's last row to finish completes the output from
+// the positions' bits); above that, verify_kernel does it with one
+// workgroup per request from the rows' records (emit_request).
 //
 // With per-request draft counts (inclusive cumulative offsets, as the
 // notes' rejection kernel reads its range from cu_num_draft_tokens),
