@@ -161,23 +161,27 @@ __device__ __forceinline__ uint64_t dense_key(float s, int id) {
 __device__ __forceinline__ int dense_key_id(uint64_t k) { return (int)(0xFFFFFFFFu - (uint32_t)k); }
 __device__ __forceinline__ float dense_key_val(uint64_t k) { return unord32((uint32_t)(k >> 32)); }
 
+// Butterfly reductions over the wave (distances 32, 16, .., 1; every lane
+// ends with the result), exchanging through DPP and the row-swap permutes
+// rather than the LDS crossbar.
+template <int O = 32>
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint64_t x = __shfl_xor(k, o, WAVE);
-        k = x > k ? x : k;
-    }
-    return k;
+    const uint64_t x = xor_lane64<O>(k);
+    k = x > k ? x : k;
+    if constexpr (O > 1) return wave_max_u64<O / 2>(k);
+    else return k;
 }
+template <int O = 32>
 __device__ __forceinline__ float wave_max_f(float x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, WAVE));
-    return x;
+    x = fmaxf(x, __uint_as_float(xor_lane<O>(__float_as_uint(x))));
+    if constexpr (O > 1) return wave_max_f<O / 2>(x);
+    else return x;
 }
+template <int O = 32>
 __device__ __forceinline__ float wave_sum_f(float x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, WAVE);
-    return x;
+    x += __uint_as_float(xor_lane<O>(__float_as_uint(x)));
+    if constexpr (O > 1) return wave_sum_f<O / 2>(x);
+    else return x;
 }
 
 template <int DT>
