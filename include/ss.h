@@ -50,13 +50,17 @@ extern "C" {
 #define SS_KMAX 128        /* bounded candidate set (SonicSampler section 3.3) */
 #define SS_GAMMA_MAX 16    /* largest number of draft tokens per request */
 #define SS_V_MAX (1 << 24) /* largest vocabulary */
+/* size of the static workspace behind ss_sample_step_noalloc, per GPU */
+#define SS_NOALLOC_WS_BYTES (16u << 20)
 
 typedef enum {
     SS_OK = 0,
     SS_ERR_INVALID_ARG = -1, /* null pointer, bad size, bad stride */
     SS_ERR_UNSUPPORTED = -2, /* dtype, V or gamma outside what is supported */
     SS_ERR_WORKSPACE = -3,   /* workspace missing, too small or misaligned */
-    SS_ERR_HIP = -4          /* a kernel launch failed */
+    SS_ERR_HIP = -4,         /* a kernel launch failed */
+    SS_ERR_NOALLOC_LIMIT = -5 /* ss_sample_step_noalloc: the call needs more than
+                                 SS_NOALLOC_WS_BYTES of workspace */
 } ss_status;
 
 typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
@@ -193,6 +197,27 @@ int ss_sample_step(const void* logits, int dtype, int B, int V, int64_t ld,
                    int32_t* out_tokens, int32_t* out_topk_ids, float* out_probs,
                    int32_t* out_kept, float* out_mass, int32_t* out_status,
                    void* ws, size_t ws_bytes, void* stream);
+
+/* ss_sample_step for callers that cannot allocate device memory (code
+ * under hipGraph capture that must not call hipMalloc, tight serving loops,
+ * harnesses that forbid allocation): the same arguments, computation,
+ * outputs and errors, without the workspace arguments.  Its workspace is a
+ * device array inside the library, SS_NOALLOC_WS_BYTES (16 MiB) on each GPU
+ * it runs on, held until the process ends; its address on the current
+ * device is looked up on the first call there.  A call whose
+ * ss_workspace_bytes(B, V, dtype) exceeds SS_NOALLOC_WS_BYTES returns
+ * SS_ERR_NOALLOC_LIMIT before anything is launched (e.g. B = 256 at V =
+ * 2^18 bf16 needs about 1.7 MiB; B = 2048 at V = 2^18 fp32 is too large).
+ * The call allocates nothing and launches the same kernels as
+ * ss_sample_step.  Every call on one GPU shares that GPU's array, which
+ * keeps the last call's contents (a call reads only what it wrote itself,
+ * so nothing needs clearing): calls that overlap in time on one GPU, e.g.
+ * on two streams, race and give wrong results; serialise them.  The
+ * current device must be the device of `stream`. */
+int ss_sample_step_noalloc(const void* logits, int dtype, int B, int V, int64_t ld,
+                           const ss_req* req, const ss_aux* aux, ss_rng* rng, uint64_t rng_advance,
+                           int32_t* out_tokens, int32_t* out_topk_ids, float* out_probs,
+                           int32_t* out_kept, float* out_mass, int32_t* out_status, void* stream);
 
 /* Speculative verification of `gamma` draft tokens per request
  * (SonicSampler "multi-step mode").  target_logits has B*(gamma+1) rows;

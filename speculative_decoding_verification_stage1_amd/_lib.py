@@ -26,6 +26,8 @@ SS_ERR_INVALID_ARG = -1
 SS_ERR_UNSUPPORTED = -2
 SS_ERR_WORKSPACE = -3
 SS_ERR_HIP = -4
+SS_ERR_NOALLOC_LIMIT = -5
+NOALLOC_WS_BYTES = 16 << 20
 
 ROW_OK = 0
 ROW_ALL_MASKED = 1
@@ -74,6 +76,8 @@ def _load():
     L.ss_tile_size.restype = i32
     L.ss_sample_step.argtypes = [P, i32, i32, i32, i64, P, P, P, u64, P, P, P, P, P, P, P, sz, P]
     L.ss_sample_step.restype = i32
+    L.ss_sample_step_noalloc.argtypes = [P, i32, i32, i32, i64, P, P, P, u64, P, P, P, P, P, P, P]
+    L.ss_sample_step_noalloc.restype = i32
     L.ss_verify_step.argtypes = [P, i32, i32, i32, i32, i64, P, P, P, u64, P, P, P, P, P, P, sz, P]
     L.ss_verify_step.restype = i32
     L.ss_verify_step_var.argtypes = [P, i32, i32, i32, i32, i64, P, P, P, u64, P, P, P, P, P, P, P, sz, P]
@@ -101,7 +105,7 @@ def _load():
 
 lib = _load()
 
-EXPORTS = ["ss_workspace_bytes", "ss_tile_size", "ss_sample_step", "ss_verify_step", "ss_verify_step_var",
+EXPORTS = ["ss_workspace_bytes", "ss_tile_size", "ss_sample_step", "ss_sample_step_noalloc", "ss_verify_step", "ss_verify_step_var",
            "ss_verify_dense_workspace_bytes", "ss_verify_step_dense", "ss_topk_step", "ss_topk_step_radix",
            "ss_topk_single_pass", "ss_tile_topk", "ss_rng_advance", "ss_stream_read", "ss_status_str"]
 
@@ -230,6 +234,17 @@ def ss_sample_step(logits, dreq: DeviceRequests, rng, out_tokens, out_topk_ids=N
                             ctypes.byref(dreq.aux), ptr(rng), rng_advance, ptr(out_tokens), ptr(out_topk_ids),
                             ptr(out_probs), ptr(out_kept), ptr(out_mass), ptr(out_status), ptr(ws),
                             0 if ws is None else ws.numel(), stream_handle(stream))
+    return _check(rc)
+
+
+def ss_sample_step_noalloc(logits, dreq: DeviceRequests, rng, out_tokens, out_topk_ids=None, out_probs=None,
+                           out_kept=None, out_mass=None, out_status=None, stream=None,
+                           rng_advance: int = 0) -> int:
+    B, V = logits.shape
+    rc = lib.ss_sample_step_noalloc(ptr(logits), dtype_code(logits), B, V, logits.stride(0), ptr(dreq.req),
+                                    ctypes.byref(dreq.aux), ptr(rng), rng_advance, ptr(out_tokens),
+                                    ptr(out_topk_ids), ptr(out_probs), ptr(out_kept), ptr(out_mass),
+                                    ptr(out_status), stream_handle(stream))
     return _check(rc)
 
 

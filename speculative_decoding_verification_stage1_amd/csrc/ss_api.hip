@@ -1,11 +1,19 @@
 // libss: C ABI entry points (declared in include/ss.h).  Host code checks
 // the arguments, carves the caller's workspace and queues fixed-grid
 // kernels on the caller's stream; it never allocates or synchronises.
+#include <mutex>
+
 #include "ss_kernels.h"
 #include "ss_dense.h"
 #include "ss_radix.h"
 
 using namespace ssd;
+
+// The workspace of ss_sample_step_noalloc: a file-scope device array, one
+// copy per GPU, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: kernels receive the address that
+// hipGetSymbolAddress returns for the current device (noalloc_scratch).
+static __device__ __align__(256) unsigned char scratch[SS_NOALLOC_WS_BYTES];
 
 namespace {
 
@@ -126,6 +134,32 @@ Stage2Params make_s2(const Stage1Params& s1, const ss_rng* rng, int mode, const 
     return f;
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex noalloc_mu;
+void* noalloc_ptr[NOALLOC_MAX_DEVICES];
+
+int noalloc_scratch(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return SS_ERR_HIP;
+    }
+    if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return SS_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(noalloc_mu);
+    if (!noalloc_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return SS_ERR_HIP;
+        }
+        noalloc_ptr[dev] = p;
+    }
+    *out = noalloc_ptr[dev];
+    return SS_OK;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -228,6 +262,7 @@ const char* ss_status_str(int status) {
         case SS_ERR_UNSUPPORTED: return "unsupported dtype, size or gamma";
         case SS_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
         case SS_ERR_HIP: return "kernel launch failed";
+        case SS_ERR_NOALLOC_LIMIT: return "call needs more workspace than the allocation-free entry point holds";
         default: return "unknown status";
     }
 }
@@ -260,6 +295,27 @@ int ss_sample_step(const void* logits, int dtype, int B, int V, int64_t ld, cons
     f.status = out_status;
     launch_stage2<MODE_SAMPLE>(dtype, f, s);
     return launched();
+}
+
+int ss_sample_step_noalloc(const void* logits, int dtype, int B, int V, int64_t ld, const ss_req* req,
+                           const ss_aux* aux, ss_rng* rng, uint64_t rng_advance, int32_t* out_tokens,
+                           int32_t* out_topk_ids, float* out_probs, int32_t* out_kept, float* out_mass,
+                           int32_t* out_status, void* stream) {
+    // the same checks as ss_sample_step first, so that argument errors keep
+    // their codes; then the size limit of the static workspace
+    int rc = check_logits(logits, dtype, B, V, ld);
+    if (rc) return rc;
+    if ((rc = check_aux(aux, V))) return rc;
+    if (B == 0) return SS_OK;
+    if (!req || !rng || !out_tokens) return SS_ERR_INVALID_ARG;
+    const size_t need = ss_workspace_bytes(B, V, dtype);
+    if (need > (size_t)SS_NOALLOC_WS_BYTES) return SS_ERR_NOALLOC_LIMIT;
+    void* ws = nullptr;
+    if ((rc = noalloc_scratch(&ws))) return rc;
+    // sampling reads nothing from the workspace that the same call did not
+    // write first, so the array needs no clearing
+    return ss_sample_step(logits, dtype, B, V, ld, req, aux, rng, rng_advance, out_tokens, out_topk_ids, out_probs,
+                          out_kept, out_mass, out_status, ws, (size_t)SS_NOALLOC_WS_BYTES, stream);
 }
 
 int ss_verify_step(const void* target_logits, int dtype, int B, int gamma, int V, int64_t ld,

@@ -115,6 +115,14 @@ def test_argument_errors_return_before_launch(L):
                               fake, 10**9, P) == L.SS_ERR_INVALID_ARG
     # B = 0 is a no-op
     assert lib.ss_sample_step(fake, 1, 0, 100, 100, P, None, P, 0, P, P, P, P, P, P, P, 0, P) == L.SS_OK
+    # the allocation-free variant: same argument checks, then its size limit
+    assert lib.ss_sample_step_noalloc(fake, 5, 4, 100, 100, fake, None, fake, 0, fake, P, P, P, P, P, P) == L.SS_ERR_UNSUPPORTED
+    assert lib.ss_sample_step_noalloc(fake, 1, 4, 100, 100, P, None, fake, 0, fake, P, P, P, P, P, P) == L.SS_ERR_INVALID_ARG
+    assert lib.ss_sample_step_noalloc(fake, 1, 0, 100, 100, P, None, P, 0, P, P, P, P, P, P, P) == L.SS_OK
+    assert L.ss_workspace_bytes(2048, 1 << 18, L.SS_F32) > L.NOALLOC_WS_BYTES
+    assert lib.ss_sample_step_noalloc(fake, 0, 2048, 1 << 18, 1 << 18, fake, None, fake, 0, fake, P, P, P, P, P,
+                                      P) == L.SS_ERR_NOALLOC_LIMIT
+    assert lib.ss_status_str(L.SS_ERR_NOALLOC_LIMIT).startswith(b"call needs more workspace")
     # verify: gamma range
     assert lib.ss_verify_step(fake, 1, 2, 0, 100, 100, fake, None, fake, 0, fake, fake, fake, fake, P, fake, 10**9, P) == L.SS_ERR_UNSUPPORTED
     assert lib.ss_verify_step(fake, 1, 2, 17, 100, 100, fake, None, fake, 0, fake, fake, fake, fake, P, fake, 10**9, P) == L.SS_ERR_UNSUPPORTED
