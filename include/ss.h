@@ -157,13 +157,11 @@ typedef struct ss_aux {
 
 /* Bytes of workspace a call over `rows` logits rows of width V needs (rows
  * = B for sampling and top-k, B*(gamma+1) for verification).  Pure host
- * function; the workspace must be 256-byte aligned.  Its first 4096 bytes
- * hold per-request decision words of verification (used when B <= 512)
- * and must be zero before the workspace's first use, e.g. a zero-filled
- * allocation; every entry point leaves them zero (also under graph
- * replay), so one workspace can serve any sequence of calls.  The rest
- * needs no initialisation.  Calls that share a workspace must not overlap
- * in time. */
+ * function; the workspace must be 256-byte aligned and needs no
+ * initialisation (its first 4096 bytes hold verification's per-request
+ * decision words, which each verification step clears in its first launch).
+ * One workspace can serve any sequence of calls and graph replays; calls
+ * that share a workspace must not overlap in time. */
 size_t ss_workspace_bytes(int rows, int V, int dtype);
 
 /* Vocabulary tile width used for `dtype` (B_N of the two-stage top-k). */
@@ -323,7 +321,9 @@ int ss_topk_single_pass(const void* logits, int dtype, int B, int V, int64_t ld,
  * token ids, [rows, ceil(V/tile), 128] int32 (-1 where a tile has fewer).
  * Tokens named by an active penalty or bias list are left out of the
  * tiles (they are ranked in Stage 2).  `rows_per_req` maps row r to
- * request r / rows_per_req (1 for sampling).  req and aux may be NULL. */
+ * request r / rows_per_req (1 for sampling).  req and aux may be NULL; with
+ * req the launch also ranks the rows' listed tokens into the workspace,
+ * which makes it the same launch as the sampling step's first one. */
 int ss_tile_topk(const void* logits, int dtype, int rows, int V, int64_t ld, int rows_per_req,
                  const ss_req* req, const ss_aux* aux, int32_t* out_ids,
                  void* ws, size_t ws_bytes, void* stream);

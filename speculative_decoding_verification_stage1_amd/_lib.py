@@ -205,12 +205,16 @@ def make_rng(seed: int = 0, offset: int = 0, device="cuda"):
     return torch.from_numpy(a.copy()).to(device)
 
 
-def workspace(rows: int, V: int, dtype: int, device="cuda"):
-    """A zero-filled workspace (the library keeps its counters at zero
-    between calls; torch allocations are 256-byte aligned)."""
+def workspace(rows: int, V: int, dtype: int, device="cuda", fill: int | None = None):
+    """A workspace for `rows` rows of width V (torch allocations are
+    256-byte aligned; the library needs no initialisation).  `fill` sets
+    every byte, for tests that the library reads nothing it did not write."""
     import torch
     n = int(lib.ss_workspace_bytes(rows, V, dtype))
-    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+    t = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    if fill is not None:
+        t.fill_(fill)
+    return t
 
 
 def dtype_code(t) -> int:
@@ -270,11 +274,15 @@ def ss_verify_step_var(target, B: int, gamma: int, dreq: DeviceRequests, rng, cu
     return _check(rc)
 
 
-def dense_workspace(B: int, gamma: int, V: int, device="cuda"):
-    """Workspace of ss_verify_step_dense (256-byte aligned torch allocation)."""
+def dense_workspace(B: int, gamma: int, V: int, device="cuda", fill: int | None = None):
+    """Workspace of ss_verify_step_dense (256-byte aligned torch allocation,
+    no initialisation needed; `fill` as for workspace())."""
     import torch
     n = int(lib.ss_verify_dense_workspace_bytes(B, gamma, V))
-    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+    t = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    if fill is not None:
+        t.fill_(fill)
+    return t
 
 
 def ss_verify_step_dense(target, B: int, gamma: int, dreq: DeviceRequests, rng, draft_ids, draft_probs,

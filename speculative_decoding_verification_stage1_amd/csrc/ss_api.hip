@@ -32,10 +32,8 @@ size_t rec_bytes(int rows) { return align256((size_t)rows * sizeof(RowRec)); }
 size_t listed_bytes(int rows) { return align256((size_t)rows * KMAX * sizeof(uint64_t)); }
 constexpr size_t RNG_SNAP_BYTES = 256;
 // Verification's per-request decision words (64 bits: arrivals and
-// per-position bits), at the start of every workspace layout - the same
-// bytes whatever the call - so that a workspace shared by several entry
-// points keeps them at zero: only verification writes them, and every
-// launch leaves them zero.
+// per-position bits), at the start of the workspace; each verification
+// step zeroes its requests' words in its Stage-1 launch.
 constexpr size_t ARRIVE_BYTES = 4096;
 constexpr int ARRIVE_REQUESTS_MAX = (int)(ARRIVE_BYTES / sizeof(uint64_t));
 
@@ -350,6 +348,10 @@ int ss_verify_step_var(const void* target_logits, int dtype, int B, int gamma, i
     s1.rng = rng;
     s1.rng_snap = W.rng_snap;
     s1.rng_advance = rng_advance;
+    if (B <= ARRIVE_REQUESTS_MAX) {   // Stage 2 decides and emits: its words start at zero
+        s1.clear_words = (uint64_t*)W.arrive;
+        s1.n_clear = B;
+    }
     launch_stage1(dtype, s1, s);
     Stage2Params f = make_s2(s1, W.rng_snap, MODE_VERIFY, W);
     f.gamma = gamma;
@@ -530,6 +532,10 @@ int ss_tile_topk(const void* logits, int dtype, int rows, int V, int64_t ld, int
     hipStream_t s = (hipStream_t)stream;
     const WsLayout W = ws_layout(ws, rows, V, dtype);
     Stage1Params s1 = make_s1(logits, dtype, rows, V, ld, rows_per_req, req, aux, W.scratch, out_ids);
+    if (req) {   // the steps' own Stage-1 launch: the rows' listed tokens are ranked too
+        s1.listed = W.listed;
+        s1.listed_rows = rows;
+    }
     launch_stage1(dtype, s1, s);
     return launched();
 }

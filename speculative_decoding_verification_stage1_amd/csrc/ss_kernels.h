@@ -30,6 +30,11 @@ __global__ __launch_bounds__(S1_THREADS) void stage1_kernel(Stage1Params P) {
         *P.rng_snap = r;
         if (P.rng && P.rng_advance) P.rng->offset = r.offset + P.rng_advance;
     }
+    // verification: the requests' decision words start at zero (Stage 2
+    // adds to them with device-scope atomics after this launch has
+    // completed; device-coherent stores, as for the rest of that hand-off)
+    if (blockIdx.x == 0)
+        for (int i = tid; i < P.n_clear; i += S1_THREADS) store_coherent(P.clear_words + i, (uint64_t)0);
     const int nlw = (P.listed_rows + S1_WAVES - 1) / S1_WAVES;
     if ((int)blockIdx.x < nlw) {
         const int wave = tid / WAVE;

@@ -82,6 +82,8 @@ struct Stage1Params {
     uint64_t rng_advance;   // ... after which rng->offset += rng_advance
     const int32_t* cu_num_draft;   // verification with per-request draft counts (or null)
     const int32_t* draft_ids;      // verification: [requests, rows_per_req - 1] drafts (or null)
+    uint64_t* clear_words;         // verification: decision words zeroed by workgroup 0 (or null)
+    int n_clear;
 };
 
 // Number of earlier drafts in row `row`'s penalty history: its position j

@@ -842,7 +842,8 @@ __device__ __forceinline__ void row_epilogue(const Stage2Params& F, const RowPar
         // 64-bit word; the last arrival has every position's bits from the
         // add's return value, finds where the request stops, and writes -1
         // past it (also device-coherent, so that it lands after the rows'
-        // writes), the count and the status, and clears the word.
+        // writes), the count and the status.  (The step's Stage-1 launch
+        // zeroed the word.)
         if (lane == 0) {
             const int G = F.gamma;
             int32_t* out = F.v_tokens + (int64_t)b * (G + 1);
@@ -871,7 +872,6 @@ __device__ __forceinline__ void row_epilogue(const Stage2Params& F, const RowPar
                 for (int j = emitted; j <= G; ++j) store_coherent(out + j, -1);
                 F.v_n_emit[b] = emitted;
                 if (F.v_status) F.v_status[b] = st;
-                store_coherent(word, (uint64_t)0);
             }
         }
     } else {   // MODE_VERIFY, records for verify_kernel

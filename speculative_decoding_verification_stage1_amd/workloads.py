@@ -254,6 +254,53 @@ def workload_c2(rows: Optional[int] = None) -> SampleWorkload:
     return workload_mixed(2, 256, 262144, grammar=True, rows=rows)
 
 
+STRESS_KINDS = ("logprob", "sparse_grammar", "listed_tile")
+
+
+def workload_c2_stress(kind: str, rows: Optional[int] = None, B: int = 256, V: int = 262144) -> SampleWorkload:
+    """c2's batch (B=256, V=2^18 bf16, the same per-request settings) with
+    one thing changed, to exercise the tile stage off its usual path:
+
+    * ``logprob``: every row replaced by its log-softmax (float64
+      log-sum-exp, rounded to fp32 then bf16), so that every logit is
+      negative, as when the sampler is fed log-probabilities;
+    * ``sparse_grammar``: grammar bitmask with 0.1 % of the tokens allowed
+      (Bernoulli(0.001), one of the raw top-10 forced allowed): about 33
+      allowed tokens per 32768-token tile;
+    * ``listed_tile``: no grammar; each request's prior list holds 200
+      distinct ids drawn from [0, 32768) with counts U{1..5} (plus the 16
+      bias ids anywhere), so one vocabulary tile holds more than 128 tokens
+      named by the lists.
+    """
+    if kind not in STRESS_KINDS:
+        raise ValueError(kind)
+    n = B if rows is None else rows
+    rng = np.random.default_rng(data_seed(2))
+    raw = peaked_logits(rng, n, V)
+    req = mixed_requests(rng, n, V)
+    req.bitmask = grammar_bitmask(rng, raw)
+    req.use_grammar = np.ones(n, bool)
+    rs = np.random.default_rng(data_seed(2) + 100 + STRESS_KINDS.index(kind))
+    if kind == "logprob":
+        x = raw.astype(np.float64)
+        m = x.max(axis=1, keepdims=True)
+        lse = m + np.log(np.exp(x - m).sum(axis=1, keepdims=True))
+        raw = (x - lse).astype(np.float32)
+    elif kind == "sparse_grammar":
+        req.bitmask = grammar_bitmask(rs, raw, allowed_frac=0.001)
+    else:
+        req.bitmask = None
+        req.use_grammar = np.zeros(n, bool)
+        P = 200
+        req.prior_ids = np.full((n, P), -1, np.int32)
+        req.prior_cnt = np.zeros((n, P), np.int32)
+        for r in range(n):
+            req.prior_ids[r] = rs.choice(min(32768, V), size=P, replace=False)
+            req.prior_cnt[r] = rs.integers(1, 6, size=P)
+        req.n_prior = np.full(n, P, np.int32)
+    return SampleWorkload(f"c2-{kind}", DTYPE_BF16, to_bf16_bits(raw), req)
+
+
 @dataclasses.dataclass
 class VerifyWorkload:
     name: str

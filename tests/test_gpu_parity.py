@@ -48,7 +48,7 @@ def run_sample(logits_np, dtype, req, seed=0, offset=0, flags=None):
                kept=torch.full((B,), -7, dtype=torch.int32, device="cuda"),
                mass=torch.full((B,), -7.0, dtype=torch.float32, device="cuda"),
                status=torch.full((B,), -7, dtype=torch.int32, device="cuda"))
-    ws = lib.workspace(B, V, dtype)
+    ws = lib.workspace(B, V, dtype, fill=0xA7)   # garbage: nothing may be read before it is written
     lib.ss_sample_step(x, dreq, rng, out["tokens"], out["topk_ids"], out["probs"], out["kept"],
                        out["mass"], out["status"], ws)
     torch.cuda.synchronize()
@@ -139,7 +139,7 @@ def run_sample_strided(logits_np, dtype, req, ld, seed=0, offset=0):
                kept=torch.full((B,), -7, dtype=torch.int32, device="cuda"),
                mass=torch.full((B,), -7.0, dtype=torch.float32, device="cuda"),
                status=torch.full((B,), -7, dtype=torch.int32, device="cuda"))
-    ws = lib.workspace(B, V, dtype)
+    ws = lib.workspace(B, V, dtype, fill=0xA7)   # garbage: nothing may be read before it is written
     lib.ss_sample_step(x, dreq, rng, out["tokens"], out["topk_ids"], out["probs"], out["kept"],
                        out["mass"], out["status"], ws)
     torch.cuda.synchronize()
@@ -327,7 +327,7 @@ def run_verify(wl, seed=0, offset=0, rng_advance=0, cu_num_draft=None, flags=Non
     toks = torch.full((B, G + 1), -7, dtype=torch.int32, device="cuda")
     ne = torch.full((B,), -7, dtype=torch.int32, device="cuda")
     st = torch.full((B,), -7, dtype=torch.int32, device="cuda")
-    ws = lib.workspace(rows, V, wl.dtype)
+    ws = lib.workspace(rows, V, wl.dtype, fill=0xA7)   # garbage, decision words included
     if cu_num_draft is None:
         lib.ss_verify_step(x, B, G, dreq, rng, d, q, toks, ne, st, ws, rng_advance=rng_advance)
     else:
@@ -366,8 +366,9 @@ def test_verify_request_count_limit(B):
 
 def test_verify_graph_replays():
     """Bounded verification captured once and replayed: every replay uses
-    the offset it finds and matches the oracle (the per-request arrival
-    counters are back at zero after each launch)."""
+    the offset it finds and matches the oracle, also when the workspace
+    (decision words included) is overwritten with garbage between
+    replays."""
     lib = L()
     wl = W.workload_verify(B=12, gamma=3, V=30000)
     x = _dev_logits(wl.target, wl.dtype)
@@ -377,7 +378,7 @@ def test_verify_graph_replays():
     q = torch.from_numpy(np.ascontiguousarray(wl.draft_probs, np.float32)).cuda()
     toks = torch.zeros((wl.B, wl.gamma + 1), dtype=torch.int32, device="cuda")
     ne = torch.zeros(wl.B, dtype=torch.int32, device="cuda")
-    ws = lib.workspace(rows, V, wl.dtype)
+    ws = lib.workspace(rows, V, wl.dtype, fill=0xFF)
     rng = lib.make_rng(9, 0)
     s = torch.cuda.Stream()
     torch.cuda.synchronize()
@@ -393,21 +394,21 @@ def test_verify_graph_replays():
                           seed=9, offset=20 + i, threads=16)
         assert np.array_equal(toks.cpu().numpy(), o["tokens"]), i
         assert np.array_equal(ne.cpu().numpy(), o["n_emit"]), i
-        assert int(ws[:4096].count_nonzero()) == 0, i
+        ws.fill_(0x5A + i)
         _ = (x.float().sum()).item()
 
 
 def test_workspace_shared_across_entry_points():
-    """One zero-filled workspace serves verification, top-k and sampling in
-    turn: the arrival counters at its start are zero after every call, and
-    every call matches the oracle."""
+    """One workspace, filled with garbage at the start, serves verification,
+    top-k and sampling in turn, and every call matches the oracle (each
+    verification step clears its own decision words)."""
     lib = L()
     sw = W.workload_mixed(2, 24, 70000, grammar=True)
     vw = W.workload_verify(B=6, gamma=4, V=70000)
     rows_v = vw.B * (vw.gamma + 1)
     n = max(int(lib.lib.ss_workspace_bytes(rows_v, 70000, W.DTYPE_F32)),
             int(lib.lib.ss_workspace_bytes(sw.logits.shape[0], 70000, sw.dtype)))
-    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    ws = torch.full((n,), 0xC3, dtype=torch.uint8, device="cuda")
     xs = _dev_logits(sw.logits, sw.dtype)
     dreq = lib.DeviceRequests(sw.req)
     ref = oracle.sample(sw.logits, sw.dtype, sw.req, seed=11, offset=3, threads=16)
@@ -427,15 +428,12 @@ def test_workspace_shared_across_entry_points():
     for i in range(3):
         lib.ss_verify_step(xv, vw.B, vw.gamma, vreq, lib.make_rng(1, 1), d, q, vt, ve, None, ws)
         torch.cuda.synchronize()
-        assert int(ws[:4096].count_nonzero()) == 0, ("after verify", i)
         assert np.array_equal(vt.cpu().numpy(), vref["tokens"]), i
         lib.ss_topk_step(kx, 128, kid, ws=ws)
         torch.cuda.synchronize()
-        assert int(ws[:4096].count_nonzero()) == 0, ("after top-k", i)
         assert np.array_equal(kid.cpu().numpy(), kref), i
         lib.ss_sample_step(xs, dreq, lib.make_rng(11, 3), toks, ws=ws)
         torch.cuda.synchronize()
-        assert int(ws[:4096].count_nonzero()) == 0, ("after sample", i)
         assert np.array_equal(toks.cpu().numpy(), ref["tokens"]), i
 
 
@@ -625,7 +623,7 @@ def run_verify_dense(target_np, dtype, B, G, req, draft_ids, draft_probs, seed=0
     toks = torch.full((B, G + 1), -7, dtype=torch.int32, device="cuda")
     ne = torch.full((B,), -7, dtype=torch.int32, device="cuda")
     st = torch.full((B,), -7, dtype=torch.int32, device="cuda")
-    ws = lib.dense_workspace(B, G, V)
+    ws = lib.dense_workspace(B, G, V, fill=0xA7)
     lib.ss_verify_step_dense(x, B, G, dreq, rng, d, q, toks, ne, st, ws, cu_num_draft=cu, rng_advance=rng_advance)
     torch.cuda.synchronize()
     return dict(tokens=toks.cpu().numpy(), n_emit=ne.cpu().numpy(), status=st.cpu().numpy(),
@@ -892,6 +890,7 @@ def test_graph_replay_dense_verify_and_radix_topk():
         torch.cuda.synchronize()
         o = oracle.verify_dense(z, W.DTYPE_F32, B, G, req, d, q, seed=5, offset=i, threads=16)
         ok = o["fragile"] == 0
+        assert (~ok).sum() <= 2, ((~ok).sum(), i)
         assert np.array_equal(toks.cpu().numpy()[ok], o["tokens"][ok]), i
         assert np.array_equal(ne.cpu().numpy()[ok], o["n_emit"][ok]), i
         assert np.array_equal(ids.cpu().numpy(), ref_ids), i
