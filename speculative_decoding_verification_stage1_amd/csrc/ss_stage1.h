@@ -13,23 +13,38 @@
 // token" (tail of a short tile).  Ties in value therefore rank the lower
 // token id first, the order used throughout.
 //
-// Selection is exact.  Fast path: raw bit patterns read as signed integers
-// order like the floats they hold whenever the threshold below is positive,
-// so no per-element key transform is needed.  Grammar-masked elements and
-// those past the end of V take the smallest pattern.  Each lane holds 16
-// chunks of 16 bytes and takes the maximum of every chunk and of its whole
-// slice; each wave finds the k-th largest of its 64 lane maxima, k = 32 +
-// ceil(L/4) for L listed tokens in the tile, and the smallest of the four is
-// a threshold tau with at least 128 + L tokens at or above it - so the 128
-// best unlisted tokens are all at or above tau.  Chunks whose maximum
-// reaches tau (typically a few dozen per wave) are copied from registers to
-// the wave's LDS area; each lane then takes one such chunk, and its elements
-// >= tau that are not listed become keys, one per lane per round.  Each
-// wave sorts its keys in registers, and a two-level merge tree gives the
-// tile's 128.  Tiles where the test does not apply (tau <= 0, a positive
-// NaN, more listed tokens or survivors than the LDS areas hold) take the
-// general path: exact keys for every element and a bisection for the 128th
-// key.
+// Selection is exact, and on the common paths every element stays in
+// registers after its one load.  Each lane holds 16 chunks of 16 bytes and takes the maximum of
+// every chunk and of its whole slice; each wave finds the k-th largest of
+// its 64 lane maxima, k = 32 + ceil(L/4) for L listed tokens still in the
+// data, and the smallest of the four is a threshold tau with at least 128 +
+// L tokens at or above it - so the 128 best unlisted tokens are all at or
+// above tau.  Chunks whose maximum reaches tau (typically a few dozen per
+// wave) are copied from registers to the wave's LDS area; each lane then
+// takes one such chunk, and its elements >= tau that are not listed become
+// keys, one per lane per round.  Each wave sorts its keys in registers, and
+// a two-level merge tree gives the tile's 128.
+//
+// The comparisons run on one of two value forms held in the registers:
+//   raw    the bit patterns read as signed integers; they order like the
+//          floats only among positive values, so this form is used when
+//          tau >= 1 (the usual case for logits);
+//   order  the two's-complement order value v >= 0 ? v : -(v & magnitude)
+//          of the bit pattern (bf16: per 16-bit half), which orders like
+//          the floats over the whole range with -0 equal to +0; used when
+//          the raw threshold is not positive (log-probabilities, sparse
+//          grammars), with tau raised to the most negative finite value.
+//          If fewer than 128 finite tokens remain (a grammar allowing few
+//          tokens), the tile's remaining ranks are its -inf tokens (masked,
+//          -inf or NaN) in id order.
+// Masked tokens become all-ones patterns (a negative NaN: below any positive
+// raw threshold, below -inf in the order form); elements past the end of V
+// hold the smallest pattern.  Tiles with a positive NaN, or with more
+// values tied near the threshold than the LDS areas hold, and rows that do
+// not start on a 16-byte boundary take the exact path from memory
+// (tile_exact_mem): the tile is read again, a radix select over LDS
+// histograms finds the 128th value, and ties at it are taken in token
+// order.
 #pragma once
 
 #include "ss_device.h"
@@ -46,21 +61,27 @@ constexpr int S1_WAVES = S1_THREADS / WAVE;
 constexpr int S1_CPT = 16;            // 16-byte chunks per thread
 constexpr int S1_CCAP = 128;          // flagged chunks held per wave (fast path)
 constexpr int S1_KCAP = 256;          // survivors held per wave (fast path)
-constexpr int S1_LIST_CAP = 528;      // >= 255 prior + 255 bias entries + SS_GAMMA_MAX drafts
-constexpr int S1_NL_FAST = 128;       // listed tokens per tile the fast path absorbs
+constexpr int S1_LIST_W = 2 * WAVE + SS_GAMMA_MAX;   // listed tokens one wave records: 64 prior, 64 bias, drafts
+constexpr int S1_NL_FAST = 128;       // listed tokens per tile left in the data (more are masked out)
 
 template <int DT> struct S1Traits;
 template <> struct S1Traits<SS_BF16> {
     using Key = uint32_t;
     static constexpr int EPC = 8;                            // elements per chunk
     static constexpr int BN = EPC * S1_CPT * S1_THREADS;     // tile width 32768
-    static constexpr int VAL_BITS = 16;                      // fast-path value range (int16)
+    static constexpr int VAL_BITS = 16;                      // value range (int16)
+    static constexpr int FINITE_MIN = -0x7F7F;               // order value of the most negative finite
+    static constexpr int NINF_V = -0x7F80;                   // order value of -inf
+    static constexpr int PINF_V = 0x7F80;                    // order value of +inf (kept: ranks above finite)
 };
 template <> struct S1Traits<SS_F32> {
     using Key = uint64_t;
     static constexpr int EPC = 4;
     static constexpr int BN = EPC * S1_CPT * S1_THREADS;     // 16384
     static constexpr int VAL_BITS = 32;
+    static constexpr int FINITE_MIN = -0x7F7FFFFF;
+    static constexpr int NINF_V = -0x7F800000;
+    static constexpr int PINF_V = 0x7F7FFFFF;                // +inf counts as FLT_MAX
 };
 
 struct Stage1Params {
@@ -151,33 +172,56 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
     return before + incl - v;
 }
 
-// Exact key of one element of a bf16 tile.
-__device__ __forceinline__ uint32_t key_bf16(uint32_t raw16, int local, bool present, bool allowed) {
-    if (!present) return 0u;
-    const uint32_t k16 = allowed ? ord16_canon(raw16) : K16_NINF;
-    return (k16 << 16) | (0xFFFFu - (uint32_t)local);
+// Two's-complement order value of a raw pattern (bf16: of each 16-bit
+// half): v >= 0 ? v : -(v & magnitude).  Monotone in the float value, with
+// -0 and +0 equal.
+template <int DT>
+__device__ __forceinline__ uint32_t order_value(uint32_t x) {
+    if constexpr (DT == SS_BF16) {
+        const s16x2 s = bits_s16x2(x) >> (s16x2){15, 15};   // -1 on negative halves
+        const s16x2 t = bits_s16x2(x & 0x7FFF7FFFu) ^ s;
+        return s16x2_bits(t - s);
+    } else {
+        const int32_t s = (int32_t)x >> 31;
+        return (uint32_t)((((int32_t)(x & 0x7FFFFFFFu)) ^ s) - s);
+    }
 }
-__device__ __forceinline__ uint64_t key_f32(uint32_t raw, int local, bool present, bool allowed) {
-    if (!present) return 0ull;
-    const uint32_t k32 = allowed ? ord32(canon(bitsf(raw))) : ord32(bitsf(F32_NINF_BITS));
-    return ((uint64_t)k32 << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)local);
+
+// Packed key of a present element from its (finite or +inf) value in either
+// register form - a positive raw pattern is its own order value - and its
+// index in the tile.
+template <int DT>
+__device__ __forceinline__ typename S1Traits<DT>::Key value_key(int v, int local) {
+    if constexpr (DT == SS_BF16) {
+        const uint32_t k16 = (uint32_t)(v + 0x8000 - (v < 0 ? 1 : 0));
+        return (k16 << 16) | (0xFFFFu - (uint32_t)local);
+    } else {
+        const uint32_t k32 = (uint32_t)min(v, S1Traits<SS_F32>::PINF_V) + 0x80000000u - (v < 0 ? 1u : 0u);
+        return ((uint64_t)k32 << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)local);
+    }
+}
+template <int DT>
+__device__ __forceinline__ typename S1Traits<DT>::Key ninf_key(int local) {
+    return value_key<DT>(S1Traits<DT>::NINF_V, local);
 }
 
 template <int DT>
 struct S1Shared {
     using Key = typename S1Traits<DT>::Key;
-    uint4 chunks[S1_WAVES][S1_CCAP + WAVE];   // flagged chunks, per wave (fast path)
+    uint4 chunks[S1_WAVES][S1_CCAP + WAVE];   // flagged chunks, per wave (fast path); exact path: bitmap
     int cid[S1_WAVES][S1_CCAP + WAVE];        // their chunk index in the tile
-    Key keys[S1_WAVES][S1_KCAP];       // survivors per wave (fast path); general path: flat
+    Key keys[S1_WAVES][S1_KCAP];       // survivors per wave (fast path); exact path: flat
     Key wl[S1_WAVES][KMAX];            // per-wave sorted lists
-    Key surv[KMAX];                    // result: the tile's 128 best, sorted
-    uint4 gtab[256];                   // bf16 grammar: dword masks of a chunk by its allowed byte
-    uint32_t gmw[S1Traits<DT>::BN / 32];   // the tile's grammar bitmask
-    int listed[S1_LIST_CAP];           // tile-local index of each listed token
-    int2 lcb[S1_LIST_CAP];             // its chunk, and its bit in a chunk's survivor mask
-    int nl;
+    Key surv[KMAX];                    // result: the tile's 128 best, sorted; -inf ranks of sparse tiles
+    uint4 gtab[256];                   // bf16 masks: dword keep masks of a chunk by its allowed byte
+    uint32_t gmw[S1Traits<DT>::BN / 32];   // the tile's mask (grammar and/or listed tokens)
+    int listed[S1_WAVES][S1_LIST_W];   // tile-local index of each listed token, per recording wave
+    int2 lcb[S1_WAVES][S1_LIST_W];     // its chunk, and its bit in a chunk's survivor mask
+    alignas(16) int nlw[S1_WAVES];
     int tau[S1_WAVES];
+    int tau2[S1_WAVES];
     int special[S1_WAVES];
+    int nk[S1_WAVES];
     int ovf;
     int scan[S1_WAVES];
     int red[2][S1_WAVES];
@@ -223,7 +267,7 @@ __device__ __forceinline__ int chunk_elem(int p) {
     if constexpr (DT == SS_BF16) return 2 * (15 - (p & 15)) + (p >> 4);
     else return p;
 }
-// Elements of a chunk whose value (raw pattern read as signed) is >= tau.
+// Elements of a chunk whose value (in its register form) is >= tau.
 template <int DT>
 __device__ __forceinline__ uint32_t chunk_survivors(const uint4& d, int tau) {
     if constexpr (DT == SS_BF16) {
@@ -246,7 +290,7 @@ template <int DT>
 struct S1In {
     uint32_t raw[S1_CPT * 4];   // dword q: dword (q & 3) of this thread's chunk (q >> 2)
     uint32_t gw[S1_CPT * S1Traits<DT>::EPC / 32];   // the tile's bitmask words tid + 256k
-    int l_pid, l_pct, l_bid;    // lead wave: first 64 entries of the request's lists
+    int l_pid, l_pct, l_bid;    // entries 64lw .. 64lw+63 of the request's lists (lw: wave after the lead)
     int l_did;                  // lead wave: draft `lane` of the request (verification), or -1
     uint32_t rq_flags, rq_lists; // the request's flags and its n_prior | n_bias << 8
 };
@@ -273,7 +317,7 @@ __device__ __forceinline__ int s1_lead_wave() { return (int)((blockIdx.x >> 3) &
     const bool full = (nvalid == BN);                                                \
     const bool vec = full && P.aligned16;                                            \
     const char* rowp = (const char*)P.logits + ((int64_t)row * P.ld + base) * (DT == SS_BF16 ? 2 : 4); \
-    (void)wave; (void)lead; (void)lane; (void)b; (void)vec; (void)NQ; (void)PAD;
+    (void)wave; (void)lead; (void)lane; (void)b; (void)vec; (void)NQ; (void)PAD; (void)full;
 
 // Dword q of this thread's slice (chunk q >> 2, dword q & 3); elements past
 // the end of V read as the smallest signed pattern.
@@ -299,18 +343,21 @@ __device__ __forceinline__ uint32_t tile_dword(const char* rowp, bool vec, int n
 template <int DT>
 __device__ __forceinline__ void tile_fetch(const Stage1Params& P, int row, int tile, S1In<DT>& in) {
     S1_TILE_GEOMETRY
-    // the lead wave: the first 64 entries of the request's lists
+    // the wave lw places after the lead (lw = 0: the lead): entries 64lw ..
+    // 64lw+63 of the request's lists
     in.l_pid = -1;
     in.l_pct = 0;
     in.l_bid = -1;
-    if (wave == lead) {
-        if (P.aux.prior_ids && P.aux.prior_cnt && lane < P.aux.prior_stride) {
-            const int64_t o = (int64_t)b * P.aux.prior_stride + lane;
+    {
+        const int j0 = ((wave - lead) & (S1_WAVES - 1)) * WAVE;   // wave-uniform
+        const int j = j0 + lane;
+        if (P.aux.prior_ids && P.aux.prior_cnt && j0 < P.aux.prior_stride && j < P.aux.prior_stride) {
+            const int64_t o = (int64_t)b * P.aux.prior_stride + j;
             in.l_pid = gmem(P.aux.prior_ids)[o];
             in.l_pct = gmem(P.aux.prior_cnt)[o];
         }
-        if (P.aux.bias_ids && lane < P.aux.bias_stride)
-            in.l_bid = gmem(P.aux.bias_ids)[(int64_t)b * P.aux.bias_stride + lane];
+        if (P.aux.bias_ids && j0 < P.aux.bias_stride && j < P.aux.bias_stride)
+            in.l_bid = gmem(P.aux.bias_ids)[(int64_t)b * P.aux.bias_stride + j];
     }
     in.l_did = -1;
     if (wave == lead && P.draft_ids) {   // drafts before this row's position (read if the flag asks)
@@ -358,21 +405,21 @@ __device__ __forceinline__ void tile_fetch(const Stage1Params& P, int row, int t
 
 // Tiles that are not whole 16-byte chunks of an aligned row: chunks not
 // wholly inside V become PAD, and the one that straddles the end is
-// completed by its owner thread from the elements inside V (rows that do
-// not start on a 16-byte boundary are all PAD: the exact general path reads
-// their elements itself).  Waits for the tile's loads, so full tiles skip it.
+// completed by its owner thread from the elements inside V.  Waits for the
+// tile's loads, so full aligned tiles skip it.  (Rows that do not start on
+// a 16-byte boundary load nothing here: the exact path reads them.)
 template <int DT>
 __device__ __forceinline__ void tile_patch(const Stage1Params& P, int row, int tile, S1In<DT>& in) {
     S1_TILE_GEOMETRY
     if (vec) return;
-    const int cp = P.aligned16 ? nvalid / EPC : 0;   // first chunk not wholly inside V
+    if (!P.aligned16) return;   // read by the exact path instead
+    const int cp = nvalid / EPC;   // first chunk not wholly inside V
 #pragma unroll
     for (int j = 0; j < CPT; ++j)
         if (j * S1_THREADS + tid >= cp) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) in.raw[4 * j + k] = PAD;
         }
-    if (!P.aligned16) return;
     const int rem = nvalid - cp * EPC;   // its elements inside V
     if (rem == 0 || (cp & (S1_THREADS - 1)) != tid) return;
     uint32_t pv[4] = {PAD, PAD, PAD, PAD};
@@ -397,21 +444,356 @@ __device__ __forceinline__ void tile_patch(const Stage1Params& P, int row, int t
         }
 }
 
+// Keep masks of this thread's chunk j from an LDS bitmap laid out like the
+// grammar bitmask (bit e of byte c: element e of chunk c): per dword, all
+// ones on the elements whose bit is set (clear, with `invert`).  bf16 goes
+// through the 256-entry table of dword masks.
+template <int DT>
+__device__ __forceinline__ uint4 chunk_keep(const S1Shared<DT>& sh, const uint32_t* bm, int j, bool invert) {
+    const uint8_t* by = (const uint8_t*)bm;
+    const int c = j * S1_THREADS + (int)threadIdx.x;
+    if constexpr (DT == SS_BF16) {
+        const uint32_t g = by[c] ^ (invert ? 0xFFu : 0u);
+        return sh.gtab[g];
+    } else {
+        const uint32_t g = ((uint32_t)by[c >> 1] >> ((c & 1) * 4)) ^ (invert ? 0xFu : 0u);
+        return make_uint4(0u - (g & 1u), 0u - ((g >> 1) & 1u), 0u - ((g >> 2) & 1u), 0u - ((g >> 3) & 1u));
+    }
+}
+
+// chunk_keep from the bitmap byte alone, without the table (the rarely
+// taken paths use it: table reads there cost the kernel registers).
+template <int DT>
+__device__ __forceinline__ uint4 chunk_keep_alu(const uint32_t* bm, int j, bool invert) {
+    const uint8_t* by = (const uint8_t*)bm;
+    const int c = j * S1_THREADS + (int)threadIdx.x;
+    if constexpr (DT == SS_BF16) {
+        const uint32_t g = by[c] ^ (invert ? 0xFFu : 0u);
+        uint32_t mk[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            mk[k] = ((0u - ((g >> (2 * k)) & 1u)) & 0x0000FFFFu) | ((0u - ((g >> (2 * k + 1)) & 1u)) & 0xFFFF0000u);
+        return make_uint4(mk[0], mk[1], mk[2], mk[3]);
+    } else {
+        const uint32_t g = ((uint32_t)by[c >> 1] >> ((c & 1) * 4)) ^ (invert ? 0xFu : 0u);
+        return make_uint4(0u - (g & 1u), 0u - ((g >> 1) & 1u), 0u - ((g >> 2) & 1u), 0u - ((g >> 3) & 1u));
+    }
+}
+
+// Elements of a ragged tile past the end of V take PAD (any register form).
+template <int DT>
+__device__ __forceinline__ void pad_absent(uint32_t (&raw)[S1_CPT * 4], int nvalid) {
+    constexpr int EPC = S1Traits<DT>::EPC;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < S1_CPT; ++j) {
+        const int n = nvalid - (j * S1_THREADS + tid) * EPC;   // elements of the chunk inside V
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if constexpr (DT == SS_BF16) {
+                const uint32_t keep = (2 * k < n ? 0x0000FFFFu : 0u) | (2 * k + 1 < n ? 0xFFFF0000u : 0u);
+                raw[4 * j + k] = (raw[4 * j + k] & keep) | (0x80008000u & ~keep);
+            } else {
+                raw[4 * j + k] = k < n ? raw[4 * j + k] : 0x80000000u;
+            }
+        }
+    }
+}
+
+// Maximum of chunk j (signed, per half for bf16 then both halves).
+template <int DT>
+__device__ __forceinline__ uint32_t chunk_max(const uint32_t (&raw)[S1_CPT * 4], int j) {
+    if constexpr (DT == SS_BF16) {
+        const s16x2 a = __builtin_elementwise_max(bits_s16x2(raw[4 * j]), bits_s16x2(raw[4 * j + 1]));
+        const s16x2 c = __builtin_elementwise_max(bits_s16x2(raw[4 * j + 2]), bits_s16x2(raw[4 * j + 3]));
+        return s16x2_bits(__builtin_elementwise_max(a, c));
+    } else {
+        return (uint32_t)max(max((int)raw[4 * j], (int)raw[4 * j + 1]), max((int)raw[4 * j + 2], (int)raw[4 * j + 3]));
+    }
+}
+// Largest value of the lane (signed); `clamp`: fp32 +inf counts as FLT_MAX.
+template <int DT>
+__device__ __forceinline__ int lane_max(const uint32_t (&cmx)[S1_CPT], bool clamp) {
+    if constexpr (DT == SS_BF16) {
+        s16x2 mm = bits_s16x2(cmx[0]);
+#pragma unroll
+        for (int j = 1; j < S1_CPT; ++j) mm = __builtin_elementwise_max(mm, bits_s16x2(cmx[j]));
+        return max((int)mm.x, (int)mm.y);
+    } else {
+        int m = (int)cmx[0];
+#pragma unroll
+        for (int j = 1; j < S1_CPT; ++j) m = max(m, (int)cmx[j]);
+        return clamp ? min(m, (int)F32_MAX_BITS) : m;
+    }
+}
+
+// The tile's tokens left out of the selection, as a bitmap over the tile
+// (bit (i & 31) of word i >> 5): its listed tokens and the elements past V.
+// Written over the chunk areas; ends with a barrier.
+template <int DT>
+__device__ __forceinline__ uint32_t* exclusion_bitmap(S1Shared<DT>& sh, int nvalid) {
+    constexpr int BN = S1Traits<DT>::BN;
+    static_assert(BN / 32 * 4 <= (int)sizeof(sh.chunks), "exclusion bitmap");
+    uint32_t* ebm = (uint32_t*)&sh.chunks[0][0];
+    for (int i = threadIdx.x; i < BN / 32; i += S1_THREADS) {
+        const int lo = i * 32;
+        ebm[i] = lo + 32 <= nvalid ? 0u : (lo >= nvalid ? ~0u : ~((1u << (nvalid - lo)) - 1u));
+    }
+    __syncthreads();
+    for (int w = 0; w < S1_WAVES; ++w)
+        for (int i = threadIdx.x; i < sh.nlw[w]; i += S1_THREADS)
+            atomicOr(&ebm[sh.listed[w][i] >> 5], 1u << (sh.listed[w][i] & 31));
+    __syncthreads();
+    return ebm;
+}
+
+// Chunks holding a value >= tau (register form of `raw`, chunk maxima
+// `cmx`) go to the wave's LDS area; their elements >= tau that are not
+// among the nl_data listed tokens become keys, one per lane per round; each
+// wave's best 128 go to sh.wl[wave], its survivor count to sh.nk[wave], and
+// sh.ovf is set when a wave has more chunks or survivors than its areas
+// hold.  No barrier.
+template <int DT>
+__device__ __forceinline__ void select_ge(const uint32_t (&raw)[S1_CPT * 4], const uint32_t (&cmx)[S1_CPT], int tau,
+                                          int nl_data, S1Shared<DT>& sh) {
+    using Key = typename S1Traits<DT>::Key;
+    constexpr int EPC = S1Traits<DT>::EPC;
+    const int tid = threadIdx.x;
+    const int wave = tid / WAVE;
+    const int lane = lane_id();
+    int wcnt = 0;
+    const uint32_t T2 = ((uint32_t)(tau - 1) & 0xFFFFu) * 0x10001u;
+#pragma unroll
+    for (int j = 0; j < S1_CPT; ++j) {
+        bool f;
+        if constexpr (DT == SS_BF16)
+            f = s16x2_bits(__builtin_elementwise_max(bits_s16x2(cmx[j]), bits_s16x2(T2))) != T2;
+        else
+            f = (int)cmx[j] >= tau;
+        const uint64_t bal = __ballot(f);
+        if (f && wcnt <= S1_CCAP) {   // slots up to S1_CCAP + 63 exist
+            const int s = wcnt + lane_prefix(bal);
+            sh.chunks[wave][s] = make_uint4(raw[4 * j], raw[4 * j + 1], raw[4 * j + 2], raw[4 * j + 3]);
+            sh.cid[wave][s] = j * S1_THREADS + tid;
+        }
+        wcnt += __popcll(bal);
+    }
+    wave_lds_sync();
+    const int nck = min(wcnt, S1_CCAP);
+    int nk = 0;
+    for (int s0 = 0; s0 < nck; s0 += WAVE) {
+        const int s = s0 + lane;
+        uint32_t sm = 0;
+        int c = 0;
+        if (s < nck) {
+            c = sh.cid[wave][s];
+            sm = chunk_survivors<DT>(sh.chunks[wave][s], tau);
+            if (nl_data > 0)
+                for (int w = 0; w < S1_WAVES; ++w)
+                    for (int i = 0; i < sh.nlw[w]; ++i) {
+                        const int2 e = sh.lcb[w][i];
+                        if (e.x == c) sm &= ~(uint32_t)e.y;
+                    }
+        }
+        const auto elems = (const uint8_t*)&sh.chunks[wave][s < nck ? s : 0];
+        for (;;) {
+            const bool act = sm != 0;
+            const uint64_t bal = __ballot(act);
+            if (bal == 0ull) break;
+            if (act) {
+                const int e = chunk_elem<DT>(__builtin_ctz(sm));
+                sm &= sm - 1u;
+                const int slot = nk + lane_prefix(bal);
+                const int local = c * EPC + e;
+                if (slot < S1_KCAP) {   // a finite value (or +inf) here
+                    int v;
+                    if constexpr (DT == SS_BF16) v = (int)*(const short*)(elems + 2 * e);
+                    else v = *(const int*)(elems + 4 * e);
+                    sh.keys[wave][slot] = value_key<DT>(v, local);
+                }
+            }
+            nk += __popcll(bal);
+        }
+    }
+    wave_lds_sync();
+    if (wcnt > S1_CCAP || nk > S1_KCAP) {
+        if (lane == 0) sh.ovf = 1;
+    } else {
+        const WList<Key> mine = wave_top128(sh.keys[wave], nk);
+        sh.wl[wave][lane] = mine.lo;
+        sh.wl[wave][lane + WAVE] = mine.hi;
+    }
+    if (lane == 0) sh.nk[wave] = nk;
+}
+
+// Merge tree over the four wave lists, in the lead wave's order (lw = 0 is
+// the lead): (0+1) on lw 0 and (2+3) on lw 1, then both.  One barrier; the
+// result is valid in the lead wave.
+template <int DT>
+__device__ __forceinline__ WList<typename S1Traits<DT>::Key> merge_lists(S1Shared<DT>& sh) {
+    using Key = typename S1Traits<DT>::Key;
+    const int wave = threadIdx.x / WAVE;
+    const int lane = lane_id();
+    const int lead = s1_lead_wave();
+    const int lw = (wave - lead) & (S1_WAVES - 1);
+    auto wl_of = [&](int l) -> WList<Key> {
+        const int w = (l + lead) & (S1_WAVES - 1);
+        return WList<Key>{sh.wl[w][lane], sh.wl[w][lane + WAVE]};
+    };
+    const int w2 = (lead + 2) & (S1_WAVES - 1);
+    WList<Key> r{0, 0};
+    if (lw < 2) {
+        r = wave_merge(wl_of(2 * lw), wl_of(2 * lw + 1));
+        if (lw == 1) {
+            sh.wl[w2][lane] = r.lo;
+            sh.wl[w2][lane + WAVE] = r.hi;
+        }
+    }
+    __syncthreads();
+    if (lw == 0) r = wave_merge(r, WList<Key>{sh.wl[w2][lane], sh.wl[w2][lane + WAVE]});
+    return r;
+}
+
+// Exact path for the tiles the threshold select cannot take (a positive
+// NaN, or more values tied near the threshold than its LDS areas hold):
+// the tile is read again from memory, element by element, thread t taking
+// tile indices [t*BN/256, (t+1)*BN/256), so that thread order is token
+// order.  Each element's canonical order value: -inf for masked tokens and
+// NaN, +inf as FLT_MAX for fp32; tokens left out (listed, past V: set in
+// the LDS bitmap `ebm`) are skipped.  A radix select on the order key, 8
+// bits per pass over an LDS histogram, finds the 128th largest value T;
+// every token above T is kept (fewer than 128), and the first 128 - #{> T}
+// tokens equal to T in token order (a block scan of per-thread counts).
+// The keys are sorted by the lead wave into sh.surv.  Not inlined: the
+// common path keeps the tile in registers and this path must not add to
+// them.  Ends with a barrier.
+template <int DT>
+__device__ __attribute__((noinline)) void tile_exact_mem(const char* rowp, int nvalid, bool use_mask,
+                                                          S1Shared<DT>& sh, const uint32_t* ebm) {
+    using TT = S1Traits<DT>;
+    using Key = typename TT::Key;
+    constexpr int EPT = TT::BN / S1_THREADS;   // tile indices per thread
+    const int tid = threadIdx.x;
+    const int wave = tid / WAVE;
+    const int lane = lane_id();
+    const int i0 = tid * EPT;
+    const int i1 = min(i0 + EPT, nvalid);
+    // order key u (unsigned, larger = better) of the token at tile index i;
+    // false for a token left out
+    auto key_at = [&](int i, uint32_t& u, int& v) -> bool {
+        if ((ebm[i >> 5] >> (i & 31)) & 1u) return false;
+        const bool masked = use_mask && !((sh.gmw[i >> 5] >> (i & 31)) & 1u);
+        if constexpr (DT == SS_BF16) {
+            const uint32_t h = gmem((const uint16_t*)rowp)[i];
+            const bool nan = (h & 0x7FFFu) > 0x7F80u;
+            v = (h & 0x8000u) ? -(int)(h & 0x7FFFu) : (int)h;
+            if (masked || nan) v = TT::NINF_V;
+            u = (uint32_t)(v + 0x8000);
+        } else {
+            const uint32_t x = gmem((const uint32_t*)rowp)[i];
+            const bool nan = (x & 0x7FFFFFFFu) > 0x7F800000u;
+            v = (x & 0x80000000u) ? -(int)(x & 0x7FFFFFFFu) : (int)x;
+            v = min(v, TT::PINF_V);
+            if (masked || nan) v = TT::NINF_V;
+            u = (uint32_t)v ^ 0x80000000u;
+        }
+        return true;
+    };
+    int* hist = &sh.cid[0][0];
+    static_assert(sizeof(sh.cid) >= 256 * sizeof(int), "histogram");
+    constexpr int KBITS = DT == SS_BF16 ? 16 : 32;
+    uint32_t prefix = 0;   // the digits of T's key found so far
+    int kneed = KMAX;      // how many of the tokens with this prefix are still wanted
+    int n_all = 0;
+    bool take_all = false;
+    for (int shift = KBITS - 8; shift >= 0; shift -= 8) {   // block-uniform
+        hist[tid] = 0;
+        __syncthreads();
+        for (int i = i0; i < i1; ++i) {
+            uint32_t u;
+            int v;
+            if (key_at(i, u, v) && (shift + 8 >= KBITS || (u >> (shift + 8)) == prefix))
+                atomicAdd(&hist[(u >> shift) & 255u], 1);
+        }
+        __syncthreads();
+        // the digit b of the kneed-th largest: lane l sums bins 4l..4l+3,
+        // suffix sums from the top give the lane, then its bins
+        int s4[4], s = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            s4[k] = hist[4 * lane + k];
+            s += s4[k];
+        }
+        const int pre = wave_incl_scan(s);
+        const int tot = __shfl(pre, WAVE - 1, WAVE);
+        const int suffix = tot - pre + s;   // bins 4*lane .. 255
+        if (shift == KBITS - 8) {
+            n_all = __builtin_amdgcn_readfirstlane(tot);
+            if (n_all <= KMAX) {   // the tile holds no more than 128 tokens: all of them
+                take_all = true;
+                break;
+            }
+        }
+        const uint64_t ok = __ballot(suffix >= kneed);
+        const int L = 63 - __builtin_clzll(ok);   // highest lane whose suffix reaches kneed
+        const int above = __shfl(suffix - s, L, WAVE);   // bins above lane L's
+        int b = 4 * L + 3, acc = above;
+        const int h3 = __shfl(s4[3], L, WAVE), h2 = __shfl(s4[2], L, WAVE);
+        const int h1 = __shfl(s4[1], L, WAVE), h0 = __shfl(s4[0], L, WAVE);
+        if (acc + h3 >= kneed) b = 4 * L + 3;
+        else if (acc + h3 + h2 >= kneed) { b = 4 * L + 2; acc += h3; }
+        else if (acc + h3 + h2 + h1 >= kneed) { b = 4 * L + 1; acc += h3 + h2; }
+        else { b = 4 * L; acc += h3 + h2 + h1; }
+        (void)h0;
+        kneed -= __builtin_amdgcn_readfirstlane(acc);
+        prefix = (prefix << 8) | (uint32_t)__builtin_amdgcn_readfirstlane(b);
+        __syncthreads();   // the histogram is read before the next pass clears it
+    }
+    // T's key is `prefix`; `kneed` tokens equal to T are wanted
+    int* ctr = &sh.red[0][0];
+    if (tid == 0) *ctr = 0;
+    __syncthreads();
+    Key* g = &sh.keys[0][0];
+    const int n_gt = KMAX - kneed;
+    int nties = 0;
+    for (int i = i0; i < i1; ++i) {
+        uint32_t u;
+        int v;
+        if (!key_at(i, u, v)) continue;
+        if (take_all || u > prefix) g[atomicAdd(ctr, 1)] = value_key<DT>(v, i);
+        else if (u == prefix) ++nties;
+    }
+    int total;
+    int r = block_excl_scan(take_all ? 0 : nties, sh.scan, &total);   // ties before this thread's
+    if (!take_all && r < kneed) {
+        for (int i = i0; i < i1 && r < kneed; ++i) {
+            uint32_t u;
+            int v;
+            if (key_at(i, u, v) && u == prefix) g[n_gt + r++] = value_key<DT>(v, i);
+        }
+    }
+    __syncthreads();
+    const int n = take_all ? n_all : KMAX;
+    if (wave == s1_lead_wave()) {
+        WList<Key> l{lane < n ? g[lane] : (Key)0, lane + WAVE < n ? g[lane + WAVE] : (Key)0};
+        l = wave_sort128(l);
+        sh.surv[lane] = l.lo;
+        sh.surv[lane + WAVE] = l.hi;
+    }
+    __syncthreads();
+}
+
 // The 128 best tokens of tile `tile` of row `row` (whose data `in` holds),
 // sorted best first (key 0 = no token): left in sh.surv[0..128) behind a
 // final barrier, or, with `to_regs`, handed to the lead wave's registers
-// with no final barrier (the other waves return early).  `next()` is called
-// as soon as the registers of `in` are no longer needed (the candidate
-// chunks are in LDS by then).
-template <int DT, typename Next>
+// with no final barrier (the other waves return early).
+template <int DT>
 __device__ __forceinline__ void tile_process(const Stage1Params& P, int row, int tile, S1In<DT>& in,
-                                             S1Shared<DT>& sh, Next&& next,
-                                             WList<typename S1Traits<DT>::Key>* to_regs = nullptr) {
+                                             S1Shared<DT>& sh, WList<typename S1Traits<DT>::Key>* to_regs = nullptr) {
     S1_TILE_GEOMETRY
     using Key = typename T::Key;
     static_assert(S1_WAVES == 4, "merge tree");
     uint32_t(&raw)[NQ] = in.raw;
-    auto load_dword = [&](int q) -> uint32_t { return tile_dword<DT>(rowp, vec, nvalid, q); };
 
     const uint32_t flags = __builtin_amdgcn_readfirstlane(in.rq_flags);
     const uint32_t lists = __builtin_amdgcn_readfirstlane(in.rq_lists);
@@ -423,12 +805,10 @@ __device__ __forceinline__ void tile_process(const Stage1Params& P, int row, int
     const bool use_prior = (flags & (SS_REP | SS_FREQPRES)) && P.aux.prior_ids && P.aux.prior_cnt && n_prior > 0;
     const bool use_bias = (flags & SS_BIAS) && P.aux.bias_ids && n_bias > 0;
 
-    // the tile's grammar words go to LDS; each thread then reads the bits
-    // of its own chunks
-    if (use_grammar) {
-#pragma unroll
-        for (int k = 0; k < CPT * EPC / 32; ++k) sh.gmw[tid + k * S1_THREADS] = in.gw[k];
-        if (DT == SS_BF16) {   // entry tid: bit 2k -> low half of dword k, bit 2k+1 -> high half
+    // the 256-entry table of dword keep masks (bf16): entry g sets the low
+    // half of dword k when bit 2k of g is set, the high half for bit 2k + 1
+    auto build_gtab = [&] {
+        if constexpr (DT == SS_BF16) {
             uint32_t mk[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k)
@@ -436,146 +816,151 @@ __device__ __forceinline__ void tile_process(const Stage1Params& P, int row, int
                         (((uint32_t)tid >> (2 * k + 1)) & 1u ? 0xFFFF0000u : 0u);
             sh.gtab[tid] = make_uint4(mk[0], mk[1], mk[2], mk[3]);
         }
+    };
+    // the tile's grammar words go to LDS; each thread then reads the bits
+    // of its own chunks
+    if (use_grammar) {
+#pragma unroll
+        for (int k = 0; k < CPT * EPC / 32; ++k) sh.gmw[tid + k * S1_THREADS] = in.gw[k];
+        build_gtab();
     }
     const int l_pid = in.l_pid, l_pct = in.l_pct, l_bid = in.l_bid;
 
-    // ---- the lead wave: tokens of this tile named by an active list (ranked in
-    // Stage 2, left out here) ----
-    if (wave == lead) {
+    // ---- tokens of this tile named by an active list (ranked in Stage 2,
+    // left out here): the wave lw places after the lead records list
+    // entries 64lw .. 64lw+63 (the lists hold at most 255 entries), the lead
+    // wave also the earlier drafts ----
+    const int lw = (wave - lead) & (S1_WAVES - 1);
+    const bool has_slice = (use_prior && n_prior > lw * WAVE) || (use_bias && n_bias > lw * WAVE) || wave == lead;
+    if (has_slice) {   // wave-uniform
         int nl = 0;
+        int* const lst = sh.listed[wave];
+        int2* const lcbw = sh.lcb[wave];
         auto record = [&](bool ok, int loc) {
             const uint64_t bal = __ballot(ok);
             if (ok) {
                 const int i = nl + lane_prefix(bal);
-                sh.listed[i] = loc;
-                sh.lcb[i] = make_int2(loc / EPC, (int)chunk_bit<DT>(loc % EPC));
+                lst[i] = loc;
+                lcbw[i] = make_int2(loc / EPC, (int)chunk_bit<DT>(loc % EPC));
             }
             nl += __popcll(bal);
         };
-        // entries 0..63 come from the early request; longer lists load the
-        // rest now
+        const int j = lw * WAVE + lane;
         if (use_prior) {
             const int loc = l_pid - base;
-            record(lane < n_prior && l_pct >= 1 && l_pid >= 0 && l_pid < P.V && loc >= 0 && loc < nvalid, loc);
-            if (n_prior > WAVE) {
-                const auto ids = gmem(P.aux.prior_ids + (int64_t)b * P.aux.prior_stride);
-                const auto cts = gmem(P.aux.prior_cnt + (int64_t)b * P.aux.prior_stride);
-                for (int j0 = WAVE; j0 < n_prior; j0 += WAVE) {
-                    const int j = j0 + lane;
-                    const int id = j < n_prior ? ids[j] : -1;
-                    const int ct = j < n_prior ? cts[j] : 0;
-                    const int lc = id - base;
-                    record(j < n_prior && ct >= 1 && id >= 0 && id < P.V && lc >= 0 && lc < nvalid, lc);
-                }
-            }
+            record(j < n_prior && l_pct >= 1 && l_pid >= 0 && l_pid < P.V && loc >= 0 && loc < nvalid, loc);
         }
         if (use_bias) {
             const int loc = l_bid - base;
-            record(lane < n_bias && l_bid >= 0 && l_bid < P.V && loc >= 0 && loc < nvalid, loc);
-            if (n_bias > WAVE) {
-                const auto ids = gmem(P.aux.bias_ids + (int64_t)b * P.aux.bias_stride);
-                for (int j0 = WAVE; j0 < n_bias; j0 += WAVE) {
-                    const int j = j0 + lane;
-                    const int id = j < n_bias ? ids[j] : -1;
-                    const int lc = id - base;
-                    record(j < n_bias && id >= 0 && id < P.V && lc >= 0 && lc < nvalid, lc);
-                }
-            }
+            record(j < n_bias && l_bid >= 0 && l_bid < P.V && loc >= 0 && loc < nvalid, loc);
         }
         // earlier drafts in the penalty history (verification)
-        const int nh = draft_hist_len(P, flags, row);
+        const int nh = wave == lead ? draft_hist_len(P, flags, row) : 0;
         if (nh > 0) {
             const int loc = in.l_did - base;
             record(lane < nh && in.l_did >= 0 && in.l_did < P.V && loc >= 0 && loc < nvalid, loc);
         }
         if (lane == 0) {
-            sh.nl = nl;
-            sh.ovf = 0;
+            sh.nlw[wave] = nl;
+            if (wave == lead) sh.ovf = 0;
         }
+    } else if (lane == 0) {
+        sh.nlw[wave] = 0;
     }
     __syncthreads();   // listed tokens, grammar table
-    const int nl = sh.nl;
-    // grammar rows: the tile's listed tokens are cleared from its grammar
-    // words, so the mask leaves them out like any disallowed token and the
-    // threshold and survivor steps need not know about them
-    const bool fold = use_grammar && nl > 0;   // block-uniform
+    const int4 nl4 = *(const int4*)sh.nlw;   // one read
+    const int nl = __builtin_amdgcn_readfirstlane(nl4.x + nl4.y + nl4.z + nl4.w);
+    // The tile's listed tokens are cleared from the mask when the row has a
+    // grammar mask, or when there are too many of them to leave in the data:
+    // the mask then leaves them out like any disallowed token, and the
+    // threshold and survivor steps need not know about them.
+    const bool fold = nl > 0 && (use_grammar || nl > S1_NL_FAST);   // block-uniform
+    const bool use_mask = use_grammar || fold;
     if (fold) {
-        for (int i = tid; i < nl; i += S1_THREADS) {
-            const int loc = sh.listed[i];
-            atomicAnd(&sh.gmw[loc >> 5], ~(1u << (loc & 31)));
+        if (!use_grammar) {   // an all-ones mask to clear them from
+            for (int i = tid; i < BN / 32; i += S1_THREADS) sh.gmw[i] = ~0u;
+            build_gtab();
+            __syncthreads();
         }
+        const int nlv[S1_WAVES] = {nl4.x, nl4.y, nl4.z, nl4.w};
+#pragma unroll
+        for (int w = 0; w < S1_WAVES; ++w)
+            for (int i = tid; i < nlv[w]; i += S1_THREADS) {
+                const int loc = sh.listed[w][i];
+                atomicAnd(&sh.gmw[loc >> 5], ~(1u << (loc & 31)));
+            }
         __syncthreads();
     }
-    const int nl_data = fold ? 0 : nl;   // listed tokens still present in the data
+    const int nl_data = fold ? 0 : nl;   // listed tokens still present in the data (<= 128)
+    WList<Key> r{0, 0};
+    auto exact = [&] {   // the exact path, from memory (sh.surv, then the lead wave's registers)
+        const uint32_t* ebm = exclusion_bitmap<DT>(sh, nvalid);
+        tile_exact_mem<DT>(rowp, nvalid, use_mask, sh, ebm);
+        if (wave == lead) r = WList<Key>{sh.surv[lane], sh.surv[lane + WAVE]};
+    };
+    auto finish = [&] {
+        if (wave == lead) {
+            if (to_regs) {   // the caller takes the lead wave's registers
+                *to_regs = r;
+                return;
+            }
+            sh.surv[lane] = r.lo;
+            sh.surv[lane + WAVE] = r.hi;
+        }
+        if (to_regs) return;
+        __syncthreads();
+    };
+    if (!P.aligned16) {   // rows not on a 16-byte boundary (block-uniform)
+        exact();
+        finish();
+        return;
+    }
 
-    // ---- grammar mask (masked elements take PAD) and maxima per chunk and
-    // per lane (raw patterns read as signed), chunk by chunk in the order
-    // the loads were issued, so that each waits only for its own data ----
-    uint32_t gbits[CPT];   // bits of chunk j's elements allowed by the grammar (bit e: element e)
-    if (use_grammar) {
+    // ---- mask and maxima per chunk and per lane (raw patterns read as
+    // signed), chunk by chunk in the order the loads were issued, so that
+    // each waits only for its own data.  A masked element becomes all ones,
+    // a negative NaN: below any positive threshold in the raw form, below
+    // -inf in the order form, and -inf in the exact path, as the mask asks ----
+    uint32_t cmx[CPT];
+    if (use_mask) {
+        // every chunk's mask byte first (independent reads), then one table
+        // read per chunk in arrival order
+        uint32_t gbits[CPT];
         const uint8_t* gb = (const uint8_t*)sh.gmw;
 #pragma unroll
         for (int j = 0; j < CPT; ++j)
             gbits[j] = DT == SS_BF16 ? gb[j * S1_THREADS + tid]
                                      : (uint32_t)gb[(j * S1_THREADS + tid) >> 1] >> ((tid & 1) * 4);
-    }
-    uint32_t cmx[CPT];
-    auto chunk_max = [&](int j) {
-        if constexpr (DT == SS_BF16) {
-            const s16x2 a = __builtin_elementwise_max(bits_s16x2(raw[4 * j]), bits_s16x2(raw[4 * j + 1]));
-            const s16x2 c = __builtin_elementwise_max(bits_s16x2(raw[4 * j + 2]), bits_s16x2(raw[4 * j + 3]));
-            cmx[j] = s16x2_bits(__builtin_elementwise_max(a, c));
-        } else {
-            cmx[j] = (uint32_t)max(max((int)raw[4 * j], (int)raw[4 * j + 1]),
-                                   max((int)raw[4 * j + 2], (int)raw[4 * j + 3]));
-        }
-    };
-    if (use_grammar) {
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
+            uint4 M;
             if constexpr (DT == SS_BF16) {
-                const uint4 M = sh.gtab[gbits[j]];
-                const uint32_t m4[4] = {M.x, M.y, M.z, M.w};
-#pragma unroll
-                for (int k = 0; k < 4; ++k) raw[4 * j + k] = (raw[4 * j + k] & m4[k]) | (PAD & ~m4[k]);
+                M = sh.gtab[gbits[j]];
             } else {
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const uint32_t M = 0u - ((gbits[j] >> k) & 1u);
-                    raw[4 * j + k] = (raw[4 * j + k] & M) | (PAD & ~M);
-                }
+                const uint32_t g = gbits[j];
+                M = make_uint4(0u - (g & 1u), 0u - ((g >> 1) & 1u), 0u - ((g >> 2) & 1u), 0u - ((g >> 3) & 1u));
             }
-            chunk_max(j);
+            const uint32_t m4[4] = {M.x, M.y, M.z, M.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) raw[4 * j + k] |= ~m4[k];   // masked: all ones
+            cmx[j] = chunk_max<DT>(raw, j);
             __builtin_amdgcn_sched_barrier(0);   // chunks in arrival order
         }
     } else {
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
-            chunk_max(j);
+            cmx[j] = chunk_max<DT>(raw, j);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    int m;
-    if constexpr (DT == SS_BF16) {
-        s16x2 mm = bits_s16x2(cmx[0]);
-#pragma unroll
-        for (int j = 1; j < CPT; ++j) mm = __builtin_elementwise_max(mm, bits_s16x2(cmx[j]));
-        m = max((int)mm.x, (int)mm.y);
-    } else {
-        m = (int)cmx[0];
-#pragma unroll
-        for (int j = 1; j < CPT; ++j) m = max(m, (int)cmx[j]);
-    }
-
-    // positive NaN anywhere in the tile -> general path; +inf of fp32 counts
-    // as FLT_MAX for the threshold
-    const int nan_floor = DT == SS_BF16 ? 0x7F80 : (int)F32_PINF_BITS;
-    const bool special = m > nan_floor;
-    if (DT == SS_F32) m = min(m, (int)F32_MAX_BITS);
+    // a positive NaN (the largest signed patterns) sends the tile to the
+    // exact path; fp32 +inf counts as FLT_MAX for the threshold
+    const int mraw = lane_max<DT>(cmx, false);
+    const bool special = mraw > (DT == SS_BF16 ? 0x7F80 : (int)F32_PINF_BITS);
+    int m = DT == SS_F32 ? min(mraw, (int)F32_MAX_BITS) : mraw;
     // at least 128 + nl tokens at or above tau, so that 128 remain once the
     // listed ones are set aside
-    const bool nl_ok = nl_data <= S1_NL_FAST;
-    const int kw = KMAX / S1_WAVES + (nl_ok ? (nl_data + S1_WAVES - 1) / S1_WAVES : 0);
+    const int kw = KMAX / S1_WAVES + (nl_data + S1_WAVES - 1) / S1_WAVES;
     const int tau_w = wave_kth_largest<T::VAL_BITS>(m, kw);
     const uint64_t sp = __ballot(special);
     if (lane == 0) {
@@ -590,185 +975,73 @@ __device__ __forceinline__ void tile_process(const Stage1Params& P, int row, int
         tau = min(tau, sh.tau[w]);
         any_special |= sh.special[w] != 0;
     }
-    const bool fast = !any_special && tau >= 1 && nl_ok && P.aligned16;   // block-uniform
-
-    if (fast) {
-        // ---- chunks holding a value >= tau go to the wave's LDS area ----
-        int wcnt = 0;
-        const uint32_t T2 = ((uint32_t)(tau - 1) & 0xFFFFu) * 0x10001u;
+    // block-uniform: raw form (tau >= 1), order form, or the exact path
+    tau = __builtin_amdgcn_readfirstlane(tau);
+    any_special = __builtin_amdgcn_readfirstlane((int)any_special) != 0;
+    const bool ordered = !any_special && tau < 1;
+    if (ordered) {
+        // the order form (masked elements fall below -inf by themselves);
+        // elements past V back to PAD
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-            bool f;
-            if constexpr (DT == SS_BF16)
-                f = s16x2_bits(__builtin_elementwise_max(bits_s16x2(cmx[j]), bits_s16x2(T2))) != T2;
-            else
-                f = (int)cmx[j] >= tau;
-            const uint64_t bal = __ballot(f);
-            if (f && wcnt <= S1_CCAP) {   // slots up to S1_CCAP + 63 exist
-                const int s = wcnt + lane_prefix(bal);
-                sh.chunks[wave][s] = make_uint4(raw[4 * j], raw[4 * j + 1], raw[4 * j + 2], raw[4 * j + 3]);
-                sh.cid[wave][s] = j * S1_THREADS + tid;
-            }
-            wcnt += __popcll(bal);
-        }
-        next();   // in.raw is free from here on
-        wave_lds_sync();
+        for (int q = 0; q < NQ; ++q) raw[q] = order_value<DT>(raw[q]);
+        if (!full) pad_absent<DT>(raw, nvalid);
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) cmx[j] = chunk_max<DT>(raw, j);
+        m = lane_max<DT>(cmx, true);
+        const int t2 = wave_kth_largest<T::VAL_BITS>(m, kw);
+        if (lane == 0) sh.tau2[wave] = t2;
+        __syncthreads();
+        tau = sh.tau2[0];
+#pragma unroll
+        for (int w = 1; w < S1_WAVES; ++w) tau = min(tau, sh.tau2[w]);
+        tau = __builtin_amdgcn_readfirstlane(max(tau, T::FINITE_MIN));   // below it: -inf, NaN, masked
+    }
 
-        // ---- their elements >= tau that are not listed become keys, one
-        // per lane per round ----
-        const int nck = min(wcnt, S1_CCAP);
-        int nk = 0;
-        for (int s0 = 0; s0 < nck; s0 += WAVE) {
-            const int s = s0 + lane;
-            uint32_t sm = 0;
-            int c = 0;
-            if (s < nck) {
-                c = sh.cid[wave][s];
-                sm = chunk_survivors<DT>(sh.chunks[wave][s], tau);
-                for (int i = 0; i < nl_data; ++i) {
-                    const int2 e = sh.lcb[i];
-                    if (e.x == c) sm &= ~(uint32_t)e.y;
+    if (!any_special) select_ge<DT>(raw, cmx, tau, nl_data, sh);
+    __syncthreads();   // wave lists, ovf, survivor counts
+
+    if (!any_special && __builtin_amdgcn_readfirstlane(sh.ovf) == 0) {
+        // survivors in all: fewer than 128 only in the order form (the finite
+        // tokens of a tile whose grammar allows few); the remaining ranks are
+        // the tile's -inf tokens in token order, found among its first
+        // S1_THREADS chunks (the first 128 + listed + finite indices lie there)
+        const int n_fin = ordered ? __builtin_amdgcn_readfirstlane(sh.nk[0] + sh.nk[1] + sh.nk[2] + sh.nk[3]) : KMAX;
+        const bool fill = n_fin < KMAX;   // block-uniform; only in the order form
+        if (fill) {
+            if (tid < KMAX && tid >= n_fin) sh.surv[tid] = (Key)0;
+            const uint32_t* ebm = exclusion_bitmap<DT>(sh, nvalid);
+            const uint4 E = chunk_keep_alu<DT>(ebm, 0, true);   // chunk tid: tile indices tid*EPC ..
+            const uint32_t e4[4] = {E.x, E.y, E.z, E.w};
+            uint32_t fm = 0;   // bit e: element e is a -inf token
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if constexpr (DT == SS_BF16) {
+                    const int lo16 = (int)(short)(raw[k] & 0xFFFFu), hi16 = (int)(short)(raw[k] >> 16);
+                    fm |= ((lo16 < T::FINITE_MIN && (e4[k] & 0xFFFFu)) ? 1u : 0u) << (2 * k);
+                    fm |= ((hi16 < T::FINITE_MIN && (e4[k] >> 16)) ? 1u : 0u) << (2 * k + 1);
+                } else {
+                    fm |= (((int)raw[k] < T::FINITE_MIN && e4[k]) ? 1u : 0u) << k;
                 }
             }
-            const auto elems = (const uint8_t*)&sh.chunks[wave][s < nck ? s : 0];
-            for (;;) {
-                const bool act = sm != 0;
-                const uint64_t bal = __ballot(act);
-                if (bal == 0ull) break;
-                if (act) {
-                    const int e = chunk_elem<DT>(__builtin_ctz(sm));
-                    sm &= sm - 1u;
-                    const int slot = nk + lane_prefix(bal);
-                    const int local = c * EPC + e;
-                    if (slot < S1_KCAP) {   // value > 0 and not NaN here
-                        if constexpr (DT == SS_BF16) {
-                            const uint32_t h = *(const uint16_t*)(elems + 2 * e);
-                            sh.keys[wave][slot] = ((h | 0x8000u) << 16) | (0xFFFFu - (uint32_t)local);
-                        } else {
-                            const uint32_t h = *(const uint32_t*)(elems + 4 * e);
-                            sh.keys[wave][slot] = key_f32(h, local, true, true);
-                        }
-                    }
-                }
-                nk += __popcll(bal);
+            int tot;
+            int rk = n_fin + block_excl_scan(__builtin_popcount(fm), sh.scan, &tot);
+            while (fm) {
+                const int e = __builtin_ctz(fm);
+                fm &= fm - 1u;
+                if (rk < KMAX) sh.surv[rk] = ninf_key<DT>(tid * EPC + e);
+                ++rk;
             }
+            __syncthreads();
         }
-        wave_lds_sync();
-        if (wcnt > S1_CCAP || nk > S1_KCAP) {
-            if (lane == 0) sh.ovf = 1;
-        } else {
-            const WList<Key> mine = wave_top128(sh.keys[wave], nk);
-            sh.wl[wave][lane] = mine.lo;
-            sh.wl[wave][lane + WAVE] = mine.hi;
+        r = merge_lists<DT>(sh);
+        if (wave == lead && fill) {
+            if (lane >= n_fin) r.lo = sh.surv[lane];
+            if (lane + WAVE >= n_fin) r.hi = sh.surv[lane + WAVE];
         }
     } else {
-        next();
+        exact();
     }
-    __syncthreads();   // wave lists, ovf
-
-    if (fast && sh.ovf == 0) {
-        // ---- merge tree over the wave lists, in the lead wave's order
-        // (lw = 0 is the lead): (0+1) on lw 0 and (2+3) on lw 1, then both ----
-        const int lw = (wave - lead) & (S1_WAVES - 1);
-        auto wl_of = [&](int l) -> WList<Key> {
-            const int w = (l + lead) & (S1_WAVES - 1);
-            return WList<Key>{sh.wl[w][lane], sh.wl[w][lane + WAVE]};
-        };
-        const int w2 = (lead + 2) & (S1_WAVES - 1);
-        WList<Key> r{0, 0};
-        if (lw < 2) {
-            r = wave_merge(wl_of(2 * lw), wl_of(2 * lw + 1));
-            if (lw == 1) {
-                sh.wl[w2][lane] = r.lo;
-                sh.wl[w2][lane + WAVE] = r.hi;
-            }
-        }
-        __syncthreads();
-        if (lw == 0) {
-            r = wave_merge(r, WList<Key>{sh.wl[w2][lane], sh.wl[w2][lane + WAVE]});
-            if (to_regs) {   // the caller takes the lead wave's registers
-                *to_regs = r;
-                return;
-            }
-            sh.surv[lane] = r.lo;
-            sh.surv[lane + WAVE] = r.hi;
-        }
-        if (to_regs) return;
-        __syncthreads();
-        return;
-    }
-
-    // ---- general path: exact keys for every element (re-read from cache),
-    // bisection for the 128th key.  The tile's listed tokens go to a bitmap
-    // in LDS (over the chunk areas, no longer in use). ----
-    uint32_t* lbm = (uint32_t*)&sh.chunks[0][0];
-    static_assert(BN / 32 * 4 <= (int)sizeof(sh.chunks), "listed bitmap");
-    for (int i = tid; i < BN / 32; i += S1_THREADS) lbm[i] = 0u;
-    __syncthreads();
-    for (int i = tid; i < nl; i += S1_THREADS) atomicOr(&lbm[sh.listed[i] >> 5], 1u << (sh.listed[i] & 31));
-    __syncthreads();
-    const auto gmask = gmem(P.aux.bitmask + (use_grammar ? (int64_t)row * P.aux.bitmask_stride : 0));
-    auto ekey = [&](int q, int h) -> Key {
-        const uint32_t d = load_dword(q);
-        const int c = (q >> 2) * S1_THREADS + tid;
-        const int e = DT == SS_BF16 ? 2 * (q & 3) + h : (q & 3);
-        const int loc = c * EPC + e;
-        const bool present = loc < nvalid && !((lbm[loc >> 5] >> (loc & 31)) & 1u);
-        const bool allowed = present && (!use_grammar || ((gmask[(base + loc) >> 5] >> ((base + loc) & 31)) & 1u));
-        if constexpr (DT == SS_BF16)
-            return (Key)key_bf16(h ? (d >> 16) : (d & 0xFFFFu), loc, present, allowed);
-        else
-            return (Key)key_f32(d, loc, present, allowed);
-    };
-    constexpr int HALVES = DT == SS_BF16 ? 2 : 1;
-    constexpr int KB = (int)sizeof(Key) * 8;
-    Key res = 0;
-    int parity = 0;
-    for (int bit = KB - 1; bit >= 0; --bit) {
-        const Key cand = res | ((Key)1 << bit);
-        int c = 0;
-#pragma nounroll
-        for (int q = 0; q < NQ; ++q)
-#pragma unroll
-            for (int h = 0; h < HALVES; ++h) c += ekey(q, h) >= cand;
-        c = wave_sum(c);
-        if (lane == 0) sh.red[parity][wave] = c;
-        __syncthreads();
-        int tot = 0;
-#pragma unroll
-        for (int w = 0; w < S1_WAVES; ++w) tot += sh.red[parity][w];
-        parity ^= 1;
-        if (tot >= KMAX) res = cand;
-    }
-    const Key thr = res > (Key)1 ? res : (Key)1;   // key 0 = no token
-    int cnt = 0;
-#pragma nounroll
-    for (int q = 0; q < NQ; ++q)
-#pragma unroll
-        for (int h = 0; h < HALVES; ++h) cnt += ekey(q, h) >= thr;
-    int total;
-    int off = block_excl_scan(cnt, sh.scan, &total);   // total <= 128 (keys are unique)
-    Key* g = &sh.keys[0][0];
-#pragma nounroll
-    for (int q = 0; q < NQ; ++q)
-#pragma unroll
-        for (int h = 0; h < HALVES; ++h) {
-            const Key k = ekey(q, h);
-            if (k >= thr) g[off++] = k;
-        }
-    __syncthreads();
-    if (wave == lead) {
-        WList<Key> l{lane < total ? g[lane] : (Key)0, lane + WAVE < total ? g[lane + WAVE] : (Key)0};
-        l = wave_sort128(l);
-        if (to_regs) {
-            *to_regs = l;
-            return;
-        }
-        sh.surv[lane] = l.lo;
-        sh.surv[lane + WAVE] = l.hi;
-    }
-    if (to_regs) return;
-    __syncthreads();
+    finish();
 }
 
 // One tile, requested and processed in turn.  Without `to_regs` the sorted
@@ -781,7 +1054,7 @@ __device__ __forceinline__ void stage1_tile(const Stage1Params& P, int row, int 
     S1In<DT> in;
     tile_fetch<DT>(P, row, tile, in);
     tile_patch<DT>(P, row, tile, in);
-    tile_process<DT>(P, row, tile, in, sh, [] {}, to_regs);
+    tile_process<DT>(P, row, tile, in, sh, to_regs);
 }
 
 }  // namespace ssd

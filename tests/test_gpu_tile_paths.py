@@ -1,0 +1,178 @@
+"""The tile stage off its usual path, against the CPU oracle.
+
+Stage 1 compares raw bit patterns while its threshold is positive, and
+switches to two's-complement order values when it is not (log-probability
+rows, rows with few positive values, sparse grammars), fills the ranks of a
+tile with fewer than 128 finite tokens with its -inf tokens in id order,
+folds more than 128 listed tokens of one tile into its mask, and takes an
+exact register bisection for positive NaN or heavy ties.  Each row below is
+built to take one of those paths; the per-tile lists (bit-exact against
+the oracle's tile view) and the whole sampling step (tokens, candidates,
+kept counts, statuses bit-exact, probabilities to 1e-5 relative) are
+checked, with contiguous rows and with rows that do not start on a 16-byte
+boundary, in bf16 and fp32.  The full c2-shape stress workloads (the bench's
+stress legs) are checked on every row.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from speculative_decoding_verification_stage1_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+RTOL = 1e-5
+
+
+def _lib():
+    from speculative_decoding_verification_stage1_amd import _lib
+    return _lib
+
+
+def _dev(x, dtype, pad=0):
+    """Device logits; with pad > 0 the rows lie V + pad elements apart in a
+    wider buffer whose extra columns hold large values."""
+    rows, V = x.shape
+    if pad:
+        wide = np.zeros((rows, V + pad), dtype=x.dtype)
+        wide[:, :V] = x
+        wide[:, V:] = W.to_bf16_bits(np.full((rows, pad), 1e4, np.float32)) if dtype == W.DTYPE_BF16 else 1e4
+        x = wide
+    x = np.ascontiguousarray(x)
+    t = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16) if dtype == W.DTYPE_BF16 \
+        else torch.from_numpy(x).cuda()
+    return t[:, :V] if pad else t
+
+
+def _rows(V, rng):
+    """fp32 logits [11, V] and their requests, one row per path."""
+    n = 11
+    x = (rng.standard_normal((n, V)) * 2).astype(np.float32)
+    req = W.plain_requests(n, temperature=0.9, top_p=0.95, prior_len=300, bias_len=8)
+    bm = np.full((n, (V + 31) // 32), 0xFFFFFFFF, np.uint32)
+    req.bitmask = bm
+    # 0: log-softmax row, every value negative
+    z = x[0].astype(np.float64)
+    x[0] = (z - (z.max() + np.log(np.exp(z - z.max()).sum()))).astype(np.float32)
+    # 1: few positive values per tile, the rest negative
+    x[1] = -np.abs(x[1]) - 0.5
+    x[1, rng.choice(V, 40, replace=False)] = rng.uniform(0.5, 3.0, 40).astype(np.float32)
+    # 2: negative, heavily tied (quarter steps): more ties near the
+    #    threshold than the survivor areas hold
+    x[2] = np.round(-np.abs(x[2]) * 1) / 4 - 3
+    # 3: a grammar allowing 0.1 %, with penalty and bias lists
+    allowed = rng.random(V) < 0.001
+    allowed[rng.integers(0, V)] = True
+    p = np.zeros(bm.shape[1] * 32, bool)
+    p[:V] = allowed
+    bm[3] = np.packbits(p, bitorder="little").view("<u4")
+    req.use_grammar[3] = True
+    req.use_penalties[3] = True
+    req.prior_ids[3, :40] = rng.choice(np.nonzero(allowed)[0], min(40, allowed.sum()), replace=True)[:40] \
+        if allowed.sum() >= 1 else -1
+    req.prior_cnt[3, :40] = 2
+    req.n_prior[3] = 40
+    req.rep_penalty[3] = 1.2
+    # 4: a grammar allowing only tokens of the last tile
+    bm[4] = 0
+    bm[4, -3:] = 0x01010101
+    req.use_grammar[4] = True
+    # 5: -0, +0 and negative values (ties of -0 with +0)
+    x[5] = -np.abs(x[5]) - 1
+    idx = rng.choice(V, 300, replace=False)
+    x[5, idx[:150]] = -0.0
+    x[5, idx[150:]] = 0.0
+    # 6: negative values with negative NaN and -inf among them
+    x[6] = -np.abs(x[6])
+    x[6, rng.choice(V, 500, replace=False)] = -np.inf
+    x[6, rng.choice(V, 500, replace=False)] = -np.float32(np.nan)
+    # 7: a positive NaN in a negative row (exact path)
+    x[7] = -np.abs(x[7])
+    x[7, rng.integers(0, V)] = np.nan
+    # 8: -inf except a few finite values
+    x[8] = -np.inf
+    x[8, rng.choice(V, 60, replace=False)] = rng.standard_normal(60).astype(np.float32)
+    # 9, 10: more than 128 listed tokens in one tile, no grammar; row 10
+    #        negative
+    x[10] = -np.abs(x[10]) - 0.25
+    for r in (9, 10):
+        req.use_penalties[r] = True
+        req.prior_ids[r] = rng.choice(6000, 300, replace=False)
+        req.prior_cnt[r] = rng.integers(1, 4, 300)
+        req.n_prior[r] = 255
+        req.rep_penalty[r] = 1.1
+        req.freq_penalty[r] = 0.1
+        req.use_bias[r] = True
+        req.bias_ids[r] = rng.choice(6000, 8, replace=False)
+        req.bias_val[r] = rng.uniform(-2, 2, 8).astype(np.float32)
+        req.n_bias[r] = 8
+    req.greedy[1] = True
+    return x, req
+
+
+def _tile_parity(x, dtype, req, pad):
+    lib = _lib()
+    tile = lib.ss_tile_size(dtype)
+    xd = _dev(x, dtype, pad)
+    rows, V = xd.shape
+    Zv = (V + tile - 1) // tile
+    dreq = lib.DeviceRequests(req)
+    out = torch.full((rows, Zv, 128), -7, dtype=torch.int32, device="cuda")
+    lib.ss_tile_topk(xd, 1, dreq, out, lib.workspace(rows, V, dtype, fill=0xA7))
+    torch.cuda.synchronize()
+    ref = oracle.tile_topk(x, dtype, tile, req)
+    got = out.cpu().numpy()
+    bad = np.argwhere((got != ref).any(axis=2))
+    assert len(bad) == 0, ("rows/tiles differ", bad[:10].tolist())
+
+
+def _sample_parity(x, dtype, req, pad, seed):
+    lib = _lib()
+    xd = _dev(x, dtype, pad)
+    B, V = xd.shape
+    dreq = lib.DeviceRequests(req)
+    o = dict(tokens=torch.full((B,), -7, dtype=torch.int32, device="cuda"),
+             topk_ids=torch.full((B, 128), -7, dtype=torch.int32, device="cuda"),
+             probs=torch.full((B, 128), -7.0, dtype=torch.float32, device="cuda"),
+             kept=torch.full((B,), -7, dtype=torch.int32, device="cuda"),
+             mass=torch.full((B,), -7.0, dtype=torch.float32, device="cuda"),
+             status=torch.full((B,), -7, dtype=torch.int32, device="cuda"))
+    lib.ss_sample_step(xd, dreq, lib.make_rng(seed, 3), o["tokens"], o["topk_ids"], o["probs"], o["kept"],
+                       o["mass"], o["status"], lib.workspace(B, V, dtype, fill=0xA7))
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in o.items()}
+    ref = oracle.sample(x, dtype, req, seed=seed, offset=3, threads=16)
+    for r in range(B):
+        for k in ("status", "topk_ids", "kept", "tokens"):
+            assert np.array_equal(g[k][r], ref[k][r]), (k, r)
+        np.testing.assert_allclose(g["probs"][r], ref["probs"][r], rtol=RTOL, atol=1e-30, err_msg=str(r))
+        np.testing.assert_allclose(g["mass"][r], ref["mass"][r], rtol=RTOL, atol=1e-30, err_msg=str(r))
+
+
+@pytest.mark.parametrize("pad", [0, 3])
+@pytest.mark.parametrize("dtype", [W.DTYPE_BF16, W.DTYPE_F32])
+def test_tile_paths(dtype, pad):
+    rng = np.random.default_rng(2024)
+    x, req = _rows(70001, rng)   # bf16: 3 tiles, fp32: 5 tiles, both with a ragged last tile
+    logits = W.to_bf16_bits(x) if dtype == W.DTYPE_BF16 else x
+    _tile_parity(logits, dtype, req, pad)
+    _sample_parity(logits, dtype, req, pad, seed=7)
+
+
+@pytest.mark.parametrize("dtype", [W.DTYPE_BF16, W.DTYPE_F32])
+def test_tile_paths_whole_tiles(dtype):
+    """The same rows at a vocabulary of whole tiles (no ragged tail)."""
+    rng = np.random.default_rng(99)
+    x, req = _rows(65536, rng)
+    logits = W.to_bf16_bits(x) if dtype == W.DTYPE_BF16 else x
+    _tile_parity(logits, dtype, req, 0)
+    _sample_parity(logits, dtype, req, 0, seed=8)
+
+
+@pytest.mark.parametrize("kind", W.STRESS_KINDS)
+def test_c2_stress_full(kind):
+    """The bench's stress legs at c2's full shape (256 x 2^18 bf16), every
+    row against the oracle."""
+    wl = W.workload_c2_stress(kind)
+    _sample_parity(wl.logits, wl.dtype, wl.req, 0, seed=0)
