@@ -310,9 +310,15 @@ int ss_topk_step(const void* logits, int dtype, int B, int V, int64_t ld, int k,
 int ss_topk_step_radix(const void* logits, int dtype, int B, int V, int64_t ld, int k,
                        int32_t* out_ids, float* out_vals, void* ws, size_t ws_bytes, void* stream);
 
-/* The same result from a single-program-per-row streaming kernel (one
- * workgroup walks the whole vocabulary; the design the two-stage method
- * replaces, SonicSampler section 3.2).  Needs no workspace. */
+/* The same result as ss_topk_step from one program per row (the design the
+ * two-stage method replaces, SonicSampler section 3.2; radix select as
+ * section 3.1 "Top-k selection primitives" describes it): one workgroup per
+ * row streams the whole row once per pass, each pass histograms the next
+ * 8-bit digit of the order key among the elements matching the digits of
+ * the k-th key found so far, and once at most 1024 elements lie at or above
+ * that prefix one more pass gathers them for an exact sort; ties at a fully
+ * resolved k-th value are settled by a radix select over the token index
+ * (lower id first).  Needs no workspace; errors as ss_topk_step. */
 int ss_topk_single_pass(const void* logits, int dtype, int B, int V, int64_t ld, int k,
                         int32_t* out_ids, float* out_vals, void* stream);
 

@@ -6,6 +6,7 @@
 #include "ss_kernels.h"
 #include "ss_dense.h"
 #include "ss_radix.h"
+#include "ss_radix_row.h"
 
 using namespace ssd;
 
@@ -160,48 +161,7 @@ int noalloc_scratch(void** out) {
 
 }  // namespace
 
-// ---------------------------------------------------------------------------
-// single-program-per-row top-k: one workgroup walks every tile of its row
-// and folds each tile's 128 best into a running list
-// ---------------------------------------------------------------------------
 namespace ssd {
-
-template <int DT>
-__global__ __launch_bounds__(S1_THREADS) void topk_single_pass_kernel(Stage1Params P, int k, int32_t* out_ids,
-                                                                      float* out_vals) {
-    __shared__ S1Shared<DT> sh;
-    __shared__ uint64_t acc[KMAX];
-    const int row = blockIdx.x;
-    const int tid = threadIdx.x;
-    for (int i = tid; i < KMAX; i += S1_THREADS) acc[i] = 0ull;
-    for (int t = 0; t < P.Zv; ++t) {
-        stage1_tile<DT>(P, row, t, sh);   // ends with a barrier
-        if (tid < KMAX) {
-            const uint64_t a = acc[tid];
-            const uint64_t bb = merge_key<DT>(sh.surv[KMAX - 1 - tid], t);
-            acc[tid] = a > bb ? a : bb;
-        }
-        __syncthreads();
-        for (int j = KMAX / 2; j > 0; j >>= 1) {
-            if (tid < KMAX / 2) {
-                const int i = (tid / j) * 2 * j + (tid % j);
-                const uint64_t a = acc[i], c = acc[i + j];
-                if (a < c) {
-                    acc[i] = c;
-                    acc[i + j] = a;
-                }
-            }
-            __syncthreads();
-        }
-    }
-    if (tid < k) {
-        const uint64_t key = acc[tid];
-        const bool have = key != 0ull && tid < P.V;
-        out_ids[(int64_t)row * k + tid] = have ? (int)(0xFFFFFFFFu - (uint32_t)key) : -1;
-        if (out_vals)
-            out_vals[(int64_t)row * k + tid] = have ? unord32((uint32_t)(key >> 32)) : bitsf(F32_NINF_BITS);
-    }
-}
 
 __global__ void rng_advance_kernel(ss_rng* rng, uint64_t delta) {
     if (threadIdx.x == 0 && blockIdx.x == 0) rng->offset += delta;
@@ -511,13 +471,13 @@ int ss_topk_single_pass(const void* logits, int dtype, int B, int V, int64_t ld,
     if (B == 0) return SS_OK;
     if (!out_ids) return SS_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)stream;
-    Stage1Params s1 = make_s1(logits, dtype, B, V, ld, 1, nullptr, nullptr, nullptr, nullptr);
+    const int al = aligned16(logits, dtype, ld);
     if (dtype == SS_BF16)
-        hipLaunchKernelGGL(topk_single_pass_kernel<SS_BF16>, dim3((unsigned)B), dim3(S1_THREADS), 0, s, s1, k,
-                           out_ids, out_vals);
+        hipLaunchKernelGGL(topk_radix_row_kernel<SS_BF16>, dim3((unsigned)B), dim3(RR_THREADS), 0, s, logits, V, ld,
+                           al, k, out_ids, out_vals);
     else
-        hipLaunchKernelGGL(topk_single_pass_kernel<SS_F32>, dim3((unsigned)B), dim3(S1_THREADS), 0, s, s1, k,
-                           out_ids, out_vals);
+        hipLaunchKernelGGL(topk_radix_row_kernel<SS_F32>, dim3((unsigned)B), dim3(RR_THREADS), 0, s, logits, V, ld,
+                           al, k, out_ids, out_vals);
     return launched();
 }
 

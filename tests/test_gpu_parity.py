@@ -582,6 +582,77 @@ def test_topk_c4_rows(regime):
     assert np.array_equal(vals.cpu().numpy(), ref_vals)
 
 
+@pytest.mark.parametrize("regime", ["peaked", "flat"])
+def test_topk_c4_full_launch(regime):
+    """The c4 launch as the bench runs it (512 x 262144 fp32, k = 128): every
+    row of the two-stage path and of the single-program radix select against
+    the oracle, ids and values."""
+    lib = L()
+    wl = W.workload_c4(regime)
+    x = _dev_logits(wl.logits, wl.dtype)
+    B, V = x.shape
+    ref_ids, ref_vals = oracle.topk(wl.logits, wl.dtype, 128, threads=16)
+    for name, run in (("two-stage", lambda i, v: lib.ss_topk_step(x, 128, i, v, lib.workspace(B, V, wl.dtype, fill=0xA7))),
+                      ("radix single pass", lambda i, v: lib.ss_topk_single_pass(x, 128, i, v))):
+        ids = torch.full((B, 128), -7, dtype=torch.int32, device="cuda")
+        vals = torch.zeros((B, 128), dtype=torch.float32, device="cuda")
+        run(ids, vals)
+        torch.cuda.synchronize()
+        bad = np.nonzero((ids.cpu().numpy() != ref_ids).any(axis=1))[0]
+        assert len(bad) == 0, (name, bad[:10])
+        assert np.array_equal(vals.cpu().numpy().view(np.uint32), ref_vals.view(np.uint32)), name
+
+
+def _single_pass_vs_oracle(x_np, dtype, k, pad=0, tag=""):
+    lib = L()
+    rows, V = x_np.shape
+    if pad:
+        wide = np.zeros((rows, V + pad), dtype=x_np.dtype)
+        wide[:, :V] = x_np
+        x = _dev_logits(wide, dtype)[:, :V]
+    else:
+        x = _dev_logits(x_np, dtype)
+    ref_ids, ref_vals = oracle.topk(x_np, dtype, k)
+    ids = torch.full((rows, k), -7, dtype=torch.int32, device="cuda")
+    vals = torch.zeros((rows, k), dtype=torch.float32, device="cuda")
+    lib.ss_topk_single_pass(x, k, ids, vals)
+    torch.cuda.synchronize()
+    g = ids.cpu().numpy()
+    bad = np.nonzero((g != ref_ids).any(axis=1))[0]
+    assert len(bad) == 0, (tag, bad[:10], g[bad[0]][:10] if len(bad) else None, ref_ids[bad[0]][:10] if len(bad) else None)
+    assert np.array_equal(vals.cpu().numpy().view(np.uint32), ref_vals.view(np.uint32)), tag
+
+
+@pytest.mark.parametrize("dtype", [W.DTYPE_BF16, W.DTYPE_F32])
+def test_topk_single_pass_radix_paths(dtype):
+    """The radix select's branches: an early gather (distinct values), every
+    digit resolved with more ties at the k-th value than the gather holds
+    (all-equal rows, a 3000-way tie at the 100th value: the token-index
+    radix), special values, and rows shorter than k."""
+    rng = np.random.default_rng(17)
+    V = 50001
+    x = (rng.standard_normal((8, V)) * 2).astype(np.float32)
+    x[1] = 1.0                                    # all equal
+    x[2] = rng.standard_normal(V).astype(np.float32) - 10
+    x[2, rng.choice(V, 99, replace=False)] = 5.0 + rng.random(99).astype(np.float32)
+    x[2, rng.choice(V, 3000, replace=False)] = 2.5    # ties at the k-th value
+    x[3, ::5] = np.nan
+    x[3, 7] = np.inf
+    x[3, 11] = -0.0
+    x[4] = -np.inf
+    x[4, 123] = 1.0
+    x[5] = -0.0
+    x[5, rng.choice(V, 60, replace=False)] = 0.0       # -0 and +0 tie
+    x[6] = -np.abs(x[6])                               # all negative
+    x[7] = np.round(x[7] * 2) / 2                      # coarse: many ties
+    logits = W.to_bf16_bits(x) if dtype == W.DTYPE_BF16 else x
+    for k in (128, 100, 1):
+        _single_pass_vs_oracle(logits, dtype, k, tag=f"k={k}")
+    _single_pass_vs_oracle(logits, dtype, 128, pad=3, tag="unaligned rows")
+    for Vs in (1, 77, 128, 129):
+        _single_pass_vs_oracle(np.ascontiguousarray(logits[:, :Vs]), dtype, 128, tag=f"V={Vs}")
+
+
 @pytest.mark.parametrize("k", [1, 7, 128])
 def test_topk_small_k_and_bf16(k):
     lib = L()
