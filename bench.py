@@ -193,7 +193,7 @@ def summarize_rocprof(d: str, out: str) -> None:
         fh.write("\n".join(ll) + "\n")
 
 
-LEGS = ("c2", "verify", "stress", "c0", "c1", "c4", "ref")
+LEGS = ("c2", "verify", "stress", "c0", "c1", "c4", "lmhead", "ref")
 
 
 def _events_us(fn, n, stream=None):
@@ -626,6 +626,8 @@ def extra_measurements(args, dev, L, W, stream, legs):
                           "ids_equal": same, "torch_topk_us": round(tt, 1)}
             del xk
         out["c4_topk"] = c4
+    if "lmhead" in legs:
+        out["lmhead"] = lmhead_measurements(L, W, dev)
     if "ref" in legs:   # the library's streaming read of 1 GiB (four times the last-level cache)
         rbuf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         rout = torch.zeros(2048, dtype=torch.int32, device=dev)
@@ -636,6 +638,76 @@ def extra_measurements(args, dev, L, W, stream, legs):
         del rbuf
     torch.cuda.empty_cache()
     return out
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+LMHEAD_SHAPES = ((64, 4096, 131072), (256, 4096, 262144))
+
+
+def lmhead_measurements(L, W, dev):
+    """The LM head fused with sampling, per shape (B, D, V): the fused step,
+    the logits launch alone, and the unfused form (logits to memory, then
+    the fp32 sampling step), mean of back-to-back launches (HIP events);
+    the GEMM's rate against the bf16 matrix-core peak and the weight stream
+    against HBM.  The weights (1-2 GiB) exceed the last-level cache, so
+    every step streams them from HBM.  torch's bf16 GEMM of the same shape
+    (fp32 accumulation, bf16 output) is context."""
+    import torch
+    res = {}
+    for B, D, V in LMHEAD_SHAPES:
+        h, w, req = W.lmhead_device_inputs(B, D, V, device=dev)
+        dreq = L.DeviceRequests(req)
+        rng = L.make_rng(0, 0)
+        tok = torch.zeros(B, dtype=torch.int32, device=dev)
+        ws = L.lmhead_workspace(B, V, device=dev)
+        z = torch.empty((B, V), dtype=torch.float32, device=dev)
+        ws32 = L.workspace(B, V, L.SS_F32, device=dev)
+
+        def fused(i):
+            L.ss_lmhead_sample_step(h, w, dreq, rng, tok, ws=ws, rng_advance=1)
+
+        def logits(i):
+            L.ss_lmhead_logits(h, w, z)
+
+        def unfused(i):
+            L.ss_lmhead_logits(h, w, z)
+            L.ss_sample_step(z, dreq, rng, tok, ws=ws32, rng_advance=1)
+
+        def linear(i):
+            torch.nn.functional.linear(h, w)
+
+        for f in (fused, logits, unfused, linear):
+            f(0)
+            f(1)
+        torch.cuda.synchronize()
+        n = 10
+        t_f = _events_us(fused, n)
+        t_l = _events_us(logits, n)
+        t_u = _events_us(unfused, n)
+        t_t = _events_us(linear, n)
+        flops = 2.0 * B * D * V
+        wbytes = 2.0 * V * D + 2.0 * B * D
+        # the GEMM's roofline: the weight stream at the HBM peak or the
+        # products at the bf16 matrix-core peak, whichever takes longer
+        t_hbm = wbytes / (HBM_PEAK_GBPS * 1e9) * 1e6
+        t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e6
+        t_roof = max(t_hbm, t_mfma)
+        res[f"B{B}_D{D}_V{V}"] = {
+            "fused_step_us": round(t_f, 1), "logits_only_us": round(t_l, 1), "unfused_step_us": round(t_u, 1),
+            "fused_speedup_vs_unfused": round(t_u / t_f, 3),
+            "fused_tokens_per_s": round(B / (t_f * 1e-6), 1),
+            "roofline": {"bound": "hbm" if t_hbm >= t_mfma else "mfma", "roofline_us": round(t_roof, 1),
+                         "hbm_us": round(t_hbm, 1), "mfma_us": round(t_mfma, 1),
+                         "logits_frac": round(t_roof / t_l, 3), "fused_frac": round(t_roof / t_f, 3)},
+            "logits_TFLOPs": round(flops / (t_l * 1e-6) / 1e12, 1),
+            "logits_frac_mfma_bf16": round(flops / (t_l * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 3),
+            "logits_weight_GBps": round(wbytes / (t_l * 1e-6) / 1e9, 1),
+            "logits_frac_hbm": round(wbytes / (t_l * 1e-6) / 1e9 / HBM_PEAK_GBPS, 3),
+            "torch_linear_bf16_us": round(t_t, 1),
+        }
+        del h, w, ws, z, ws32
+        torch.cuda.empty_cache()
+    return res
 
 
 def _subset(req, n):

@@ -334,6 +334,52 @@ int ss_tile_topk(const void* logits, int dtype, int rows, int V, int64_t ld, int
                  const ss_req* req, const ss_aux* aux, int32_t* out_ids,
                  void* ws, size_t ws_bytes, void* stream);
 
+/* LM head fused with sampling (SonicSampler section 2, "Fused sampling
+ * kernels": FlashSampling performs the vocabulary projection and the
+ * sampling in one pass, so the logits never reach memory).
+ *   hidden [B, ldh] bf16 (raw 16-bit patterns), D used per row;
+ *   weight [V, ldw] bf16, one row of D values per vocabulary token;
+ *   logits z[b, v] = sum_d hidden[b, d] * weight[v, d], the products exact
+ *   and summed in fp32 on the matrix cores (v_mfma_f32_32x32x16_bf16, k in
+ *   ascending steps of 16; the summation order inside a step is the
+ *   hardware's).  Every entry point below computes a given z[b, v] with the
+ *   same instruction sequence, so they all see the same fp32 values.
+ * Requirements (else SS_ERR_UNSUPPORTED): D a multiple of 128, D <= 65536,
+ * ldh and ldw multiples of 8, hidden and weight 16-byte aligned.
+ * ldh < D or ldw < D, a NULL pointer with B > 0: SS_ERR_INVALID_ARG. */
+
+/* Bytes of workspace ss_lmhead_sample_step needs (256-byte aligned, no
+ * initialisation): B * V * 4 (logits of the probe columns, and of the
+ * other columns for rows whose candidates overflow) + B * 4096 * 8
+ * (candidate lists) + the tile stage's share; 0 for B < 0 or V outside
+ * [1, SS_V_MAX]. */
+size_t ss_lmhead_workspace_bytes(int B, int V);
+
+/* The logits alone: out_logits [B, ldo] fp32 (ldo >= V), z[b, v] at
+ * out_logits[b * ldo + v].  Together with ss_sample_step (dtype SS_F32, aux
+ * NULL) it is the unfused form of ss_lmhead_sample_step. */
+int ss_lmhead_logits(const void* hidden, int64_t ldh, const void* weight, int64_t ldw, int B, int D, int V,
+                     float* out_logits, int64_t ldo, void* stream);
+
+/* Sampling straight from the hidden states: the same outputs, statuses,
+ * generator use (rng, rng_advance) and noise as ss_sample_step applied to
+ * the fp32 logits z with aux = NULL; req[b] as there.  Requests that ask for
+ * a grammar mask or name prior or bias entries are SS_ROW_INVALID (no side
+ * lists here).  The first P columns (P = V when V <= 16384, else whole
+ * tiles of 16384 covering at least 16384 and V / 16) are computed first
+ * and give each row its 128 best there; the 128th of them bounds from
+ * below the row's 128th best overall, so the GEMM over the other columns
+ * keeps only the tokens above it (up to 4096 per row, about (V / P - 1) *
+ * 128 on typical rows) and writes no logits.  A row with more (e.g. tied,
+ * or peaked far from the first columns) has its other logits stored in the
+ * workspace and selected from there.  ws: at least
+ * ss_lmhead_workspace_bytes(B, V) bytes.  Errors as ss_sample_step plus the
+ * LM-head requirements above. */
+int ss_lmhead_sample_step(const void* hidden, int64_t ldh, const void* weight, int64_t ldw, int B, int D, int V,
+                          const ss_req* req, ss_rng* rng, uint64_t rng_advance, int32_t* out_tokens,
+                          int32_t* out_topk_ids, float* out_probs, int32_t* out_kept, float* out_mass,
+                          int32_t* out_status, void* ws, size_t ws_bytes, void* stream);
+
 /* The bandwidth reference of the measurements: reads every byte of the
  * device buffer [p, p + bytes) once with 16-byte loads (p 16-byte aligned,
  * bytes a multiple of 16) on `nblocks` workgroups of 256 threads, and

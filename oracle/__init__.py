@@ -316,3 +316,138 @@ def tile_topk(logits, dtype: int, tile: int, req=None, rows_per_req: int = 1, bi
     if rc != 0:
         raise ValueError("oracle_tile_topk rejected its arguments")
     return out
+
+
+# ---------------------------------------------------------------------------
+# LM head (the fused projection + sampling variant)
+# ---------------------------------------------------------------------------
+
+def _widen_bf16(bits) -> np.ndarray:
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def lmhead_logits(hidden_bits, weight_bits) -> np.ndarray:
+    """LM-head logits z = H W^T in float64 from raw bf16 patterns: hidden
+    [B, D], weight [V, D] (each token's weight row contiguous), widened
+    exactly; the product is a float64 matrix product (a library routine as
+    one step of the definition)."""
+    return _widen_bf16(hidden_bits) @ _widen_bf16(weight_bits).T
+
+
+def lmhead_error_bound(hidden_bits, weight_bits) -> np.ndarray:
+    """Bound on |z32 - z| for any binary32 evaluation that sums the D products
+    h_d w_vd in any order: each product of two bf16 values is exact in
+    binary32 (8-bit significands), and a sum of n terms in binary32, in any
+    order and with or without fused multiply-adds, lies within
+    gamma_{n-1} * sum |terms| of the exact sum, gamma_m = m u / (1 - m u),
+    u = 2^-24 (Higham, "Accuracy and Stability of Numerical Algorithms",
+    section 4.2)."""
+    h = np.abs(_widen_bf16(hidden_bits))
+    w = np.abs(_widen_bf16(weight_bits))
+    D = h.shape[1]
+    m = max(D - 1, 0)
+    u = 2.0 ** -24
+    return (m * u / (1.0 - m * u)) * (h @ w.T)
+
+
+def lmhead_sample(hidden_bits, weight_bits, req, seed: int = 0, offset: int = 0, threads: int = 1,
+                  exact: bool = False, rows=None):
+    """The sampler applied to the LM head's logits: oracle.sample on the
+    float64 logits rounded to binary32, plus `fragile` [B] bool: rows whose
+    candidate list, kept count or token could change when every logit moves
+    by up to its rounding bound (lmhead_error_bound + half an ulp of the
+    value).  `exact`: inputs whose products and partial sums are all exact
+    in binary32 (the bound is then zero and no row is fragile).  `rows`: only
+    these rows are computed (the others' results are meaningless); each row
+    keeps its own index in the noise counters."""
+    h = np.asarray(hidden_bits)
+    B = h.shape[0]
+    V = np.asarray(weight_bits).shape[0]
+    rows = list(range(B)) if rows is None else list(rows)
+    zr = lmhead_logits(h[rows], weight_bits)
+    z32 = np.zeros((B, V), np.float32)
+    z32[rows] = zr.astype(np.float32)
+    req = _lmhead_requests(req)
+    out = sample(z32, 0, req, seed=seed, offset=offset, threads=threads)
+    fragile = np.zeros(B, bool)
+    if not exact:
+        eps = lmhead_error_bound(h[rows], weight_bits) + np.abs(zr) * 2.0 ** -24
+        for i, b in enumerate(rows):
+            fragile[b] = _lmhead_row_fragile(zr[i], eps[i], out, b, req, seed, offset)
+    out["fragile"] = fragile
+    return out
+
+
+def _lmhead_requests(req):
+    """The LM-head step takes no side lists: a request asking for a grammar
+    mask, or naming prior or bias entries, is an invalid row (expressed here
+    as a stochastic row with a NaN temperature, which the sampler rejects)."""
+    import copy
+    r = copy.deepcopy(req)
+    bad = r.use_grammar | (r.use_penalties & (r.n_prior > 0)) | (r.use_bias & (r.n_bias > 0))
+    r.greedy = np.where(bad, False, r.greedy)
+    r.temperature = np.where(bad, np.float32(np.nan), r.temperature).astype(np.float32)
+    r.use_grammar = np.zeros_like(r.use_grammar)
+    r.use_penalties = np.zeros_like(r.use_penalties)
+    r.use_bias = np.zeros_like(r.use_bias)
+    r.bitmask = None
+    return r
+
+
+def _lmhead_row_fragile(z, eps, out, b, req, seed, offset) -> bool:
+    """Whether row b's token, kept count or set of candidates could change
+    when every logit moves by up to `eps`: the boundary of the candidate set
+    (rank K against rank K + 1; greedy rows: rank 1 against rank 2), then,
+    for stochastic rows, the top-p and min-p cut decisions and the ranks on
+    either side of the final cut, and the Gumbel-max margin, with v = z / T
+    moving by at most max(eps) / T (float64 estimates with a small slack for
+    the binary32 epilogue).  The order inside the candidate list is not
+    checked: it changes neither the kept set's sums beyond the slack nor the
+    token."""
+    V = z.shape[0]
+    if out["status"][b] not in (STATUS_OK, STATUS_TOPK_CLAMPED):
+        return False
+    K = int(min(req.top_k[b] if req.top_k[b] > 0 else KMAX, KMAX, V))
+    order = np.lexsort((np.arange(V), -z))[:min(K + 1, V)]
+    zs, es = z[order], eps[order]
+
+    def split(r):   # ranks r and r + 1 (0-based) within the moves?
+        return r + 1 < len(order) and zs[r] - zs[r + 1] <= es[r] + es[r + 1]
+
+    greedy = bool(req.greedy[b]) or req.temperature[b] <= 0 or (req.top_k[b] == 1)
+    if greedy:
+        return split(0)
+    if split(K - 1):
+        return True
+    T = float(req.temperature[b])
+    dv = float(es[:K].max()) / T
+    slack = 1e-6
+    v = zs[:K] / T
+    e = np.exp(v - v[0])
+    Z = e.sum()
+    E = np.concatenate([[0.0], np.cumsum(e)])
+    n = K
+    if req.top_p[b] < 1.0:
+        p = float(req.top_p[b])
+        n_p = int(np.sum(E[:K] < p * Z))
+        for k in (n_p, n_p + 1):   # the last kept and the first dropped rank
+            if 1 <= k <= K and abs(E[k - 1] - p * Z) <= (4 * dv + slack) * Z:
+                return True
+        n = min(n, n_p)
+    if req.min_p[b] > 0.0:
+        L = np.log(float(req.min_p[b]))
+        n_m = int(np.sum(v - v[0] >= L))
+        for k in (n_m, n_m + 1):
+            if 1 <= k <= K and abs(v[k - 1] - v[0] - L) <= 2 * dv + slack:
+                return True
+        n = min(n, n_m)
+    if n < K and split(n - 1):
+        return True
+    ids = order[:n]
+    g = np.array([float(gumbel(seed, offset, int(i), b, 0)) for i in ids])
+    s = v[:n] + g
+    if n >= 2:
+        s2 = np.sort(s)
+        if s2[-1] - s2[-2] <= 2 * dv + slack * max(1.0, abs(s2[-1])):
+            return True
+    return False

@@ -98,6 +98,12 @@ def _load():
     L.ss_tile_topk.restype = i32
     L.ss_rng_advance.argtypes = [P, u64, P]
     L.ss_rng_advance.restype = i32
+    L.ss_lmhead_workspace_bytes.argtypes = [i32, i32]
+    L.ss_lmhead_workspace_bytes.restype = sz
+    L.ss_lmhead_logits.argtypes = [P, i64, P, i64, i32, i32, i32, P, i64, P]
+    L.ss_lmhead_logits.restype = i32
+    L.ss_lmhead_sample_step.argtypes = [P, i64, P, i64, i32, i32, i32, P, P, u64, P, P, P, P, P, P, P, sz, P]
+    L.ss_lmhead_sample_step.restype = i32
     L.ss_status_str.argtypes = [i32]
     L.ss_status_str.restype = ctypes.c_char_p
     return L
@@ -107,7 +113,8 @@ lib = _load()
 
 EXPORTS = ["ss_workspace_bytes", "ss_tile_size", "ss_sample_step", "ss_sample_step_noalloc", "ss_verify_step", "ss_verify_step_var",
            "ss_verify_dense_workspace_bytes", "ss_verify_step_dense", "ss_topk_step", "ss_topk_step_radix",
-           "ss_topk_single_pass", "ss_tile_topk", "ss_rng_advance", "ss_stream_read", "ss_status_str"]
+           "ss_topk_single_pass", "ss_tile_topk", "ss_lmhead_workspace_bytes", "ss_lmhead_logits",
+           "ss_lmhead_sample_step", "ss_rng_advance", "ss_stream_read", "ss_status_str"]
 
 
 class SsError(RuntimeError):
@@ -331,6 +338,52 @@ def ss_tile_topk(logits, rows_per_req: int = 1, dreq: DeviceRequests | None = No
                           None if dreq is None else ptr(dreq.req),
                           None if dreq is None else ctypes.byref(dreq.aux),
                           ptr(out_ids), ptr(ws), 0 if ws is None else ws.numel(), stream_handle(stream))
+    return _check(rc)
+
+
+def lmhead_workspace(B: int, V: int, device="cuda", fill: int | None = None):
+    """Workspace of ss_lmhead_sample_step (no initialisation needed; `fill`
+    as for workspace())."""
+    import torch
+    n = int(lib.ss_lmhead_workspace_bytes(B, V))
+    t = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    if fill is not None:
+        t.fill_(fill)
+    return t
+
+
+def _bf16_2d(t):
+    import torch
+    if t.dtype not in (torch.bfloat16, torch.int16):
+        raise TypeError(f"LM-head operands are bf16 (or their int16 patterns), got {t.dtype}")
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("LM-head operands are row-major 2-D tensors")
+    return t
+
+
+def ss_lmhead_logits(hidden, weight, out, stream=None) -> int:
+    """out[b, v] = hidden[b] . weight[v] (fp32), hidden [B, D], weight [V, D]."""
+    _bf16_2d(hidden)
+    _bf16_2d(weight)
+    B, D = hidden.shape
+    V = weight.shape[0]
+    rc = lib.ss_lmhead_logits(ptr(hidden), hidden.stride(0), ptr(weight), weight.stride(0), B, D, V, ptr(out),
+                              out.stride(0), stream_handle(stream))
+    return _check(rc)
+
+
+def ss_lmhead_sample_step(hidden, weight, dreq: DeviceRequests, rng, out_tokens, out_topk_ids=None,
+                          out_probs=None, out_kept=None, out_mass=None, out_status=None, ws=None, stream=None,
+                          rng_advance: int = 0, D: int | None = None) -> int:
+    _bf16_2d(hidden)
+    _bf16_2d(weight)
+    B = hidden.shape[0]
+    D = hidden.shape[1] if D is None else D
+    V = weight.shape[0]
+    rc = lib.ss_lmhead_sample_step(ptr(hidden), hidden.stride(0), ptr(weight), weight.stride(0), B, D, V,
+                                   ptr(dreq.req), ptr(rng), rng_advance, ptr(out_tokens), ptr(out_topk_ids),
+                                   ptr(out_probs), ptr(out_kept), ptr(out_mass), ptr(out_status), ptr(ws),
+                                   0 if ws is None else ws.numel(), stream_handle(stream))
     return _check(rc)
 
 

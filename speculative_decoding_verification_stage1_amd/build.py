@@ -23,6 +23,9 @@ HIPCC_FLAGS = [
     "-fno-fast-math",
     # keep the compiler from forming packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep private arrays (the GEMM's staged loads) in registers: moving
+    # them into LDS would take the LDS the GEMM's tiles need
+    "-mllvm", "-disable-promote-alloca-to-lds",
 ]
 
 

@@ -7,6 +7,7 @@
 #include "ss_dense.h"
 #include "ss_radix.h"
 #include "ss_radix_row.h"
+#include "ss_lmhead.h"
 
 using namespace ssd;
 
@@ -511,6 +512,202 @@ int ss_stream_read(const void* p, size_t bytes, int nblocks, uint32_t* out, void
 int ss_rng_advance(ss_rng* rng, uint64_t delta, void* stream) {
     if (!rng) return SS_ERR_INVALID_ARG;
     hipLaunchKernelGGL(rng_advance_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, rng, delta);
+    return launched();
+}
+
+}  // extern "C"
+
+namespace {
+
+// probe columns: whole fp32 tiles, at least LM_PROBE_MIN and V / 16, so
+// that about (V / P - 1) * 128 <= 15 * 128 tokens per row pass its
+// threshold
+int lm_probe_cols(int V) {
+    const int64_t t = S1Traits<SS_F32>::BN;
+    int64_t p = ((int64_t)V / 16 + t - 1) / t * t;
+    if (p < LM_PROBE_MIN) p = LM_PROBE_MIN;
+    return (int)(p < V ? p : V);
+}
+
+// LM-head workspace: [Stage-1 workspace of the probe][probe logits
+// B x P fp32][candidates B x LM_CAP][counts B][logits of the other columns
+// B x (V - P) fp32, written only for rows whose candidates overflowed]
+struct LmWs {
+    void* std_ws;
+    size_t std_bytes;
+    float* probe;
+    uint64_t* cand;
+    int32_t* cnt;
+    float* rest;
+    size_t bytes;
+};
+LmWs lm_ws(void* ws, int B, int V) {
+    const int P = lm_probe_cols(V);
+    LmWs L;
+    char* p = (char*)ws;
+    size_t o = 0;
+    L.std_ws = p;
+    L.std_bytes = ss_workspace_bytes(B, P, SS_F32);
+    o += align256(L.std_bytes);
+    L.probe = (float*)(p + o);
+    o += align256((size_t)B * P * sizeof(float));
+    L.cand = (uint64_t*)(p + o);
+    o += align256((size_t)B * LM_CAP * sizeof(uint64_t));
+    L.cnt = (int32_t*)(p + o);
+    o += align256((size_t)B * sizeof(int32_t));
+    L.rest = (float*)(p + o);
+    o += align256((size_t)B * (V - P) * sizeof(float));
+    L.bytes = o;
+    return L;
+}
+
+int check_lmhead(const void* hidden, int64_t ldh, const void* weight, int64_t ldw, int B, int D, int V) {
+    if (B < 0 || V < 1 || D < 1 || ldh < D || ldw < D) return SS_ERR_INVALID_ARG;
+    if (V > SS_V_MAX || D % 128 != 0 || D > (1 << 16) || (ldh % 8) || (ldw % 8)) return SS_ERR_UNSUPPORTED;
+    if (B > 0 && (!hidden || !weight)) return SS_ERR_INVALID_ARG;
+    if (((uintptr_t)hidden & 15u) || ((uintptr_t)weight & 15u)) return SS_ERR_UNSUPPORTED;
+    return SS_OK;
+}
+
+// launch shapes: B <= 64 one row tile of 64 (waves side by side), else row
+// tiles of 128 (2 x 2 waves); the probe uses narrower column tiles so that
+// its fewer columns still give every CU work
+template <int MODE, int WM, int WN, int KB>
+void lm_launch(LmParams p, hipStream_t s) {
+    constexpr int MT = 64 * WM, NT = (4 / WM) * 32 * WN;
+    const int ncols = p.col_end - p.col_begin;
+    p.ncol_tiles = (ncols + NT - 1) / NT;
+    p.nrow_tiles = (p.B + MT - 1) / MT;
+    const int64_t blocks = p.nrow_tiles == 1 ? p.ncol_tiles
+                                             : (int64_t)(p.ncol_tiles + 7) / 8 * 8 * p.nrow_tiles;
+    hipLaunchKernelGGL((lmhead_gemm_kernel<MODE, WM, WN, KB>), dim3((unsigned)blocks), dim3(LM_THREADS), 0, s, p);
+}
+
+// launch shapes: B <= 64 one row tile of 64 (waves side by side), else row
+// tiles of 128 (2 x 2 waves); the probe uses narrower column tiles, so that
+// its fewer columns still spread over many CUs, and longer k stages, since
+// each of its workgroups runs alone on a CU and waits on memory
+template <int MODE>
+void lm_launch_shape(LmParams p, bool probe, hipStream_t s) {
+    if (p.B <= 64) {
+        if (probe) lm_launch<MODE, 1, 1, 128>(p, s);
+        else lm_launch<MODE, 1, 2, 64>(p, s);
+    } else {
+        if (probe) lm_launch<MODE, 2, 2, 128>(p, s);
+        else lm_launch<MODE, 2, 4, 64>(p, s);
+    }
+}
+
+void launch_lm_gemm(int mode, LmParams p, bool probe, hipStream_t s) {
+    const int ncols = p.col_end - p.col_begin;
+    if (ncols <= 0 || p.B == 0) return;
+    if (mode == LM_STORE) lm_launch_shape<LM_STORE>(p, probe, s);
+    else if (mode == LM_THRESH) lm_launch_shape<LM_THRESH>(p, probe, s);
+    else lm_launch_shape<LM_REDO>(p, probe, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ss_lmhead_workspace_bytes(int B, int V) {
+    if (B < 0 || V < 1 || V > SS_V_MAX) return 0;
+    return lm_ws(nullptr, B, V).bytes;
+}
+
+int ss_lmhead_logits(const void* hidden, int64_t ldh, const void* weight, int64_t ldw, int B, int D, int V,
+                     float* out_logits, int64_t ldo, void* stream) {
+    int rc = check_lmhead(hidden, ldh, weight, ldw, B, D, V);
+    if (rc) return rc;
+    if (ldo < V) return SS_ERR_INVALID_ARG;
+    if (B == 0) return SS_OK;
+    if (!out_logits) return SS_ERR_INVALID_ARG;
+    LmParams p{};
+    p.H = (const uint16_t*)hidden;
+    p.ldh = ldh;
+    p.W = (const uint16_t*)weight;
+    p.ldw = ldw;
+    p.B = B;
+    p.D = D;
+    p.V = V;
+    p.col_begin = 0;
+    p.col_end = V;
+    p.out = out_logits;
+    p.ldo = ldo;
+    launch_lm_gemm(LM_STORE, p, false, (hipStream_t)stream);
+    return launched();
+}
+
+int ss_lmhead_sample_step(const void* hidden, int64_t ldh, const void* weight, int64_t ldw, int B, int D, int V,
+                          const ss_req* req, ss_rng* rng, uint64_t rng_advance, int32_t* out_tokens,
+                          int32_t* out_topk_ids, float* out_probs, int32_t* out_kept, float* out_mass,
+                          int32_t* out_status, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_lmhead(hidden, ldh, weight, ldw, B, D, V);
+    if (rc) return rc;
+    if ((int64_t)B * tiles_of(lm_probe_cols(V), SS_F32) > 0x7FFFFFFFLL) return SS_ERR_UNSUPPORTED;
+    if (B == 0) return SS_OK;
+    if (!req || !rng || !out_tokens) return SS_ERR_INVALID_ARG;
+    if ((rc = check_ws(ws, ws_bytes, ss_lmhead_workspace_bytes(B, V)))) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    const int P = lm_probe_cols(V);
+    const LmWs L = lm_ws(ws, B, V);
+    // 1. the probe columns' logits
+    LmParams g{};
+    g.H = (const uint16_t*)hidden;
+    g.ldh = ldh;
+    g.W = (const uint16_t*)weight;
+    g.ldw = ldw;
+    g.B = B;
+    g.D = D;
+    g.V = V;
+    g.col_begin = 0;
+    g.col_end = P;
+    g.out = L.probe;
+    g.ldo = P;
+    launch_lm_gemm(LM_STORE, g, true, s);
+    // 2. their 128 best per row and probe tile; the step's generator copy;
+    //    the candidate counts cleared
+    const WsLayout W = ws_layout(L.std_ws, B, P, SS_F32);
+    Stage1Params s1 = make_s1(L.probe, SS_F32, B, P, P, 1, req, nullptr, W.scratch, nullptr);
+    s1.rng = rng;
+    s1.rng_snap = W.rng_snap;
+    s1.rng_advance = rng_advance;
+    s1.clear_words = (uint64_t*)L.cnt;
+    s1.n_clear = (B + 1) / 2;
+    launch_stage1(SS_F32, s1, s);
+    // 3. the other columns: every token above the probe's 128th
+    g.col_begin = P;
+    g.col_end = V;
+    g.out = nullptr;
+    g.probe_keys = (const uint64_t*)W.scratch;
+    g.Zp = tiles_of(P, SS_F32);
+    g.cand = L.cand;
+    g.cnt = L.cnt;
+    launch_lm_gemm(LM_THRESH, g, false, s);
+    // 4. rows whose candidates overflowed: their other columns stored
+    g.probe_keys = nullptr;
+    g.cand = nullptr;
+    g.out = L.rest;
+    g.ldo = V - P;
+    launch_lm_gemm(LM_REDO, g, false, s);
+    // 5. merge and sample
+    LmStage2Params q{};
+    q.f = make_s2(s1, W.rng_snap, MODE_SAMPLE, W);
+    q.f.s1.V = V;
+    q.f.tokens = out_tokens;
+    q.f.topk_ids = out_topk_ids;
+    q.f.probs = out_probs;
+    q.f.kept = out_kept;
+    q.f.mass = out_mass;
+    q.f.status = out_status;
+    q.probe_keys = (const uint64_t*)W.scratch;
+    q.Zp = tiles_of(P, SS_F32);
+    q.cand = L.cand;
+    q.cnt = L.cnt;
+    q.probe = L.probe;
+    q.rest = L.rest;
+    q.P = P;
+    hipLaunchKernelGGL(lmhead_stage2_kernel, dim3((unsigned)B), dim3(S2_THREADS), 0, s, q);
     return launched();
 }
 

@@ -1,0 +1,339 @@
+// LM head fused with the sampler's first stage (the fused sampling kernels
+// the SonicSampler paper's related work names: the vocabulary projection
+// and sampling in one pass, so that the logits never reach memory).
+//
+// logits[b, v] = sum_d H[b, d] * W[v, d]: H [B, D] and W [V, D] bf16, both
+// K-contiguous; fp32 accumulation on the matrix cores
+// (v_mfma_f32_32x32x16_bf16, k ascending in steps of 16; lane l of an
+// operand holds row or column l % 32 and the 8 consecutive k at 8 * (l /
+// 32) of the step).  Every launch shape below issues that same sequence for
+// every output, so a logit has the same fp32 value whichever launch
+// computes it.
+//
+// GEMM: a workgroup of 4 waves owns MT = 64 * WM rows and NT = (4 / WM) *
+// 32 * WN vocabulary columns; a wave owns 64 rows x 32 * WN columns as
+// 2 x WN blocks of 32 x 32.  The k loop runs in stages of KB (64 or 128):
+// each thread loads its share of the stage's H and W rows with 16-byte
+// loads (KB / 8 lanes read one row segment) one stage ahead into
+// registers, then writes it to an LDS double buffer whose 16-byte slots
+// are XOR-swizzled by row (slot c of row r at c ^ (r & 7)), so the
+// fragment reads (32 rows at one k offset) meet no bank conflicts.  When several row blocks share
+// a column tile, the blocks of one tile are given ids 8 apart, which the
+// dispatcher places on the same XCD: the second read of a W tile then
+// comes from that XCD's L2.
+//
+// The sampled result must be the bounded sampler applied to these logits,
+// so the epilogue keeps every token that can be among a row's 128 best:
+//  1. a probe launch computes the first P columns (whole fp32 tiles of
+//     16384, at least one and V / 16) into the workspace, and the fp32 tile stage gives each row the exact
+//     128 best of each probe tile; the largest of the tiles' 128th values
+//     is a lower bound theta on the row's 128th best over the whole
+//     vocabulary (any subset's k-th largest is at most the whole set's);
+//  2. the main launch computes the other columns, and its epilogue appends
+//     every token whose value exceeds theta (a tie with theta ranks below it:
+//     higher id) to the row's candidate list - about (V/P - 1) * 128 tokens
+//     per row - with its exact merge key;
+//  3. the fused Stage 2 merges the probe lists with the sorted candidates
+//     and runs the sampling epilogue.
+// A row with more candidates than the list holds (inputs tied or peaked far
+// from the probe columns) is handled by a third launch of the GEMM between
+// 2 and 3: its workgroups return at once unless one of their rows
+// overflowed, and otherwise store those columns' logits to the workspace,
+// where Stage 2 radix-selects the row.
+#pragma once
+
+#include "ss_stage2.h"
+#include "ss_radix_row.h"
+
+namespace ssd {
+
+constexpr int LM_THREADS = 256;
+constexpr int LM_CAP = 4096;     // candidates kept per row
+constexpr int LM_PROBE_MIN = 16384;
+
+enum { LM_STORE = 0, LM_THRESH = 1, LM_REDO = 2 };
+
+typedef __bf16 lm_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float lm_f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int lm_u32x4 __attribute__((ext_vector_type(4)));
+
+struct LmParams {
+    const uint16_t* H;
+    int64_t ldh;
+    const uint16_t* W;
+    int64_t ldw;
+    int B, D, V;
+    int col_begin, col_end;        // columns this launch covers
+    int ncol_tiles, nrow_tiles;    // tiles of this launch's shape
+    float* out;                    // LM_STORE, LM_REDO: [B, ldo] logits of columns col_begin..
+    int64_t ldo;
+    const uint64_t* probe_keys;    // LM_THRESH: the probe tiles' sorted 128 per row ([B][Zp][128] fp32 tile keys)
+    int Zp;
+    uint64_t* cand;                // LM_THRESH: [B, LM_CAP] merge keys
+    int32_t* cnt;                  // LM_THRESH, LM_REDO: [B] candidates appended (may exceed LM_CAP)
+};
+
+// workgroup id -> (column tile, row tile): the row tiles of one column tile
+// get ids 8 apart (the same XCD under round-robin dispatch)
+__device__ __forceinline__ bool lm_tile(const LmParams& p, int& ct, int& rt) {
+    const int L = blockIdx.x;
+    if (p.nrow_tiles == 1) {
+        ct = L;
+        rt = 0;
+    } else {
+        const int g = L / (8 * p.nrow_tiles), i = L % (8 * p.nrow_tiles);
+        ct = g * 8 + (i & 7);
+        rt = i >> 3;
+    }
+    return ct < p.ncol_tiles;
+}
+
+template <int MODE, int WM, int WN, int KB>
+__global__ __launch_bounds__(LM_THREADS) void lmhead_gemm_kernel(LmParams p) {
+    constexpr int MT = 64 * WM;                 // rows per workgroup
+    constexpr int NWN = 4 / WM;                 // waves along the columns
+    constexpr int NT = NWN * 32 * WN;           // columns per workgroup
+    constexpr int CPR = KB / 8;                 // 16-byte chunks per row and stage
+    constexpr int SROW = KB * 2;                // LDS bytes per row and stage
+    constexpr int RPP = LM_THREADS / CPR;       // rows one pass of the threads loads
+    constexpr int AB = MT * SROW, WB = NT * SROW;
+    constexpr int NA = MT / RPP, NW = NT / RPP; // 16-byte loads per thread and stage
+    static_assert(MT % RPP == 0 && NT % RPP == 0 && KB % 16 == 0, "tile shape");
+    __shared__ __attribute__((aligned(16))) unsigned char lds[2][AB + WB];
+    int ct, rt;
+    if (!lm_tile(p, ct, rt)) return;
+    const int tid = threadIdx.x;
+    const int wave = tid / WAVE;
+    const int lane = lane_id();
+    const int row0 = rt * MT;
+    const int col0 = p.col_begin + ct * NT;
+    if (MODE == LM_REDO) {   // only blocks holding an overflowed row go on
+        bool over = false;
+        for (int i = tid; i < MT; i += LM_THREADS) {
+            const int r = row0 + i;
+            over |= r < p.B && p.cnt[r] > LM_CAP;
+        }
+        if (!__syncthreads_or(over)) return;
+    }
+    // global sources: thread t loads 16-byte chunk t % CPR of rows t / CPR +
+    // RPP i (rows past the end read the last valid row; their results are
+    // dropped)
+    const int chunk = tid % CPR, lrow = tid / CPR;
+    const uint16_t* ga[NA];
+    const uint16_t* gw[NW];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+        const int r = row0 + lrow + RPP * i;
+        ga[i] = p.H + (int64_t)(r < p.B ? r : p.B - 1) * p.ldh + chunk * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const int c = col0 + lrow + RPP * i;
+        gw[i] = p.W + (int64_t)(c < p.col_end ? c : p.col_end - 1) * p.ldw + chunk * 8;
+    }
+    lm_u32x4 ra[NA], rw[NW];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < NA; ++i) ra[i] = *(const lm_u32x4*)(ga[i] + k0);
+#pragma unroll
+        for (int i = 0; i < NW; ++i) rw[i] = *(const lm_u32x4*)(gw[i] + k0);
+    };
+    // LDS slot of (row, chunk): row * SROW + 16 * (chunk ^ (row & 7))
+    auto slot = [](int r, int c) { return r * SROW + 16 * (c ^ (r & 7)); };
+    auto lstore = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < NA; ++i) *(lm_u32x4*)(&lds[buf][slot(lrow + RPP * i, chunk)]) = ra[i];
+#pragma unroll
+        for (int i = 0; i < NW; ++i) *(lm_u32x4*)(&lds[buf][AB + slot(lrow + RPP * i, chunk)]) = rw[i];
+    };
+    const int wr = (wave / NWN) * 64;            // this wave's rows and columns in the tile
+    const int wc = (wave % NWN) * 32 * WN;
+    lm_f32x16 acc[2][WN];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j) acc[i][j] = lm_f32x16{};
+    auto compute = [&](int buf) {
+        const unsigned char* la = lds[buf];
+        const unsigned char* lw = lds[buf] + AB;
+#pragma unroll
+        for (int u = 0; u < KB / 16; ++u) {
+            const int c = 2 * u + (lane >> 5);   // this lane's 16-byte chunk of the step
+            lm_bf16x8 a[2], b[WN];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                a[i] = __builtin_bit_cast(lm_bf16x8, *(const lm_u32x4*)(la + slot(wr + 32 * i + (lane & 31), c)));
+#pragma unroll
+            for (int j = 0; j < WN; ++j)
+                b[j] = __builtin_bit_cast(lm_bf16x8, *(const lm_u32x4*)(lw + slot(wc + 32 * j + (lane & 31), c)));
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < WN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+    };
+    const int S = p.D / KB;
+    gload(0);
+    lstore(0);
+    if (S > 1) gload(KB);
+    __syncthreads();
+    for (int s = 0; s < S; ++s) {
+        compute(s & 1);
+        if (s + 1 < S) lstore((s + 1) & 1);
+        if (s + 2 < S) gload((s + 2) * KB);
+        __syncthreads();
+    }
+    // THRESH: the rows' thresholds (the largest 128th key over the probe
+    // tiles), then the candidates gathered per row in LDS (the stage
+    // buffers are free now; up to RSLOT per row, more go straight to the
+    // row's global list), then one global atomic per row reserves the
+    // block's share of the row's list
+    constexpr int RSLOT = 32;
+    static_assert(MT * (12 + 8 * RSLOT) <= 2 * (AB + WB), "candidate staging");
+    uint64_t* rkeys = (uint64_t*)&lds[0][0];                  // [MT][RSLOT]
+    uint32_t* theta = (uint32_t*)(rkeys + MT * RSLOT);        // [MT]
+    uint32_t* rcnt = theta + MT;                              // [MT]
+    uint32_t* rbase = rcnt + MT;                              // [MT]
+    if (MODE == LM_THRESH) {
+        for (int i = tid; i < MT; i += LM_THREADS) {
+            const int r = row0 + i;
+            uint32_t t = 0xFFFFFFFFu;
+            if (r < p.B) {
+                t = 0u;
+                for (int z = 0; z < p.Zp; ++z) {
+                    const uint32_t k = (uint32_t)(p.probe_keys[((int64_t)r * p.Zp + z) * KMAX + (KMAX - 1)] >> 32);
+                    t = k > t ? k : t;
+                }
+            }
+            theta[i] = t;
+            rcnt[i] = 0u;
+        }
+        __syncthreads();
+    }
+    // accumulator block (i, j), register q: row 32i + 8(q/4) + 4(l/32) + q%4,
+    // column 32j + l%32 of this wave's
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int rl = wr + 32 * i + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                const int r = row0 + rl;
+                const int c = col0 + wc + 32 * j + (lane & 31);
+                if (r >= p.B || c >= p.col_end) continue;
+                const float v = acc[i][j][q];
+                if (MODE != LM_THRESH) {
+                    p.out[(int64_t)r * p.ldo + (c - p.col_begin)] = v;
+                } else {
+                    const uint32_t k32 = ord32(canon(v));
+                    if (k32 > theta[rl]) {
+                        const uint64_t key = ((uint64_t)k32 << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)c);
+                        const uint32_t pos = atomicAdd(rcnt + rl, 1u);
+                        if (pos < (uint32_t)RSLOT) {
+                            rkeys[rl * RSLOT + pos] = key;
+                        } else {
+                            const int at = atomicAdd(p.cnt + r, 1);
+                            if (at < LM_CAP) p.cand[(int64_t)r * LM_CAP + at] = key;
+                        }
+                    }
+                }
+            }
+    if (MODE == LM_THRESH) {
+        __syncthreads();
+        for (int i = tid; i < MT; i += LM_THREADS) {
+            const uint32_t m = rcnt[i] < (uint32_t)RSLOT ? rcnt[i] : (uint32_t)RSLOT;
+            if (m > 0u) rbase[i] = (uint32_t)atomicAdd(p.cnt + row0 + i, (int)m);
+        }
+        __syncthreads();
+        for (int e = tid; e < MT * RSLOT; e += LM_THREADS) {
+            const int i = e / RSLOT, pos = e % RSLOT;
+            if ((uint32_t)pos < rcnt[i]) {
+                const uint32_t at = rbase[i] + (uint32_t)pos;
+                if (at < (uint32_t)LM_CAP) p.cand[(int64_t)(row0 + i) * LM_CAP + at] = rkeys[e];
+            }
+        }
+    }
+}
+
+// Fused Stage 2 for the LM head: one workgroup per row.
+struct LmStage2Params {
+    Stage2Params f;                // request records, outputs, generator copy (f.s1.V = the vocabulary)
+    const uint64_t* probe_keys;    // [B][Zp][128] fp32 tile keys of columns 0 .. P-1
+    int Zp;
+    const uint64_t* cand;          // [B, LM_CAP]
+    const int32_t* cnt;            // [B]
+    const float* probe;            // [B, P] logits of columns 0 .. P-1
+    const float* rest;             // [B, V - P] logits of columns P .. V-1 (overflowed rows only)
+    int P;
+};
+
+union LmStage2Shared {
+    S2Shared s2;
+    RowRadixShared rr;
+};
+
+__global__ __launch_bounds__(S2_THREADS) void lmhead_stage2_kernel(LmStage2Params q) {
+    __shared__ LmStage2Shared shu;
+    const int row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int wave = tid / WAVE;
+    const int lane = lane_id();
+    const Stage2Params& F = q.f;
+    const int n = __builtin_amdgcn_readfirstlane(q.cnt[row]);
+    WL64 best{0ull, 0ull};
+    if (n <= LM_CAP) {   // block-uniform
+        // the probe tiles' sorted lists and the candidates in sorted chunks
+        // of 128, dealt to the waves in turn; then the cross-wave tree
+        const uint64_t* c = q.cand + (int64_t)row * LM_CAP;
+        const int items = q.Zp + (n + KMAX - 1) / KMAX;
+        WL64 mine{0ull, 0ull};
+        bool any = false;
+        for (int it = wave; it < items; it += S2_WAVES) {
+            WL64 l;
+            if (it < q.Zp) {
+                const uint64_t* pk = q.probe_keys + ((int64_t)row * q.Zp + it) * KMAX;
+                l = WL64{merge_key<SS_F32>(pk[lane], it), merge_key<SS_F32>(pk[lane + WAVE], it)};
+            } else {
+                const int i0 = (it - q.Zp) * KMAX + lane, i1 = i0 + WAVE;
+                l = wave_sort128(WL64{i0 < n ? c[i0] : 0ull, i1 < n ? c[i1] : 0ull});
+            }
+            mine = any ? wave_merge(mine, l) : l;
+            any = true;
+        }
+        S2Shared& sh = shu.s2;
+        sh.wl[wave][0][lane] = mine.lo;
+        sh.wl[wave][1][lane] = mine.hi;
+        __syncthreads();
+        auto wl = [&](int w) -> WL64 { return WL64{sh.wl[w][0][lane], sh.wl[w][1][lane]}; };
+        if (wave == 1) {
+            const WL64 z = wave_merge(wl(2), wl(3));
+            sh.wl[2][0][lane] = z.lo;
+            sh.wl[2][1][lane] = z.hi;
+        }
+        if (wave == 0) best = wave_merge(mine, wl(1));
+        __syncthreads();
+        if (wave == 0) best = wave_merge(best, wl(2));
+    } else {
+        // more candidates than the list holds: a radix select over the
+        // row's stored logits
+        const float* pr = q.probe + (int64_t)row * q.P;
+        const float* rr = q.rest + (int64_t)row * (F.s1.V - q.P);
+        best = radix_row_select<SS_F32>(
+            [&](auto&& f) {
+                for (int v = tid; v < q.P; v += S2_THREADS) f(v, fbits(pr[v]));
+                for (int v = q.P + tid; v < F.s1.V; v += S2_THREADS) f(v, fbits(rr[v - q.P]));
+            },
+            F.s1.V, KMAX, shu.rr);
+    }
+    if (tid >= WAVE) return;
+    const int b = row;
+    ss_rng rg{0ull, 0ull};
+    if (F.rng) rg = *F.rng;
+    const RowParams rp = row_params(F.s1, b);
+    VerifyPre vp{DraftCount{0, true}, -1};
+    row_epilogue<SS_F32, MODE_SAMPLE>(F, rp, row, b, best, rg, shu.s2, vp);
+}
+
+}  // namespace ssd

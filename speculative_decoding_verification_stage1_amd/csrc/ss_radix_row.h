@@ -118,16 +118,16 @@ __device__ __forceinline__ void rr_pick(RowRadixShared& sh, int kneed, bool from
     }
 }
 
-template <int DT>
-__global__ __launch_bounds__(RR_THREADS) void topk_radix_row_kernel(const void* logits, int V, int64_t ld,
-                                                                    int aligned, int k, int32_t* out_ids,
-                                                                    float* out_vals) {
-    __shared__ RowRadixShared sh;
-    const int row = blockIdx.x;
+// The k best elements of one row (k <= 128) into wave 0's registers, sorted (key: 32-bit order key of the canonical fp32 value,
+// then the lower id; 0 past the row's length).  `stream(f)` must call
+// f(i, raw) once for every element i in [0, V) of the row (raw: the bf16
+// pattern or the fp32 bits), across the workgroup, the same values on every
+// call; it is called once per pass.  The whole workgroup calls this.
+template <int DT, typename Stream>
+__device__ __forceinline__ WList<uint64_t> radix_row_select(Stream&& stream, int V, int k, RowRadixShared& sh) {
     const int tid = threadIdx.x;
     const int wave = tid / WAVE;
     const int lane = lane_id();
-    const char* rowp = (const char*)logits + (int64_t)row * ld * (DT == SS_BF16 ? 2 : 4);
     constexpr int KB = DT == SS_BF16 ? 16 : 32;
     const int K = min(k, V);
 
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(RR_THREADS) void topk_radix_row_kernel(const void* 
         const int sft = shift - 8;
         clear_hist();
         __syncthreads();
-        rr_stream<DT>(rowp, V, aligned != 0, [&](int i, uint32_t raw) {
+        stream([&](int i, uint32_t raw) {
             const uint32_t u = rr_key<DT>(raw);
             const bool in = shift >= KB || (u >> shift) == prefix;
             rr_count(sh.hist[wave], (u >> sft) & 255u, in);
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(RR_THREADS) void topk_radix_row_kernel(const void* 
         if (above + cnt_b <= RR_CAP) {   // gather every element at or above the prefix
             if (tid == 0) sh.ctr = 0;
             __syncthreads();
-            rr_stream<DT>(rowp, V, aligned != 0, [&](int i, uint32_t raw) {
+            stream([&](int i, uint32_t raw) {
                 const uint32_t u = rr_key<DT>(raw);
                 if ((u >> shift) >= prefix) sh.cand[atomicAdd(&sh.ctr, 1)] = rr_key64<DT>(u, i);
             });
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(RR_THREADS) void topk_radix_row_kernel(const void* 
             const int sft = ish - 8;
             clear_hist();
             __syncthreads();
-            rr_stream<DT>(rowp, V, aligned != 0, [&](int i, uint32_t raw) {
+            stream([&](int i, uint32_t raw) {
                 const bool in = rr_key<DT>(raw) == prefix && (ish >= 24 || ((uint32_t)i >> ish) == ipre);
                 rr_count(sh.hist[wave], ((uint32_t)i >> sft) & 255u, in);
             });
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(RR_THREADS) void topk_radix_row_kernel(const void* 
             __syncthreads();
         }
         // ipre: the kneed-th lowest id among the ties
-        rr_stream<DT>(rowp, V, aligned != 0, [&](int i, uint32_t raw) {
+        stream([&](int i, uint32_t raw) {
             const uint32_t u = rr_key<DT>(raw);
             if (u > prefix || (u == prefix && (uint32_t)i <= ipre)) sh.cand[atomicAdd(&sh.ctr, 1)] = rr_key64<DT>(u, i);
         });
@@ -239,11 +239,30 @@ __global__ __launch_bounds__(RR_THREADS) void topk_radix_row_kernel(const void* 
     if (wave == 0) {
         const WList<uint64_t> o{sh.cand[KMAX + lane], sh.cand[KMAX + lane + WAVE]};
         mine = wave_merge(mine, o);
+        // ranks past K hold no element
+        if (lane >= K) mine.lo = 0ull;
+        if (lane + WAVE >= K) mine.hi = 0ull;
+    }
+    __syncthreads();   // the candidate area may be reused
+    return mine;
+}
+
+template <int DT>
+__global__ __launch_bounds__(RR_THREADS) void topk_radix_row_kernel(const void* logits, int V, int64_t ld,
+                                                                    int aligned, int k, int32_t* out_ids,
+                                                                    float* out_vals) {
+    __shared__ RowRadixShared sh;
+    const int row = blockIdx.x;
+    const char* rowp = (const char*)logits + (int64_t)row * ld * (DT == SS_BF16 ? 2 : 4);
+    const WList<uint64_t> best = radix_row_select<DT>(
+        [&](auto&& f) { rr_stream<DT>(rowp, V, aligned != 0, f); }, V, k, sh);
+    if (threadIdx.x < WAVE) {
+        const int lane = lane_id();
         for (int h = 0; h < 2; ++h) {
             const int r = lane + WAVE * h;
-            const uint64_t key = h ? mine.hi : mine.lo;
+            const uint64_t key = h ? best.hi : best.lo;
             if (r < k) {
-                const bool have = r < K && key != 0ull;
+                const bool have = key != 0ull;
                 out_ids[(int64_t)row * k + r] = have ? (int)(0xFFFFFFFFu - (uint32_t)key) : -1;
                 if (out_vals)
                     out_vals[(int64_t)row * k + r] = have ? unord32((uint32_t)(key >> 32)) : bitsf(F32_NINF_BITS);

@@ -382,3 +382,80 @@ def workload_c4(regime: str, rows: Optional[int] = None, B: int = 512, V: int = 
     else:
         raise ValueError(regime)
     return TopkWorkload(f"c4-{regime}", DTYPE_F32, x, 128)
+
+
+# ----------------------------------------------------------------------------
+# LM head (hidden states and vocabulary weights)
+# ----------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class LmheadWorkload:
+    name: str
+    hidden: np.ndarray   # uint16 [B, D] bf16 patterns
+    weight: np.ndarray   # uint16 [V, D] bf16 patterns, one row per token
+    req: Requests
+    exact: bool          # every product and partial sum exact in binary32
+
+
+LMHEAD_KINDS = ("normal", "grid")
+
+
+def workload_lmhead(kind: str = "normal", B: int = 64, D: int = 4096, V: int = 131072,
+                    seed: Optional[int] = None) -> LmheadWorkload:
+    """Synthetic LM head (seed data_seed(5) unless given).
+    'normal': weight ~ N(0, (2/sqrt(D))^2), hidden ~ N(0, 1), so logits have
+    a standard deviation of about 2; every second row also has a few
+    (2..8) tokens lifted by adding 4/|w_t|^2 * w_t per token to the hidden
+    state (about +4 on those logits), a peaked distribution.
+    'grid': hidden in {-1, -7/8, .., 1} and weights in {-1, -63/64, .., 1}
+    (uniform), so every product is a multiple of 2^-9 and every partial sum
+    stays below 2^12 in magnitude: the logits are exact in binary32 for any
+    summation order (D <= 4096), with many exact ties.
+    Requests: mixed_requests without lists (greedy half, T, top-k, top-p,
+    min-p mixes)."""
+    rng = np.random.default_rng(data_seed(5) if seed is None else seed)
+    req = mixed_requests(rng, B, V, penalties=False, bias=False)
+    if kind == "grid":
+        if D > 4096:
+            raise ValueError("grid inputs are exact only up to D = 4096")
+        h = to_bf16_bits((rng.integers(-8, 9, (B, D)) / 8).astype(np.float32))
+        w = to_bf16_bits((rng.integers(-64, 65, (V, D), dtype=np.int16) / np.float32(64)).astype(np.float32))
+        return LmheadWorkload(f"lmhead-grid-{B}x{D}x{V}", h, w, req, True)
+    if kind != "normal":
+        raise ValueError(kind)
+    wf = np.empty((V, D), np.float32)
+    step = max(1, (1 << 24) // D)
+    for v0 in range(0, V, step):   # in slices, to bound the float64 temporaries
+        wf[v0:v0 + step] = rng.standard_normal((min(step, V - v0), D), dtype=np.float32) * np.float32(2 / np.sqrt(D))
+    w = to_bf16_bits(wf)
+    wf = bf16_bits_to_f32(w)
+    hf = rng.standard_normal((B, D), dtype=np.float32)
+    for b in range(1, B, 2):
+        for t in rng.choice(V, int(rng.integers(2, 9)), replace=False):
+            hf[b] += np.float32(4.0 / float(np.dot(wf[t], wf[t]))) * wf[t]
+    del wf
+    return LmheadWorkload(f"lmhead-normal-{B}x{D}x{V}", to_bf16_bits(hf), w, req, False)
+
+
+def lmhead_device_inputs(B: int, D: int, V: int, seed: Optional[int] = None, device="cuda"):
+    """The 'normal' LM-head recipe of workload_lmhead drawn on the device
+    with torch's seeded generator (fast at vocabulary scale; not the same
+    values as the host recipe): bf16 hidden [B, D] and weight [V, D] and the
+    host requests."""
+    import torch
+    s = data_seed(5) if seed is None else seed
+    rng = np.random.default_rng(s)
+    req = mixed_requests(rng, B, V, penalties=False, bias=False)
+    g = torch.Generator(device=device)
+    g.manual_seed(s)
+    w = torch.empty((V, D), dtype=torch.bfloat16, device=device)
+    step = max(1, (1 << 26) // D)
+    for v0 in range(0, V, step):
+        n = min(step, V - v0)
+        w[v0:v0 + n] = (torch.randn((n, D), generator=g, device=device) * (2.0 / D ** 0.5)).to(torch.bfloat16)
+    h = torch.randn((B, D), generator=g, device=device)
+    for b in range(1, B, 2):
+        for t in rng.choice(V, int(rng.integers(2, 9)), replace=False):
+            wt = w[int(t)].float()
+            h[b] += (4.0 / float(torch.dot(wt, wt))) * wt
+    return h.to(torch.bfloat16), w, req

@@ -175,3 +175,35 @@ def test_request_packing(L):
         assert bool(f & L.SS_GRAMMAR)
         assert bool(f & L.SS_TOPK) == (wl.req.top_k[i] > 0)
     assert np.all(a["n_prior"] == 64) and np.all(a["n_bias"] == 16)
+
+
+def test_lmhead_argument_errors_return_before_launch(L):
+    lib = L.lib
+    P = None
+    f = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1008)
+    ws = L.lib.ss_lmhead_workspace_bytes(4, 50000)
+    assert ws >= 4 * 50000 * 4 + 4 * 4096 * 8 and ws % 256 == 0
+    assert L.lib.ss_lmhead_workspace_bytes(-1, 10) == 0
+    assert L.lib.ss_lmhead_workspace_bytes(4, 0) == 0
+
+    def step(h=f, ldh=256, w=f, ldw=256, B=4, D=256, V=50000, req=f, rng=f, tok=f, wsp=f, wsb=10**10):
+        return lib.ss_lmhead_sample_step(h, ldh, w, ldw, B, D, V, req, rng, 0, tok, P, P, P, P, P, wsp, wsb, P)
+
+    assert step(D=200, ldh=200, ldw=200) == L.SS_ERR_UNSUPPORTED      # D not a multiple of 128
+    assert step(D=1 << 17, ldh=1 << 17, ldw=1 << 17) == L.SS_ERR_UNSUPPORTED
+    assert step(ldh=260) == L.SS_ERR_UNSUPPORTED                      # row stride not a multiple of 8
+    assert step(ldh=128) == L.SS_ERR_INVALID_ARG                      # stride < D
+    assert step(h=odd) == L.SS_ERR_UNSUPPORTED                        # not 16-byte aligned
+    assert step(w=P) == L.SS_ERR_INVALID_ARG
+    assert step(req=P) == L.SS_ERR_INVALID_ARG
+    assert step(tok=P) == L.SS_ERR_INVALID_ARG
+    assert step(wsp=P) == L.SS_ERR_WORKSPACE
+    assert step(wsb=ws - 256) == L.SS_ERR_WORKSPACE
+    assert step(V=0) == L.SS_ERR_INVALID_ARG
+    assert step(V=(1 << 24) + 1) == L.SS_ERR_UNSUPPORTED
+    assert step(B=0, h=P, w=P, req=P, rng=P, tok=P, wsp=P, wsb=0) == L.SS_OK
+    assert lib.ss_lmhead_logits(f, 256, f, 256, 4, 256, 1000, f, 999, P) == L.SS_ERR_INVALID_ARG   # ldo < V
+    assert lib.ss_lmhead_logits(f, 256, f, 256, 4, 256, 1000, P, 1000, P) == L.SS_ERR_INVALID_ARG
+    assert lib.ss_lmhead_logits(f, 256, f, 256, 4, 192, 1000, f, 1000, P) == L.SS_ERR_UNSUPPORTED
+    assert lib.ss_lmhead_logits(P, 256, P, 256, 0, 256, 1000, P, 1000, P) == L.SS_OK
