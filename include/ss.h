@@ -388,6 +388,35 @@ int ss_lmhead_sample_step(const void* hidden, int64_t ldh, const void* weight, i
  * effect. */
 int ss_stream_read(const void* p, size_t bytes, int nblocks, uint32_t* out, void* stream);
 
+/* The sampling epilogue's written functions, for checking them against an
+ * independent implementation over their whole domains (diagnostic; the
+ * same inline device functions the sampling kernels call).  Element i
+ * (0 <= i < n <= 2^32) takes the 32-bit argument a = first + i (mod 2^32)
+ * and out[i] (device, [n] uint32) receives the result's bit pattern:
+ *   SS_SPEC_EXP          exp of the float with bits a, for the arguments
+ *                        x = v_k - v_1 <= 0 of the epilogue (ss_sample_step;
+ *                        below -86 gives 0; NaN is outside the domain)
+ *   SS_SPEC_LOG          ln of the float with bits a (every input)
+ *   SS_SPEC_LOG_NORMAL   ln for positive normal finite floats (the
+ *                        branch-free form used inside the noise)
+ *   SS_SPEC_GUMBEL_WORD  -ln(-ln u) for u = (a + 1/2) 2^-23, the uniform of
+ *                        every Philox word whose top 23 bits are a (a < 2^23)
+ *   SS_SPEC_PHILOX       the Philox word for counter {a, c1, c2, offset_lo}
+ *                        under key {seed_lo, seed_hi ^ offset_hi}
+ *   SS_SPEC_GUMBEL       the Gumbel noise for that counter
+ * Errors: SS_ERR_INVALID_ARG for an unknown fn, n outside [0, 2^32] or a
+ * NULL out with n > 0. */
+enum {
+    SS_SPEC_EXP = 0,
+    SS_SPEC_LOG = 1,
+    SS_SPEC_LOG_NORMAL = 2,
+    SS_SPEC_GUMBEL_WORD = 3,
+    SS_SPEC_PHILOX = 4,
+    SS_SPEC_GUMBEL = 5
+};
+int ss_spec_eval(int fn, uint32_t first, int64_t n, uint32_t c1, uint32_t c2, uint64_t seed, uint64_t offset,
+                 uint32_t* out, void* stream);
+
 /* rng->offset += delta on the device (one tiny kernel; capturable). */
 int ss_rng_advance(ss_rng* rng, uint64_t delta, void* stream);
 

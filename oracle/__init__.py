@@ -68,6 +68,9 @@ def lib():
         L.oracle_log_spec.restype = ctypes.c_float
         L.oracle_exp_spec_n.argtypes = [P, P, i64]
         L.oracle_log_spec_n.argtypes = [P, P, i64]
+        L.oracle_spec_sweep.argtypes = [i32, ctypes.c_uint32, i64, ctypes.c_uint32, ctypes.c_uint32, u64, u64, P,
+                                        i32]
+        L.oracle_spec_sweep.restype = i32
         L.oracle_uniform.argtypes = [ctypes.c_uint32]
         L.oracle_uniform.restype = ctypes.c_float
         L.oracle_philox_word.argtypes = [u64, u64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32]
@@ -134,6 +137,20 @@ def log_spec_n(x) -> np.ndarray:
 
 def uniform(w: int) -> np.float32:
     return np.float32(lib().oracle_uniform(int(w)))
+
+
+SWEEP_EXP, SWEEP_LOG, SWEEP_GUMBEL_WORD, SWEEP_PHILOX, SWEEP_GUMBEL = range(5)
+
+
+def spec_sweep(fn: int, first: int, n: int, c1: int = 0, c2: int = 0, seed: int = 0, offset: int = 0,
+               threads: int = 1) -> np.ndarray:
+    """32-bit results of a spec function over the arguments first .. first
+    + n - 1 (float bit patterns, Philox words, or counter words c0; see
+    oracle_spec_sweep)."""
+    out = np.empty(n, np.uint32)
+    rc = lib().oracle_spec_sweep(fn, first & 0xFFFFFFFF, n, c1, c2, seed, offset, _p(out), threads)
+    assert rc == 0
+    return out
 
 
 def philox_word(seed: int, offset: int, c0: int, c1: int, c2: int) -> int:

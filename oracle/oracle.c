@@ -1026,3 +1026,59 @@ void oracle_log_spec_n(const float* x, float* y, int64_t n)
 {
     for (int64_t i = 0; i < n; ++i) y[i] = oracle_log_spec(x[i]);
 }
+
+/* ======================================================================
+ * Whole-domain sweeps of the spec functions, for the tests: element i of
+ * a range takes the 32-bit pattern first + i as its argument.
+ *   fn 0: oracle_exp_spec          (argument: float bits)
+ *   fn 1: oracle_log_spec          (argument: float bits)
+ *   fn 2: Gumbel noise -ln(-ln u) of the uniform u of the Philox words
+ *         whose top 23 bits are the argument               (argument < 2^23)
+ *   fn 3: Philox word for counter (first + i, c1, c2)    (seed, offset)
+ *   fn 4: Gumbel noise for counter (first + i, c1, c2)   (seed, offset)
+ * Results are written as 32-bit patterns.
+ * ====================================================================== */
+typedef struct {
+    int fn;
+    uint32_t first, c1, c2;
+    uint64_t seed, offset;
+    uint32_t* out;
+    int64_t lo, hi;
+} sweep_job;
+
+static uint32_t sweep_one(const sweep_job* j, uint32_t a)
+{
+    switch (j->fn) {
+    case 0: return f2u(oracle_exp_spec(u2f(a)));
+    case 1: return f2u(oracle_log_spec(u2f(a)));
+    case 2: return f2u(-oracle_log_spec(-oracle_log_spec(oracle_uniform(a << 9))));
+    case 3: return oracle_philox_word(j->seed, j->offset, a, j->c1, j->c2);
+    default: return f2u(oracle_gumbel(j->seed, j->offset, a, j->c1, j->c2));
+    }
+}
+
+static void* sweep_worker(void* p)
+{
+    sweep_job* j = (sweep_job*)p;
+    for (int64_t i = j->lo; i < j->hi; ++i) j->out[i] = sweep_one(j, j->first + (uint32_t)i);
+    return NULL;
+}
+
+int oracle_spec_sweep(int fn, uint32_t first, int64_t n, uint32_t c1, uint32_t c2, uint64_t seed,
+                      uint64_t offset, uint32_t* out, int threads)
+{
+    if (fn < 0 || fn > 4 || n < 0) return -1;
+    if (threads < 1) threads = 1;
+    if (threads > 64) threads = 64;
+    sweep_job jobs[64];
+    pthread_t tid[64];
+    for (int t = 0; t < threads; ++t) {
+        sweep_job j = {fn, first, c1, c2, seed, offset, out, n * t / threads, n * (t + 1) / threads};
+        jobs[t] = j;
+        if (threads == 1) sweep_worker(&jobs[t]);
+        else pthread_create(&tid[t], NULL, sweep_worker, &jobs[t]);
+    }
+    if (threads > 1)
+        for (int t = 0; t < threads; ++t) pthread_join(tid[t], NULL);
+    return 0;
+}

@@ -104,6 +104,8 @@ def _load():
     L.ss_lmhead_logits.restype = i32
     L.ss_lmhead_sample_step.argtypes = [P, i64, P, i64, i32, i32, i32, P, P, u64, P, P, P, P, P, P, P, sz, P]
     L.ss_lmhead_sample_step.restype = i32
+    L.ss_spec_eval.argtypes = [i32, ctypes.c_uint32, i64, ctypes.c_uint32, ctypes.c_uint32, u64, u64, P, P]
+    L.ss_spec_eval.restype = i32
     L.ss_status_str.argtypes = [i32]
     L.ss_status_str.restype = ctypes.c_char_p
     return L
@@ -114,7 +116,7 @@ lib = _load()
 EXPORTS = ["ss_workspace_bytes", "ss_tile_size", "ss_sample_step", "ss_sample_step_noalloc", "ss_verify_step", "ss_verify_step_var",
            "ss_verify_dense_workspace_bytes", "ss_verify_step_dense", "ss_topk_step", "ss_topk_step_radix",
            "ss_topk_single_pass", "ss_tile_topk", "ss_lmhead_workspace_bytes", "ss_lmhead_logits",
-           "ss_lmhead_sample_step", "ss_rng_advance", "ss_stream_read", "ss_status_str"]
+           "ss_lmhead_sample_step", "ss_spec_eval", "ss_rng_advance", "ss_stream_read", "ss_status_str"]
 
 
 class SsError(RuntimeError):
@@ -384,6 +386,17 @@ def ss_lmhead_sample_step(hidden, weight, dreq: DeviceRequests, rng, out_tokens,
                                    ptr(dreq.req), ptr(rng), rng_advance, ptr(out_tokens), ptr(out_topk_ids),
                                    ptr(out_probs), ptr(out_kept), ptr(out_mass), ptr(out_status), ptr(ws),
                                    0 if ws is None else ws.numel(), stream_handle(stream))
+    return _check(rc)
+
+
+SS_SPEC_EXP, SS_SPEC_LOG, SS_SPEC_LOG_NORMAL, SS_SPEC_GUMBEL_WORD, SS_SPEC_PHILOX, SS_SPEC_GUMBEL = range(6)
+
+
+def ss_spec_eval(fn: int, first: int, out, c1: int = 0, c2: int = 0, seed: int = 0, offset: int = 0,
+                 stream=None) -> int:
+    """out[i] = the device function fn at argument first + i (out: int32 or
+    uint32 device tensor of n elements)."""
+    rc = lib.ss_spec_eval(fn, first & 0xFFFFFFFF, out.numel(), c1, c2, seed, offset, ptr(out), stream_handle(stream))
     return _check(rc)
 
 

@@ -168,6 +168,25 @@ __global__ void rng_advance_kernel(ss_rng* rng, uint64_t delta) {
     if (threadIdx.x == 0 && blockIdx.x == 0) rng->offset += delta;
 }
 
+// The epilogue's written functions, element by element over the arguments
+// first + i (the same inline functions the sampling kernels call).
+__global__ void spec_eval_kernel(int fn, uint32_t first, int64_t n, uint32_t c1, uint32_t c2, uint64_t seed,
+                                 uint64_t offset, uint32_t* out) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const uint32_t a = first + (uint32_t)i;
+        uint32_t r;
+        switch (fn) {
+        case SS_SPEC_EXP: r = fbits(exp_fixed_nonpos(bitsf(a))); break;
+        case SS_SPEC_LOG: r = fbits(log_fixed(bitsf(a))); break;
+        case SS_SPEC_LOG_NORMAL: r = fbits(log_fixed_normal(bitsf(a))); break;
+        case SS_SPEC_GUMBEL_WORD: r = fbits(-log_fixed_normal(-log_fixed_normal(unit_open(a << 9)))); break;
+        case SS_SPEC_PHILOX: r = philox_w0(seed, offset, a, c1, c2); break;
+        default: r = fbits(gumbel_noise(seed, offset, a, c1, c2)); break;
+        }
+        out[i] = r;
+    }
+}
+
 // A plain streaming read, the bandwidth reference of the measurements:
 // 16-byte loads over the buffer (word i goes to workgroup (i mod
 // 256*gridDim) / 256), four in flight per thread, with the streaming
@@ -506,6 +525,17 @@ int ss_stream_read(const void* p, size_t bytes, int nblocks, uint32_t* out, void
     if (!out || (bytes && !p) || ((uintptr_t)p & 15u) || (bytes & 15u)) return SS_ERR_INVALID_ARG;
     hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)nblocks), dim3(256), 0, (hipStream_t)stream,
                        (const sr_u32x4*)p, (uint64_t)(bytes / 16), out);
+    return launched();
+}
+
+int ss_spec_eval(int fn, uint32_t first, int64_t n, uint32_t c1, uint32_t c2, uint64_t seed, uint64_t offset,
+                 uint32_t* out, void* stream) {
+    if (fn < SS_SPEC_EXP || fn > SS_SPEC_GUMBEL || n < 0 || n > ((int64_t)1 << 32)) return SS_ERR_INVALID_ARG;
+    if (n == 0) return SS_OK;
+    if (!out) return SS_ERR_INVALID_ARG;
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(spec_eval_kernel, dim3((unsigned)(blocks < 16384 ? blocks : 16384)), dim3(256), 0,
+                       (hipStream_t)stream, fn, first, n, c1, c2, seed, offset, out);
     return launched();
 }
 

@@ -21,7 +21,8 @@ from speculative_decoding_verification_stage1_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 
-RTOL = 1e-5
+from test_gpu_parity import same_bits  # noqa: E402
+
 KEYS = ("tokens", "topk_ids", "probs", "kept", "mass", "status")
 
 
@@ -98,8 +99,8 @@ def compare_exact(g, o, rows=None, tag=""):
         msg = f"{tag} row {r}"
         for k in ("status", "topk_ids", "kept", "tokens"):
             assert np.array_equal(g[k][r], o[k][r]), (k, msg)
-        np.testing.assert_allclose(g["probs"][r], o["probs"][r], rtol=RTOL, atol=1e-30, err_msg=msg)
-        np.testing.assert_allclose(g["mass"][r], o["mass"][r], rtol=RTOL, atol=1e-30, err_msg=msg)
+        same_bits(g["probs"][r], o["probs"][r], msg)
+        same_bits(g["mass"][r], o["mass"][r], msg)
 
 
 def compare_robust(g, o, rows=None, tag=""):

@@ -22,7 +22,7 @@ from speculative_decoding_verification_stage1_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 
-RTOL = 1e-5
+from test_gpu_parity import same_bits  # noqa: E402
 
 
 def _lib():
@@ -146,8 +146,8 @@ def _sample_parity(x, dtype, req, pad, seed):
     for r in range(B):
         for k in ("status", "topk_ids", "kept", "tokens"):
             assert np.array_equal(g[k][r], ref[k][r]), (k, r)
-        np.testing.assert_allclose(g["probs"][r], ref["probs"][r], rtol=RTOL, atol=1e-30, err_msg=str(r))
-        np.testing.assert_allclose(g["mass"][r], ref["mass"][r], rtol=RTOL, atol=1e-30, err_msg=str(r))
+        same_bits(g["probs"][r], ref["probs"][r], str(r))
+        same_bits(g["mass"][r], ref["mass"][r], str(r))
 
 
 @pytest.mark.parametrize("pad", [0, 3])

@@ -93,42 +93,58 @@ def _sweep(lo_bits, hi_bits, stride):
     return bits.view(np.float32)
 
 
+SWEEP_CHUNK = 1 << 23
+
+
+def _chunk_err(fn, a, n, ref_fn):
+    x = np.arange(a, a + n, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    y = oracle.spec_sweep(fn, a, n).view(np.float32).astype(np.float64)
+    ref = ref_fn(x.astype(np.float64))
+    nz = ref != 0
+    err = np.zeros(n)
+    err[nz] = np.abs(y[nz] - ref[nz]) / _ulp32(ref[nz])
+    i = int(np.argmax(err))
+    return float(err[i]), float(x[i])
+
+
+def _max_ulp_err(fn, lo_bits, hi_bits, ref_fn):
+    """Largest error in binary32 ulps of the oracle's fn over EVERY float
+    with bits in [lo_bits, hi_bits), against ref_fn in float64 (chunks in
+    a thread pool: the oracle's C and numpy's loops release the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
+    starts = range(lo_bits, hi_bits, SWEEP_CHUNK)
+    with ThreadPoolExecutor(max_workers=os.cpu_count() or 1) as ex:
+        res = list(ex.map(lambda a: _chunk_err(fn, a, min(SWEEP_CHUNK, hi_bits - a), ref_fn), starts))
+    return max(res)
+
+
 def test_exp_spec_within_2ulp():
-    # negative floats from -0 (0x80000000) down to -86 (0xC2AC0000)
-    xs = [_sweep(0x80000000, 0xC2AC0000, 97),
-          -np.linspace(0, 1e-3, 20001, dtype=np.float32),
-          np.linspace(-86.0, -85.0, 20001, dtype=np.float32),
-          np.linspace(-1.0, 0.0, 200001, dtype=np.float32)]
-    x = np.concatenate(xs)
-    y = oracle.exp_spec_n(x).astype(np.float64)
-    ref = np.exp(x.astype(np.float64))
-    err = np.abs(y - ref) / _ulp32(ref)
-    assert err.max() <= 2.0, (err.max(), x[np.argmax(err)])
+    # every float from -0 (0x80000000) down to -86 (0xC2AC0000): the
+    # arguments x = v - v_1 the epilogue can pass above the cut
+    worst, at = _max_ulp_err(oracle.SWEEP_EXP, 0x80000000, 0xC2AC0001, np.exp)
+    assert worst <= 2.0, (worst, at)
     assert oracle.exp_spec(0.0) == 1.0
     assert oracle.exp_spec(-np.inf) == 0.0
     assert oracle.exp_spec(-86.5) == 0.0
-    # monotone on a dense grid
+    # below the cut: every float from -86 (exclusive) to -inf gives 0
+    assert not np.any(oracle.spec_sweep(oracle.SWEEP_EXP, 0xC2AC0001, 0xFF800001 - 0xC2AC0001,
+                                        threads=os.cpu_count() or 1))
+    # monotone on a dense grid (a written polynomial can step back by an
+    # ulp between neighbouring floats; the grid's steps are far wider)
     g = np.linspace(-20, 0, 400001, dtype=np.float32)
     assert np.all(np.diff(oracle.exp_spec_n(g).astype(np.float64)) >= 0)
 
 
 def test_log_spec_within_2ulp():
-    # every positive finite float, strided; subnormals included
-    x = np.concatenate([_sweep(1, 0x7F800000, 131),
-                        np.linspace(0.99, 1.01, 200001, dtype=np.float32),
-                        (np.arange(1, 4096, dtype=np.uint32)).view(np.float32)])
-    x = x[x > 0]
-    y = oracle.log_spec_n(x).astype(np.float64)
-    ref = np.log(x.astype(np.float64))
-    nz = ref != 0
-    err = np.zeros_like(ref)
-    err[nz] = np.abs(y[nz] - ref[nz]) / _ulp32(ref[nz])
-    assert err.max() <= 2.0, (err.max(), x[np.argmax(err)])
-    assert oracle.log_spec(1.0) == 0.0
-    assert oracle.log_spec(0.0) == -np.inf
-    assert np.isnan(oracle.log_spec(-1.0))
+    # every positive finite float, subnormals included
+    worst, at = _max_ulp_err(oracle.SWEEP_LOG, 1, 0x7F800000, np.log)
+    assert worst <= 2.0, (worst, at)
     g = np.linspace(1e-6, 20, 400001, dtype=np.float32)
     assert np.all(np.diff(oracle.log_spec_n(g).astype(np.float64)) >= 0)
+    assert oracle.log_spec(1.0) == 0.0
+    assert oracle.log_spec(0.0) == -np.inf
+    assert oracle.log_spec(np.inf) == np.inf
+    assert np.isnan(oracle.log_spec(-1.0))
 
 
 def test_uniform_mapping():
