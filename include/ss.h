@@ -50,6 +50,8 @@ extern "C" {
 #define SS_KMAX 128        /* bounded candidate set (SonicSampler section 3.3) */
 #define SS_GAMMA_MAX 16    /* largest number of draft tokens per request */
 #define SS_V_MAX (1 << 24) /* largest vocabulary */
+#define SS_PRIOR_MAX 4096  /* longest prior (penalty history) list per request */
+#define SS_BIAS_MAX 1024   /* longest logit-bias list per request */
 /* size of the static workspace behind ss_sample_step_noalloc, per GPU */
 #define SS_NOALLOC_WS_BYTES (16u << 20)
 
@@ -94,23 +96,28 @@ enum {
 
 /* One request, 32 bytes, in device memory (so a captured graph can be
  * replayed with new settings).  Field semantics:
- *   temperature  stochastic rows need a finite T > 0; T <= 0 means greedy;
- *                NaN or +inf makes the row invalid (unless SS_GREEDY).
+ *   flags        SS_* bits above.
  *   top_k        with SS_TOPK: 1 means greedy, 2..128 bound the candidates,
  *                > 128 is clamped (SS_ROW_TOPK_CLAMPED), 0 is invalid.
  *                Without SS_TOPK the bound is 128.
- *   n_prior      entries of the row's prior list used (<= prior_stride).
- *   n_bias       entries of the row's bias list used (<= bias_stride).
+ *   temperature  stochastic rows need a finite T > 0; T <= 0 means greedy;
+ *                NaN or +inf makes the row invalid (unless SS_GREEDY).
+ *   n_prior      entries of the row's prior list used (<= prior_stride and
+ *                <= SS_PRIOR_MAX, else the row is invalid): the penalty
+ *                history, every distinct token generated so far with its
+ *                count.
+ *   n_bias       entries of the row's bias list used (<= bias_stride and
+ *                <= SS_BIAS_MAX, else the row is invalid).
  *   top_p        with SS_TOPP: in (0, 1]; 1 keeps every candidate.
  *   min_p        with SS_MINP: in [0, 1]; 0 keeps every candidate.
  *   rep_penalty  with SS_REP: finite, > 0 (theta).
  *   freq_penalty, pres_penalty  with SS_FREQPRES: finite. */
 typedef struct ss_req {
-    uint32_t flags;
-    float temperature;
+    uint16_t flags;
     uint16_t top_k;
-    uint8_t n_prior;
-    uint8_t n_bias;
+    float temperature;
+    uint16_t n_prior;
+    uint16_t n_bias;
     float top_p;
     float min_p;
     float rep_penalty;

@@ -284,12 +284,22 @@ typedef struct {
 
 static int finite_f(float x) { return isfinite(x); }
 
+/* Longest lists a request may name (the interface's validity rule: a
+ * longer list makes the row invalid, like one longer than its stride). */
+#define OPRIOR_MAX 4096
+#define OBIAS_MAX 1024
+
+static int lists_fit(const oreq* r, int prior_stride, int bias_stride)
+{
+    return r->n_prior >= 0 && r->n_prior <= prior_stride && r->n_prior <= OPRIOR_MAX &&
+           r->n_bias >= 0 && r->n_bias <= bias_stride && r->n_bias <= OBIAS_MAX;
+}
+
 static int validate(const oreq* r, int prior_stride, int bias_stride, const float* bias_val,
                     int* greedy)
 {
     uint32_t f = r->flags;
-    if (r->n_prior < 0 || r->n_prior > prior_stride) return 0;
-    if (r->n_bias < 0 || r->n_bias > bias_stride) return 0;
+    if (!lists_fit(r, prior_stride, bias_stride)) return 0;
     if ((f & OF_REP) && !(finite_f(r->rep) && r->rep > 0.0f)) return 0;
     if ((f & OF_FREQPRES) && !(finite_f(r->freq) && finite_f(r->pres))) return 0;
     if (f & OF_BIAS)
@@ -440,8 +450,7 @@ static void* sample_worker(void* arg)
     for (int b = J->row_begin; b < J->row_end; ++b) {
         const oreq* r = &J->req[b];
         const float* bv = J->bias_val ? J->bias_val + (int64_t)b * J->bias_stride : NULL;
-        int valid_shape = (r->n_prior >= 0 && r->n_prior <= J->prior_stride &&
-                           r->n_bias >= 0 && r->n_bias <= J->bias_stride) && arrays_ok(r, J);
+        int valid_shape = lists_fit(r, J->prior_stride, J->bias_stride) && arrays_ok(r, J);
         if (valid_shape) prelude_for(J, r, b, b, z);
         if (valid_shape) decide_row(r, z, J->V, J->prior_stride, J->bias_stride, bv, work, d);
         else { memset(d, 0, sizeof(*d)); d->status = OST_INVALID; }
@@ -598,8 +607,7 @@ static void* verify_worker(void* arg)
         int emitted = 0;
         int st = OST_OK;
         const float* bv = J->bias_val ? J->bias_val + (int64_t)b * J->bias_stride : NULL;
-        if (!(r->n_prior >= 0 && r->n_prior <= J->prior_stride &&
-              r->n_bias >= 0 && r->n_bias <= J->bias_stride) || !arrays_ok(r, &S)) {
+        if (!lists_fit(r, J->prior_stride, J->bias_stride) || !arrays_ok(r, &S)) {
             st = OST_INVALID;
         }
         /* this request's draft count: gamma, or from the cumulative offsets */
@@ -988,8 +996,8 @@ int oracle_tile_topk(const void* logits, int dtype, int rows, int V, int64_t ld,
     for (int r = 0; r < rows; ++r) {
         int b = r / rows_per_req;
         oreq q = req ? req[b] : (oreq){0};
-        if (q.n_prior < 0 || q.n_prior > prior_stride) q.n_prior = 0;
-        if (q.n_bias < 0 || q.n_bias > bias_stride) q.n_bias = 0;
+        if (q.n_prior < 0 || q.n_prior > prior_stride || q.n_prior > OPRIOR_MAX) q.n_prior = 0;
+        if (q.n_bias < 0 || q.n_bias > bias_stride || q.n_bias > OBIAS_MAX) q.n_bias = 0;
         prelude_for(&S, &q, r, b, z);
         memset(listed, 0, (size_t)V);
         if (q.flags & (OF_REP | OF_FREQPRES))

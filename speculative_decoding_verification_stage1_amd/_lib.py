@@ -45,7 +45,7 @@ SS_MINP = 1 << 7
 
 # struct ss_req (32 bytes)
 SS_REQ = np.dtype([
-    ("flags", "<u4"), ("temperature", "<f4"), ("top_k", "<u2"), ("n_prior", "u1"), ("n_bias", "u1"),
+    ("flags", "<u2"), ("top_k", "<u2"), ("temperature", "<f4"), ("n_prior", "<u2"), ("n_bias", "<u2"),
     ("top_p", "<f4"), ("min_p", "<f4"), ("rep_penalty", "<f4"), ("freq_penalty", "<f4"),
     ("pres_penalty", "<f4"),
 ])
@@ -172,8 +172,8 @@ def pack_requests(req, flags=None) -> np.ndarray:
     a["flags"] = [flags_of(req, i) for i in range(B)] if flags is None else flags
     a["temperature"] = req.temperature
     a["top_k"] = np.clip(req.top_k, 0, 65535)
-    a["n_prior"] = np.clip(req.n_prior, 0, 255)
-    a["n_bias"] = np.clip(req.n_bias, 0, 255)
+    a["n_prior"] = np.clip(req.n_prior, 0, 65535)
+    a["n_bias"] = np.clip(req.n_bias, 0, 65535)
     a["top_p"] = req.top_p
     a["min_p"] = req.min_p
     a["rep_penalty"] = req.rep_penalty

@@ -8,6 +8,7 @@
 #include "ss_radix.h"
 #include "ss_radix_row.h"
 #include "ss_lmhead.h"
+#include "ss_listed_long.h"
 
 using namespace ssd;
 
@@ -115,6 +116,17 @@ void launch_stage1(int dtype, const Stage1Params& p, hipStream_t s) {
     const dim3 grid((unsigned)(listed_wgs + p.rows * p.Zv)), block(S1_THREADS);
     if (dtype == SS_BF16) hipLaunchKernelGGL(stage1_kernel<SS_BF16>, grid, block, 0, s, p);
     else hipLaunchKernelGGL(stage1_kernel<SS_F32>, grid, block, 0, s, p);
+}
+
+// Rows whose lists are longer than LIST_SHORT are ranked by one more
+// launch, issued only when the strides allow such lists.
+void launch_listed_long(int dtype, const Stage1Params& p, hipStream_t s) {
+    const bool long_prior = p.aux.prior_ids && p.aux.prior_cnt && p.aux.prior_stride > LIST_SHORT;
+    const bool long_bias = p.aux.bias_ids && p.aux.bias_stride > LIST_SHORT;
+    if (!(long_prior || long_bias) || p.listed_rows == 0) return;
+    const dim3 grid((unsigned)p.listed_rows), block(LL_THREADS);
+    if (dtype == SS_BF16) hipLaunchKernelGGL(listed_long_kernel<SS_BF16>, grid, block, 0, s, p);
+    else hipLaunchKernelGGL(listed_long_kernel<SS_F32>, grid, block, 0, s, p);
 }
 
 template <int MODE>
@@ -264,6 +276,7 @@ int ss_sample_step(const void* logits, int dtype, int B, int V, int64_t ld, cons
     s1.rng_snap = W.rng_snap;
     s1.rng_advance = rng_advance;
     launch_stage1(dtype, s1, s);
+    launch_listed_long(dtype, s1, s);
     Stage2Params f = make_s2(s1, W.rng_snap, MODE_SAMPLE, W);
     f.tokens = out_tokens;
     f.topk_ids = out_topk_ids;
@@ -333,6 +346,7 @@ int ss_verify_step_var(const void* target_logits, int dtype, int B, int gamma, i
         s1.n_clear = B;
     }
     launch_stage1(dtype, s1, s);
+    launch_listed_long(dtype, s1, s);
     Stage2Params f = make_s2(s1, W.rng_snap, MODE_VERIFY, W);
     f.gamma = gamma;
     f.draft_ids = draft_ids;

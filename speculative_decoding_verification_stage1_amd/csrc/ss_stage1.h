@@ -292,7 +292,7 @@ struct S1In {
     uint32_t gw[S1_CPT * S1Traits<DT>::EPC / 32];   // the tile's bitmask words tid + 256k
     int l_pid, l_pct, l_bid;    // entries 64lw .. 64lw+63 of the request's lists (lw: wave after the lead)
     int l_did;                  // lead wave: draft `lane` of the request (verification), or -1
-    uint32_t rq_flags, rq_lists; // the request's flags and its n_prior | n_bias << 8
+    uint32_t rq_flags, rq_lists; // the request's flags and its n_prior | n_bias << 16
 };
 
 __device__ __forceinline__ int s1_lead_wave() { return (int)((blockIdx.x >> 3) & (S1_WAVES - 1)); }
@@ -398,8 +398,8 @@ __device__ __forceinline__ void tile_fetch(const Stage1Params& P, int row, int t
     in.rq_lists = 0;
     if (P.req) {
         const auto rq = (const uint32_t*)(P.req + b);
-        in.rq_flags = rq[0];
-        in.rq_lists = rq[2] >> 16;   // n_prior, n_bias follow the 16-bit top_k
+        in.rq_flags = rq[0] & 0xFFFFu;   // the 16-bit flags (top_k above them)
+        in.rq_lists = rq[2];              // n_prior | n_bias << 16
     }
 }
 
@@ -797,10 +797,11 @@ __device__ __forceinline__ void tile_process(const Stage1Params& P, int row, int
 
     const uint32_t flags = __builtin_amdgcn_readfirstlane(in.rq_flags);
     const uint32_t lists = __builtin_amdgcn_readfirstlane(in.rq_lists);
-    // a list longer than its stride makes the row invalid (reported by
-    // Stage 2); the tiles then use no list at all
-    const int n_prior = (int)(lists & 0xFFu) <= P.aux.prior_stride ? (int)(lists & 0xFFu) : 0;
-    const int n_bias = (int)(lists >> 8) <= P.aux.bias_stride ? (int)(lists >> 8) : 0;
+    // a list longer than its stride or its limit makes the row invalid
+    // (reported by Stage 2); the tiles then use no list at all
+    const int np_all = (int)(lists & 0xFFFFu), nb_all = (int)(lists >> 16);
+    const int n_prior = np_all <= P.aux.prior_stride && np_all <= SS_PRIOR_MAX ? np_all : 0;
+    const int n_bias = nb_all <= P.aux.bias_stride && nb_all <= SS_BIAS_MAX ? nb_all : 0;
     const bool use_grammar = (flags & SS_GRAMMAR) && P.aux.bitmask;
     const bool use_prior = (flags & (SS_REP | SS_FREQPRES)) && P.aux.prior_ids && P.aux.prior_cnt && n_prior > 0;
     const bool use_bias = (flags & SS_BIAS) && P.aux.bias_ids && n_bias > 0;
@@ -828,8 +829,9 @@ __device__ __forceinline__ void tile_process(const Stage1Params& P, int row, int
 
     // ---- tokens of this tile named by an active list (ranked in Stage 2,
     // left out here): the wave lw places after the lead records list
-    // entries 64lw .. 64lw+63 (the lists hold at most 255 entries), the lead
-    // wave also the earlier drafts ----
+    // entries 64lw .. 64lw+63, the lead wave also the earlier drafts; the
+    // entries past the first 256 of a longer list go straight into the
+    // mask below ----
     const int lw = (wave - lead) & (S1_WAVES - 1);
     const bool has_slice = (use_prior && n_prior > lw * WAVE) || (use_bias && n_bias > lw * WAVE) || wave == lead;
     if (has_slice) {   // wave-uniform
@@ -874,7 +876,8 @@ __device__ __forceinline__ void tile_process(const Stage1Params& P, int row, int
     // grammar mask, or when there are too many of them to leave in the data:
     // the mask then leaves them out like any disallowed token, and the
     // threshold and survivor steps need not know about them.
-    const bool fold = nl > 0 && (use_grammar || nl > S1_NL_FAST);   // block-uniform
+    const bool long_lists = (use_prior && n_prior > S1_WAVES * WAVE) || (use_bias && n_bias > S1_WAVES * WAVE);
+    const bool fold = (nl > 0 && (use_grammar || nl > S1_NL_FAST)) || long_lists;   // block-uniform
     const bool use_mask = use_grammar || fold;
     if (fold) {
         if (!use_grammar) {   // an all-ones mask to clear them from
@@ -889,6 +892,18 @@ __device__ __forceinline__ void tile_process(const Stage1Params& P, int row, int
                 const int loc = sh.listed[w][i];
                 atomicAnd(&sh.gmw[loc >> 5], ~(1u << (loc & 31)));
             }
+        if (long_lists) {   // the entries past the recorded 256
+            const int64_t ob = (int64_t)b * P.aux.prior_stride, obb = (int64_t)b * P.aux.bias_stride;
+            for (int j = S1_WAVES * WAVE + tid; use_prior && j < n_prior; j += S1_THREADS) {
+                const int id = gmem(P.aux.prior_ids)[ob + j], loc = id - base;
+                if (gmem(P.aux.prior_cnt)[ob + j] >= 1 && id >= 0 && id < P.V && loc >= 0 && loc < nvalid)
+                    atomicAnd(&sh.gmw[loc >> 5], ~(1u << (loc & 31)));
+            }
+            for (int j = S1_WAVES * WAVE + tid; use_bias && j < n_bias; j += S1_THREADS) {
+                const int id = gmem(P.aux.bias_ids)[obb + j], loc = id - base;
+                if (id >= 0 && id < P.V && loc >= 0 && loc < nvalid) atomicAnd(&sh.gmw[loc >> 5], ~(1u << (loc & 31)));
+            }
+        }
         __syncthreads();
     }
     const int nl_data = fold ? 0 : nl;   // listed tokens still present in the data (<= 128)

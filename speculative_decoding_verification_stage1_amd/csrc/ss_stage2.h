@@ -118,7 +118,9 @@ __device__ inline RowParams row_params(const Stage1Params& P, int b, const float
     rp.freq = r.freq_penalty;
     rp.pres = r.pres_penalty;
     bool ok = true;
-    if ((int)r.n_prior > P.aux.prior_stride || (int)r.n_bias > P.aux.bias_stride) ok = false;
+    if ((int)r.n_prior > P.aux.prior_stride || (int)r.n_bias > P.aux.bias_stride || r.n_prior > SS_PRIOR_MAX ||
+        r.n_bias > SS_BIAS_MAX)
+        ok = false;
     if ((f & SS_GRAMMAR) && !P.aux.bitmask) ok = false;
     if ((f & (SS_REP | SS_FREQPRES)) && r.n_prior > 0 && (!P.aux.prior_ids || !P.aux.prior_cnt)) ok = false;
     if ((f & SS_BIAS) && r.n_bias > 0 && (!P.aux.bias_ids || !P.aux.bias_val)) ok = false;
@@ -203,17 +205,21 @@ __device__ __forceinline__ float readlane_f(float v, int l) {
 
 using WL64 = WList<uint64_t>;
 
+// Lists up to this length are ranked by one wave of the Stage-1 launch
+// (staged in that wave's LDS area); longer ones by listed_long_kernel.
+constexpr int LIST_SHORT = 256;
+
 // The row's side lists, staged in LDS by the listed-token workgroup.
 struct S2Lists {
-    int32_t pid[256 + SS_GAMMA_MAX];   // prior entries, then entries for earlier drafts
-    int32_t pct[256 + SS_GAMMA_MAX];
-    int32_t bid[256];
-    float bval[256];
+    int32_t pid[LIST_SHORT + SS_GAMMA_MAX];   // prior entries, then entries for earlier drafts
+    int32_t pct[LIST_SHORT + SS_GAMMA_MAX];
+    int32_t bid[LIST_SHORT];
+    float bval[LIST_SHORT];
 };
 
 // Listed tokens: exact processed logits of the first
-// valid entry of every id named by an active list, sorted; at most 510
-// entries, 128 per pass (two per lane).
+// valid entry of every id named by an active list, sorted; at most
+// 2 * LIST_SHORT + SS_GAMMA_MAX entries, 128 per pass (two per lane).
 //
 // One pass over each list counts, per token, its matching entries and
 // remembers one of them.  The repetition penalty is the same map for every
@@ -334,6 +340,7 @@ __device__ __forceinline__ void listed_row_wave(const Stage1Params& P, uint64_t*
     const int nb = rp.valid ? rp.n_bias : 0;
     const int nh = rp.valid ? draft_hist_len(P, rp.flags, row) : 0;
     if (np + nb + nh == 0) return;   // wave-uniform; Stage 2 skips rows without lists
+    if (np > LIST_SHORT || nb > LIST_SHORT) return;   // ranked by listed_long_kernel
     const auto pid = gmem(P.aux.prior_ids + (int64_t)b * P.aux.prior_stride);
     const auto pct = gmem(P.aux.prior_cnt + (int64_t)b * P.aux.prior_stride);
     const auto bid = gmem(P.aux.bias_ids + (int64_t)b * P.aux.bias_stride);
