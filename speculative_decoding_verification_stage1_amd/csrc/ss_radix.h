@@ -69,6 +69,189 @@ __device__ __forceinline__ void radix_tie_fallback(const Stage1Params& P, int ro
 
 using u16x2 = unsigned short __attribute__((ext_vector_type(2)));
 
+// The fast screen of stage1_radix_kernel (see there): true when it has
+// written the tile's list.  Block-uniform result; kk holds the tile's order
+// keys (bf16: two 16-bit keys per dword; fp32: one 32-bit key), 0 past the
+// end.
+template <int DT>
+__device__ __forceinline__ bool rx_fast_screen(const Stage1Params& P, int row, int tile, const uint32_t (&kk)[S1_CPT * 4],
+                                               RadixShared<DT>& sh, int nvalid) {
+    using Key = typename S1Traits<DT>::Key;
+    constexpr int EPC = S1Traits<DT>::EPC;
+    constexpr int BN = S1Traits<DT>::BN;
+    constexpr int NCH = S1_CPT;
+    const int tid = threadIdx.x, wave = tid / WAVE, lane = lane_id();
+    // this thread's chunk maxima (screening keys); chunk j is tile chunk j * 256 + tid
+    uint32_t cmx[NCH];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        if constexpr (DT == SS_BF16) {
+            u16x2 m = __builtin_bit_cast(u16x2, kk[4 * j]);
+#pragma unroll
+            for (int i = 1; i < 4; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, kk[4 * j + i]));
+            cmx[j] = m[0] > m[1] ? m[0] : m[1];
+        } else {
+            const uint32_t a = kk[4 * j] > kk[4 * j + 1] ? kk[4 * j] : kk[4 * j + 1];
+            const uint32_t c = kk[4 * j + 2] > kk[4 * j + 3] ? kk[4 * j + 2] : kk[4 * j + 3];
+            cmx[j] = (a > c ? a : c) >> 16;
+        }
+    }
+    const int nzc = BN / EPC - (nvalid + EPC - 1) / EPC;   // chunks with no element: maximum 0
+    if (BN / EPC - nzc < KMAX) return false;               // block-uniform
+    // 6-bit screen of the chunk maxima, per-thread LDS columns as below
+#pragma unroll
+    for (int b = 0; b < RX_NB1; ++b) sh.col[b][tid] = 0u;
+#pragma unroll
+    for (int i = tid; i < RX_NB2; i += S1_THREADS) sh.hist[i] = 0u;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j)
+        __hip_atomic_fetch_add(&sh.col[cmx[j] >> 10][tid], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __syncthreads();
+    {
+        const int b = tid >> 2, part = tid & 3;
+        const uint4* src = (const uint4*)&sh.col[b][part * 64];
+        uint32_t s = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint4 v = src[(i + b) & 15];
+            s += v.x + v.y + v.z + v.w;
+        }
+        s += xor_lane<1>(s);
+        s += xor_lane<2>(s);
+        if (part == 0) sh.h1[b] = s;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        int c = (int)sh.h1[RX_NB1 - 1 - lane];
+        if (lane == RX_NB1 - 1) c -= nzc;
+        const int incl = wave_incl_scan(c);
+        const uint64_t reach = __ballot(incl >= KMAX);
+        const int l = reach ? __builtin_ctzll(reach) : 0;
+        if (lane == 0) {
+            sh.sel[0] = RX_NB1 - 1 - l;
+            sh.sel[1] = __builtin_amdgcn_readlane(incl, l) - __builtin_amdgcn_readlane(c, l);
+        }
+    }
+    __syncthreads();
+    // 10-bit refinement inside that bucket: T0 exactly
+    const int d = sh.sel[0];
+    const int need = KMAX - sh.sel[1];
+    const uint32_t lo = (uint32_t)d << 10;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        const uint32_t dg = cmx[j] - lo;
+        if (dg < (uint32_t)RX_NB2)
+            __hip_atomic_fetch_add(&sh.hist[dg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    __syncthreads();
+    {
+        const uint4 v = *(const uint4*)&sh.hist[RX_NB2 - 4 - 4 * tid];
+        uint32_t c3 = v.w, c2 = v.z, c1 = v.y, c0 = v.x;
+        if (tid == S1_THREADS - 1 && d == 0) c0 -= nzc;
+        const int s = (int)(c0 + c1 + c2 + c3);
+        const int wincl = wave_incl_scan(s);
+        if (lane == WAVE - 1) sh.wsum[wave] = wincl;
+        __syncthreads();
+        int before = wincl - s;
+#pragma unroll
+        for (int w = 0; w < S1_WAVES; ++w) before += w < wave ? sh.wsum[w] : 0;
+        const int cs[4] = {(int)c3, (int)c2, (int)c1, (int)c0};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (before < need && before + cs[j] >= need) sh.sel[2] = RX_NB2 - 1 - 4 * tid - j;   // exactly one
+            before += cs[j];
+        }
+    }
+    __syncthreads();
+    const uint32_t T0 = lo + (uint32_t)sh.sel[2];   // >= 1: the 128 maxima are elements
+    // the chunks whose maximum reaches T0, copied per wave (the column area
+    // is free now); more than S1_CCAP in a wave takes the element screen
+    uint4* const ch = (uint4*)&sh.col[0][0] + wave * (S1_CCAP + WAVE);
+    int* const cid = (int*)((uint4*)&sh.col[0][0] + S1_WAVES * (S1_CCAP + WAVE)) + wave * (S1_CCAP + WAVE);
+    int wcnt = 0;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        const bool f = cmx[j] >= T0;
+        const uint64_t bal = __ballot(f);
+        if (f && wcnt <= S1_CCAP) {
+            const int sl = wcnt + lane_prefix(bal);
+            ch[sl] = make_uint4(kk[4 * j], kk[4 * j + 1], kk[4 * j + 2], kk[4 * j + 3]);
+            cid[sl] = j * S1_THREADS + tid;
+        }
+        wcnt += __popcll(bal);
+    }
+    // the elements >= T0 of those chunks: count, then place
+    const int nck = wcnt < S1_CCAP ? wcnt : S1_CCAP;
+    wave_lds_sync();
+    int mine = 0;
+    for (int s0 = 0; s0 < nck; s0 += WAVE) {
+        const int sl = s0 + lane;
+        if (sl < nck) {
+            const uint4 v = ch[sl];
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (DT == SS_BF16) mine += ((w4[e] & 0xFFFFu) >= T0) + ((w4[e] >> 16) >= T0);
+                else mine += (w4[e] >> 16) >= T0;
+            }
+        }
+    }
+    int wtot = mine;
+    wtot += xor_lane<1>(wtot);
+    wtot += xor_lane<2>(wtot);
+    wtot += xor_lane<4>(wtot);
+    wtot += xor_lane<8>(wtot);
+    wtot += xor_lane<16>(wtot);
+    wtot += xor_lane<32>(wtot);
+    if (lane == 0) sh.flag[wave] = wcnt > S1_CCAP ? -1 : wtot;
+    __syncthreads();
+    int total = 0, pos = 0;
+    bool bad = false;
+#pragma unroll
+    for (int w = 0; w < S1_WAVES; ++w) {
+        const int f = sh.flag[w];
+        bad |= f < 0;
+        pos += w < wave ? f : 0;
+        total += f;
+    }
+    if (bad || total > RX_CAP) return false;   // block-uniform
+    pos += wave_incl_scan(mine) - mine;
+    for (int s0 = 0; s0 < nck; s0 += WAVE) {
+        const int sl = s0 + lane;
+        if (sl < nck) {
+            const uint4 v = ch[sl];
+            const int c = cid[sl];
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (DT == SS_BF16) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const uint32_t k16 = h ? w4[e] >> 16 : w4[e] & 0xFFFFu;
+                        if (k16 >= T0) {
+                            const uint32_t loc = (uint32_t)(c * EPC + 2 * e + h);
+                            sh.keys[pos++] = (Key)((k16 << 16) | (0xFFFFu - loc));
+                        }
+                    }
+                } else {
+                    if ((w4[e] >> 16) >= T0) {
+                        const uint32_t loc = (uint32_t)(c * EPC + e);
+                        sh.keys[pos++] = (Key)(((uint64_t)w4[e] << 32) | (uint64_t)(0xFFFFFFFFu - loc));
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const WList<Key> best = wave_top128(sh.keys, total);
+        const int64_t o = ((int64_t)row * P.Zv + tile) * KMAX + lane;
+        ((Key*)P.scratch)[o] = best.lo;
+        ((Key*)P.scratch)[o + WAVE] = best.hi;
+    }
+    return true;
+}
+
 template <int DT>
 __global__ __launch_bounds__(S1_THREADS) void stage1_radix_kernel(Stage1Params P) {
     using Key = typename S1Traits<DT>::Key;
@@ -144,6 +327,19 @@ __global__ __launch_bounds__(S1_THREADS) void stage1_radix_kernel(Stage1Params P
         else return kk[q] >> (16 + s);
     };
     const int nzero = BN - nvalid;   // slots with no element: key 0, in bucket 0 while the prefix is 0
+
+    // ---- fast screen: the same 6 + 10-bit radix select over the tile's
+    // chunk maxima (one value per 16-byte chunk, an eighth (bf16) or a
+    // quarter (fp32) of the elements) gives T0, the 16-bit screening key of
+    // the 128th largest chunk maximum.  Those 128 maxima are distinct
+    // elements, so the 128th best element's screening key is >= T0; only the
+    // chunks whose maximum reaches T0 can hold elements that high, and their
+    // elements >= T0 (usually a little over 128) go to the bitonic finish at
+    // once.  Ties at 16-bit precision (more than 256 such elements), more
+    // such chunks than the copy area holds, and tiles with fewer than 128
+    // chunks take the element screen below. ----
+    if (rx_fast_screen<DT>(P, row, tile, kk, sh, nvalid)) return;
+    __syncthreads();   // the shared area is reused
 
     // ---- screen: the 6 most significant bits.  Every thread counts its own
     // elements in its own LDS column (no two threads touch one word, and a
