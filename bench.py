@@ -61,16 +61,23 @@ PROFILE_CMDS = {
                   "python3 bench.py --steps 8 --warmup 2 --no-cpu --legs c2 --copy-calibration",
     "extra": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof/extra -o run -- "
              "python3 bench.py --steps 8 --warmup 2 --no-cpu --median-replays 5 --legs verify,stress,c0,c1,c4",
+    "lmhead": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof/lmhead -o run -- "
+              "python3 bench.py --steps 8 --warmup 2 --no-cpu --median-replays 5 --legs lmhead",
 }
 
 
+# the sources the sampling step's Stage-1 launch is built from (its kernel,
+# the listed-token waves it runs, the helpers both use, the request layout)
+STAGE1_SOURCES = ("ss_device.h", "ss_wavesort.h", "ss_stage1.h", "ss_kernels.h", "ss_stage2.h")
+
+
 def kernel_source_hash() -> str:
-    """sha256 over the HIP sources and the C header: recorded HBM counters
-    apply only to the kernels they were taken on."""
+    """sha256 over the Stage-1 sources and the C header: recorded HBM
+    counters apply only to the kernel they were taken on."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "speculative_decoding_verification_stage1_amd", "csrc")
-    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc)) + [os.path.join(ROOT, "include", "ss.h")]
+    files = [os.path.join(csrc, f) for f in STAGE1_SOURCES] + [os.path.join(ROOT, "include", "ss.h")]
     for f in files:
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
@@ -190,6 +197,21 @@ def summarize_rocprof(d: str, out: str) -> None:
                       f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
     ll += ["", "## per launch shape (kernel_trace.csv)", ""] + shape_table(perx, lambda n, g: True)
     with open(os.path.join(os.path.dirname(out), "other_workloads.md"), "w") as fh:
+        fh.write("\n".join(ll) + "\n")
+
+    # the LM head fused with sampling
+    ld = os.path.join(d, "lmhead")
+    if not os.path.isdir(ld):
+        return
+    perl = per_shape(os.path.join(ld, "run_kernel_trace.csv"))
+    ll = ["# LM head fused with sampling: B=64, D=4096, V=131072 and B=256, D=4096, V=262144 "
+          "(bf16 hidden and weights, synthetic)", "",
+          "Command (run from the repository root with TMPDIR=/tmp):", "", "    " + PROFILE_CMDS["lmhead"], "",
+          "Grid sizes are in threads (256 per workgroup).  lmhead_gemm_kernel<mode, WM, WN, KB>: mode 0 stores "
+          "logits (the logits launch, and the fused step's probe), 1 keeps the tokens above the probe's "
+          "threshold, 2 stores the logits of rows whose candidates overflowed (returns at once otherwise).", "",
+          "## per launch shape (kernel_trace.csv)", ""] + shape_table(perl, lambda n, g: True)
+    with open(os.path.join(os.path.dirname(out), "lmhead_b64_b256.md"), "w") as fh:
         fh.write("\n".join(ll) + "\n")
 
 
