@@ -526,7 +526,8 @@ def stress_measurements(L, W, stream, head):
         del wl
         torch.cuda.empty_cache()
     out["inputs"] = ("c2 batch with one change each (workloads.workload_c2_stress): log-softmax rows; "
-                     "grammar 0.1% allowed; 200 prior ids in the first 32768-token tile, no grammar; "
+                     "grammar 0.1% allowed; 200 (listed_tile) or 100 (listed_100) prior ids in the first 32768-token tile, "
+                     "no grammar; "
                      "4 rotating copies")
     return out
 

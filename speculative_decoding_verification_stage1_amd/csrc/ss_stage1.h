@@ -62,7 +62,7 @@ constexpr int S1_CPT = 16;            // 16-byte chunks per thread
 constexpr int S1_CCAP = 128;          // flagged chunks held per wave (fast path)
 constexpr int S1_KCAP = 256;          // survivors held per wave (fast path)
 constexpr int S1_LIST_W = 2 * WAVE + SS_GAMMA_MAX;   // listed tokens one wave records: 64 prior, 64 bias, drafts
-constexpr int S1_NL_FAST = 128;       // listed tokens per tile left in the data (more are masked out)
+constexpr int S1_NL_FAST = 32;        // listed tokens per tile left in the data (more are masked out)
 
 template <int DT> struct S1Traits;
 template <> struct S1Traits<SS_BF16> {
@@ -668,39 +668,92 @@ __device__ __forceinline__ WList<typename S1Traits<DT>::Key> merge_lists(S1Share
 // common path keeps the tile in registers and this path must not add to
 // them.  Ends with a barrier.
 template <int DT>
-__device__ __attribute__((noinline)) void tile_exact_mem(const char* rowp, int nvalid, bool use_mask,
-                                                          S1Shared<DT>& sh, const uint32_t* ebm) {
+__device__ __attribute__((noinline)) void tile_exact_mem(const char* rowp, int nvalid, bool use_mask, bool aligned,
+                                                          S1Shared<DT>& shg, const uint32_t* ebm_g) {
     using TT = S1Traits<DT>;
     using Key = typename TT::Key;
-    constexpr int EPT = TT::BN / S1_THREADS;   // tile indices per thread
+    constexpr int EPC = TT::EPC;                    // elements per 16-byte chunk
+    constexpr int CPT = TT::BN / EPC / S1_THREADS;  // chunks per thread
     const int tid = threadIdx.x;
     const int wave = tid / WAVE;
     const int lane = lane_id();
-    const int i0 = tid * EPT;
-    const int i1 = min(i0 + EPT, nvalid);
-    // order key u (unsigned, larger = better) of the token at tile index i;
-    // false for a token left out
-    auto key_at = [&](int i, uint32_t& u, int& v) -> bool {
-        if ((ebm[i >> 5] >> (i & 31)) & 1u) return false;
-        const bool masked = use_mask && !((sh.gmw[i >> 5] >> (i & 31)) & 1u);
-        if constexpr (DT == SS_BF16) {
-            const uint32_t h = gmem((const uint16_t*)rowp)[i];
-            const bool nan = (h & 0x7FFFu) > 0x7F80u;
-            v = (h & 0x8000u) ? -(int)(h & 0x7FFFu) : (int)h;
-            if (masked || nan) v = TT::NINF_V;
-            u = (uint32_t)(v + 0x8000);
+    // The LDS arrays with their address space spelled out: this function is
+    // not inlined, so `shg` arrives as a generic pointer, and generic
+    // accesses would have to wait for every global load in flight.
+    using L32 = __attribute__((address_space(3))) uint32_t;
+    using LI = __attribute__((address_space(3))) int;
+    using LK = __attribute__((address_space(3))) Key;
+    const L32* ebm = (const L32*)ebm_g;
+    const L32* gmw = (const L32*)shg.gmw;
+    LI* hist = (LI*)&shg.cid[0][0];
+    static_assert(sizeof(shg.cid) >= 256 * sizeof(int), "histogram");
+    LI* ctr = (LI*)&shg.red[0][0];
+    LK* g = (LK*)&shg.keys[0][0];
+    const int nfull = aligned ? nvalid / EPC : 0;   // chunks read with one 16-byte load
+    // chunk c's data as four dwords (element e of a bf16 chunk: half e & 1
+    // of dword e >> 1); elements past the end read as zero
+    auto load = [&](int c, uint32_t (&w)[4]) {
+        if (c < nfull) {
+            const vu32x4 d = gmem((const vu32x4*)rowp)[c];
+            w[0] = d.x;
+            w[1] = d.y;
+            w[2] = d.z;
+            w[3] = d.w;
         } else {
-            const uint32_t x = gmem((const uint32_t*)rowp)[i];
-            const bool nan = (x & 0x7FFFFFFFu) > 0x7F800000u;
-            v = (x & 0x80000000u) ? -(int)(x & 0x7FFFFFFFu) : (int)x;
-            v = min(v, TT::PINF_V);
-            if (masked || nan) v = TT::NINF_V;
-            u = (uint32_t)v ^ 0x80000000u;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) w[k] = 0u;
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) {
+                const int i = c * EPC + e;
+                if (i >= nvalid) continue;
+                if constexpr (DT == SS_BF16) w[e >> 1] |= (uint32_t)gmem((const uint16_t*)rowp)[i] << (16 * (e & 1));
+                else w[e] = gmem((const uint32_t*)rowp)[i];
+            }
         }
-        return true;
     };
-    int* hist = &sh.cid[0][0];
-    static_assert(sizeof(sh.cid) >= 256 * sizeof(int), "histogram");
+    // f(i, u, v) for every token of chunk c that is not left out: u its
+    // unsigned order key (larger = better), v its order value
+    auto chunk_keys = [&](int c, const uint32_t (&w)[4], auto&& f) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+            const int i = c * EPC + e;
+            if (i >= nvalid || ((ebm[i >> 5] >> (i & 31)) & 1u)) continue;
+            const bool masked = use_mask && !((gmw[i >> 5] >> (i & 31)) & 1u);
+            int v;
+            uint32_t u;
+            if constexpr (DT == SS_BF16) {
+                const uint32_t h = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                const bool nan = (h & 0x7FFFu) > 0x7F80u;
+                v = (h & 0x8000u) ? -(int)(h & 0x7FFFu) : (int)h;
+                if (masked || nan) v = TT::NINF_V;
+                u = (uint32_t)(v + 0x8000);
+            } else {
+                const uint32_t x = w[e];
+                const bool nan = (x & 0x7FFFFFFFu) > 0x7F800000u;
+                v = (x & 0x80000000u) ? -(int)(x & 0x7FFFFFFFu) : (int)x;
+                v = min(v, TT::PINF_V);
+                if (masked || nan) v = TT::NINF_V;
+                u = (uint32_t)v ^ 0x80000000u;
+            }
+            f(i, u, v);
+        }
+    };
+    // chunks chunk_of(0 .. CPT-1), their loads issued in batches of eight
+    // before any is used
+    constexpr int BATCH = 8;
+    static_assert(CPT % BATCH == 0, "batches");
+    auto chunks = [&](auto&& chunk_of, auto&& f) {
+        for (int k0 = 0; k0 < CPT; k0 += BATCH) {
+            uint32_t w[BATCH][4];
+#pragma unroll
+            for (int b = 0; b < BATCH; ++b) load(chunk_of(k0 + b), w[b]);
+#pragma unroll
+            for (int b = 0; b < BATCH; ++b) chunk_keys(chunk_of(k0 + b), w[b], f);
+        }
+    };
+    // the tile in coalesced order (chunk k * 256 + tid), for the passes
+    // whose order does not matter
+    auto tile_pass = [&](auto&& f) { chunks([&](int k) { return k * S1_THREADS + tid; }, f); };
     constexpr int KBITS = DT == SS_BF16 ? 16 : 32;
     uint32_t prefix = 0;   // the digits of T's key found so far
     int kneed = KMAX;      // how many of the tokens with this prefix are still wanted
@@ -709,12 +762,10 @@ __device__ __attribute__((noinline)) void tile_exact_mem(const char* rowp, int n
     for (int shift = KBITS - 8; shift >= 0; shift -= 8) {   // block-uniform
         hist[tid] = 0;
         __syncthreads();
-        for (int i = i0; i < i1; ++i) {
-            uint32_t u;
-            int v;
-            if (key_at(i, u, v) && (shift + 8 >= KBITS || (u >> (shift + 8)) == prefix))
-                atomicAdd(&hist[(u >> shift) & 255u], 1);
-        }
+        tile_pass([&](int, uint32_t u, int) {
+            if (shift + 8 >= KBITS || (u >> (shift + 8)) == prefix)
+                __hip_atomic_fetch_add(&hist[(u >> shift) & 255u], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        });
         __syncthreads();
         // the digit b of the kneed-th largest: lane l sums bins 4l..4l+3,
         // suffix sums from the top give the lane, then its bins
@@ -739,46 +790,41 @@ __device__ __attribute__((noinline)) void tile_exact_mem(const char* rowp, int n
         const int above = __shfl(suffix - s, L, WAVE);   // bins above lane L's
         int b = 4 * L + 3, acc = above;
         const int h3 = __shfl(s4[3], L, WAVE), h2 = __shfl(s4[2], L, WAVE);
-        const int h1 = __shfl(s4[1], L, WAVE), h0 = __shfl(s4[0], L, WAVE);
+        const int h1 = __shfl(s4[1], L, WAVE);
         if (acc + h3 >= kneed) b = 4 * L + 3;
         else if (acc + h3 + h2 >= kneed) { b = 4 * L + 2; acc += h3; }
         else if (acc + h3 + h2 + h1 >= kneed) { b = 4 * L + 1; acc += h3 + h2; }
         else { b = 4 * L; acc += h3 + h2 + h1; }
-        (void)h0;
         kneed -= __builtin_amdgcn_readfirstlane(acc);
         prefix = (prefix << 8) | (uint32_t)__builtin_amdgcn_readfirstlane(b);
         __syncthreads();   // the histogram is read before the next pass clears it
     }
     // T's key is `prefix`; `kneed` tokens equal to T are wanted
-    int* ctr = &sh.red[0][0];
     if (tid == 0) *ctr = 0;
     __syncthreads();
-    Key* g = &sh.keys[0][0];
     const int n_gt = KMAX - kneed;
+    tile_pass([&](int i, uint32_t u, int v) {
+        if (take_all || u > prefix)
+            g[__hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)] = value_key<DT>(v, i);
+    });
+    // ties at T in token order: thread t owns the contiguous chunks
+    // t * CPT .. t * CPT + CPT - 1
+    auto own = [&](int k) { return tid * CPT + k; };
     int nties = 0;
-    for (int i = i0; i < i1; ++i) {
-        uint32_t u;
-        int v;
-        if (!key_at(i, u, v)) continue;
-        if (take_all || u > prefix) g[atomicAdd(ctr, 1)] = value_key<DT>(v, i);
-        else if (u == prefix) ++nties;
-    }
+    if (!take_all) chunks(own, [&](int, uint32_t u, int) { nties += u == prefix; });
     int total;
-    int r = block_excl_scan(take_all ? 0 : nties, sh.scan, &total);   // ties before this thread's
-    if (!take_all && r < kneed) {
-        for (int i = i0; i < i1 && r < kneed; ++i) {
-            uint32_t u;
-            int v;
-            if (key_at(i, u, v) && u == prefix) g[n_gt + r++] = value_key<DT>(v, i);
-        }
-    }
+    int r = block_excl_scan(take_all ? 0 : nties, (int*)shg.scan, &total);   // ties before this thread's
+    if (!take_all && r < kneed)
+        chunks(own, [&](int i, uint32_t u, int v) {
+            if (u == prefix && r < kneed) g[n_gt + r++] = value_key<DT>(v, i);
+        });
     __syncthreads();
     const int n = take_all ? n_all : KMAX;
     if (wave == s1_lead_wave()) {
         WList<Key> l{lane < n ? g[lane] : (Key)0, lane + WAVE < n ? g[lane + WAVE] : (Key)0};
         l = wave_sort128(l);
-        sh.surv[lane] = l.lo;
-        sh.surv[lane + WAVE] = l.hi;
+        shg.surv[lane] = l.lo;
+        shg.surv[lane + WAVE] = l.hi;
     }
     __syncthreads();
 }
@@ -873,9 +919,11 @@ __device__ __forceinline__ void tile_process(const Stage1Params& P, int row, int
     const int4 nl4 = *(const int4*)sh.nlw;   // one read
     const int nl = __builtin_amdgcn_readfirstlane(nl4.x + nl4.y + nl4.z + nl4.w);
     // The tile's listed tokens are cleared from the mask when the row has a
-    // grammar mask, or when there are too many of them to leave in the data:
-    // the mask then leaves them out like any disallowed token, and the
-    // threshold and survivor steps need not know about them.
+    // grammar mask, or when there are too many of them to leave in the data
+    // (each wave keeps a quarter of them as extra candidates, which lowers
+    // the threshold; past S1_NL_FAST the flagged chunks overflow into the
+    // exact path): the mask then leaves them out like any disallowed token,
+    // and the threshold and survivor steps need not know about them.
     const bool long_lists = (use_prior && n_prior > S1_WAVES * WAVE) || (use_bias && n_bias > S1_WAVES * WAVE);
     const bool fold = (nl > 0 && (use_grammar || nl > S1_NL_FAST)) || long_lists;   // block-uniform
     const bool use_mask = use_grammar || fold;
@@ -910,7 +958,7 @@ __device__ __forceinline__ void tile_process(const Stage1Params& P, int row, int
     WList<Key> r{0, 0};
     auto exact = [&] {   // the exact path, from memory (sh.surv, then the lead wave's registers)
         const uint32_t* ebm = exclusion_bitmap<DT>(sh, nvalid);
-        tile_exact_mem<DT>(rowp, nvalid, use_mask, sh, ebm);
+        tile_exact_mem<DT>(rowp, nvalid, use_mask, P.aligned16 != 0, sh, ebm);
         if (wave == lead) r = WList<Key>{sh.surv[lane], sh.surv[lane + WAVE]};
     };
     auto finish = [&] {

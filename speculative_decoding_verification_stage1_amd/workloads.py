@@ -254,7 +254,7 @@ def workload_c2(rows: Optional[int] = None) -> SampleWorkload:
     return workload_mixed(2, 256, 262144, grammar=True, rows=rows)
 
 
-STRESS_KINDS = ("logprob", "sparse_grammar", "listed_tile")
+STRESS_KINDS = ("logprob", "sparse_grammar", "listed_tile", "listed_100")
 
 
 def workload_c2_stress(kind: str, rows: Optional[int] = None, B: int = 256, V: int = 262144) -> SampleWorkload:
@@ -270,7 +270,9 @@ def workload_c2_stress(kind: str, rows: Optional[int] = None, B: int = 256, V: i
     * ``listed_tile``: no grammar; each request's prior list holds 200
       distinct ids drawn from [0, 32768) with counts U{1..5} (plus the 16
       bias ids anywhere), so one vocabulary tile holds more than 128 tokens
-      named by the lists.
+      named by the lists;
+    * ``listed_100``: the same with 100 prior ids, so that one tile holds
+      about 100 listed tokens (fewer than 128).
     """
     if kind not in STRESS_KINDS:
         raise ValueError(kind)
@@ -291,7 +293,7 @@ def workload_c2_stress(kind: str, rows: Optional[int] = None, B: int = 256, V: i
     else:
         req.bitmask = None
         req.use_grammar = np.zeros(n, bool)
-        P = 200
+        P = 200 if kind == "listed_tile" else 100
         req.prior_ids = np.full((n, P), -1, np.int32)
         req.prior_cnt = np.zeros((n, P), np.int32)
         for r in range(n):

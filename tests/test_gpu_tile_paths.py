@@ -176,3 +176,33 @@ def test_c2_stress_full(kind):
     row against the oracle."""
     wl = W.workload_c2_stress(kind)
     _sample_parity(wl.logits, wl.dtype, wl.req, 0, seed=0)
+
+
+@pytest.mark.parametrize("dtype", [W.DTYPE_BF16, W.DTYPE_F32])
+def test_many_listed_tokens_under_the_fold(dtype):
+    """Many listed tokens in one tile: up to 32 stay in the data (each wave
+    keeps that many more candidates), more are cleared from the mask; rows
+    with 20, 32, 60 and 128 listed tokens in tile 0, with and without a
+    grammar, positive and negative."""
+    rng = np.random.default_rng(31)
+    V, n = 70001, 8
+    x = (rng.standard_normal((n, V)) * 2).astype(np.float32)
+    x[4:] = -np.abs(x[4:]) - 0.5
+    req = W.plain_requests(n, temperature=0.9, top_p=0.95, prior_len=128, bias_len=8)
+    req.use_penalties[:] = True
+    req.rep_penalty[:] = 1.1
+    req.freq_penalty[:] = 0.1
+    for r in range(n):
+        k = (20, 32, 60, 128)[r % 4]
+        req.prior_ids[r, :k] = rng.choice(16384, k, replace=False)
+        req.prior_cnt[r, :k] = rng.integers(1, 4, k)
+        req.n_prior[r] = k
+    bm = np.full((n, (V + 31) // 32), 0xFFFFFFFF, np.uint32)
+    p = np.zeros(bm.shape[1] * 32, bool)
+    p[:V] = rng.random(V) < 0.3
+    bm[1::2] = np.packbits(p, bitorder="little").view("<u4")
+    req.bitmask = bm
+    req.use_grammar[1::2] = True
+    logits = W.to_bf16_bits(x) if dtype == W.DTYPE_BF16 else x
+    _tile_parity(logits, dtype, req, 0)
+    _sample_parity(logits, dtype, req, 0, seed=9)
