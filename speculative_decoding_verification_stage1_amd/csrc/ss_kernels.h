@@ -12,7 +12,7 @@ namespace ssd {
 template <int DT>
 union S1KernelShared {
     S1Shared<DT> tile;
-    S2Lists lists[S1_WAVES];
+    ListedArea lists[S1_WAVES];
 };
 
 // The first ceil(listed_rows / 4) workgroups compute the rows' listed

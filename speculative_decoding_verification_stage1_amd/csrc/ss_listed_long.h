@@ -2,18 +2,10 @@
 // (penalty histories up to SS_PRIOR_MAX entries, bias lists up to
 // SS_BIAS_MAX): the same result as listed_row_wave - the exact processed
 // logit of every token named by an active list entry, as merge keys, the
-// row's best 128 - by one workgroup per row instead of one wave.
-//
-// The row's entries (prior entries, then the earlier drafts of a
-// verification row, then bias entries) become keys id << 16 | position and
-// are sorted in LDS, so the entries of one token lie together in list
-// order.  The first entry of each token then walks its entries and applies
-// the list arithmetic in the order of the logits-processing definition:
-// the repetition map once per live prior entry, then each prior entry's
-// frequency/presence subtraction, then each bias addition; a token's
-// earlier drafts add to the count of its first live prior entry, or form
-// one appended entry.  The tokens' keys are then reduced to the best 128
-// with the register bitonic sorts and merges of Stage 2.
+// row's best 128 - by one workgroup per row instead of one wave, with the
+// sorting form of ss_stage2.h (listed_entry_key, listed_token_key) over
+// up to LL_CAP entries in LDS.  The tokens' keys are then reduced to the
+// best 128 with the register bitonic sorts and merges of Stage 2.
 #pragma once
 
 #include "ss_stage2.h"
@@ -63,82 +55,17 @@ __global__ __launch_bounds__(LL_THREADS) void listed_long_kernel(Stage1Params P)
     int ns = 256;
     while (ns < n) ns <<= 1;
     const int tid = threadIdx.x;
-    const int64_t po = (int64_t)b * P.aux.prior_stride, bo = (int64_t)b * P.aux.bias_stride;
-    // 1. entry keys (entries that name no token sort last)
-    for (int i = tid; i < ns; i += LL_THREADS) {
-        uint64_t key = ~0ull;
-        if (i < n) {
-            int id;
-            bool ok;
-            if (i < np) {
-                id = gmem(P.aux.prior_ids)[po + i];
-                ok = gmem(P.aux.prior_cnt)[po + i] >= 1;
-            } else if (i < np + nh) {
-                id = gmem(P.draft_ids)[(int64_t)b * (P.rows_per_req - 1) + (i - np)];
-                ok = true;
-            } else {
-                id = gmem(P.aux.bias_ids)[bo + (i - np - nh)];
-                ok = true;
-            }
-            if (ok && id >= 0 && id < P.V) key = ((uint64_t)(uint32_t)id << 16) | (uint64_t)i;
-        }
-        sh.k[i] = key;
-    }
+    // 1. entry keys (entries that name no token sort last), sorted
+    for (int i = tid; i < ns; i += LL_THREADS) sh.k[i] = i < n ? listed_entry_key(P, b, i, np, nh) : ~0ull;
     __syncthreads();
     ll_sort(sh.k, ns);
-    // 2. each token's processed logit, by the thread holding its first entry
-    const bool grammar = (rp.flags & SS_GRAMMAR) != 0;
-    const bool do_rep = (rp.flags & SS_REP) != 0;
-    const bool do_fp = (rp.flags & SS_FREQPRES) != 0;
-    const bool do_bias = (rp.flags & SS_BIAS) != 0;
+    // 2. each token's key, by the thread holding its first entry
     constexpr int PER = LL_CAP / LL_THREADS;
     uint64_t res[PER];
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
-        res[q] = 0ull;
         const int i = tid + q * LL_THREADS;
-        if (i >= ns) continue;
-        const uint64_t e = sh.k[i];
-        if (e == ~0ull) continue;
-        const uint32_t id = (uint32_t)(e >> 16);
-        if (i > 0 && sh.k[i - 1] != ~0ull && (uint32_t)(sh.k[i - 1] >> 16) == id) continue;   // not the first
-        int end = i + 1;
-        while (end < ns && sh.k[end] != ~0ull && (uint32_t)(sh.k[end] >> 16) == id) ++end;
-        int first_prior = -1, ndraft = 0;
-        for (int t = i; t < end; ++t) {
-            const int pos = (int)(sh.k[t] & 0xFFFFu);
-            if (pos < np) {
-                if (first_prior < 0) first_prior = pos;
-            } else if (pos < np + nh) {
-                ++ndraft;
-            }
-        }
-        const bool appended = first_prior < 0 && ndraft > 0;
-        float z;
-        if (DT == SS_BF16) z = widen_bf16(((const uint16_t*)P.logits)[(int64_t)row * P.ld + id]);
-        else z = ((const float*)P.logits)[(int64_t)row * P.ld + id];
-        if (grammar && !((P.aux.bitmask[(int64_t)row * P.aux.bitmask_stride + (id >> 5)] >> (id & 31)) & 1u))
-            z = bitsf(F32_NINF_BITS);
-        if (do_rep) {
-            for (int t = i; t < end; ++t)
-                if ((int)(sh.k[t] & 0xFFFFu) < np) z = (z > 0.0f) ? z / rp.rep : z * rp.rep;
-            if (appended) z = (z > 0.0f) ? z / rp.rep : z * rp.rep;
-        }
-        if (do_fp) {
-            for (int t = i; t < end; ++t) {
-                const int pos = (int)(sh.k[t] & 0xFFFFu);
-                if (pos >= np) continue;
-                const int c = gmem(P.aux.prior_cnt)[po + pos] + (pos == first_prior ? ndraft : 0);
-                z = z - ((float)c * rp.freq + rp.pres);
-            }
-            if (appended) z = z - ((float)ndraft * rp.freq + rp.pres);
-        }
-        if (do_bias)
-            for (int t = i; t < end; ++t) {
-                const int pos = (int)(sh.k[t] & 0xFFFFu);
-                if (pos >= np + nh) z = z + gmem(P.aux.bias_val)[bo + (pos - np - nh)];
-            }
-        res[q] = ((uint64_t)ord32(canon(z)) << 32) | (uint64_t)(0xFFFFFFFFu - id);
+        res[q] = i < ns ? listed_token_key<DT>(P, rp, row, b, sh.k, ns, i, np, nh) : 0ull;
     }
     __syncthreads();
 #pragma unroll

@@ -327,13 +327,155 @@ __device__ __forceinline__ WL64 listed_list(const Stage1Params& P, const RowPara
     return acc;
 }
 
+// ---- listed tokens by sorting: the row's entries (prior entries, then the
+// earlier drafts of a verification row, then bias entries) become keys
+// id << 16 | position; sorted, the entries of one token lie together in
+// list order, and the entry that starts a token walks them.  Used by one
+// wave for rows with more than 128 entries, and by listed_long_kernel (one
+// workgroup per row) for lists longer than LIST_SHORT. ----
+
+// Entry key of combined position i (~0: the entry names no token).
+__device__ __forceinline__ uint64_t listed_entry_key(const Stage1Params& P, int b, int i, int np, int nh) {
+    int id;
+    bool ok;
+    if (i < np) {
+        const int64_t o = (int64_t)b * P.aux.prior_stride + i;
+        id = gmem(P.aux.prior_ids)[o];
+        ok = gmem(P.aux.prior_cnt)[o] >= 1;
+    } else if (i < np + nh) {
+        id = gmem(P.draft_ids)[(int64_t)b * (P.rows_per_req - 1) + (i - np)];
+        ok = true;
+    } else {
+        id = gmem(P.aux.bias_ids)[(int64_t)b * P.aux.bias_stride + (i - np - nh)];
+        ok = true;
+    }
+    return ok && id >= 0 && id < P.V ? ((uint64_t)(uint32_t)id << 16) | (uint64_t)i : ~0ull;
+}
+
+// The merge key of the token whose entries start at sorted position i of
+// k[0, ns), or 0 if position i does not start one: its logit (grammar
+// mask applied), the repetition map once per live prior entry, then each
+// prior entry's frequency/presence subtraction in list order, then each
+// bias addition; the earlier drafts add to the count of the token's first
+// live prior entry, or form one appended entry.
+template <int DT, typename KP>
+__device__ __forceinline__ uint64_t listed_token_key(const Stage1Params& P, const RowParams& rp, int row, int b,
+                                                     KP k, int ns, int i, int np, int nh) {
+    const uint64_t e = k[i];
+    if (e == ~0ull) return 0ull;
+    const uint32_t id = (uint32_t)(e >> 16);
+    if (i > 0 && k[i - 1] != ~0ull && (uint32_t)(k[i - 1] >> 16) == id) return 0ull;   // not the first
+    int end = i + 1;
+    while (end < ns && k[end] != ~0ull && (uint32_t)(k[end] >> 16) == id) ++end;
+    int first_prior = -1, ndraft = 0;
+    for (int t = i; t < end; ++t) {
+        const int pos = (int)(k[t] & 0xFFFFu);
+        if (pos < np) {
+            if (first_prior < 0) first_prior = pos;
+        } else if (pos < np + nh) {
+            ++ndraft;
+        }
+    }
+    const bool appended = first_prior < 0 && ndraft > 0;
+    const int64_t po = (int64_t)b * P.aux.prior_stride, bo = (int64_t)b * P.aux.bias_stride;
+    float z;
+    if (DT == SS_BF16) z = widen_bf16(((const uint16_t*)P.logits)[(int64_t)row * P.ld + id]);
+    else z = ((const float*)P.logits)[(int64_t)row * P.ld + id];
+    if ((rp.flags & SS_GRAMMAR) &&
+        !((P.aux.bitmask[(int64_t)row * P.aux.bitmask_stride + (id >> 5)] >> (id & 31)) & 1u))
+        z = bitsf(F32_NINF_BITS);
+    if (rp.flags & SS_REP) {
+        for (int t = i; t < end; ++t)
+            if ((int)(k[t] & 0xFFFFu) < np) z = (z > 0.0f) ? z / rp.rep : z * rp.rep;
+        if (appended) z = (z > 0.0f) ? z / rp.rep : z * rp.rep;
+    }
+    if (rp.flags & SS_FREQPRES) {
+        for (int t = i; t < end; ++t) {
+            const int pos = (int)(k[t] & 0xFFFFu);
+            if (pos >= np) continue;
+            const int c = gmem(P.aux.prior_cnt)[po + pos] + (pos == first_prior ? ndraft : 0);
+            z = z - ((float)c * rp.freq + rp.pres);
+        }
+        if (appended) z = z - ((float)ndraft * rp.freq + rp.pres);
+    }
+    if (rp.flags & SS_BIAS)
+        for (int t = i; t < end; ++t) {
+            const int pos = (int)(k[t] & 0xFFFFu);
+            if (pos >= np + nh) z = z + gmem(P.aux.bias_val)[bo + (pos - np - nh)];
+        }
+    return ((uint64_t)ord32(canon(z)) << 32) | (uint64_t)(0xFFFFFFFFu - id);
+}
+
+// Entries of a row with more than 128 in one wave's area (keys of up to
+// 2 * LIST_SHORT + SS_GAMMA_MAX entries, padded to a power of two).
+constexpr int LW_CAP = 1024;
+static_assert(2 * LIST_SHORT + SS_GAMMA_MAX <= LW_CAP, "wave sort capacity");
+
+// One wave's LDS area in the listed-token workgroups: the staged lists, or
+// the entry keys of the sorting form.
+union ListedArea {
+    S2Lists lists;
+    uint64_t keys[LW_CAP];
+};
+
+// The sorting form in one wave: out[row] = the best 128 listed tokens.
+// (Made a separate, not inlined function, c2's Stage 1 took twice as
+// long, although c2's rows never call it.)
+template <int DT>
+__device__ __forceinline__ void listed_row_sorted(const Stage1Params& P, const RowParams& rp, uint64_t* out,
+                                                  int row, int b, int np, int nh, int nb, uint64_t* k) {
+    const int lane = lane_id();
+    const int n = np + nh + nb;
+    int ns = 2 * KMAX;
+    while (ns < n) ns <<= 1;
+    for (int i = lane; i < ns; i += WAVE) k[i] = i < n ? listed_entry_key(P, b, i, np, nh) : ~0ull;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    for (int size = 2; size <= ns; size <<= 1)   // ascending bitonic sort
+        for (int j = size >> 1; j > 0; j >>= 1) {
+            for (int i = lane; i < ns / 2; i += WAVE) {
+                const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
+                const int hi = lo + j;
+                const uint64_t a = k[lo], c = k[hi];
+                if ((a > c) == ((lo & size) == 0)) {
+                    k[lo] = c;
+                    k[hi] = a;
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+        }
+    constexpr int PER = LW_CAP / WAVE;
+    uint64_t res[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int i = lane + q * WAVE;
+        res[q] = i < ns ? listed_token_key<DT>(P, rp, row, b, k, ns, i, np, nh) : 0ull;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int q = 0; q < PER; ++q)
+        if (lane + q * WAVE < ns) k[lane + q * WAVE] = res[q];
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    WL64 acc{0ull, 0ull};
+    for (int c0 = 0; c0 < ns; c0 += KMAX) {
+        const WL64 l = wave_sort128(WL64{k[c0 + lane], k[c0 + lane + WAVE]});
+        acc = c0 == 0 ? l : wave_merge(acc, l);
+    }
+    out[(int64_t)row * KMAX + lane] = acc.lo;
+    out[(int64_t)row * KMAX + lane + WAVE] = acc.hi;
+}
+
 // One workgroup of the Stage-1 launch per row computes the row's listed
 // tokens (wave 0) and stores the best 128 as merge keys; it runs alongside
 // the tile workgroups, so Stage 2 only has to load one more sorted list.
 // One wave computes row `row`'s listed tokens: its lists are staged in the
 // wave's own LDS area, then ranked as exact keys (list order arithmetic).
 template <int DT>
-__device__ __forceinline__ void listed_row_wave(const Stage1Params& P, uint64_t* out, int row, S2Lists& lists) {
+__device__ __forceinline__ void listed_row_wave(const Stage1Params& P, uint64_t* out, int row, ListedArea& area) {
+    S2Lists& lists = area.lists;
     const int b = __builtin_amdgcn_readfirstlane(div_uniform(row, P.rows_per_req));
     const RowParams rp = row_params(P, b);
     int np = rp.valid ? rp.n_prior : 0;
@@ -341,6 +483,10 @@ __device__ __forceinline__ void listed_row_wave(const Stage1Params& P, uint64_t*
     const int nh = rp.valid ? draft_hist_len(P, rp.flags, row) : 0;
     if (np + nb + nh == 0) return;   // wave-uniform; Stage 2 skips rows without lists
     if (np > LIST_SHORT || nb > LIST_SHORT) return;   // ranked by listed_long_kernel
+    if (np + nb + nh > KMAX) {   // more than one pass of the scan below: sort instead
+        listed_row_sorted<DT>(P, rp, out, row, b, np, nh, nb, area.keys);
+        return;
+    }
     const auto pid = gmem(P.aux.prior_ids + (int64_t)b * P.aux.prior_stride);
     const auto pct = gmem(P.aux.prior_cnt + (int64_t)b * P.aux.prior_stride);
     const auto bid = gmem(P.aux.bias_ids + (int64_t)b * P.aux.bias_stride);
