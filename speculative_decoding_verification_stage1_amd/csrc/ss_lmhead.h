@@ -16,8 +16,8 @@
 // each thread loads its share of the stage's H and W rows with 16-byte
 // loads (KB / 8 lanes read one row segment) one stage ahead into
 // registers, then writes it to an LDS double buffer whose 16-byte slots
-// are XOR-swizzled by row (slot c of row r at c ^ (r & 7)), so the
-// fragment reads (32 rows at one k offset) meet no bank conflicts.  When several row blocks share
+// are XOR-swizzled by row, so the fragment reads (32 rows at one k
+// offset) meet no bank conflicts.  When several row blocks share
 // a column tile, the blocks of one tile are given ids 8 apart, which the
 // dispatcher places on the same XCD: the second read of a W tile then
 // comes from that XCD's L2.
@@ -139,7 +139,18 @@ __global__ __launch_bounds__(LM_THREADS) void lmhead_gemm_kernel(LmParams p) {
         for (int i = 0; i < NW; ++i) rw[i] = *(const lm_u32x4*)(gw[i] + k0);
     };
     // LDS slot of (row, chunk): row * SROW + 16 * (chunk ^ (row & 7))
-    auto slot = [](int r, int c) { return r * SROW + 16 * (c ^ (r & 7)); };
+    // slot of chunk c of row r: c ^ f(r), with f chosen so that the 16
+    // rows one 16-lane phase of a fragment read touches (and the rows a
+    // store phase writes) land on distinct 16-byte bank groups of a
+    // 256-byte window, and any 8 consecutive rows on distinct groups of a
+    // 128-byte one
+    auto slot = [](int r, int c) {
+        int f;
+        if constexpr (CPR >= 16) f = r & 15;
+        else if constexpr (CPR == 8) f = (r & 7) ^ ((r >> 3) & 1);
+        else f = r & (CPR - 1);
+        return r * SROW + 16 * (c ^ f);
+    };
     auto lstore = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < NA; ++i) *(lm_u32x4*)(&lds[buf][slot(lrow + RPP * i, chunk)]) = ra[i];
