@@ -223,7 +223,19 @@ __global__ __launch_bounds__(LM_THREADS) void lmhead_gemm_kernel(LmParams p) {
         __syncthreads();
     }
     // accumulator block (i, j), register q: row 32i + 8(q/4) + 4(l/32) + q%4,
-    // column 32j + l%32 of this wave's
+    // column 32j + l%32 of this wave's.  THRESH with four column blocks per
+    // wave: the thresholds of the lane's 32 rows go to registers first, so
+    // that the 128 compares below read no LDS (each read would wait behind
+    // the candidate stores before it); with fewer blocks the registers
+    // bought nothing measurable
+    constexpr bool TH_REGS = WN >= 4;
+    uint32_t th[2][16];
+    if (MODE == LM_THRESH && TH_REGS) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) th[i][q] = theta[wr + 32 * i + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)];
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -239,7 +251,7 @@ __global__ __launch_bounds__(LM_THREADS) void lmhead_gemm_kernel(LmParams p) {
                     p.out[(int64_t)r * p.ldo + (c - p.col_begin)] = v;
                 } else {
                     const uint32_t k32 = ord32(canon(v));
-                    if (k32 > theta[rl]) {
+                    if (k32 > (TH_REGS ? th[i][q] : theta[rl])) {
                         const uint64_t key = ((uint64_t)k32 << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)c);
                         const uint32_t pos = atomicAdd(rcnt + rl, 1u);
                         if (pos < (uint32_t)RSLOT) {
