@@ -196,16 +196,24 @@ __global__ __launch_bounds__(LM_THREADS) void lmhead_gemm_kernel(LmParams p) {
         __syncthreads();
     }
     // THRESH: the rows' thresholds (the largest 128th key over the probe
-    // tiles), then the candidates gathered per row in LDS (the stage
-    // buffers are free now; up to RSLOT per row, more go straight to the
-    // row's global list), then one global atomic per row reserves the
-    // block's share of the row's list
-    constexpr int RSLOT = 32;
-    static_assert(MT * (12 + 8 * RSLOT) <= 2 * (AB + WB), "candidate staging");
-    uint64_t* rkeys = (uint64_t*)&lds[0][0];                  // [MT][RSLOT]
-    uint32_t* theta = (uint32_t*)(rkeys + MT * RSLOT);        // [MT]
+    // tiles); then each wave appends the values above their row's
+    // threshold to its own LDS list, slots given by a ballot prefix (no
+    // atomic waits inside the compares: up to CAPW per wave, more go
+    // straight to the row's global list); then the block counts its
+    // candidates per row, one global atomic per row reserves the block's
+    // share of the row's list, and the keys are written there.  (The stage
+    // buffers are free after the k loop.)
+    constexpr int NWAVES = LM_THREADS / WAVE;
+    constexpr int CAPW = 512;
+    static_assert(NWAVES * CAPW * (8 + 2 + 2) + 3 * MT * 4 + 16 <= 2 * (AB + WB), "candidate staging");
+    static_assert(MT <= 65536, "row index in 16 bits");
+    uint64_t* wkeys = (uint64_t*)&lds[0][0];                  // [NWAVES][CAPW] keys
+    uint16_t* wrow = (uint16_t*)(wkeys + NWAVES * CAPW);      // [NWAVES][CAPW] their rows in the tile
+    uint16_t* wpos = wrow + NWAVES * CAPW;                    // [NWAVES][CAPW] their slots in the row's share
+    uint32_t* theta = (uint32_t*)(wpos + NWAVES * CAPW);      // [MT]
     uint32_t* rcnt = theta + MT;                              // [MT]
     uint32_t* rbase = rcnt + MT;                              // [MT]
+    uint32_t* wn = rbase + MT;                                // [NWAVES]
     if (MODE == LM_THRESH) {
         for (int i = tid; i < MT; i += LM_THREADS) {
             const int r = row0 + i;
@@ -223,19 +231,26 @@ __global__ __launch_bounds__(LM_THREADS) void lmhead_gemm_kernel(LmParams p) {
         __syncthreads();
     }
     // accumulator block (i, j), register q: row 32i + 8(q/4) + 4(l/32) + q%4,
-    // column 32j + l%32 of this wave's.  THRESH with four column blocks per
-    // wave: the thresholds of the lane's 32 rows go to registers first, so
-    // that the 128 compares below read no LDS (each read would wait behind
-    // the candidate stores before it); with fewer blocks the registers
-    // bought nothing measurable
-    constexpr bool TH_REGS = WN >= 4;
-    uint32_t th[2][16];
-    if (MODE == LM_THRESH && TH_REGS) {
+    // column 32j + l%32 of this wave's.  THRESH: the thresholds of the
+    // lane's 32 rows go to registers first, as floats: with t the key's
+    // canonical value, ord32(canon(v)) > key holds exactly when v > t as
+    // floats (NaN compares false and maps to -inf, -0 compares equal to +0
+    // and maps to +0), except that +inf maps to FLT_MAX, so a threshold of
+    // FLT_MAX becomes +inf; the key 0xFFFFFFFF of rows past B becomes a NaN
+    // (no candidates).  Every probe tile is full, so its 128th key belongs
+    // to a token and is at least the key of -inf.
+    float thf[2][16];
+    if (MODE == LM_THRESH) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int q = 0; q < 16; ++q) th[i][q] = theta[wr + 32 * i + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)];
+            for (int q = 0; q < 16; ++q) {
+                const uint32_t t = theta[wr + 32 * i + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)];
+                const float f = unord32(t);
+                thf[i][q] = f == bitsf(F32_MAX_BITS) ? bitsf(F32_PINF_BITS) : f;
+            }
     }
+    int nw = 0;   // THRESH: this wave's candidates so far (wave-uniform)
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -245,37 +260,63 @@ __global__ __launch_bounds__(LM_THREADS) void lmhead_gemm_kernel(LmParams p) {
                 const int rl = wr + 32 * i + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
                 const int r = row0 + rl;
                 const int c = col0 + wc + 32 * j + (lane & 31);
-                if (r >= p.B || c >= p.col_end) continue;
+                const bool in = r < p.B && c < p.col_end;
                 const float v = acc[i][j][q];
                 if (MODE != LM_THRESH) {
-                    p.out[(int64_t)r * p.ldo + (c - p.col_begin)] = v;
+                    if (in) p.out[(int64_t)r * p.ldo + (c - p.col_begin)] = v;
                 } else {
-                    const uint32_t k32 = ord32(canon(v));
-                    if (k32 > (TH_REGS ? th[i][q] : theta[rl])) {
-                        const uint64_t key = ((uint64_t)k32 << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)c);
-                        const uint32_t pos = atomicAdd(rcnt + rl, 1u);
-                        if (pos < (uint32_t)RSLOT) {
-                            rkeys[rl * RSLOT + pos] = key;
-                        } else {
-                            const int at = atomicAdd(p.cnt + r, 1);
-                            if (at < LM_CAP) p.cand[(int64_t)r * LM_CAP + at] = key;
+                    const bool cand = in && v > thf[i][q];
+                    const uint64_t bal = __ballot(cand);
+                    if (__builtin_expect(bal != 0ull, 0)) {   // wave-uniform; rare: kept out of line
+                        if (cand) {
+                            const uint32_t k32 = ord32(canon(v));
+                            const uint64_t key = ((uint64_t)k32 << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)c);
+                            const int pos = nw + lane_prefix(bal);
+                            if (pos < CAPW) {
+                                wkeys[wave * CAPW + pos] = key;
+                                wrow[wave * CAPW + pos] = (uint16_t)rl;
+                            } else {
+                                const int at = atomicAdd(p.cnt + r, 1);
+                                if (at < LM_CAP) p.cand[(int64_t)r * LM_CAP + at] = key;
+                            }
                         }
+                        nw += __popcll(bal);
                     }
                 }
             }
     if (MODE == LM_THRESH) {
+        if (lane == 0) wn[wave] = (uint32_t)(nw < CAPW ? nw : CAPW);
         __syncthreads();
-        for (int i = tid; i < MT; i += LM_THREADS) {
-            const uint32_t m = rcnt[i] < (uint32_t)RSLOT ? rcnt[i] : (uint32_t)RSLOT;
-            if (m > 0u) rbase[i] = (uint32_t)atomicAdd(p.cnt + row0 + i, (int)m);
+        uint32_t nwv[NWAVES], tot = 0;
+#pragma unroll
+        for (int w = 0; w < NWAVES; ++w) {
+            nwv[w] = wn[w];
+            tot += nwv[w];
+        }
+        // entry e of the waves' lists, in wave order -> (wave, index)
+        auto at_e = [&](uint32_t e) -> int {
+            int w = 0;
+#pragma unroll
+            for (int u = 0; u < NWAVES - 1; ++u)
+                if (w == u && e >= nwv[u]) {
+                    e -= nwv[u];
+                    w = u + 1;
+                }
+            return w * CAPW + (int)e;
+        };
+        for (uint32_t e = tid; e < tot; e += LM_THREADS) {
+            const int x = at_e(e);
+            wpos[x] = (uint16_t)atomicAdd(rcnt + wrow[x], 1u);
         }
         __syncthreads();
-        for (int e = tid; e < MT * RSLOT; e += LM_THREADS) {
-            const int i = e / RSLOT, pos = e % RSLOT;
-            if ((uint32_t)pos < rcnt[i]) {
-                const uint32_t at = rbase[i] + (uint32_t)pos;
-                if (at < (uint32_t)LM_CAP) p.cand[(int64_t)(row0 + i) * LM_CAP + at] = rkeys[e];
-            }
+        for (int i = tid; i < MT; i += LM_THREADS)
+            if (rcnt[i] > 0u) rbase[i] = (uint32_t)atomicAdd(p.cnt + row0 + i, (int)rcnt[i]);
+        __syncthreads();
+        for (uint32_t e = tid; e < tot; e += LM_THREADS) {
+            const int x = at_e(e);
+            const int i = wrow[x];
+            const uint32_t at = rbase[i] + wpos[x];
+            if (at < (uint32_t)LM_CAP) p.cand[(int64_t)(row0 + i) * LM_CAP + at] = wkeys[x];
         }
     }
 }
