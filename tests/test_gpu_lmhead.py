@@ -219,6 +219,69 @@ def test_fused_candidate_overflow():
         assert np.array_equal(g[k], u[k]), k
 
 
+def _special_case(seed):
+    """Rows whose logits hold infinities, NaNs and zeros around the probe's
+    threshold.  Hidden row r is 2 on dimension r (and on r + 64 for the NaN
+    rows), so logit[r, c] = 2 w[c, r] (+ 2 w[c, r + 64]): a weight of
+    3.39e38 (the largest bf16) gives +inf, its negative -inf, and the two on
+    one column a NaN (+inf + -inf)."""
+    rng = np.random.default_rng(seed)
+    B, D, P, V = 8, 128, 16384, 16384 + 4000
+    BIG = 3.3895314e38
+    h = np.zeros((B, D), np.float32)
+    for r in range(B):
+        h[r, r] = 2.0
+    h[2, 66] = 2.0
+    h[3, 67] = 2.0
+    w = (rng.integers(-8, 9, (V, D)) / 64).astype(np.float32)
+    w[:, 64:] = 0.0
+    pick = lambda lo, hi, n: rng.choice(np.arange(lo, hi), n, replace=False)
+    # row 0: 200 probe columns and 50 later ones at +inf: the probe's 128th
+    # key is the key of FLT_MAX, which no later column beats
+    w[pick(0, P, 200), 0] = BIG
+    w[pick(P, V, 50), 0] = BIG
+    # row 1: 100 probe columns at +inf, 50 later ones too (later +inf ties)
+    w[pick(0, P, 100), 1] = BIG
+    w[pick(P, V, 50), 1] = BIG
+    # row 2: NaNs in the probe and after it
+    for c in np.concatenate([pick(0, P, 30), pick(P, V, 60)]):
+        w[c, 2], w[c, 66] = BIG, -BIG
+    # row 3: only 50 finite probe values, the others -inf or NaN: the
+    # threshold is the key of -inf and every finite later column is kept
+    keep = pick(0, P, 50)
+    neg = np.ones(P, bool)
+    neg[keep] = False
+    w[np.nonzero(neg)[0], 3] = -BIG
+    for c in pick(0, P, 20):
+        if neg[c]:
+            w[c, 3], w[c, 67] = BIG, -BIG
+    # row 4: all probe values zero; later ones zero or tiny of either sign
+    w[:P, 4] = 0.0
+    w[P:, 4] = rng.choice([0.0, 2.0 ** -120, -(2.0 ** -120)], V - P)
+    # row 5: 127 large finite probe values, then a later one just above them
+    w[pick(0, P, 127), 5] = 1.5e38
+    w[P + 7, 5] = 1.6e38
+    req = W.mixed_requests(rng, B, V, penalties=False, bias=False)
+    return W.to_bf16_bits(h), W.to_bf16_bits(w), req
+
+
+def test_fused_special_values_equal_unfused():
+    """The thresholded pass keeps exactly the columns whose merge key beats
+    the probe's 128th, also for infinities, NaNs and zeros: the fused step
+    equals the unfused one (logits launch, then the sampling step) bit for
+    bit."""
+    h, w, req = _special_case(seed=21)
+    z = gpu_logits(h, w)
+    assert np.isposinf(z[0]).sum() == 250 and np.isnan(z[2]).sum() == 90
+    assert np.isneginf(z[3, :16384]).sum() > 16000 and np.all(z[4, :16384] == 0.0)
+    g = run_fused(h, w, req, seed=8, offset=3)
+    u = run_unfused(h, w, req, seed=8, offset=3)
+    for k in KEYS:
+        assert np.array_equal(g[k], u[k]), k
+    # the tied +inf tokens of row 0 rank by id: the probe's own come first
+    assert np.all(g["topk_ids"][0] < 16384)
+
+
 def test_fused_rng_advance():
     """rng_advance: two calls in a row draw with offsets o and o + 1."""
     lib = _lib()
