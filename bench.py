@@ -319,7 +319,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--copies", type=int, default=16)
-    ap.add_argument("--median-replays", type=int, default=50,
+    ap.add_argument("--median-replays", type=int, default=200,
                     help="event-timed graph replays behind the median step time")
     ap.add_argument("--legs", default=",".join(LEGS),
                     help="comma list of workloads to run besides the headline: " + ",".join(LEGS[1:]))

@@ -62,7 +62,12 @@ constexpr int S1_CPT = 16;            // 16-byte chunks per thread
 constexpr int S1_CCAP = 128;          // flagged chunks held per wave (fast path)
 constexpr int S1_KCAP = 256;          // survivors held per wave (fast path)
 constexpr int S1_LIST_W = 2 * WAVE + SS_GAMMA_MAX;   // listed tokens one wave records: 64 prior, 64 bias, drafts
-constexpr int S1_NL_FAST = 32;        // listed tokens per tile left in the data (more are masked out)
+// listed tokens per tile left in the data (more are masked out): skipping
+// them at the survivor step costs one LDS read per listed token and flagged
+// chunk, the mask a fixed price per tile; measured on bf16 rows without a
+// grammar, masking is faster from about ten per tile on, and no slower
+// with five
+constexpr int S1_NL_FAST = 4;
 
 template <int DT> struct S1Traits;
 template <> struct S1Traits<SS_BF16> {
@@ -919,10 +924,10 @@ __device__ __forceinline__ void tile_process(const Stage1Params& P, int row, int
     const int4 nl4 = *(const int4*)sh.nlw;   // one read
     const int nl = __builtin_amdgcn_readfirstlane(nl4.x + nl4.y + nl4.z + nl4.w);
     // The tile's listed tokens are cleared from the mask when the row has a
-    // grammar mask, or when there are too many of them to leave in the data
-    // (each wave keeps a quarter of them as extra candidates, which lowers
-    // the threshold; past S1_NL_FAST the flagged chunks overflow into the
-    // exact path): the mask then leaves them out like any disallowed token,
+    // grammar mask, or when there are more than S1_NL_FAST of them (each
+    // wave keeps a quarter of those left in the data as extra candidates,
+    // which lowers the threshold, and the survivor step skips them one by
+    // one): the mask then leaves them out like any disallowed token,
     // and the threshold and survivor steps need not know about them.
     const bool long_lists = (use_prior && n_prior > S1_WAVES * WAVE) || (use_bias && n_bias > S1_WAVES * WAVE);
     const bool fold = (nl > 0 && (use_grammar || nl > S1_NL_FAST)) || long_lists;   // block-uniform

@@ -180,10 +180,11 @@ def test_c2_stress_full(kind):
 
 @pytest.mark.parametrize("dtype", [W.DTYPE_BF16, W.DTYPE_F32])
 def test_many_listed_tokens_under_the_fold(dtype):
-    """Many listed tokens in one tile: up to 32 stay in the data (each wave
-    keeps that many more candidates), more are cleared from the mask; rows
-    with 20, 32, 60 and 128 listed tokens in tile 0, with and without a
-    grammar, positive and negative."""
+    """Listed tokens in one tile: up to 4 stay in the data on rows without
+    a grammar (each wave keeps a quarter of them as extra candidates and the
+    survivor step skips them), more - and all of them on grammar rows - are
+    cleared from the mask; rows with 3 to 128 listed tokens in tile 0, with
+    and without a grammar, positive and negative logits."""
     rng = np.random.default_rng(31)
     V, n = 70001, 8
     x = (rng.standard_normal((n, V)) * 2).astype(np.float32)
@@ -193,7 +194,7 @@ def test_many_listed_tokens_under_the_fold(dtype):
     req.rep_penalty[:] = 1.1
     req.freq_penalty[:] = 0.1
     for r in range(n):
-        k = (20, 32, 60, 128)[r % 4]
+        k = (3, 20, 5, 128, 4, 4, 60, 32)[r]   # grammar on the odd rows
         req.prior_ids[r, :k] = rng.choice(16384, k, replace=False)
         req.prior_cnt[r, :k] = rng.integers(1, 4, k)
         req.n_prior[r] = k
