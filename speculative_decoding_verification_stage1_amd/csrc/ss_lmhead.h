@@ -13,11 +13,11 @@
 // GEMM: a workgroup of 4 waves owns MT = 64 * WM rows and NT = (4 / WM) *
 // 32 * WN vocabulary columns; a wave owns 64 rows x 32 * WN columns as
 // 2 x WN blocks of 32 x 32.  The k loop runs in stages of KB (64 or 128):
-// each thread loads its share of the stage's H and W rows with 16-byte
-// loads (KB / 8 lanes read one row segment) one stage ahead into
-// registers, then writes it to an LDS double buffer whose 16-byte slots
-// are XOR-swizzled by row, so the fragment reads (32 rows at one k
-// offset) meet no bank conflicts.  When several row blocks share
+// the stage's H and W rows go straight from global memory to one of two or
+// three LDS stage buffers (16-byte direct loads, two stages ahead where
+// three buffers fit), whose 16-byte slots are XOR-swizzled by row, so the
+// fragment reads (32 rows at one k offset) meet no bank conflicts.  When
+// several row blocks share
 // a column tile, the blocks of one tile are given ids 8 apart, which the
 // dispatcher places on the same XCD: the second read of a W tile then
 // comes from that XCD's L2.
@@ -95,11 +95,33 @@ __global__ __launch_bounds__(LM_THREADS) void lmhead_gemm_kernel(LmParams p) {
     constexpr int NT = NWN * 32 * WN;           // columns per workgroup
     constexpr int CPR = KB / 8;                 // 16-byte chunks per row and stage
     constexpr int SROW = KB * 2;                // LDS bytes per row and stage
-    constexpr int RPP = LM_THREADS / CPR;       // rows one pass of the threads loads
     constexpr int AB = MT * SROW, WB = NT * SROW;
-    constexpr int NA = MT / RPP, NW = NT / RPP; // 16-byte loads per thread and stage
-    static_assert(MT % RPP == 0 && NT % RPP == 0 && KB % 16 == 0, "tile shape");
-    __shared__ __attribute__((aligned(16))) unsigned char lds[2][AB + WB];
+    static_assert(KB % 16 == 0, "tile shape");
+    // LDS stages: NST buffers of (A tile | W tile), each row's 16-byte
+    // chunks XOR-swizzled (slot below).  The global loads write LDS
+    // directly (global_load_lds_dwordx4: each wave instruction fills 1 KiB,
+    // lane L at byte 16 L of it, so lane L loads the chunk that the swizzle
+    // puts there), NST - 1 stages ahead of the one being multiplied: no
+    // registers stage the data and nothing waits for a load issued one
+    // stage earlier.  The buffers are separate arrays, used in a fixed
+    // rotation, so the compiler sees which one each LDS read touches and
+    // does not wait for the loads in flight to the others.
+    // Two stages when two workgroups' pairs fit in a CU's 160 KiB (the
+    // 64-row tiles, whose registers also allow two workgroups per CU: one
+    // workgroup's multiplies then cover the other's loads), else three when
+    // they fit, else two.  Measured at B=64, D=4096, V=2^17: 203 us with
+    // two stages and two workgroups per CU, 263 us with three stages and one.
+    constexpr int LDS_CU = 160 * 1024;
+    constexpr int NST = 4 * (AB + WB) <= LDS_CU ? 2 : (3 * (AB + WB) <= LDS_CU - 16 * 1024 ? 3 : 2);
+    constexpr int RPI = 1024 / SROW;                      // rows one wave instruction fills
+    constexpr int NINS = (MT + NT) / RPI;                 // instructions per stage
+    constexpr int LPW = NINS / (LM_THREADS / WAVE);       // per wave
+    static_assert(1024 % SROW == 0 && MT % RPI == 0 && NT % RPI == 0 && NINS % (LM_THREADS / WAVE) == 0,
+                  "direct loads");
+    static_assert(LPW <= 31, "vmcnt range");
+    __shared__ __attribute__((aligned(16))) unsigned char lds0[AB + WB];
+    __shared__ __attribute__((aligned(16))) unsigned char lds1[AB + WB];
+    __shared__ __attribute__((aligned(16))) unsigned char lds2[NST == 3 ? AB + WB : 16];
     int ct, rt;
     if (!lm_tile(p, ct, rt)) return;
     const int tid = threadIdx.x;
@@ -115,47 +137,43 @@ __global__ __launch_bounds__(LM_THREADS) void lmhead_gemm_kernel(LmParams p) {
         }
         if (!__syncthreads_or(over)) return;
     }
-    // global sources: thread t loads 16-byte chunk t % CPR of rows t / CPR +
-    // RPP i (rows past the end read the last valid row; their results are
-    // dropped)
-    const int chunk = tid % CPR, lrow = tid / CPR;
-    const uint16_t* ga[NA];
-    const uint16_t* gw[NW];
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-        const int r = row0 + lrow + RPP * i;
-        ga[i] = p.H + (int64_t)(r < p.B ? r : p.B - 1) * p.ldh + chunk * 8;
-    }
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-        const int c = col0 + lrow + RPP * i;
-        gw[i] = p.W + (int64_t)(c < p.col_end ? c : p.col_end - 1) * p.ldw + chunk * 8;
-    }
-    lm_u32x4 ra[NA], rw[NW];
-    auto gload = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < NA; ++i) ra[i] = *(const lm_u32x4*)(ga[i] + k0);
-#pragma unroll
-        for (int i = 0; i < NW; ++i) rw[i] = *(const lm_u32x4*)(gw[i] + k0);
-    };
-    // LDS slot of (row, chunk): row * SROW + 16 * (chunk ^ (row & 7))
     // slot of chunk c of row r: c ^ f(r), with f chosen so that the 16
-    // rows one 16-lane phase of a fragment read touches (and the rows a
-    // store phase writes) land on distinct 16-byte bank groups of a
+    // rows one 16-lane phase of a fragment read touches (and the rows one
+    // load instruction writes) land on distinct 16-byte bank groups of a
     // 256-byte window, and any 8 consecutive rows on distinct groups of a
     // 128-byte one
-    auto slot = [](int r, int c) {
-        int f;
-        if constexpr (CPR >= 16) f = r & 15;
-        else if constexpr (CPR == 8) f = (r & 7) ^ ((r >> 3) & 1);
-        else f = r & (CPR - 1);
-        return r * SROW + 16 * (c ^ f);
+    auto swz = [](int r) {
+        if constexpr (CPR >= 16) return r & 15;
+        else if constexpr (CPR == 8) return (r & 7) ^ ((r >> 3) & 1);
+        else return r & (CPR - 1);
     };
-    auto lstore = [&](int buf) {
+    auto slot = [&](int r, int c) { return r * SROW + 16 * (c ^ swz(r)); };
+    // this lane's source for each of its wave's LPW instructions (rows past
+    // the end read the last valid row; their results are dropped), and the
+    // instruction's LDS offset in a stage buffer
+    const uint16_t* src[LPW];
+    int dst[LPW];
 #pragma unroll
-        for (int i = 0; i < NA; ++i) *(lm_u32x4*)(&lds[buf][slot(lrow + RPP * i, chunk)]) = ra[i];
+    for (int i = 0; i < LPW; ++i) {
+        const int ins = wave + (LM_THREADS / WAVE) * i;
+        const bool is_a = ins < MT / RPI;
+        const int rb = (is_a ? ins : ins - MT / RPI) * RPI;   // first row of the instruction's block
+        const int r = rb + lane / CPR;
+        const int c = (lane % CPR) ^ swz(r);                    // the chunk that lands at this lane's slot
+        if (is_a) {
+            const int g = row0 + r;
+            src[i] = p.H + (int64_t)(g < p.B ? g : p.B - 1) * p.ldh + c * 8;
+        } else {
+            const int g = col0 + r;
+            src[i] = p.W + (int64_t)(g < p.col_end ? g : p.col_end - 1) * p.ldw + c * 8;
+        }
+        dst[i] = (is_a ? 0 : AB) + rb * SROW;
+    }
+    auto issue = [&](int k0, unsigned char* buf) {
 #pragma unroll
-        for (int i = 0; i < NW; ++i) *(lm_u32x4*)(&lds[buf][AB + slot(lrow + RPP * i, chunk)]) = rw[i];
+        for (int i = 0; i < LPW; ++i)
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src[i] + k0),
+                                             (__attribute__((address_space(3))) void*)(buf + dst[i]), 16, 0, 0);
     };
     const int wr = (wave / NWN) * 64;            // this wave's rows and columns in the tile
     const int wc = (wave % NWN) * 32 * WN;
@@ -164,9 +182,9 @@ __global__ __launch_bounds__(LM_THREADS) void lmhead_gemm_kernel(LmParams p) {
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < WN; ++j) acc[i][j] = lm_f32x16{};
-    auto compute = [&](int buf) {
-        const unsigned char* la = lds[buf];
-        const unsigned char* lw = lds[buf] + AB;
+    auto compute = [&](const unsigned char* buf) {
+        const unsigned char* la = buf;
+        const unsigned char* lw = buf + AB;
 #pragma unroll
         for (int u = 0; u < KB / 16; ++u) {
             const int c = 2 * u + (lane >> 5);   // this lane's 16-byte chunk of the step
@@ -184,17 +202,61 @@ __global__ __launch_bounds__(LM_THREADS) void lmhead_gemm_kernel(LmParams p) {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
         }
     };
+    // stage s: wait for this wave's loads of s (the loads of the stages
+    // after it, at most NST - 2, may stay in flight), then a barrier - every
+    // wave's part of s has landed and every wave is done with stage s - 1,
+    // whose buffer the loads of s + NST - 1 then reuse.  The barrier is the
+    // bare s_barrier: a workgroup fence would wait for every load in flight.
+    auto wait_stage = [&](bool last) {
+        constexpr int VM = NST == 3 ? LPW : 0;
+        constexpr int ENC = (VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8);   // vmcnt(VM), others free
+        if (last || NST == 2) __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0)
+        else __builtin_amdgcn_s_waitcnt(ENC);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
     const int S = p.D / KB;
-    gload(0);
-    lstore(0);
-    if (S > 1) gload(KB);
-    __syncthreads();
-    for (int s = 0; s < S; ++s) {
-        compute(s & 1);
-        if (s + 1 < S) lstore((s + 1) & 1);
-        if (s + 2 < S) gload((s + 2) * KB);
-        __syncthreads();
+    // the main loop issues the loads of stage s + NST - 1 unconditionally
+    // (past the last stage they reload the last stage's data into a buffer
+    // no later stage reads), so its body is straight-line code: a branch
+    // around the loads would make the compiler wait for all of them before
+    // the next LDS read
+    auto step = [&](int s, const unsigned char* cur, unsigned char* refill) {
+        wait_stage(false);
+        const int sn = s + NST - 1;
+        issue((sn < S ? sn : S - 1) * KB, refill);
+        compute(cur);
+    };
+    issue(0, lds0);
+    if (NST == 3) issue((S > 1 ? 1 : 0) * KB, lds1);
+    int s0 = 0;
+    if constexpr (NST == 3) {
+        for (; s0 + 3 <= S; s0 += 3) {
+            step(s0, lds0, lds2);
+            step(s0 + 1, lds1, lds0);
+            step(s0 + 2, lds2, lds1);
+        }
+        // the last one or two stages: their data is issued already
+        if (s0 < S) {
+            wait_stage(true);
+            compute(lds0);
+            if (s0 + 1 < S) {
+                wait_stage(true);
+                compute(lds1);
+            }
+        }
+    } else {
+        for (; s0 + 2 <= S; s0 += 2) {
+            step(s0, lds0, lds1);
+            step(s0 + 1, lds1, lds0);
+        }
+        if (s0 < S) {
+            wait_stage(true);
+            compute(lds0);
+        }
     }
+    __syncthreads();   // every wave is done with the stage buffers, and every load has landed
     // THRESH: the rows' thresholds (the largest 128th key over the probe
     // tiles); then each wave appends the values above their row's
     // threshold to its own LDS list, slots given by a ballot prefix (no
@@ -205,9 +267,9 @@ __global__ __launch_bounds__(LM_THREADS) void lmhead_gemm_kernel(LmParams p) {
     // buffers are free after the k loop.)
     constexpr int NWAVES = LM_THREADS / WAVE;
     constexpr int CAPW = 512;
-    static_assert(NWAVES * CAPW * (8 + 2 + 2) + 3 * MT * 4 + 16 <= 2 * (AB + WB), "candidate staging");
+    static_assert(NWAVES * CAPW * (8 + 2 + 2) + 3 * MT * 4 + 16 <= AB + WB, "candidate staging");
     static_assert(MT <= 65536, "row index in 16 bits");
-    uint64_t* wkeys = (uint64_t*)&lds[0][0];                  // [NWAVES][CAPW] keys
+    uint64_t* wkeys = (uint64_t*)&lds0[0];                    // [NWAVES][CAPW] keys
     uint16_t* wrow = (uint16_t*)(wkeys + NWAVES * CAPW);      // [NWAVES][CAPW] their rows in the tile
     uint16_t* wpos = wrow + NWAVES * CAPW;                    // [NWAVES][CAPW] their slots in the row's share
     uint32_t* theta = (uint32_t*)(wpos + NWAVES * CAPW);      // [MT]
