@@ -217,114 +217,116 @@ struct S2Lists {
     float bval[LIST_SHORT];
 };
 
+// Open-addressing table of the ids named by a row's lists (at most KMAX
+// entries, so the table is never more than half full): the id, the
+// smallest combined position (prior entries first, then bias entries)
+// naming it, and its live prior entries (low 16 bits) and bias entries
+// (high 16 bits).
+constexpr int LIST_HASH = 256;
+struct ListedTable {
+    uint32_t id[LIST_HASH];   // ~0: empty
+    uint32_t first[LIST_HASH];
+    uint32_t cnt[LIST_HASH];
+};
+
+__device__ __forceinline__ void listed_table_clear(ListedTable& T) {
+    const uint4 ones{~0u, ~0u, ~0u, ~0u}, zero{0u, 0u, 0u, 0u};
+    for (int i = lane_id(); i < LIST_HASH / 4; i += WAVE) {
+        ((uint4*)T.id)[i] = ones;
+        ((uint4*)T.first)[i] = ones;
+        ((uint4*)T.cnt)[i] = zero;
+    }
+}
+
 // Listed tokens: exact processed logits of the first
-// valid entry of every id named by an active list, sorted; at most
-// 2 * LIST_SHORT + SS_GAMMA_MAX entries, 128 per pass (two per lane).
+// valid entry of every id named by an active list, sorted; at most KMAX
+// combined entries (two per lane).
 //
-// One pass over each list counts, per token, its matching entries and
-// remembers one of them.  The repetition penalty is the same map for every
-// entry, so m matching entries apply it m times.  Frequency/presence and
-// bias differ per entry and must be applied in list order; with one
-// matching entry (the usual case) that is a single subtraction / addition,
-// and tokens with several entries take a sequential walk of the list.
+// Each valid entry enters its id into the row's table, which gives every
+// entry its id's first position and its number of prior and bias entries;
+// only the first entry of an id makes a key.  The repetition penalty is the
+// same map for every entry, so m matching entries apply it m times.
+// Frequency/presence and bias differ per entry and must be applied in list
+// order; with one matching entry (the usual case) that is the entry's own
+// subtraction / addition, and tokens with several entries take a sequential
+// walk of the list.  The logits at the listed ids are requested before the
+// table is built, so the table hides their latency.
 template <int DT>
 __device__ __forceinline__ WL64 listed_list(const Stage1Params& P, const RowParams& rp, int row, int np, int nb,
-                            const S2Lists& L) {
+                                            const S2Lists& L, ListedTable& T) {
     const int lane = lane_id();
     const int ncomb = np + nb;
     const bool grammar = (rp.flags & SS_GRAMMAR) != 0;
     const bool do_rep = (rp.flags & SS_REP) != 0;
     const bool do_fp = (rp.flags & SS_FREQPRES) != 0;
     const bool do_bias = (rp.flags & SS_BIAS) != 0;
-    WL64 acc{0ull, 0ull};
-    for (int c0 = 0; c0 < ncomb; c0 += 2 * WAVE) {   // uniform
-        int t[2], id[2], mp[2], ip[2], mb[2], ib[2];
-        bool ok[2], dup[2];
-        float z[2];
+    int t[2], id[2];
+    bool ok[2];
+    uint32_t raw[2], word[2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            t[h] = c0 + h * WAVE + lane;
-            id[h] = -1;
-            ok[h] = false;
-            if (t[h] < np) {
-                id[h] = L.pid[t[h]];
-                ok[h] = L.pct[t[h]] >= 1 && id[h] >= 0 && id[h] < P.V;
-            } else if (t[h] < ncomb) {
-                id[h] = L.bid[t[h] - np];
-                ok[h] = id[h] >= 0 && id[h] < P.V;
-            }
-            z[h] = 0.0f;
-            if (ok[h]) {
-                if (DT == SS_BF16) z[h] = widen_bf16(((const uint16_t*)P.logits)[(int64_t)row * P.ld + id[h]]);
-                else z[h] = ((const float*)P.logits)[(int64_t)row * P.ld + id[h]];
-                if (grammar &&
-                    !((P.aux.bitmask[(int64_t)row * P.aux.bitmask_stride + (id[h] >> 5)] >> (id[h] & 31)) & 1u))
-                    z[h] = bitsf(F32_NINF_BITS);
-            }
-            mp[h] = 0;
-            ip[h] = 0;
-            mb[h] = 0;
-            ib[h] = 0;
-            dup[h] = false;
+    for (int h = 0; h < 2; ++h) {
+        t[h] = h * WAVE + lane;
+        id[h] = -1;
+        ok[h] = false;
+        if (t[h] < np) {
+            id[h] = L.pid[t[h]];
+            ok[h] = L.pct[t[h]] >= 1 && id[h] >= 0 && id[h] < P.V;
+        } else if (t[h] < ncomb) {
+            id[h] = L.bid[t[h] - np];
+            ok[h] = id[h] >= 0 && id[h] < P.V;
         }
-        // one pass over each list; entries are LDS broadcasts
-#pragma unroll 4
-        for (int u = 0; u < np; ++u) {
-            const int iu = L.pid[u];
-            const bool valid = L.pct[u] >= 1;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const bool m = valid && iu == id[h];
-                mp[h] += m;
-                ip[h] = m ? u : ip[h];
-                dup[h] |= m && u < t[h];
-            }
-        }
-#pragma unroll 4
-        for (int u = 0; u < nb; ++u) {
-            const int iu = L.bid[u];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const bool m = iu == id[h];
-                mb[h] += m;
-                ib[h] = m ? u : ib[h];
-                dup[h] |= m && np + u < t[h];
-            }
-        }
-        uint64_t key[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            float zz = z[h];
-            if (ok[h] && !dup[h]) {
-                if (do_rep)
-                    for (int r = 0; r < mp[h]; ++r) zz = (zz > 0.0f) ? zz / rp.rep : zz * rp.rep;
-                if (do_fp) {
-                    if (mp[h] == 1) {
-                        const float pen = (float)L.pct[ip[h]] * rp.freq + rp.pres;
-                        zz = zz - pen;
-                    } else if (mp[h] > 1) {
-                        for (int u = 0; u < np; ++u)
-                            if (L.pct[u] >= 1 && L.pid[u] == id[h]) {
-                                const float pen = (float)L.pct[u] * rp.freq + rp.pres;
-                                zz = zz - pen;
-                            }
-                    }
-                }
-                if (do_bias) {
-                    if (mb[h] == 1) zz = zz + L.bval[ib[h]];
-                    else if (mb[h] > 1)
-                        for (int u = 0; u < nb; ++u)
-                            if (L.bid[u] == id[h]) zz = zz + L.bval[u];
-                }
-            }
-            key[h] = (ok[h] && !dup[h])
-                         ? (((uint64_t)ord32(canon(zz)) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id[h]))
-                         : 0ull;
-        }
-        const WL64 srt = wave_sort128(WL64{key[0], key[1]});
-        acc = c0 == 0 ? srt : wave_merge(acc, srt);
+        const int ic = ok[h] ? id[h] : 0;   // every lane loads, from column 0 if it has no entry
+        if (DT == SS_BF16) raw[h] = ((const uint16_t*)P.logits)[(int64_t)row * P.ld + ic];
+        else raw[h] = __float_as_uint(((const float*)P.logits)[(int64_t)row * P.ld + ic]);
+        word[h] = grammar ? P.aux.bitmask[(int64_t)row * P.aux.bitmask_stride + (ic >> 5)] : ~0u;
     }
-    return acc;
+    uint32_t slot[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        slot[h] = 0;
+        if (ok[h]) {
+            uint32_t s = ((uint32_t)id[h] * 0x9E3779B1u) >> 24;
+            for (;;) {   // ends: fewer entries than slots
+                const uint32_t o = atomicCAS(&T.id[s], ~0u, (uint32_t)id[h]);
+                if (o == ~0u || o == (uint32_t)id[h]) break;
+                s = (s + 1) & (LIST_HASH - 1);
+            }
+            slot[h] = s;
+            atomicMin(&T.first[s], (uint32_t)t[h]);
+            atomicAdd(&T.cnt[s], t[h] < np ? 1u : 0x10000u);
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    uint64_t key[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const bool lead = ok[h] && T.first[slot[h]] == (uint32_t)t[h];
+        const uint32_t c = T.cnt[slot[h]];
+        const int mp = (int)(c & 0xFFFFu), mb = (int)(c >> 16);
+        float zz = DT == SS_BF16 ? widen_bf16((uint16_t)raw[h]) : __uint_as_float(raw[h]);
+        if (!((word[h] >> (id[h] & 31)) & 1u)) zz = bitsf(F32_NINF_BITS);
+        if (lead) {
+            if (do_rep)
+                for (int r = 0; r < mp; ++r) zz = (zz > 0.0f) ? zz / rp.rep : zz * rp.rep;
+            if (do_fp) {
+                if (mp == 1) {   // the entry itself (prior entries come first)
+                    zz = zz - ((float)L.pct[t[h]] * rp.freq + rp.pres);
+                } else if (mp > 1) {
+                    for (int u = 0; u < np; ++u)
+                        if (L.pct[u] >= 1 && L.pid[u] == id[h]) zz = zz - ((float)L.pct[u] * rp.freq + rp.pres);
+                }
+            }
+            if (do_bias) {
+                if (mb == 1 && t[h] >= np) zz = zz + L.bval[t[h] - np];   // the entry itself
+                else if (mb >= 1)
+                    for (int u = 0; u < nb; ++u)
+                        if (L.bid[u] == id[h]) zz = zz + L.bval[u];
+            }
+        }
+        key[h] = lead ? (((uint64_t)ord32(canon(zz)) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id[h])) : 0ull;
+    }
+    return wave_sort128(WL64{key[0], key[1]});
 }
 
 // ---- listed tokens by sorting: the row's entries (prior entries, then the
@@ -413,10 +415,15 @@ static_assert(2 * LIST_SHORT + SS_GAMMA_MAX <= LW_CAP, "wave sort capacity");
 
 // One wave's LDS area in the listed-token workgroups: the staged lists, or
 // the entry keys of the sorting form.
-union ListedArea {
+struct ListedStage {
     S2Lists lists;
+    ListedTable table;
+};
+union ListedArea {
+    ListedStage st;
     uint64_t keys[LW_CAP];
 };
+static_assert(sizeof(ListedStage) <= sizeof(uint64_t) * LW_CAP, "listed staging area");
 
 // The sorting form in one wave: out[row] = the best 128 listed tokens.
 // (Made a separate, not inlined function, c2's Stage 1 took twice as
@@ -475,7 +482,7 @@ __device__ __forceinline__ void listed_row_sorted(const Stage1Params& P, const R
 // wave's own LDS area, then ranked as exact keys (list order arithmetic).
 template <int DT>
 __device__ __forceinline__ void listed_row_wave(const Stage1Params& P, uint64_t* out, int row, ListedArea& area) {
-    S2Lists& lists = area.lists;
+    S2Lists& lists = area.st.lists;
     const int b = __builtin_amdgcn_readfirstlane(div_uniform(row, P.rows_per_req));
     const RowParams rp = row_params(P, b);
     int np = rp.valid ? rp.n_prior : 0;
@@ -492,6 +499,7 @@ __device__ __forceinline__ void listed_row_wave(const Stage1Params& P, uint64_t*
     const auto bid = gmem(P.aux.bias_ids + (int64_t)b * P.aux.bias_stride);
     const auto bvl = gmem(P.aux.bias_val + (int64_t)b * P.aux.bias_stride);
     const int lane = lane_id();
+    listed_table_clear(area.st.table);
     for (int u = lane; u < np; u += WAVE) {
         lists.pid[u] = pid[u];
         lists.pct[u] = pct[u];
@@ -529,7 +537,7 @@ __device__ __forceinline__ void listed_row_wave(const Stage1Params& P, uint64_t*
             __builtin_amdgcn_wave_barrier();
         }
     }
-    const WL64 l = listed_list<DT>(P, rp, row, np, nb, lists);
+    const WL64 l = listed_list<DT>(P, rp, row, np, nb, lists, area.st.table);
     out[(int64_t)row * KMAX + lane] = l.lo;
     out[(int64_t)row * KMAX + lane + WAVE] = l.hi;
 }

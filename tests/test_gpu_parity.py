@@ -281,6 +281,70 @@ def test_heavy_lists():
     sample_parity(W.SampleWorkload("lists-f32", W.DTYPE_F32, W.bf16_bits_to_f32(x), req), seed=6)
 
 
+def _colliding_ids(V, n, slot=250):
+    """n ids in [0, V) that the listed-token id table of the tile stage
+    (256 slots, Fibonacci hashing: (id * 0x9E3779B1 mod 2^32) >> 24) sends
+    to one slot near the end, so that its probe chains are long and wrap."""
+    ids = np.arange(V, dtype=np.uint64)
+    h = ((ids * np.uint64(0x9E3779B1)) & np.uint64(0xFFFFFFFF)) >> np.uint64(24)
+    return ids[h == slot][:n].astype(np.int32)
+
+
+def test_listed_tokens_duplicates_and_collisions():
+    """Rows whose lists (at most 128 entries) take the one-wave listed-token
+    path, with many repeated ids: repeats within the prior list, within the
+    bias list and across both, dead entries (count 0), out-of-range ids,
+    exactly 128 entries, and ids that share one table slot.  The listed
+    region's logits are raised so that listed tokens fill much of the
+    128-candidate list; top-k/top-p/min-p are off so all 128 probabilities
+    are compared."""
+    V, B, NP, NB = 50021, 12, 128, 128
+    rng = np.random.default_rng(31)
+    xf = rng.standard_normal((B, V)).astype(np.float32)
+    xf[:, :300] += 4.0
+    coll = _colliding_ids(V, 70)
+    xf[:, coll] += 4.0
+    x = W.to_bf16_bits(xf)
+    req = W.plain_requests(B, temperature=1.0, prior_len=NP, bias_len=NB)
+    req.use_penalties[:] = True
+    req.use_bias[:] = True
+    req.rep_penalty[:] = 1.3
+    req.freq_penalty[:] = 0.4
+    req.pres_penalty[:] = 0.2
+
+    def put(r, pid, pct, bid):
+        np_, nb_ = len(pid), len(bid)
+        assert np_ + nb_ <= 128
+        req.prior_ids[r, :np_] = pid
+        req.prior_cnt[r, :np_] = pct
+        req.n_prior[r] = np_
+        req.bias_ids[r, :nb_] = bid
+        req.bias_val[r, :nb_] = rng.uniform(-4.0, 4.0, nb_).astype(np.float32)
+        req.n_bias[r] = nb_
+
+    put(0, rng.integers(0, 200, 100), rng.integers(0, 5, 100), rng.integers(0, 200, 28))   # exactly 128
+    put(1, np.full(64, 7), rng.integers(0, 4, 64), np.concatenate([[7] * 30, rng.integers(0, 300, 34)]))
+    put(2, np.array([-1, V, V + 5, 3, 3, -7, 2**30, 4]), np.array([1, 2, 3, 1, 2, 1, 1, 0]), np.array([V, -2, 4, 3]))
+    put(3, np.array([11]), np.array([2]), np.zeros(0, np.int32))
+    put(4, np.zeros(0, np.int32), np.zeros(0, np.int32), np.array([5, 9, 5, 5, 9]))
+    put(5, np.arange(20, 147), rng.integers(1, 6, 127), np.array([60]))
+    put(6, coll[:64], rng.integers(1, 3, 64), coll[:64][::-1])                                # one slot, 64 ids
+    put(7, coll[:70], rng.integers(0, 3, 70), np.concatenate([coll[:40], rng.integers(0, 300, 18)]))
+    for r in range(8, B):
+        n = int(rng.integers(1, 129))
+        np_ = int(rng.integers(0, n + 1))
+        pool = np.concatenate([np.arange(300), coll])
+        put(r, rng.choice(pool, np_), rng.integers(0, 5, np_), rng.choice(pool, n - np_))
+    bm = (rng.random((B, (V + 31) // 32)) < 0.8).astype(np.uint32) * np.uint32(0xFFFFFFFF)
+    bm ^= rng.integers(0, 2**32, bm.shape, dtype=np.uint64).astype(np.uint32) & np.uint32(0x11111111)
+    req.bitmask = bm
+    req.use_grammar[1::2] = True
+    g, o = sample_parity(W.SampleWorkload("listed_dups", W.DTYPE_BF16, x, req), seed=6)
+    listed = [set(req.prior_ids[r, :req.n_prior[r]]) | set(req.bias_ids[r, :req.n_bias[r]]) for r in range(B)]
+    hits = [len(listed[r] & set(o["topk_ids"][r].tolist())) for r in range(B)]
+    assert sum(hits) >= 100 and min(hits[r] for r in (0, 1, 6, 7)) >= 5, hits   # listed tokens are candidates
+
+
 def test_workspace_reuse_alternating_inputs():
     """One workspace and one set of output buffers reused across calls with
     different inputs: every call must match the oracle for its own input."""
