@@ -607,38 +607,47 @@ LmWs lm_ws(void* ws, int B, int V) {
 
 int check_lmhead(const void* hidden, int64_t ldh, const void* weight, int64_t ldw, int B, int D, int V) {
     if (B < 0 || V < 1 || D < 1 || ldh < D || ldw < D) return SS_ERR_INVALID_ARG;
-    if (V > SS_V_MAX || D % 128 != 0 || D > (1 << 16) || (ldh % 8) || (ldw % 8)) return SS_ERR_UNSUPPORTED;
+    if (V > SS_V_MAX || D % 128 != 0 || D > (1 << 16) || (ldh % 8) || (ldw % 8) || ldh > (1 << 21) || ldw > (1 << 21))
+        return SS_ERR_UNSUPPORTED;
     if (B > 0 && (!hidden || !weight)) return SS_ERR_INVALID_ARG;
     if (((uintptr_t)hidden & 15u) || ((uintptr_t)weight & 15u)) return SS_ERR_UNSUPPORTED;
     return SS_OK;
 }
 
-// launch shapes: B <= 64 one row tile of 64 (waves side by side), else row
-// tiles of 128 (2 x 2 waves); the probe uses narrower column tiles so that
-// its fewer columns still give every CU work
-template <int MODE, int WM, int WN, int KB>
+template <int MODE, int WM, int WNW, int WN, int KB, bool SPLIT, bool NTW>
 void lm_launch(LmParams p, hipStream_t s) {
-    constexpr int MT = 64 * WM, NT = (4 / WM) * 32 * WN;
+    constexpr int MT = 64 * WM, NT = WNW * 32 * WN;
+    constexpr int threads = (WM * WNW + (SPLIT ? 4 : 0)) * WAVE;
     const int ncols = p.col_end - p.col_begin;
     p.ncol_tiles = (ncols + NT - 1) / NT;
     p.nrow_tiles = (p.B + MT - 1) / MT;
     const int64_t blocks = p.nrow_tiles == 1 ? p.ncol_tiles
                                              : (int64_t)(p.ncol_tiles + 7) / 8 * 8 * p.nrow_tiles;
-    hipLaunchKernelGGL((lmhead_gemm_kernel<MODE, WM, WN, KB>), dim3((unsigned)blocks), dim3(LM_THREADS), 0, s, p);
+    hipLaunchKernelGGL((lmhead_gemm_kernel<MODE, WM, WNW, WN, KB, SPLIT, NTW>), dim3((unsigned)blocks),
+                       dim3(threads), 0, s, p);
 }
 
-// launch shapes: B <= 64 one row tile of 64 (waves side by side), else row
-// tiles of 128 (2 x 2 waves); the probe uses narrower column tiles, so that
-// its fewer columns still spread over many CUs, and longer k stages, since
-// each of its workgroups runs alone on a CU and waits on memory
+// launch shapes (four multiplying waves each; rows x columns per
+// workgroup): B <= 64 one row tile of 64 rows (waves side by side);
+// B <= 128 one row tile of 128 (2 x 2 waves); larger B row tiles of 256
+// (waves stacked, 128 columns), so that each weight column is read by
+// fewer workgroups, with four more waves issuing the loads.  A launch with
+// one row tile reads the weights with the nt policy.  The probe uses
+// narrower column tiles, so that its fewer columns still spread over many
+// CUs, and longer k stages, since each of its workgroups runs alone on a CU
+// and waits on memory.  Measured at B=256, D=4096, V=2^18 (logits / fused
+// step, one run): 128-row tiles 657 / 791 us, 256-row tiles with the
+// loading waves and the nt policy 592 / 743 us.
 template <int MODE>
 void lm_launch_shape(LmParams p, bool probe, hipStream_t s) {
     if (p.B <= 64) {
-        if (probe) lm_launch<MODE, 1, 1, 128>(p, s);
-        else lm_launch<MODE, 1, 2, 64>(p, s);
+        if (probe) lm_launch<MODE, 1, 4, 1, 128, false, false>(p, s);
+        else lm_launch<MODE, 1, 4, 2, 64, false, true>(p, s);
     } else {
-        if (probe) lm_launch<MODE, 2, 2, 128>(p, s);
-        else lm_launch<MODE, 2, 4, 64>(p, s);
+        if (probe) lm_launch<MODE, 2, 2, 2, 128, false, false>(p, s);
+        else if (p.B <= 128) lm_launch<MODE, 2, 2, 4, 64, false, true>(p, s);
+        else if (p.B <= 256) lm_launch<MODE, 4, 1, 4, 64, true, true>(p, s);
+        else lm_launch<MODE, 4, 1, 4, 64, true, false>(p, s);
     }
 }
 

@@ -88,15 +88,24 @@ __device__ __forceinline__ bool lm_tile(const LmParams& p, int& ct, int& rt) {
     return ct < p.ncol_tiles;
 }
 
-template <int MODE, int WM, int WN, int KB>
-__global__ __launch_bounds__(LM_THREADS) void lmhead_gemm_kernel(LmParams p) {
+// Workgroup: WM x WNW = 4 waves multiply, each a tile of 64 rows by 32 WN
+// columns; with SPLIT, four more waves only issue the global loads (so that
+// a wave stalled on issuing a load never holds up the multiplies).  NTW:
+// the weight rows are read with the nt policy (a launch with one row tile
+// reads each weight once; the hidden rows, read by every workgroup, then
+// stay in L2).
+template <int MODE, int WM, int WNW, int WN, int KB, bool SPLIT, bool NTW>
+__global__ __launch_bounds__((WM * WNW + (SPLIT ? 4 : 0)) * WAVE) void lmhead_gemm_kernel(LmParams p) {
+    constexpr int NWC = WM * WNW;               // multiplying waves
+    constexpr int NTC = NWC * WAVE;             // their threads
+    constexpr int NTH = NTC + (SPLIT ? 4 * WAVE : 0);
+    constexpr int NWL = SPLIT ? 4 : NWC;        // waves issuing the loads
     constexpr int MT = 64 * WM;                 // rows per workgroup
-    constexpr int NWN = 4 / WM;                 // waves along the columns
-    constexpr int NT = NWN * 32 * WN;           // columns per workgroup
+    constexpr int NT = WNW * 32 * WN;           // columns per workgroup
     constexpr int CPR = KB / 8;                 // 16-byte chunks per row and stage
     constexpr int SROW = KB * 2;                // LDS bytes per row and stage
     constexpr int AB = MT * SROW, WB = NT * SROW;
-    static_assert(KB % 16 == 0, "tile shape");
+    static_assert(KB % 16 == 0 && NWC == 4, "tile shape");
     // LDS stages: NST buffers of (A tile | W tile), each row's 16-byte
     // chunks XOR-swizzled (slot below).  The global loads write LDS
     // directly (global_load_lds_dwordx4: each wave instruction fills 1 KiB,
@@ -115,23 +124,26 @@ __global__ __launch_bounds__(LM_THREADS) void lmhead_gemm_kernel(LmParams p) {
     constexpr int NST = 4 * (AB + WB) <= LDS_CU ? 2 : (3 * (AB + WB) <= LDS_CU - 16 * 1024 ? 3 : 2);
     constexpr int RPI = 1024 / SROW;                      // rows one wave instruction fills
     constexpr int NINS = (MT + NT) / RPI;                 // instructions per stage
-    constexpr int LPW = NINS / (LM_THREADS / WAVE);       // per wave
-    static_assert(1024 % SROW == 0 && MT % RPI == 0 && NT % RPI == 0 && NINS % (LM_THREADS / WAVE) == 0,
-                  "direct loads");
-    static_assert(LPW <= 31, "vmcnt range");
+    constexpr int LPW = NINS / NWL;                       // per loading wave
+    static_assert(1024 % SROW == 0 && MT % RPI == 0 && NT % RPI == 0 && NINS % NWL == 0, "direct loads");
+    static_assert((NST - 2) * LPW <= 63 && LPW <= 63, "vmcnt range");
+    static_assert((MT / RPI) % NWL == 0, "each loading wave's first instructions are the A rows");
     __shared__ __attribute__((aligned(16))) unsigned char lds0[AB + WB];
     __shared__ __attribute__((aligned(16))) unsigned char lds1[AB + WB];
-    __shared__ __attribute__((aligned(16))) unsigned char lds2[NST == 3 ? AB + WB : 16];
+    __shared__ __attribute__((aligned(16))) unsigned char lds2[NST > 2 ? AB + WB : 16];
+    unsigned char* const bufs[3] = {lds0, lds1, lds2};
     int ct, rt;
     if (!lm_tile(p, ct, rt)) return;
     const int tid = threadIdx.x;
-    const int wave = tid / WAVE;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
     const int lane = lane_id();
+    const bool loader = SPLIT && wave >= NWC;   // SPLIT: the last four waves issue the loads
+    const int lwave = SPLIT ? wave - NWC : wave;
     const int row0 = rt * MT;
     const int col0 = p.col_begin + ct * NT;
     if (MODE == LM_REDO) {   // only blocks holding an overflowed row go on
         bool over = false;
-        for (int i = tid; i < MT; i += LM_THREADS) {
+        for (int i = tid; i < MT; i += NTH) {
             const int r = row0 + i;
             over |= r < p.B && p.cnt[r] > LM_CAP;
         }
@@ -155,7 +167,7 @@ __global__ __launch_bounds__(LM_THREADS) void lmhead_gemm_kernel(LmParams p) {
     int dst[LPW];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-        const int ins = wave + (LM_THREADS / WAVE) * i;
+        const int ins = lwave + NWL * i;
         const bool is_a = ins < MT / RPI;
         const int rb = (is_a ? ins : ins - MT / RPI) * RPI;   // first row of the instruction's block
         const int r = rb + lane / CPR;
@@ -171,12 +183,15 @@ __global__ __launch_bounds__(LM_THREADS) void lmhead_gemm_kernel(LmParams p) {
     }
     auto issue = [&](int k0, unsigned char* buf) {
 #pragma unroll
-        for (int i = 0; i < LPW; ++i)
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src[i] + k0),
-                                             (__attribute__((address_space(3))) void*)(buf + dst[i]), 16, 0, 0);
+        for (int i = 0; i < LPW; ++i) {
+            const auto g = (const __attribute__((address_space(1))) void*)(src[i] + k0);
+            const auto l = (__attribute__((address_space(3))) void*)(buf + dst[i]);
+            if (NTW && i >= MT / RPI / NWL) __builtin_amdgcn_global_load_lds(g, l, 16, 0, LD_STREAM);
+            else __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+        }
     };
-    const int wr = (wave / NWN) * 64;            // this wave's rows and columns in the tile
-    const int wc = (wave % NWN) * 32 * WN;
+    const int wr = (wave / WNW) * 64;            // this wave's rows and columns in the tile
+    const int wc = (wave % WNW) * 32 * WN;
     lm_f32x16 acc[2][WN];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -207,54 +222,79 @@ __global__ __launch_bounds__(LM_THREADS) void lmhead_gemm_kernel(LmParams p) {
     // wave's part of s has landed and every wave is done with stage s - 1,
     // whose buffer the loads of s + NST - 1 then reuse.  The barrier is the
     // bare s_barrier: a workgroup fence would wait for every load in flight.
-    auto wait_stage = [&](bool last) {
-        constexpr int VM = NST == 3 ? LPW : 0;
-        constexpr int ENC = (VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8);   // vmcnt(VM), others free
-        if (last || NST == 2) __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0)
-        else __builtin_amdgcn_s_waitcnt(ENC);
+    auto barrier = [] {
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
     };
-    const int S = p.D / KB;
-    // the main loop issues the loads of stage s + NST - 1 unconditionally
-    // (past the last stage they reload the last stage's data into a buffer
-    // no later stage reads), so its body is straight-line code: a branch
-    // around the loads would make the compiler wait for all of them before
-    // the next LDS read
-    auto step = [&](int s, const unsigned char* cur, unsigned char* refill) {
-        wait_stage(false);
-        const int sn = s + NST - 1;
-        issue((sn < S ? sn : S - 1) * KB, refill);
-        compute(cur);
+    auto wait_stage = [&](bool last) {
+        constexpr int VM = (NST - 2) * LPW;
+        constexpr int ENC = (VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8);   // vmcnt(VM), others free
+        if (last) __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0)
+        else __builtin_amdgcn_s_waitcnt(ENC);
+        barrier();
     };
-    issue(0, lds0);
-    if (NST == 3) issue((S > 1 ? 1 : 0) * KB, lds1);
-    int s0 = 0;
-    if constexpr (NST == 3) {
-        for (; s0 + 3 <= S; s0 += 3) {
-            step(s0, lds0, lds2);
-            step(s0 + 1, lds1, lds0);
-            step(s0 + 2, lds2, lds1);
-        }
-        // the last one or two stages: their data is issued already
-        if (s0 < S) {
-            wait_stage(true);
-            compute(lds0);
-            if (s0 + 1 < S) {
-                wait_stage(true);
-                compute(lds1);
+    const int S = p.D / KB;
+    // the loads of stage s + NST - 1 are issued unconditionally (past the
+    // last stage they reload the last stage's data into a buffer no later
+    // stage reads), so the loop body is straight-line code: a branch around
+    // the loads would make the compiler wait for all of them before the
+    // next LDS read.  The loop runs whole rotations of the buffers; the
+    // last stages (fewer than NST, their loads issued already) follow it.
+    if constexpr (!SPLIT) {
+#pragma unroll
+        for (int j = 0; j < NST - 1; ++j) issue((j < S ? j : S - 1) * KB, bufs[j]);
+        int s0 = 0;
+        for (; s0 + NST <= S; s0 += NST) {
+#pragma unroll
+            for (int j = 0; j < NST; ++j) {
+                wait_stage(false);
+                const int sn = s0 + j + NST - 1;
+                issue((sn < S ? sn : S - 1) * KB, bufs[(j + NST - 1) % NST]);
+                compute(bufs[j]);
             }
         }
+#pragma unroll
+        for (int j = 0; j < NST - 1; ++j)
+            if (s0 + j < S) {
+                wait_stage(true);
+                compute(bufs[j]);
+            }
+    } else if (loader) {
+        // the same barriers as the multiplying waves, one per stage: wait
+        // for this wave's loads of stage s, meet the others, then refill
+        // the buffer of stage s - 1
+#pragma unroll
+        for (int j = 0; j < NST - 1; ++j) issue((j < S ? j : S - 1) * KB, bufs[j]);
+        int s0 = 0;
+        for (; s0 + NST <= S; s0 += NST) {
+#pragma unroll
+            for (int j = 0; j < NST; ++j) {
+                wait_stage(false);
+                const int sn = s0 + j + NST - 1;
+                issue((sn < S ? sn : S - 1) * KB, bufs[(j + NST - 1) % NST]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NST - 1; ++j)
+            if (s0 + j < S) wait_stage(true);
+        __syncthreads();   // after its own loads have landed (the fence waits for them)
+        return;            // a barrier waits only for the waves still running
     } else {
-        for (; s0 + 2 <= S; s0 += 2) {
-            step(s0, lds0, lds1);
-            step(s0 + 1, lds1, lds0);
+        int s0 = 0;
+        for (; s0 + NST <= S; s0 += NST) {
+#pragma unroll
+            for (int j = 0; j < NST; ++j) {
+                barrier();
+                compute(bufs[j]);
+            }
         }
-        if (s0 < S) {
-            wait_stage(true);
-            compute(lds0);
-        }
+#pragma unroll
+        for (int j = 0; j < NST - 1; ++j)
+            if (s0 + j < S) {
+                barrier();
+                compute(bufs[j]);
+            }
     }
     __syncthreads();   // every wave is done with the stage buffers, and every load has landed
     // THRESH: the rows' thresholds (the largest 128th key over the probe
@@ -265,7 +305,7 @@ __global__ __launch_bounds__(LM_THREADS) void lmhead_gemm_kernel(LmParams p) {
     // candidates per row, one global atomic per row reserves the block's
     // share of the row's list, and the keys are written there.  (The stage
     // buffers are free after the k loop.)
-    constexpr int NWAVES = LM_THREADS / WAVE;
+    constexpr int NWAVES = NWC;
     constexpr int CAPW = 512;
     static_assert(NWAVES * CAPW * (8 + 2 + 2) + 3 * MT * 4 + 16 <= AB + WB, "candidate staging");
     static_assert(MT <= 65536, "row index in 16 bits");
@@ -277,7 +317,7 @@ __global__ __launch_bounds__(LM_THREADS) void lmhead_gemm_kernel(LmParams p) {
     uint32_t* rbase = rcnt + MT;                              // [MT]
     uint32_t* wn = rbase + MT;                                // [NWAVES]
     if (MODE == LM_THRESH) {
-        for (int i = tid; i < MT; i += LM_THREADS) {
+        for (int i = tid; i < MT; i += NTC) {
             const int r = row0 + i;
             uint32_t t = 0xFFFFFFFFu;
             if (r < p.B) {
@@ -366,15 +406,15 @@ __global__ __launch_bounds__(LM_THREADS) void lmhead_gemm_kernel(LmParams p) {
                 }
             return w * CAPW + (int)e;
         };
-        for (uint32_t e = tid; e < tot; e += LM_THREADS) {
+        for (uint32_t e = tid; e < tot; e += NTC) {
             const int x = at_e(e);
             wpos[x] = (uint16_t)atomicAdd(rcnt + wrow[x], 1u);
         }
         __syncthreads();
-        for (int i = tid; i < MT; i += LM_THREADS)
+        for (int i = tid; i < MT; i += NTC)
             if (rcnt[i] > 0u) rbase[i] = (uint32_t)atomicAdd(p.cnt + row0 + i, (int)rcnt[i]);
         __syncthreads();
-        for (uint32_t e = tid; e < tot; e += LM_THREADS) {
+        for (uint32_t e = tid; e < tot; e += NTC) {
             const int x = at_e(e);
             const int i = wrow[x];
             const uint32_t at = rbase[i] + wpos[x];

@@ -9,8 +9,10 @@ width and below 128, rows whose candidates overflow the list); equal to the
 unfused form (the logits launch, then ss_sample_step on them) on normal
 inputs, bit for bit, overflowed rows included; and against the oracle on
 normal inputs on every row the oracle does not flag as fragile (token, kept
-count, status and candidate set).  Full-size runs (B = 64, D = 4096, V =
-2^17) check sampled rows.
+count, status and candidate set).  Batch sizes cover every GEMM launch
+shape: B <= 64 (row tiles of 64), 70 (one tile of 128), 200 (one tile of
+256, weights read with the nt policy) and 300 (two tiles of 256).
+Full-size runs (B = 64, D = 4096, V = 2^17) check sampled rows.
 """
 import numpy as np
 import pytest
@@ -134,8 +136,9 @@ def test_logits_within_rounding_bound(pad):
     assert np.all(err <= eps), float((err / eps).max())
 
 
-def test_logits_grid_exact():
-    wl = W.workload_lmhead("grid", B=70, D=512, V=20001, seed=12)
+@pytest.mark.parametrize("B", [70, 200, 300])   # row tiles of 128, one of 256, two of 256
+def test_logits_grid_exact(B):
+    wl = W.workload_lmhead("grid", B=B, D=512, V=20001, seed=12)
     g = gpu_logits(wl.hidden, wl.weight)
     z = oracle.lmhead_logits(wl.hidden, wl.weight)
     np.testing.assert_array_equal(g, z.astype(np.float32))
@@ -161,17 +164,18 @@ def _with_odd_rows(req, V):
     return req
 
 
-@pytest.mark.parametrize("V", [100, 16384, 16385, 40000])
-def test_fused_grid_exact(V):
-    wl = W.workload_lmhead("grid", B=70, D=256, V=V, seed=13)
+@pytest.mark.parametrize("V,B", [(100, 70), (16384, 70), (16385, 70), (40000, 70), (16385, 300)])
+def test_fused_grid_exact(V, B):
+    wl = W.workload_lmhead("grid", B=B, D=256, V=V, seed=13)
     req = _with_odd_rows(wl.req, V)
     g = run_fused(wl.hidden, wl.weight, req, seed=3, offset=9, pad=8)
     o = oracle.lmhead_sample(wl.hidden, wl.weight, req, seed=3, offset=9, threads=16, exact=True)
-    compare_exact(g, o, tag=f"V={V}")
+    compare_exact(g, o, tag=f"V={V} B={B}")
 
 
-def test_fused_equals_unfused():
-    wl = W.workload_lmhead("normal", B=70, D=256, V=50001, seed=14)
+@pytest.mark.parametrize("B", [70, 200, 300])
+def test_fused_equals_unfused(B):
+    wl = W.workload_lmhead("normal", B=B, D=256, V=50001, seed=14)
     req = _with_odd_rows(wl.req, 50001)
     g = run_fused(wl.hidden, wl.weight, req, seed=4, offset=2)
     u = run_unfused(wl.hidden, wl.weight, req, seed=4, offset=2)
@@ -204,8 +208,9 @@ def _overflow_case(B, D, V, seed):
     return W.to_bf16_bits(h), W.to_bf16_bits(w), req
 
 
-def test_fused_candidate_overflow():
-    h, w, req = _overflow_case(B=70, D=128, V=16384 + 9000, seed=16)
+@pytest.mark.parametrize("B", [70, 300])
+def test_fused_candidate_overflow(B):
+    h, w, req = _overflow_case(B=B, D=128, V=16384 + 9000, seed=16)
     z = oracle.lmhead_logits(h, w)
     P = 16384
     theta = np.sort(z[:, :P], axis=1)[:, -128]
