@@ -352,8 +352,7 @@ int ss_tile_topk(const void* logits, int dtype, int rows, int V, int64_t ld, int
  *   hardware's).  Every entry point below computes a given z[b, v] with the
  *   same instruction sequence, so they all see the same fp32 values.
  * Requirements (else SS_ERR_UNSUPPORTED): D a multiple of 128, D <= 65536,
- * ldh and ldw multiples of 8 and at most 2^21, hidden and weight 16-byte
- * aligned.
+ * ldh and ldw multiples of 8, hidden and weight 16-byte aligned.
  * ldh < D or ldw < D, a NULL pointer with B > 0: SS_ERR_INVALID_ARG. */
 
 /* Bytes of workspace ss_lmhead_sample_step needs (256-byte aligned, no

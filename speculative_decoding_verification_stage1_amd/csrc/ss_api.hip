@@ -607,8 +607,7 @@ LmWs lm_ws(void* ws, int B, int V) {
 
 int check_lmhead(const void* hidden, int64_t ldh, const void* weight, int64_t ldw, int B, int D, int V) {
     if (B < 0 || V < 1 || D < 1 || ldh < D || ldw < D) return SS_ERR_INVALID_ARG;
-    if (V > SS_V_MAX || D % 128 != 0 || D > (1 << 16) || (ldh % 8) || (ldw % 8) || ldh > (1 << 21) || ldw > (1 << 21))
-        return SS_ERR_UNSUPPORTED;
+    if (V > SS_V_MAX || D % 128 != 0 || D > (1 << 16) || (ldh % 8) || (ldw % 8)) return SS_ERR_UNSUPPORTED;
     if (B > 0 && (!hidden || !weight)) return SS_ERR_INVALID_ARG;
     if (((uintptr_t)hidden & 15u) || ((uintptr_t)weight & 15u)) return SS_ERR_UNSUPPORTED;
     return SS_OK;
@@ -632,12 +631,14 @@ void lm_launch(LmParams p, hipStream_t s) {
 // B <= 128 one row tile of 128 (2 x 2 waves); larger B row tiles of 256
 // (waves stacked, 128 columns), so that each weight column is read by
 // fewer workgroups, with four more waves issuing the loads.  A launch with
-// one row tile reads the weights with the nt policy.  The probe uses
-// narrower column tiles, so that its fewer columns still spread over many
-// CUs, and longer k stages, since each of its workgroups runs alone on a CU
-// and waits on memory.  Measured at B=256, D=4096, V=2^18 (logits / fused
-// step, one run): 128-row tiles 657 / 791 us, 256-row tiles with the
-// loading waves and the nt policy 592 / 743 us.
+// one row tile reads the weights with the nt policy (B=64, D=4096,
+// V=2^17: logits 204 -> 174 us, fused step 243 -> 215 us; the probe is
+// slower with it, fused 220 -> 228 us, and keeps the default).  The probe
+// uses narrower column tiles, so that its fewer columns still spread over
+// many CUs, and longer k stages, since each of its workgroups runs alone on
+// a CU and waits on memory.  Measured at B=256, D=4096, V=2^18 (logits /
+// fused step, one run): 128-row tiles 677 / 797 us, 256-row tiles with the
+// loading waves and the nt policy 611 / 749 us.
 template <int MODE>
 void lm_launch_shape(LmParams p, bool probe, hipStream_t s) {
     if (p.B <= 64) {
