@@ -207,9 +207,12 @@ def summarize_rocprof(d: str, out: str) -> None:
     ll = ["# LM head fused with sampling: B=64, D=4096, V=131072 and B=256, D=4096, V=262144 "
           "(bf16 hidden and weights, synthetic)", "",
           "Command (run from the repository root with TMPDIR=/tmp):", "", "    " + PROFILE_CMDS["lmhead"], "",
-          "Grid sizes are in threads (256 per workgroup).  lmhead_gemm_kernel<mode, WM, WN, KB>: mode 0 stores "
-          "logits (the logits launch, and the fused step's probe), 1 keeps the tokens above the probe's "
-          "threshold, 2 stores the logits of rows whose candidates overflowed (returns at once otherwise).", "",
+          "Grid sizes are in threads (256 per workgroup, 512 with the load-issuing waves).  "
+          "lmhead_gemm_kernel<mode, WM, WNW, WN, KB, SPLIT, NTW>: a workgroup of 64 WM rows by 32 WNW WN "
+          "columns, k stages of KB; SPLIT: four more waves issue the loads; NTW: weights read with the nt "
+          "policy.  Mode 0 stores logits (the logits launch, and the fused step's probe), 1 keeps the tokens "
+          "above the probe's threshold, 2 stores the logits of rows whose candidates overflowed (returns at "
+          "once otherwise).", "",
           "## per launch shape (kernel_trace.csv)", ""] + shape_table(perl, lambda n, g: True)
     with open(os.path.join(os.path.dirname(out), "lmhead_b64_b256.md"), "w") as fh:
         fh.write("\n".join(ll) + "\n")
