@@ -632,24 +632,21 @@ void lm_launch(LmParams p, hipStream_t s) {
 // (waves stacked, 128 columns), so that each weight column is read by
 // fewer workgroups, with four more waves issuing the loads.  A launch with
 // one row tile reads the weights with the nt policy (B=64, D=4096,
-// V=2^17: logits 204 -> 174 us, fused step 243 -> 215 us; the probe is
-// slower with it, fused 220 -> 228 us, and keeps the default).  The probe
-// uses narrower column tiles, so that its fewer columns still spread over
-// many CUs, and longer k stages, since each of its workgroups runs alone on
-// a CU and waits on memory.  Measured at B=256, D=4096, V=2^18 (logits /
-// fused step, one run): 128-row tiles 677 / 797 us, 256-row tiles with the
-// loading waves and the nt policy 611 / 749 us.
+// V=2^17: logits 204 -> 174 us, fused step 243 -> 215 us).  Measured at
+// B=256, D=4096, V=2^18 (logits / fused step, one run): 128-row tiles
+// 677 / 797 us, 256-row tiles with the loading waves and the nt policy
+// 611 / 749 us.  The probe covers few columns, so it uses tiles of 128
+// rows by 64 columns (rows past B repeat the last one) and long k stages:
+// twice the workgroups of 64 x 128 or 128 x 128 tiles, and each runs alone
+// on a CU waiting on memory (fused step at B=128: 498 -> 472 us; B=64 and
+// B=256 unchanged; with the nt policy the probe is slower).
 template <int MODE>
 void lm_launch_shape(LmParams p, bool probe, hipStream_t s) {
-    if (p.B <= 64) {
-        if (probe) lm_launch<MODE, 1, 4, 1, 128, false, false>(p, s);
-        else lm_launch<MODE, 1, 4, 2, 64, false, true>(p, s);
-    } else {
-        if (probe) lm_launch<MODE, 2, 2, 2, 128, false, false>(p, s);
-        else if (p.B <= 128) lm_launch<MODE, 2, 2, 4, 64, false, true>(p, s);
-        else if (p.B <= 256) lm_launch<MODE, 4, 1, 4, 64, true, true>(p, s);
-        else lm_launch<MODE, 4, 1, 4, 64, true, false>(p, s);
-    }
+    if (probe) lm_launch<MODE, 2, 2, 1, 128, false, false>(p, s);
+    else if (p.B <= 64) lm_launch<MODE, 1, 4, 2, 64, false, true>(p, s);
+    else if (p.B <= 128) lm_launch<MODE, 2, 2, 4, 64, false, true>(p, s);
+    else if (p.B <= 256) lm_launch<MODE, 4, 1, 4, 64, true, true>(p, s);
+    else lm_launch<MODE, 4, 1, 4, 64, true, false>(p, s);
 }
 
 void launch_lm_gemm(int mode, LmParams p, bool probe, hipStream_t s) {
