@@ -6,12 +6,12 @@ prelude + top-128) and Stage 2 (merge, temperature, top-p / min-p,
 Gumbel-max) for all 256 rows, replayed from a hipGraph with the Philox
 offset advanced on the device.  Inputs are resident in HBM; sixteen copies
 of the logits and bitmask are rotated so the 256 MB last-level cache cannot
-serve a step from the previous one, and one graph holds one step per copy
-(plus a graph of the remaining steps), so that the host's replay call is
-spread over sixteen steps, as when the sampler's kernels run back to back
-inside a decode step's graph.  Exactly --steps steps are timed (wall clock,
-synchronised on both sides) for `value`; the median over --median-replays
-event-timed replays is reported beside it.
+serve a step from the previous one.  Exactly --steps steps are timed (wall
+clock, synchronised on both sides) for `value`: one graph holds them all
+(step i on copy i mod 16) and is replayed once, so the sampler's kernels
+run back to back as inside a decode loop's graph.  The median per step
+over --median-replays event-timed replays of a sixteen-step graph is
+reported beside it.
 
 Printed: one JSON line with the headline rate (sampled tokens/s), the
 Stage-1 roofline (algorithmic bytes / mean time of the step's own Stage-1
@@ -286,19 +286,20 @@ def sample_leg(L, wl, copies, stream, steps, warmup, median_replays):
     def step(i):
         L.ss_sample_step(xs[i % copies], dreqs[i % copies], rng, toks, ws=ws, stream=stream, rng_advance=1)
 
-    full = _capture(step, copies, stream)
-    rem = steps % copies
-    part = _capture(step, rem, stream) if rem else None
-    for _ in range(max(1, -(-warmup // copies))):
-        full.replay()
+    # the timed steps: one graph of exactly `steps` steps (step i on copy
+    # i mod copies), replayed once, so the steps run back to back with no
+    # host call between them; warm-up replays of the same graph first
+    timed = _capture(step, steps, stream)
+    for _ in range(max(1, -(-warmup // steps))):
+        timed.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps // copies):
-        full.replay()
-    if part is not None:
-        part.replay()
+    timed.replay()
     torch.cuda.synchronize()
     step_s = (time.perf_counter() - t0) / steps
+    del timed
+    full = _capture(step, copies, stream)
+    full.replay()
     med_us = _replay_median_us(full, median_replays) / copies
     # Stage 1 alone: ss_tile_topk with the requests is the step's first
     # launch (same grid, listed-token workgroups included)
@@ -311,7 +312,7 @@ def sample_leg(L, wl, copies, stream, steps, warmup, median_replays):
                           n1, cur)
     out = {"step_s": step_s, "median_step_us": med_us, "stage1_us": s1_us, "eager_step_us": eager_us,
            "stage1_launches": n1}
-    del full, part, xs, dreqs
+    del full, xs, dreqs
     torch.cuda.synchronize()
     return out
 
@@ -388,7 +389,7 @@ def main():
         "config": {
             "workload": "c2: B=256 V=262144 bf16 logits 2*N(0,1)+10 on 8 ids, grammar bitmask 5% allowed, "
                         "repetition/frequency/presence over 64 prior ids, 16 bias ids, mixed greedy/top-k/"
-                        "top-p/min-p; hipGraph replays of one step per rotating input copy",
+                        "top-p/min-p; the timed steps in one hipGraph, step i on rotating input copy i mod 16",
             "input_copies": args.copies,
             "global_batch": B, "vocab": V, "tile": L.ss_tile_size(L.SS_BF16), "parallelism": "single-gpu",
         },
