@@ -47,7 +47,6 @@
 
 namespace ssd {
 
-constexpr int LM_THREADS = 256;
 constexpr int LM_CAP = 4096;     // candidates kept per row
 constexpr int LM_PROBE_MIN = 16384;
 
@@ -138,7 +137,7 @@ __global__ __launch_bounds__((WM * WNW + (SPLIT ? 4 : 0)) * WAVE) void lmhead_ge
     const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
     const int lane = lane_id();
     const bool loader = SPLIT && wave >= NWC;   // SPLIT: the last four waves issue the loads
-    const int lwave = SPLIT ? wave - NWC : wave;
+    const int lwave = SPLIT ? (loader ? wave - NWC : 0) : wave;   // index among the loading waves
     const int row0 = rt * MT;
     const int col0 = p.col_begin + ct * NT;
     if (MODE == LM_REDO) {   // only blocks holding an overflowed row go on
