@@ -708,10 +708,27 @@ struct PosDecision {
     int accept;
     int token;
 };
-__device__ __forceinline__ PosDecision decide_position(const ss_rng rg, int b, int j, int n_b, int status,
+// The random numbers position j of request b may use: the acceptance
+// uniform and the residual draw's Gumbel noise of the lane's two ranks.
+// They depend only on (b, j) and the candidate ids, so a caller can work
+// them out before it knows p and q.
+struct PosNoise {
+    float u;
+    float g_lo, g_hi;
+};
+__device__ __forceinline__ PosNoise position_noise(const ss_rng rg, int b, int j, int id_lo, int id_hi) {
+    const uint32_t c2 = (2u << 24) | (uint32_t)j;
+    PosNoise z;
+    z.u = unit_open(philox_w0(rg.seed, rg.offset, 0u, (uint32_t)b, (1u << 24) | (uint32_t)j));
+    z.g_lo = gumbel_noise(rg.seed, rg.offset, (uint32_t)id_lo, (uint32_t)b, c2);
+    z.g_hi = gumbel_noise(rg.seed, rg.offset, (uint32_t)id_hi, (uint32_t)b, c2);
+    return z;
+}
+__device__ __forceinline__ PosDecision decide_position(int b, int j, int n_b, int status,
                                                        int greedy, int n, int rtoken, int best, int d, int id_lo_r,
                                                        int id_hi_r, float p_lo_r, float p_hi_r, float v_lo,
-                                                       float v_hi, float q_lo_r, float q_hi_r, float q_d_r, int V) {
+                                                       float v_hi, float q_lo_r, float q_hi_r, float q_d_r, int V,
+                                                       const PosNoise& nz) {
     const int lane = lane_id();
     int accept = 0, token = -1;
     const bool live = status == SS_ROW_OK || status == SS_ROW_TOPK_CLAMPED;
@@ -735,13 +752,11 @@ __device__ __forceinline__ PosDecision decide_position(const ss_rng rg, int b, i
         const uint64_t m_hi = __ballot(id_hi == d && id_hi >= 0);
         if (m_lo) pd = readlane_f(p_lo, __builtin_ctzll(m_lo));
         else if (m_hi) pd = readlane_f(p_hi, __builtin_ctzll(m_hi));
-        const float u = unit_open(philox_w0(rg.seed, rg.offset, 0u, (uint32_t)b, (1u << 24) | (uint32_t)j));
-        accept = qd > 0.0f && u * qd <= pd;
+        accept = qd > 0.0f && nz.u * qd <= pd;
         if (!accept) {
             // draw from norm(max(0, p - q)) by Gumbel-max on ln(rho)
-            const uint32_t c2 = (2u << 24) | (uint32_t)j;
-            const float g_lo = id_lo >= 0 ? gumbel_noise(rg.seed, rg.offset, (uint32_t)id_lo, (uint32_t)b, c2) : 0.0f;
-            const float g_hi = id_hi >= 0 ? gumbel_noise(rg.seed, rg.offset, (uint32_t)id_hi, (uint32_t)b, c2) : 0.0f;
+            const float g_lo = id_lo >= 0 ? nz.g_lo : 0.0f;
+            const float g_hi = id_hi >= 0 ? nz.g_hi : 0.0f;
             const float rho_lo = p_lo - q_lo, rho_hi = p_hi - q_hi;
             const bool ok_lo = id_lo >= 0 && rho_lo > 0.0f;
             const bool ok_hi = id_hi >= 0 && rho_hi > 0.0f;
@@ -878,6 +893,7 @@ __device__ __forceinline__ void row_epilogue(const Stage2Params& F, const RowPar
 
     int token = -1, n = 0;
     float v_lo = NINF, v_hi = NINF, e_lo = 0.0f, e_hi = 0.0f, Z = 1.0f, En = 0.0f;
+    PosNoise pz{0.0f, 0.0f, 0.0f};   // verification: the position's noise (stochastic rows)
     if (live && rp.greedy) {
         token = id0;
         n = 1;
@@ -928,6 +944,8 @@ __device__ __forceinline__ void row_epilogue(const Stage2Params& F, const RowPar
         for (int i = 0; i < KMAX / 4; ++i) eq[i] = *(const float4*)&es[4 * i];
         const float gl = gumbel_noise(rg.seed, rg.offset, (uint32_t)id_lo, c1, c2);
         const float gh = gumbel_noise(rg.seed, rg.offset, (uint32_t)id_hi, c1, c2);
+        if constexpr (MODE == MODE_VERIFY)   // the decision's noise, ahead of p and q
+            if (F.arrive) pz = position_noise(rg, b, vj, id_lo, id_hi);
         float E = 0.0f, E_lo = 0.0f, E_hi = 0.0f;
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
@@ -993,8 +1011,8 @@ __device__ __forceinline__ void row_epilogue(const Stage2Params& F, const RowPar
         const float pl = (live && !rp.greedy && lane < n) ? e_lo / En : 0.0f;
         const float ph = (live && !rp.greedy && lane + 64 < n) ? e_hi / En : 0.0f;
         const int best_id = __builtin_amdgcn_readfirstlane(idl);
-        const PosDecision pd = decide_position(rg, b, vj, dc.n, status, rp.greedy, n_r, token, best_id, vd, idl, idh,
-                                               pl, ph, v_lo, v_hi, q_lo_r, q_hi_r, q_d_r, P.V);
+        const PosDecision pd = decide_position(b, vj, dc.n, status, rp.greedy, n_r, token, best_id, vd, idl, idh,
+                                               pl, ph, v_lo, v_hi, q_lo_r, q_hi_r, q_d_r, P.V, pz);
         // Position j's output slot holds the draft if it was accepted, else
         // this row's draw: what the request emits there whenever every
         // earlier draft is accepted.  The row writes it (device-coherent,

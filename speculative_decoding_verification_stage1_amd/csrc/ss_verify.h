@@ -60,8 +60,9 @@ __global__ __launch_bounds__(VF_THREADS) void verify_kernel(Stage2Params F) {
         const float q_lo_r = q[in_v(id_lo_r) ? id_lo_r : 0];
         const float q_hi_r = q[in_v(id_hi_r) ? id_hi_r : 0];
         const float q_d_r = q[in_v(d) ? d : 0];
-        const PosDecision pd = decide_position(rg, b, j, dc.n, status, greedy, n, rtoken, best, d, id_lo_r, id_hi_r,
-                                               p_lo_r, p_hi_r, v_lo, v_hi, q_lo_r, q_hi_r, q_d_r, V);
+        const PosNoise nz = position_noise(rg, b, j, id_lo_r, id_hi_r);
+        const PosDecision pd = decide_position(b, j, dc.n, status, greedy, n, rtoken, best, d, id_lo_r, id_hi_r,
+                                               p_lo_r, p_hi_r, v_lo, v_hi, q_lo_r, q_hi_r, q_d_r, V, nz);
         if (lane == 0) {
             s_accept[j] = pd.accept;
             s_token[j] = pd.token;
