@@ -44,8 +44,9 @@ __global__ __launch_bounds__(S1_THREADS) void stage1_kernel(Stage1Params P) {
     }
     S1Shared<DT>& sh = shu.tile;
     // the tile waves issue ahead of listed-token waves sharing their SIMDs
-    // (those finish well before the tiles do): c1 Stage 1 10.31 -> 10.06 us,
-    // c3 29.52 -> 29.28 us, c2 unchanged
+    // (those finish well before the tiles do, except the sorting form, which
+    // raises its own priority above): c1 Stage 1 10.38 -> 10.03 us, c3
+    // 29.44 -> 29.18 us, c2 unchanged
     __builtin_amdgcn_s_setprio(1);
     const int wg = blockIdx.x - nlw;
     const int row = div_uniform(wg, P.Zv);

@@ -491,6 +491,9 @@ __device__ __forceinline__ void listed_row_wave(const Stage1Params& P, uint64_t*
     if (np + nb + nh == 0) return;   // wave-uniform; Stage 2 skips rows without lists
     if (np > LIST_SHORT || nb > LIST_SHORT) return;   // ranked by listed_long_kernel
     if (np + nb + nh > KMAX) {   // more than one pass of the scan below: sort instead
+        // this form can outlast the tiles: ahead of the tile waves (priority
+        // 1; the other listed-token waves keep 0)
+        __builtin_amdgcn_s_setprio(2);
         listed_row_sorted<DT>(P, rp, out, row, b, np, nh, nb, area.keys);
         return;
     }
