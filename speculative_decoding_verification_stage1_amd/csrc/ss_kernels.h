@@ -45,8 +45,9 @@ __global__ __launch_bounds__(S1_THREADS) void stage1_kernel(Stage1Params P) {
     S1Shared<DT>& sh = shu.tile;
     // the tile waves issue ahead of listed-token waves sharing their SIMDs
     // (those finish well before the tiles do, except the sorting form, which
-    // raises its own priority above): c1 Stage 1 10.38 -> 10.03 us, c3
-    // 29.44 -> 29.18 us, c2 unchanged
+    // raises its own priority above): 64 rows of 2^17 bf16, Stage 1 10.38 ->
+    // 10.03 us; verification of 64 requests x 5 rows of 2^17, 29.44 ->
+    // 29.18 us; 256 rows of 2^18 unchanged
     __builtin_amdgcn_s_setprio(1);
     const int wg = blockIdx.x - nlw;
     const int row = div_uniform(wg, P.Zv);
