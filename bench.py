@@ -51,17 +51,17 @@ def stage1_bytes_per_row(V, prior, nbias, grammar=True, dtype_bytes=2):
 
 PROFILE_MD = os.path.join(ROOT, "profiles", "stage1_bf16_c2.md")
 # the runs behind profiles/ (from the repository root, TMPDIR=/tmp); the
-# summary is written by `python3 bench.py --summarize-rocprof gpurun_out/prof`
+# summary is written by `python3 bench.py --summarize-rocprof rocprof_out`
 PROFILE_CMDS = {
-    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof/trace -o run -- "
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d rocprof_out/trace -o run -- "
              "python3 bench.py --steps 40 --warmup 8 --no-cpu --legs c2",
-    "FETCH_SIZE": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof/FETCH_SIZE -o run -- "
+    "FETCH_SIZE": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d rocprof_out/FETCH_SIZE -o run -- "
                   "python3 bench.py --steps 8 --warmup 2 --no-cpu --legs c2 --copy-calibration",
-    "WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof/WRITE_SIZE -o run -- "
+    "WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d rocprof_out/WRITE_SIZE -o run -- "
                   "python3 bench.py --steps 8 --warmup 2 --no-cpu --legs c2 --copy-calibration",
-    "extra": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof/extra -o run -- "
+    "extra": "rocprofv3 --kernel-trace --stats --output-format csv -d rocprof_out/extra -o run -- "
              "python3 bench.py --steps 8 --warmup 2 --no-cpu --median-replays 5 --legs verify,stress,c0,c1,c4",
-    "lmhead": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof/lmhead -o run -- "
+    "lmhead": "rocprofv3 --kernel-trace --stats --output-format csv -d rocprof_out/lmhead -o run -- "
               "python3 bench.py --steps 8 --warmup 2 --no-cpu --median-replays 5 --legs lmhead",
 }
 
