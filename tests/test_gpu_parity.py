@@ -1074,6 +1074,39 @@ def test_max_vocab_sample_and_topk(dtype):
         assert np.array_equal(vals.cpu().numpy(), ref_vals)
 
 
+def test_max_vocab_listed_tokens():
+    """Penalty and bias lists naming ids at the top of the largest
+    vocabulary (up to 2^24 - 1), repeated ids, and ids that share a slot of
+    the listed-token id table, raised so that they are candidates."""
+    rng = np.random.default_rng(57)
+    xf = (rng.standard_normal((2, VMAX), dtype=np.float32) * 2).astype(np.float32)
+    top = np.arange(VMAX - 40, VMAX)
+    ids = np.arange(VMAX - (1 << 20), VMAX, dtype=np.uint64)
+    h = ((ids * np.uint64(0x9E3779B1)) & np.uint64(0xFFFFFFFF)) >> np.uint64(24)
+    coll = ids[h == 7][:30].astype(np.int64)
+    listed = np.concatenate([top, coll])
+    xf[:, listed] += 20.0   # above the largest of 2^24 draws even after the penalties
+    x = W.to_bf16_bits(xf)
+    req = W.plain_requests(2, temperature=1.0, prior_len=80, bias_len=40)
+    req.use_penalties[:] = True
+    req.use_bias[:] = True
+    req.rep_penalty[:] = 1.2
+    req.freq_penalty[:] = 0.3
+    req.pres_penalty[:] = 0.1
+    for r in range(2):
+        pid = np.concatenate([top[:30], coll[:20], top[:10], coll[:10], [VMAX - 1] * 10])   # repeats
+        req.prior_ids[r, :80] = pid[:80]
+        req.prior_cnt[r, :80] = rng.integers(0, 4, 80)
+        req.n_prior[r] = 80
+        bid = np.concatenate([top[20:40], coll[15:30], [VMAX - 1] * 5])
+        req.bias_ids[r, :40] = bid[:40]
+        req.bias_val[r, :40] = rng.uniform(-3.0, 3.0, 40).astype(np.float32)
+        req.n_bias[r] = 40
+    g, o = sample_parity(W.SampleWorkload("vmax-listed", W.DTYPE_BF16, x, req), seed=8, offset=2)
+    for r in range(2):   # the case is what it claims: listed tokens are candidates
+        assert len(set(listed.tolist()) & set(o["topk_ids"][r].tolist())) >= 40, r
+
+
 def test_max_vocab_verify_bounded_and_dense():
     B, G = 1, 2
     z = _vmax_rows(B * (G + 1), 53, W.DTYPE_BF16)
