@@ -542,7 +542,7 @@ def cpu_baseline(args, wl, W):
         avail = len(os.sched_getaffinity(0))
     except AttributeError:
         avail = os.cpu_count() or 1
-    # the GPU machine gives a one-GPU job 16 host cores, whatever the machine has
+    # a one-GPU job's share of the host: 16 cores, whatever the machine has
     cores = max(1, min(avail, 16))
     out = {}
     t0 = time.perf_counter()
