@@ -48,6 +48,9 @@
 namespace ssd {
 
 constexpr int LM_CAP = 4096;     // candidates kept per row
+#ifndef LM_S2_PF
+#define LM_S2_PF 6
+#endif
 constexpr int LM_PROBE_MIN = 16384;
 
 enum { LM_STORE = 0, LM_THRESH = 1, LM_REDO = 2 };
@@ -446,24 +449,54 @@ __global__ __launch_bounds__(S2_THREADS) void lmhead_stage2_kernel(LmStage2Param
     const int wave = tid / WAVE;
     const int lane = lane_id();
     const Stage2Params& F = q.f;
-    const int n = __builtin_amdgcn_readfirstlane(q.cnt[row]);
+    // the work items: the probe tiles' sorted lists, then the candidates in
+    // chunks of 128, dealt to the waves in turn.  A wave's first LM_S2_PF
+    // items are requested together with the count (their addresses stay
+    // inside the row's probe keys and candidate area whatever the count;
+    // entries past it are dropped once it is known), so that they cost one
+    // round trip instead of one each (median of 15 launches, B=256, V=2^18:
+    // 20.5 -> 19.1 us; B=64, V=2^17: 14.6 -> 14.0 us; the chunks' sorts and
+    // merges are most of the rest)
+    const uint64_t* c = q.cand + (int64_t)row * LM_CAP;
+    const int n_raw = q.cnt[row];
+    uint64_t pre[LM_S2_PF][2];
+#pragma unroll
+    for (int u = 0; u < LM_S2_PF; ++u) {
+        const int it = wave + S2_WAVES * u;
+        const bool isp = it < q.Zp;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int j = lane + WAVE * h;
+            const int i = (it - q.Zp) * KMAX + j;
+            const uint64_t* ptr = isp ? q.probe_keys + ((int64_t)row * q.Zp + it) * KMAX + j
+                                      : c + (i < LM_CAP ? i : LM_CAP - 1);
+            pre[u][h] = *ptr;
+        }
+    }
+    const int n = __builtin_amdgcn_readfirstlane(n_raw);
     WL64 best{0ull, 0ull};
     if (n <= LM_CAP) {   // block-uniform
-        // the probe tiles' sorted lists and the candidates in sorted chunks
-        // of 128, dealt to the waves in turn; then the cross-wave tree
-        const uint64_t* c = q.cand + (int64_t)row * LM_CAP;
         const int items = q.Zp + (n + KMAX - 1) / KMAX;
         WL64 mine{0ull, 0ull};
         bool any = false;
-        for (int it = wave; it < items; it += S2_WAVES) {
-            WL64 l;
-            if (it < q.Zp) {
-                const uint64_t* pk = q.probe_keys + ((int64_t)row * q.Zp + it) * KMAX;
-                l = WL64{merge_key<SS_F32>(pk[lane], it), merge_key<SS_F32>(pk[lane + WAVE], it)};
-            } else {
-                const int i0 = (it - q.Zp) * KMAX + lane, i1 = i0 + WAVE;
-                l = wave_sort128(WL64{i0 < n ? c[i0] : 0ull, i1 < n ? c[i1] : 0ull});
+        auto item = [&](int it, uint64_t k_lo, uint64_t k_hi) -> WL64 {
+            if (it < q.Zp) return WL64{merge_key<SS_F32>(k_lo, it), merge_key<SS_F32>(k_hi, it)};
+            const int i0 = (it - q.Zp) * KMAX + lane, i1 = i0 + WAVE;
+            return wave_sort128(WL64{i0 < n ? k_lo : 0ull, i1 < n ? k_hi : 0ull});
+        };
+#pragma unroll
+        for (int u = 0; u < LM_S2_PF; ++u) {
+            const int it = wave + S2_WAVES * u;
+            if (it < items) {
+                const WL64 l = item(it, pre[u][0], pre[u][1]);
+                mine = any ? wave_merge(mine, l) : l;
+                any = true;
             }
+        }
+        for (int it = wave + S2_WAVES * LM_S2_PF; it < items; it += S2_WAVES) {
+            const int i0 = (it - q.Zp) * KMAX + lane, i1 = i0 + WAVE;
+            const WL64 l = item(it, it < q.Zp ? q.probe_keys[((int64_t)row * q.Zp + it) * KMAX + lane] : c[i0 < n ? i0 : 0],
+                                it < q.Zp ? q.probe_keys[((int64_t)row * q.Zp + it) * KMAX + lane + WAVE] : c[i1 < n ? i1 : 0]);
             mine = any ? wave_merge(mine, l) : l;
             any = true;
         }
